@@ -1,0 +1,60 @@
+"""CPU oracle for calibrated block-sparse attention (CalibAtt, arXiv 2603.05503).
+
+TEST INFRASTRUCTURE ONLY.  Plain, slow, float64 NumPy written from the
+pages' description of the method.  Only the test suite, the smoke check and
+the benchmark's CPU-baseline leg may import it; the library path never calls
+it, and it imports nothing from the library or its kernels.
+
+What it computes (each function cites the passage it follows):
+
+* ``attention``   - attention restricted to kept key blocks, the skipped
+  blocks being absent from the softmax (abstract; Fig. 5(b) caption); the
+  dense special case.
+* ``calibration`` - pooled post-softmax mass per (query block, key block)
+  (Fig. 2 caption's block-level maps; "block energies", Table S5 caption),
+  top key blocks per query block (Fig. 5(a) caption), cross-prompt agreement
+  with a threshold (Fig. 3(b) caption, Fig. 7 caption), and the kept lists as
+  CSR rows keyed by (head, query block) (abstract: per layer, head and
+  timestep).
+* ``schedule``    - the longest-row-first work order within each head.
+
+Pins: every function is checked by ``tests/test_oracle_*.py`` against facts
+that do not come from this code (library routines on the special cases they
+cover, closed forms, invariants, brute-force enumeration on tiny inputs,
+hand-worked fixtures under ``tests/golden/``).  No function here is
+"parity unpinned".
+"""
+
+from .attention import (
+    dense_attention,
+    sparse_attention_gather,
+    sparse_attention_masked_dense,
+    sparse_attention_rows,
+    csr_to_block_mask,
+)
+from .calibration import (
+    block_mass,
+    block_mass_rows,
+    topk_keep,
+    agreement,
+    min_agree_count,
+    to_csr,
+    compile_masks,
+)
+from .schedule import lpt_work_order
+
+__all__ = [
+    "dense_attention",
+    "sparse_attention_gather",
+    "sparse_attention_masked_dense",
+    "sparse_attention_rows",
+    "csr_to_block_mask",
+    "block_mass",
+    "block_mass_rows",
+    "topk_keep",
+    "agreement",
+    "min_agree_count",
+    "to_csr",
+    "compile_masks",
+    "lpt_work_order",
+]

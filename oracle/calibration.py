@@ -1,0 +1,112 @@
+"""Offline calibration: pooled mass, top key blocks, agreement, CSR (test infrastructure only).
+
+Pages (CalibAtt, arXiv 2603.05503):
+* Fig. 2 caption: post-softmax attention maps viewed at block granularity;
+  Table S5 caption: "block energies" computed on the calibration prompts.
+  Reading: the energy of tile (qb, kb) is the sum of the dense post-softmax
+  probabilities over the tile's valid (query, key) pairs; the softmax runs
+  over all valid keys (calibration sees the full map).
+* Fig. 5(a) caption: the top key blocks of each query block are kept, per
+  prompt, then the per-prompt masks are aggregated across prompts.
+  Reading: a fixed count K per row; order by mass descending, ties broken by
+  the smaller key-block index (any tie-break is valid for the method; this
+  one makes the result unique).  NaN sorts last.  The decision is taken on
+  float32 values, the precision in which the kernel stores the mass.
+* Fig. 3(b) caption: each block's keep frequency across prompts, from 0
+  (skipped for every prompt) to 1 (always kept), with an agreement
+  threshold; Fig. 7 caption: agreement threshold rho.
+  Reading: keep iff count >= ceil(rho * P), computed in exact rationals.
+* Abstract: the kept patterns are compiled per layer, head and timestep.
+  Encoding: CSR rows r = h * nqb + qb with ascending key-block indices.
+"""
+
+from fractions import Fraction
+import math
+
+import numpy as np
+
+
+def block_mass_rows(q_bh, k_bh, block, scale, seq_len, qb):
+    """Pooled mass of one query block against every key block: [nkb] float64."""
+    q_bh = np.asarray(q_bh, dtype=np.float64)
+    k_bh = np.asarray(k_bh, dtype=np.float64)
+    L = k_bh.shape[0]
+    nkb = L // block
+    mass = np.zeros(nkb, dtype=np.float64)
+    lo, hi = qb * block, min((qb + 1) * block, seq_len)
+    if hi <= lo:
+        return mass
+    s = scale * (q_bh[lo:hi] @ k_bh[:seq_len].T)
+    e = np.exp(s - s.max(axis=1, keepdims=True))
+    p = e / e.sum(axis=1, keepdims=True)               # dense post-softmax rows
+    for kb in range(nkb):
+        a, z = kb * block, min((kb + 1) * block, seq_len)
+        if z > a:
+            mass[kb] = p[:, a:z].sum()
+    return mass
+
+
+def block_mass(q, k, block, scale, seq_len):
+    """[B, H, L, d] queries/keys -> mass [B, H, nqb, nkb] float64."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, H, L, d = q.shape
+    nqb = L // block
+    out = np.zeros((B, H, nqb, nqb), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            for qb in range(nqb):
+                out[b, h, qb] = block_mass_rows(q[b, h], k[b, h], block, scale, seq_len, qb)
+    return out
+
+
+def topk_keep(mass, K, nkb_valid=None):
+    """Keep the K top key blocks of every row (last axis) by (mass desc, index asc).
+
+    Only the first ``nkb_valid`` key blocks compete; later ones are never kept."""
+    mass = np.asarray(mass, dtype=np.float32)
+    nkb = mass.shape[-1]
+    nv = nkb if nkb_valid is None else nkb_valid
+    m = mass[..., :nv].astype(np.float64)              # exact widening of float32
+    idx = np.broadcast_to(np.arange(nv), m.shape)
+    order = np.lexsort((idx, -np.nan_to_num(m, nan=0.0), np.isnan(m)), axis=-1)
+    rank = np.empty(m.shape, dtype=np.int64)
+    np.put_along_axis(rank, order, np.broadcast_to(np.arange(nv), m.shape), axis=-1)
+    keep = np.zeros(mass.shape, dtype=bool)
+    keep[..., :nv] = rank < K
+    return keep
+
+
+def min_agree_count(rho, P):
+    """Smallest prompt count meeting agreement fraction rho over P prompts: ceil(rho * P).
+
+    A float rho is read as the decimal it prints as (0.1 -> 1/10), not as the
+    binary value nearest to it."""
+    if isinstance(rho, float):
+        rho = str(rho)
+    return math.ceil(Fraction(rho) * P)
+
+
+def agreement(keep, min_agree):
+    """keep [P, ...] bool -> blocks kept by at least min_agree prompts."""
+    return np.asarray(keep, dtype=bool).sum(axis=0) >= min_agree
+
+
+def to_csr(mask):
+    """[H, nqb, nkb] bool -> (row_ptr, col_idx) int32; rows h*nqb+qb, columns ascending."""
+    mask = np.asarray(mask, dtype=bool)
+    H, nqb, nkb = mask.shape
+    row_ptr = [0]
+    cols = []
+    for h in range(H):
+        for qb in range(nqb):
+            c = [kb for kb in range(nkb) if mask[h, qb, kb]]
+            cols.extend(c)
+            row_ptr.append(row_ptr[-1] + len(c))
+    return np.array(row_ptr, dtype=np.int32), np.array(cols, dtype=np.int32)
+
+
+def compile_masks(mass, keep_topk, min_agree, nkb_valid=None):
+    """mass [P, H, nqb, nkb] -> CSR of the blocks that >= min_agree prompts keep in their top K."""
+    keep = topk_keep(mass, keep_topk, nkb_valid)
+    return to_csr(agreement(keep, min_agree))

@@ -1,0 +1,311 @@
+"""Pins for the CPU oracle: checks whose expected values do not come from the oracle.
+
+Each ``pin_*`` takes the implementation under test (the oracle's function, or
+a deliberately broken copy of it in ``test_oracle_mutants.py``) and raises
+AssertionError when it disagrees with the fact the pin encodes:
+
+* library routines on the special cases they cover (torch's
+  scaled_dot_product_attention in float64 on the CPU; NumPy sorting),
+* closed forms (Q = 0, a lone valid key, row sums of a softmax),
+* brute-force enumeration on tiny inputs (all K-subsets, per-prompt counts),
+* hand-worked values under ``tests/golden/``.
+"""
+
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _rand_csr(rng, H, nqb, nkv, density, force_empty=1, force_full=1):
+    m = rng.random((H, nqb, nkv)) < density
+    flat = m.reshape(H * nqb, nkv)
+    pick = rng.choice(H * nqb, force_empty + force_full, replace=False)
+    flat[pick[:force_empty]] = False
+    flat[pick[force_empty:]] = True
+    row_ptr = np.concatenate([[0], np.cumsum(flat.sum(1))]).astype(np.int32)
+    col_idx = np.nonzero(flat)[1].astype(np.int32)
+    return m, row_ptr, col_idx
+
+
+def _sdpa(q, k, v, scale, attn_mask=None):
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64))
+    m = None if attn_mask is None else torch.from_numpy(attn_mask)
+    return torch.nn.functional.scaled_dot_product_attention(
+        t(q), t(k), t(v), attn_mask=m, scale=scale).numpy()
+
+
+# ---------------------------------------------------------------- attention
+
+def pin_sparse_all_kept_is_sdpa(sparse_impl, seed=0):
+    """Every block kept: sparse attention is ordinary attention over the valid keys."""
+    rng = _rng(seed)
+    B, H, L, S, d, blk = 2, 2, 96, 90, 8, 16
+    q, k, v = (rng.standard_normal((B, H, L, d)) for _ in range(3))
+    nqb = L // blk
+    nkv = -(-S // blk)
+    row_ptr = (np.arange(H * nqb + 1) * nkv).astype(np.int32)
+    col_idx = np.tile(np.arange(nkv), H * nqb).astype(np.int32)
+    scale = 0.37
+    O = sparse_impl(q, k, v, row_ptr, col_idx, blk, scale, S)
+    ref = _sdpa(q[:, :, :S], k[:, :, :S], v[:, :, :S], scale)
+    assert np.max(np.abs(O[:, :, :S] - ref)) < 1e-12, "all-kept != SDPA"
+    assert np.all(O[:, :, S:] == 0.0), "padded query rows must be zero"
+
+
+def pin_sparse_is_masked_sdpa(sparse_impl, seed=1):
+    """Skipping a block == giving its scores -inf (SDPA boolean mask), rows with keys."""
+    rng = _rng(seed)
+    B, H, L, S, d, blk = 1, 3, 128, 119, 8, 16
+    q, k, v = (rng.standard_normal((B, H, L, d)) for _ in range(3))
+    nqb = L // blk
+    nkv = -(-S // blk)
+    bm, row_ptr, col_idx = _rand_csr(rng, H, nqb, nkv, 0.4)
+    O = sparse_impl(q, k, v, row_ptr, col_idx, blk, 0.5, S)
+    for h in range(H):
+        tok = np.zeros((L, L), dtype=bool)
+        for qb in range(nqb):
+            for kb in range(nkv):
+                if bm[h, qb, kb]:
+                    tok[qb * blk:(qb + 1) * blk, kb * blk:(kb + 1) * blk] = True
+        tok[:, S:] = False
+        tok = tok[:S, :S]
+        has = tok.any(axis=1)
+        ref = _sdpa(q[:, h:h + 1, :S][:, :, has], k[:, h:h + 1, :S], v[:, h:h + 1, :S], 0.5,
+                    attn_mask=tok[has])
+        got = O[:, h:h + 1, :S][:, :, has]
+        assert np.max(np.abs(got - ref)) < 1e-12, "masked attention != SDPA with -inf mask"
+        assert np.all(O[:, h, :S][:, ~has] == 0.0), "rows with no kept key must be zero"
+        assert np.all(O[:, h, S:] == 0.0), "padded query rows must be zero"
+
+
+def pin_lone_valid_key(sparse_impl):
+    """S=449, block 64: the last block holds one valid token, so a row keeping only it
+    returns that token's value row exactly."""
+    rng = _rng(2)
+    B, H, L, S, d, blk = 1, 1, 512, 449, 8, 64
+    q, k, v = (rng.standard_normal((B, H, L, d)) for _ in range(3))
+    nqb = L // blk
+    row_ptr = np.arange(nqb + 1).astype(np.int32)
+    col_idx = np.full(nqb, 7, dtype=np.int32)
+    O = sparse_impl(q, k, v, row_ptr, col_idx, blk, 0.125, S)
+    assert np.array_equal(O[0, 0, :S], np.broadcast_to(v[0, 0, 448], (S, d))), "lone key"
+
+
+def pin_zero_query_is_mean(sparse_impl):
+    """Q = 0: every kept valid key gets the same weight, O is the mean of those V rows."""
+    rng = _rng(3)
+    B, H, L, S, d, blk = 1, 2, 64, 60, 4, 16
+    k, v = (rng.standard_normal((B, H, L, d)) for _ in range(2))
+    q = np.zeros((B, H, L, d))
+    nqb = L // blk
+    bm, row_ptr, col_idx = _rand_csr(rng, H, nqb, nqb, 0.5, force_empty=0)
+    O = sparse_impl(q, k, v, row_ptr, col_idx, blk, 1.0, S)
+    for h in range(H):
+        for qb in range(nqb):
+            toks = [j for kb in range(nqb) if bm[h, qb, kb] for j in range(kb * blk, (kb + 1) * blk) if j < S]
+            lo, hi = qb * blk, min((qb + 1) * blk, S)
+            if not toks or hi <= lo:
+                continue
+            mean = v[0, h, toks].mean(axis=0)
+            assert np.max(np.abs(O[0, h, lo:hi] - mean)) < 1e-13, "Q=0 must give the kept mean"
+
+
+def pin_golden_attention(sparse_impl):
+    """Hand-worked 4-token example (tests/golden/hand_attention.json)."""
+    g = json.load(open(os.path.join(GOLDEN, "hand_attention.json")))
+    q = np.array(g["q"], dtype=np.float64)[None, None]
+    k = np.array(g["k"], dtype=np.float64)[None, None]
+    v = np.array(g["v"], dtype=np.float64)[None, None]
+    for case in g["cases"]:
+        O = sparse_impl(q, k, v, np.array(case["row_ptr"], np.int32), np.array(case["col_idx"], np.int32),
+                        g["block"], g["scale"], g["seq_len"])
+        exp = np.array([[float(Fraction(x)) for x in row] for row in case["O"]])
+        assert np.max(np.abs(O[0, 0] - exp)) < 1e-14, f"golden case {case['name']}"
+
+
+def pin_dense_is_sdpa(dense_impl, seed=4):
+    rng = _rng(seed)
+    B, H, L, S, d = 1, 2, 40, 37, 6
+    q, k, v = (rng.standard_normal((B, H, L, d)) for _ in range(3))
+    O = dense_impl(q, k, v, 0.3, S)
+    ref = _sdpa(q[:, :, :S], k[:, :, :S], v[:, :, :S], 0.3)
+    assert np.max(np.abs(O[:, :, :S] - ref)) < 1e-12, "dense != SDPA"
+    assert np.all(O[:, :, S:] == 0.0)
+
+
+# ---------------------------------------------------------------- calibration
+
+def pin_mass_row_sums(mass_impl, seed=5):
+    """Each valid query's softmax row sums to 1: row sums = valid queries, total = S."""
+    rng = _rng(seed)
+    B, H, L, S, d, blk = 1, 2, 96, 83, 8, 16
+    q, k = (rng.standard_normal((B, H, L, d)) for _ in range(2))
+    m = mass_impl(q, k, blk, 0.4, S)
+    nqb = L // blk
+    for qb in range(nqb):
+        nvalid = max(0, min((qb + 1) * blk, S) - qb * blk)
+        assert np.max(np.abs(m[:, :, qb].sum(-1) - nvalid)) < 1e-11, "row sum != valid queries"
+    assert np.max(np.abs(m.sum(axis=(-1, -2)) - S)) < 1e-10, "total mass != S"
+    assert np.all(m >= 0.0)
+
+
+def pin_mass_zero_query(mass_impl):
+    """Q = 0: uniform softmax over S keys, tile mass = nq_valid * nk_valid / S."""
+    rng = _rng(6)
+    B, H, L, S, d, blk = 1, 1, 80, 75, 4, 16
+    k = rng.standard_normal((B, H, L, d))
+    q = np.zeros_like(k)
+    m = mass_impl(q, k, blk, 1.0, S)
+    nb = L // blk
+    nv = [max(0, min((b + 1) * blk, S) - b * blk) for b in range(nb)]
+    exp = np.array([[nv[a] * nv[b] / S for b in range(nb)] for a in range(nb)])
+    assert np.max(np.abs(m[0, 0] - exp)) < 1e-13, "Q=0 closed form"
+
+
+def pin_mass_brute_force(mass_impl):
+    """Per-token softmax with math.exp loops on a tiny input."""
+    rng = _rng(7)
+    B, H, L, S, d, blk = 1, 1, 12, 11, 3, 4
+    q, k = (rng.standard_normal((B, H, L, d)) for _ in range(2))
+    sc = 0.9
+    m = mass_impl(q, k, blk, sc, S)
+    nb = L // blk
+    exp = [[0.0] * nb for _ in range(nb)]
+    for i in range(S):
+        w = [math.exp(sc * sum(q[0, 0, i, c] * k[0, 0, j, c] for c in range(d))) for j in range(S)]
+        z = sum(w)
+        for j in range(S):
+            exp[i // blk][j // blk] += w[j] / z
+    assert np.max(np.abs(m[0, 0] - np.array(exp))) < 1e-13, "brute-force mass"
+
+
+def pin_mass_golden(mass_impl):
+    g = json.load(open(os.path.join(GOLDEN, "hand_attention.json")))
+    q = np.array(g["q"], dtype=np.float64)[None, None]
+    k = np.array(g["k"], dtype=np.float64)[None, None]
+    m = mass_impl(q, k, g["block"], g["scale"], g["seq_len"])
+    exp = np.array([[float(Fraction(x)) for x in row] for row in g["mass"]])
+    assert np.max(np.abs(m[0, 0] - exp)) < 1e-14, "golden mass"
+
+
+def pin_topk_subsets(topk_impl, seed=8):
+    """nkb = 8, K = 2: the kept pair is the lexicographically first of the max-sum pairs."""
+    rng = _rng(seed)
+    rows = rng.integers(0, 4, size=(300, 8)).astype(np.float32)   # many ties
+    rows[::7] = rng.random((len(rows[::7]), 8)).astype(np.float32)
+    keep = topk_impl(rows, 2)
+    for r, row in enumerate(rows):
+        best = max(itertools.combinations(range(8), 2),
+                   key=lambda s: (float(row[s[0]]) + float(row[s[1]]), [-i for i in s]))
+        want = np.zeros(8, dtype=bool)
+        want[list(best)] = True
+        assert np.array_equal(keep[r], want), f"top-2 row {r}: {row} -> {keep[r]}, want {best}"
+
+
+def pin_topk_counts(topk_impl, seed=9):
+    """Exactly min(K, nkb_valid) kept per row; nothing at or beyond nkb_valid; NaN last."""
+    rng = _rng(seed)
+    m = rng.random((5, 7, 20)).astype(np.float32)
+    m[0, 0, 3] = np.nan
+    for K in (0, 1, 5, 17, 20, 25):
+        keep = topk_impl(m, K, 17)
+        assert np.all(keep.sum(-1) == min(K, 17)), "count per row"
+        assert not keep[..., 17:].any(), "blocks past the valid range"
+    keep = topk_impl(m, 16, 17)
+    assert not keep[0, 0, 3], "NaN must sort last"
+    # order-statistic check against a full NumPy sort on distinct values
+    x = rng.permutation(1000).astype(np.float32).reshape(10, 100)
+    keep = topk_impl(x, 10)
+    thr = np.sort(x, axis=1)[:, -10][:, None]
+    assert np.array_equal(keep, x >= thr), "top-K != sort threshold"
+
+
+def pin_agreement_brute(agree_impl, seed=10):
+    rng = _rng(seed)
+    keep = rng.random((5, 3, 4, 6)) < 0.5
+    for t in range(0, 7):
+        got = agree_impl(keep, t)
+        for idx in itertools.product(range(3), range(4), range(6)):
+            cnt = sum(int(keep[(p,) + idx]) for p in range(5))
+            assert bool(got[idx]) == (cnt >= t), "agreement count"
+    assert np.array_equal(agree_impl(keep[:1], 1), keep[0]), "P = 1 is the identity"
+    assert np.array_equal(agree_impl(keep, 5), keep.all(0)), "min_agree = P is the intersection"
+    assert np.array_equal(agree_impl(keep, 1), keep.any(0)), "min_agree = 1 is the union"
+
+
+def pin_min_agree(min_agree_impl):
+    assert min_agree_impl(0.5, 8) == 4
+    assert min_agree_impl(Fraction(1, 2), 7) == 4
+    assert min_agree_impl(Fraction(1, 3), 3) == 1
+    assert min_agree_impl(0.1, 10) == 1
+    assert min_agree_impl(1.0, 8) == 8
+    assert min_agree_impl(0.0, 8) == 0
+    for P in range(1, 65):
+        for num in range(0, P + 1):
+            rho = Fraction(num, P)
+            assert min_agree_impl(rho, P) == num, "exact fractions"
+
+
+def pin_csr(to_csr_impl, seed=11):
+    rng = _rng(seed)
+    m = rng.random((3, 5, 7)) < 0.4
+    m[1, 2] = False
+    row_ptr, col_idx = to_csr_impl(m)
+    assert row_ptr.dtype == np.int32 and col_idx.dtype == np.int32
+    assert row_ptr[0] == 0 and row_ptr[-1] == m.sum() and len(row_ptr) == 16
+    assert np.all(np.diff(row_ptr) >= 0)
+    back = np.zeros_like(m)
+    for r in range(15):
+        c = col_idx[row_ptr[r]:row_ptr[r + 1]]
+        assert np.all(np.diff(c) > 0), "ascending, unique"
+        back[r // 5, r % 5, c] = True
+    assert np.array_equal(back, m), "round trip"
+
+
+def pin_compile_brute(compile_impl, seed=12):
+    """Whole compile on a tiny bank of prompts, every step done by enumeration."""
+    rng = _rng(seed)
+    P, H, nqb, nkb, K, t = 4, 2, 3, 6, 2, 2
+    mass = rng.integers(0, 3, size=(P, H, nqb, nkb)).astype(np.float32)
+    row_ptr, col_idx = compile_impl(mass, K, t)
+    want_rows = []
+    for h in range(H):
+        for qb in range(nqb):
+            cnt = [0] * nkb
+            for p in range(P):
+                row = mass[p, h, qb]
+                best = max(itertools.combinations(range(nkb), K),
+                           key=lambda s: (sum(float(row[i]) for i in s), [-i for i in s]))
+                for i in best:
+                    cnt[i] += 1
+            want_rows.append([kb for kb in range(nkb) if cnt[kb] >= t])
+    got_rows = [list(col_idx[row_ptr[r]:row_ptr[r + 1]]) for r in range(H * nqb)]
+    assert got_rows == want_rows, "compile by enumeration"
+
+
+# ---------------------------------------------------------------- schedule
+
+def pin_lpt(lpt_impl, seed=13):
+    rng = _rng(seed)
+    H, nqb = 3, 9
+    counts = rng.integers(0, 5, size=H * nqb)
+    row_ptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    order = lpt_impl(row_ptr, H, nqb)
+    assert sorted(order.tolist()) == list(range(H * nqb)), "a permutation"
+    for h in range(H):
+        seg = order[h * nqb:(h + 1) * nqb]
+        assert np.all(seg // nqb == h), "head-major"
+        c = counts[seg]
+        for a, b_ in zip(range(nqb - 1), range(1, nqb)):
+            assert c[a] > c[b_] or (c[a] == c[b_] and seg[a] < seg[b_]), "longest first, ties by index"

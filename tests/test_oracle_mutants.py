@@ -1,0 +1,166 @@
+"""Planted mistakes in copies of the oracle must each trip at least one pin.
+
+This shows the pins are sharp enough to catch the plausible slips (a dropped
+term, a wrong index, a transposed operand, an off-by-one rule) in the oracle.
+Everything here runs on the CPU."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import attention as oa
+from tests import pins
+
+
+def _gather_with(row_fn):
+    def impl(q, k, v, row_ptr, col_idx, block, scale, seq_len):
+        q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+        B, H, L, d = q.shape
+        nqb = L // block
+        O = np.zeros((B, H, L, d))
+        for b in range(B):
+            for h in range(H):
+                for qb in range(nqb):
+                    r = h * nqb + qb
+                    O[b, h, qb * block:(qb + 1) * block] = row_fn(
+                        q[b, h], k[b, h], v[b, h], col_idx[row_ptr[r]:row_ptr[r + 1]], qb, block, scale, seq_len)
+        return O
+    return impl
+
+
+def _row_generic(qs, ks, vs, kbs, qb, block, scale, seq_len, *, key_limit=None, norm=True,
+                 scale_pow=1, zero_pad_rows=True):
+    d = vs.shape[1]
+    out = np.zeros((block, d))
+    lo = qb * block
+    hi = min(lo + block, seq_len) if zero_pad_rows else lo + block
+    if hi <= lo:
+        return out
+    lim = seq_len if key_limit is None else key_limit
+    J = [j for kb in kbs for j in range(kb * block, min((kb + 1) * block, lim))]
+    if not J:
+        return out
+    s = (scale ** scale_pow) * (qs[lo:hi] @ ks[J].T)
+    e = np.exp(s - s.max(axis=1, keepdims=True))
+    num = e @ vs[J]
+    out[: hi - lo] = num / e.sum(axis=1, keepdims=True) if norm else num
+    return out
+
+
+ATTN_MUTANTS = {
+    "padded_keys_in_softmax": _gather_with(lambda *a: _row_generic(*a, key_limit=10 ** 9)),
+    "missing_denominator": _gather_with(lambda *a: _row_generic(*a, norm=False)),
+    "scale_squared": _gather_with(lambda *a: _row_generic(*a, scale_pow=2)),
+    "padded_rows_not_zero": _gather_with(lambda *a: _row_generic(*a, zero_pad_rows=False)),
+}
+
+
+def _transposed_mask(q, k, v, row_ptr, col_idx, block, scale, seq_len):
+    B, H, L, d = np.shape(q)
+    nqb = L // block
+    bm = oracle.csr_to_block_mask(row_ptr, col_idx, H, nqb, nqb).transpose(0, 2, 1)
+    return oracle.sparse_attention_masked_dense(q, k, v, bm, block, scale, seq_len)
+
+
+ATTN_MUTANTS["transposed_block_mask"] = _transposed_mask
+
+ATTN_PINS = [pins.pin_sparse_all_kept_is_sdpa, pins.pin_sparse_is_masked_sdpa, pins.pin_lone_valid_key,
+             pins.pin_zero_query_is_mean, pins.pin_golden_attention]
+
+
+def _trips(fn, pin_list):
+    tripped = []
+    for p in pin_list:
+        try:
+            p(fn)
+        except (AssertionError, IndexError, ValueError):
+            tripped.append(p.__name__)
+    return tripped
+
+
+@pytest.mark.parametrize("name", sorted(ATTN_MUTANTS))
+def test_attention_mutant_is_caught(name):
+    assert _trips(ATTN_MUTANTS[name], ATTN_PINS), f"no pin caught mutant {name}"
+
+
+def _mass_generic(q, k, block, scale, seq_len, *, q_limit=None, transpose=False, normalise=True):
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, H, L, d = q.shape
+    nb = L // block
+    out = np.zeros((B, H, nb, nb))
+    ql = seq_len if q_limit is None else q_limit
+    for b in range(B):
+        for h in range(H):
+            s = scale * (q[b, h, :ql] @ k[b, h, :seq_len].T)
+            e = np.exp(s - s.max(axis=1, keepdims=True))
+            p = e / e.sum(axis=1, keepdims=True) if normalise else e
+            for i in range(p.shape[0]):
+                for j in range(p.shape[1]):
+                    a, c = (j // block, i // block) if transpose else (i // block, j // block)
+                    out[b, h, a, c] += p[i, j]
+    return out
+
+
+MASS_MUTANTS = {
+    "padded_queries_pooled": lambda *a: _mass_generic(*a, q_limit=np.shape(a[0])[2]),
+    "transposed_tile": lambda *a: _mass_generic(*a, transpose=True),
+    "unnormalised_exp": lambda *a: _mass_generic(*a, normalise=False),
+}
+MASS_PINS = [pins.pin_mass_row_sums, pins.pin_mass_zero_query, pins.pin_mass_brute_force, pins.pin_mass_golden]
+
+
+@pytest.mark.parametrize("name", sorted(MASS_MUTANTS))
+def test_mass_mutant_is_caught(name):
+    assert _trips(MASS_MUTANTS[name], MASS_PINS), f"no pin caught mutant {name}"
+
+
+def _topk_generic(mass, K, nkb_valid=None, *, desc_index=False, ascending=False):
+    mass = np.asarray(mass, dtype=np.float32)
+    nv = mass.shape[-1] if nkb_valid is None else nkb_valid
+    m = mass[..., :nv].astype(np.float64)
+    idx = np.broadcast_to(np.arange(nv), m.shape)
+    key = m if ascending else -m
+    order = np.lexsort(((-idx if desc_index else idx), np.nan_to_num(key), np.isnan(m)), axis=-1)
+    rank = np.empty(m.shape, dtype=np.int64)
+    np.put_along_axis(rank, order, np.broadcast_to(np.arange(nv), m.shape), axis=-1)
+    keep = np.zeros(mass.shape, dtype=bool)
+    keep[..., :nv] = rank < K
+    return keep
+
+
+TOPK_MUTANTS = {
+    "ties_by_larger_index": lambda *a: _topk_generic(*a, desc_index=True),
+    "keeps_smallest": lambda *a: _topk_generic(*a, ascending=True),
+}
+
+
+@pytest.mark.parametrize("name", sorted(TOPK_MUTANTS))
+def test_topk_mutant_is_caught(name):
+    assert _trips(TOPK_MUTANTS[name], [pins.pin_topk_subsets, pins.pin_topk_counts])
+
+
+def test_agreement_mutants_are_caught():
+    strict = lambda keep, t: np.asarray(keep).sum(0) > t
+    assert _trips(strict, [pins.pin_agreement_brute])
+    floor = lambda rho, P: math.floor(float(rho) * P)
+    assert _trips(floor, [pins.pin_min_agree])
+    binary = lambda rho, P: math.ceil(__import__("fractions").Fraction(rho) * P)
+    assert _trips(binary, [pins.pin_min_agree]), "binary reading of 0.1 must be caught"
+
+
+def test_csr_and_schedule_mutants_are_caught():
+    def desc_cols(mask):
+        rp, ci = oracle.to_csr(mask)
+        ci = ci.copy()
+        for r in range(len(rp) - 1):
+            ci[rp[r]:rp[r + 1]] = ci[rp[r]:rp[r + 1]][::-1]
+        return rp, ci
+    assert _trips(desc_cols, [pins.pin_csr])
+
+    def shortest_first(row_ptr, H, nqb):
+        o = oracle.lpt_work_order(row_ptr, H, nqb)
+        return np.concatenate([o[h * nqb:(h + 1) * nqb][::-1] for h in range(H)])
+    assert _trips(shortest_first, [pins.pin_lpt])
