@@ -1,0 +1,40 @@
+"""Calibrated block-sparse attention (CalibAtt) for AMD MI355X (gfx950).
+
+The compute lives in libcalibatt.so (HIP kernels behind a C ABI, declared in
+include/calibatt.h).  This package is the thin binding: ``capi`` mirrors the
+C entry points one to one, ``MaskBank`` keeps the compiled lists of many
+timesteps on the GPU.  Build the library with
+``python -m block_sparse_attention_calibatt_amd.build``.
+"""
+
+from ._lib import CalibattError, LIB_PATH, load
+from .capi import (
+    calibatt_sparse_attn_fwd,
+    calibatt_dense_attn_fwd,
+    calibatt_block_mass,
+    calibatt_compile_ws_bytes,
+    calibatt_compile_masks,
+    calibatt_build_schedule,
+    calibatt_validate_csr,
+    calibatt_status_string,
+    calibatt_last_error,
+    calibatt_version,
+)
+from .bank import MaskBank
+
+__all__ = [
+    "CalibattError",
+    "LIB_PATH",
+    "load",
+    "calibatt_sparse_attn_fwd",
+    "calibatt_dense_attn_fwd",
+    "calibatt_block_mass",
+    "calibatt_compile_ws_bytes",
+    "calibatt_compile_masks",
+    "calibatt_build_schedule",
+    "calibatt_validate_csr",
+    "calibatt_status_string",
+    "calibatt_last_error",
+    "calibatt_version",
+    "MaskBank",
+]

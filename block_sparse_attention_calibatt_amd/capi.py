@@ -1,0 +1,183 @@
+"""Python binding of the C ABI: one function per entry point, same names.
+
+Each function only marshals arguments: it checks that the torch tensors have
+the shapes, dtypes and devices the raw-pointer ABI assumes (the library cannot
+see tensor sizes), passes their device pointers and torch's current HIP
+stream, and raises CalibattError on a non-OK status.  All computation runs in
+the library's HIP kernels.
+"""
+
+import ctypes
+
+import numpy as np
+import torch
+
+from ._lib import BF16, F32, CalibattError, check, load
+
+_DT = {torch.bfloat16: BF16, torch.float32: F32}
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dev_tensor(t, name, dtype=None):
+    _need(isinstance(t, torch.Tensor), f"{name} must be a torch.Tensor")
+    _need(t.is_cuda, f"{name} must be on a GPU device")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+    if dtype is not None:
+        _need(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _qkv(Q, K, V, O):
+    for n, t in (("Q", Q), ("K", K), ("V", V), ("O", O)):
+        _dev_tensor(t, n)
+    _need(Q.dim() == 4, "Q must be [B, H, L, d]")
+    for n, t in (("K", K), ("V", V), ("O", O)):
+        _need(t.shape == Q.shape and t.dtype == Q.dtype and t.device == Q.device,
+              f"{n} must match Q in shape, dtype and device")
+    _need(Q.dtype in _DT, f"unsupported dtype {Q.dtype} (bfloat16 or float32)")
+    return Q.shape
+
+
+def calibatt_sparse_attn_fwd(Q, K, V, O, row_ptr, col_idx, block, scale, seq_len=None,
+                             work_order=None, queue_ws=None):
+    B, H, L, d = _qkv(Q, K, V, O)
+    seq_len = L if seq_len is None else int(seq_len)
+    _dev_tensor(row_ptr, "row_ptr", torch.int32)
+    _dev_tensor(col_idx, "col_idx", torch.int32)
+    _need(block > 0 and L % block == 0, "L must be a multiple of block")
+    rows = H * (L // block)
+    _need(row_ptr.numel() == rows + 1, f"row_ptr must have H*nqb+1 = {rows + 1} entries")
+    if work_order is not None:
+        _dev_tensor(work_order, "work_order", torch.int32)
+        _need(work_order.numel() == rows, f"work_order must have {rows} entries")
+    if queue_ws is not None:
+        _dev_tensor(queue_ws, "queue_ws", torch.int32)
+        _need(queue_ws.numel() >= 16, "queue_ws needs >= 16 int32 entries")
+    lib = load()
+    check(lib.calibatt_sparse_attn_fwd(
+        _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(row_ptr), _ptr(col_idx), int(block), float(scale),
+        B, H, L, seq_len, d, _DT[Q.dtype], _ptr(work_order), _ptr(queue_ws), col_idx.numel(),
+        _stream(Q)))
+    return O
+
+
+def calibatt_dense_attn_fwd(Q, K, V, O, block, scale, seq_len=None):
+    B, H, L, d = _qkv(Q, K, V, O)
+    seq_len = L if seq_len is None else int(seq_len)
+    lib = load()
+    check(lib.calibatt_dense_attn_fwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), int(block), float(scale),
+                                      B, H, L, seq_len, d, _DT[Q.dtype], _stream(Q)))
+    return O
+
+
+def calibatt_block_mass(Q, K, block, scale, lse_ws, mass, seq_len=None):
+    for n, t in (("Q", Q), ("K", K)):
+        _dev_tensor(t, n)
+    _need(Q.dim() == 4 and K.shape == Q.shape and K.dtype == Q.dtype, "Q, K must be [B, H, L, d] alike")
+    _need(Q.dtype in _DT, f"unsupported dtype {Q.dtype}")
+    B, H, L, d = Q.shape
+    seq_len = L if seq_len is None else int(seq_len)
+    _need(block > 0 and L % block == 0, "L must be a multiple of block")
+    nb = L // block
+    _dev_tensor(lse_ws, "lse_ws", torch.float32)
+    _dev_tensor(mass, "mass", torch.float32)
+    _need(lse_ws.numel() == B * H * L, "lse_ws must have B*H*L entries")
+    _need(mass.numel() == B * H * nb * nb, "mass must have B*H*nqb*nkb entries")
+    lib = load()
+    check(lib.calibatt_block_mass(_ptr(Q), _ptr(K), B, H, L, seq_len, d, _DT[Q.dtype], int(block),
+                                  float(scale), _ptr(lse_ws), _ptr(mass), _stream(Q)))
+    return mass
+
+
+def calibatt_compile_ws_bytes(P, H, nqb, nkb):
+    return int(load().calibatt_compile_ws_bytes(int(P), int(H), int(nqb), int(nkb)))
+
+
+def calibatt_compile_masks(mass, keep_topk, min_agree, nkb_valid=None, row_ptr=None, col_idx=None,
+                           ws=None):
+    """mass [P, H, nqb, nkb] float32 -> (row_ptr, col_idx) int32 device tensors."""
+    _dev_tensor(mass, "mass", torch.float32)
+    _need(mass.dim() == 4, "mass must be [P, H, nqb, nkb]")
+    P, H, nqb, nkb = mass.shape
+    nkb_valid = nkb if nkb_valid is None else int(nkb_valid)
+    rows = H * nqb
+    dev = mass.device
+    if row_ptr is None:
+        row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    _dev_tensor(row_ptr, "row_ptr", torch.int32)
+    _need(row_ptr.numel() == rows + 1, "row_ptr must have H*nqb+1 entries")
+    if col_idx is None:
+        col_idx = torch.empty(max(1, rows * nkb_valid), dtype=torch.int32, device=dev)
+    _dev_tensor(col_idx, "col_idx", torch.int32)
+    need = calibatt_compile_ws_bytes(P, H, nqb, nkb)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _dev_tensor(ws, "ws", torch.uint8)
+    nnz = ctypes.c_int64(0)
+    lib = load()
+    check(lib.calibatt_compile_masks(_ptr(mass), P, H, nqb, nkb, nkb_valid, int(keep_topk),
+                                     int(min_agree), _ptr(row_ptr), _ptr(col_idx), col_idx.numel(),
+                                     ctypes.byref(nnz), _ptr(ws), ws.numel(), _stream(mass)))
+    return row_ptr, col_idx[: nnz.value]
+
+
+def calibatt_build_schedule(row_ptr, H, nqb, work_order=None):
+    _dev_tensor(row_ptr, "row_ptr", torch.int32)
+    _need(row_ptr.numel() == H * nqb + 1, "row_ptr must have H*nqb+1 entries")
+    if work_order is None:
+        work_order = torch.empty(H * nqb, dtype=torch.int32, device=row_ptr.device)
+    _dev_tensor(work_order, "work_order", torch.int32)
+    _need(work_order.numel() == H * nqb, "work_order must have H*nqb entries")
+    lib = load()
+    check(lib.calibatt_build_schedule(_ptr(row_ptr), int(H), int(nqb), _ptr(work_order), _stream(row_ptr)))
+    return work_order
+
+
+def calibatt_validate_csr(row_ptr, col_idx, rows, nkb_valid):
+    """Host arrays (numpy int32); raises CalibattError(CALIBATT_ERR_CSR) on a defect."""
+    rp = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    ci = np.ascontiguousarray(col_idx, dtype=np.int32)
+    if rp.size < rows + 1:
+        raise ValueError("row_ptr shorter than rows + 1")
+    lib = load()
+    check(lib.calibatt_validate_csr(rp.ctypes.data_as(ctypes.c_void_p),
+                                    ci.ctypes.data_as(ctypes.c_void_p) if ci.size else None,
+                                    int(rows), int(nkb_valid), ci.size))
+
+
+def calibatt_status_string(status):
+    return load().calibatt_status_string(int(status)).decode()
+
+
+def calibatt_last_error():
+    return load().calibatt_last_error().decode()
+
+
+def calibatt_version():
+    return int(load().calibatt_version())
+
+
+__all__ = [
+    "CalibattError",
+    "calibatt_sparse_attn_fwd",
+    "calibatt_dense_attn_fwd",
+    "calibatt_block_mass",
+    "calibatt_compile_ws_bytes",
+    "calibatt_compile_masks",
+    "calibatt_build_schedule",
+    "calibatt_validate_csr",
+    "calibatt_status_string",
+    "calibatt_last_error",
+    "calibatt_version",
+]

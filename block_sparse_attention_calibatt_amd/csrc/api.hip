@@ -1,0 +1,294 @@
+// C ABI of the calibrated block-sparse attention library (declared in
+// include/calibatt.h).  Every argument is checked here, on the host, before
+// anything is enqueued; the checks make no HIP call, so they also run on a
+// machine without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <mutex>
+#include <string>
+
+#include "../../include/calibatt.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+calibatt_status fail(calibatt_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+calibatt_status ok() {
+  g_last_error.clear();
+  return CALIBATT_OK;
+}
+
+calibatt_status hip_fail(hipError_t e, const char* what) {
+  return fail(CALIBATT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+std::mutex g_cu_mutex;
+int g_cu_count[64] = {0};
+
+hipError_t cu_count(int* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) {
+    *out = 256;
+    return hipSuccess;
+  }
+  std::lock_guard<std::mutex> lk(g_cu_mutex);
+  if (g_cu_count[dev] == 0) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    g_cu_count[dev] = n > 0 ? n : 1;
+  }
+  *out = g_cu_count[dev];
+  return hipSuccess;
+}
+
+// Shape checks common to the attention and pooling entry points.
+calibatt_status check_qkv_shape(int B, int H, int L, int seq_len, int d, calibatt_dtype dt,
+                                int block) {
+  if (dt != CALIBATT_BF16 && dt != CALIBATT_F32) return fail(CALIBATT_ERR_DTYPE, "unknown dtype code %d", (int)dt);
+  if (B < 1 || H < 1) return fail(CALIBATT_ERR_SHAPE, "B=%d and H=%d must be >= 1", B, H);
+  if (block != 64 && block != 128) return fail(CALIBATT_ERR_UNSUPPORTED, "block=%d (supported: 64, 128)", block);
+  if (d != 64 && d != 128) return fail(CALIBATT_ERR_UNSUPPORTED, "d=%d (supported: 64, 128)", d);
+  if (L < block || L % block != 0) return fail(CALIBATT_ERR_SHAPE, "L=%d must be a positive multiple of block=%d", L, block);
+  if (seq_len < 1 || seq_len > L) return fail(CALIBATT_ERR_SHAPE, "seq_len=%d must be in [1, L=%d]", seq_len, L);
+  const long long elems = (long long)B * H * L * d;
+  if (elems >= (1LL << 31)) return fail(CALIBATT_ERR_SHAPE, "B*H*L*d=%lld must be < 2^31", elems);
+  return CALIBATT_OK;
+}
+
+calibatt_status check_ptrs4(const void* Q, const void* K, const void* V, const void* O) {
+  if (!Q || !K || !V || !O) return fail(CALIBATT_ERR_NULL, "Q, K, V and O must be non-NULL");
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16))
+    return fail(CALIBATT_ERR_ALIGN, "Q, K, V and O must be 16-byte aligned");
+  return CALIBATT_OK;
+}
+
+calibatt_status run_attention(const void* Q, const void* K, const void* V, void* O,
+                              const int32_t* row_ptr, const int32_t* col_idx, int block, float scale,
+                              int B, int H, int L, int seq_len, int d, calibatt_dtype dt,
+                              const int32_t* work_order, int32_t* queue_ws, bool dense,
+                              void* stream) {
+  int ncu = 256;
+  if (queue_ws) {
+    hipError_t e = cu_count(&ncu);
+    if (e != hipSuccess) return hip_fail(e, "querying the compute-unit count");
+  }
+  calibatt::AttnArgs a;
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.work_order = work_order;
+  a.queue = queue_ws;
+  a.B = B;
+  a.H = H;
+  a.L = L;
+  a.seq_len = seq_len;
+  a.d = d;
+  a.block = block;
+  a.nkb_valid = (seq_len + block - 1) / block;
+  a.scale = scale;
+  a.dtype_f32 = dt == CALIBATT_F32;
+  a.num_cu = ncu;
+  hipError_t e = calibatt::launch_attention(a, dense, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, dense ? "launching dense attention" : "launching sparse attention");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+calibatt_status calibatt_sparse_attn_fwd(const void* Q, const void* K, const void* V, void* O,
+                                         const int32_t* row_ptr, const int32_t* col_idx, int block,
+                                         float scale, int B, int H, int L, int seq_len, int d,
+                                         calibatt_dtype dt, const int32_t* work_order,
+                                         int32_t* queue_ws, int64_t nnz, void* stream) {
+  calibatt_status s = check_ptrs4(Q, K, V, O);
+  if (s != CALIBATT_OK) return s;
+  s = check_qkv_shape(B, H, L, seq_len, d, dt, block);
+  if (s != CALIBATT_OK) return s;
+  if (!row_ptr) return fail(CALIBATT_ERR_NULL, "row_ptr must be non-NULL");
+  if (nnz < 0) return fail(CALIBATT_ERR_CSR, "nnz=%lld must be >= 0", (long long)nnz);
+  const long long rows = (long long)H * (L / block);
+  const long long nkb_valid = (seq_len + block - 1) / block;
+  if (nnz > rows * nkb_valid)
+    return fail(CALIBATT_ERR_CSR, "nnz=%lld exceeds rows*nkb_valid=%lld", (long long)nnz, rows * nkb_valid);
+  if (nnz > 0 && !col_idx) return fail(CALIBATT_ERR_NULL, "col_idx must be non-NULL when nnz > 0");
+  if (!aligned(row_ptr, 4) || (col_idx && !aligned(col_idx, 4)) || (work_order && !aligned(work_order, 4)))
+    return fail(CALIBATT_ERR_ALIGN, "row_ptr, col_idx and work_order must be 4-byte aligned");
+  if (queue_ws && !aligned(queue_ws, 16)) return fail(CALIBATT_ERR_ALIGN, "queue_ws must be 16-byte aligned");
+  return run_attention(Q, K, V, O, row_ptr, col_idx, block, scale, B, H, L, seq_len, d, dt, work_order,
+                       queue_ws, false, stream);
+}
+
+calibatt_status calibatt_dense_attn_fwd(const void* Q, const void* K, const void* V, void* O,
+                                        int block, float scale, int B, int H, int L, int seq_len,
+                                        int d, calibatt_dtype dt, void* stream) {
+  calibatt_status s = check_ptrs4(Q, K, V, O);
+  if (s != CALIBATT_OK) return s;
+  s = check_qkv_shape(B, H, L, seq_len, d, dt, block);
+  if (s != CALIBATT_OK) return s;
+  return run_attention(Q, K, V, O, nullptr, nullptr, block, scale, B, H, L, seq_len, d, dt, nullptr,
+                       nullptr, true, stream);
+}
+
+calibatt_status calibatt_block_mass(const void* Q, const void* K, int B, int H, int L, int seq_len,
+                                    int d, calibatt_dtype dt, int block, float scale, float* lse_ws,
+                                    float* mass, void* stream) {
+  if (!Q || !K || !lse_ws || !mass) return fail(CALIBATT_ERR_NULL, "Q, K, lse_ws and mass must be non-NULL");
+  if (!aligned(Q, 16) || !aligned(K, 16)) return fail(CALIBATT_ERR_ALIGN, "Q and K must be 16-byte aligned");
+  if (!aligned(lse_ws, 4) || !aligned(mass, 4)) return fail(CALIBATT_ERR_ALIGN, "lse_ws and mass must be 4-byte aligned");
+  calibatt_status s = check_qkv_shape(B, H, L, seq_len, d, dt, block);
+  if (s != CALIBATT_OK) return s;
+  if (dt != CALIBATT_BF16) return fail(CALIBATT_ERR_UNSUPPORTED, "block_mass supports bf16 inputs only");
+  if (L / block > calibatt::kMaxKeyBlocks)
+    return fail(CALIBATT_ERR_UNSUPPORTED, "L/block=%d exceeds %d key blocks", L / block, calibatt::kMaxKeyBlocks);
+  calibatt::MassArgs a;
+  a.Q = Q;
+  a.K = K;
+  a.lse = lse_ws;
+  a.mass = mass;
+  a.B = B;
+  a.H = H;
+  a.L = L;
+  a.seq_len = seq_len;
+  a.d = d;
+  a.block = block;
+  a.nkb_valid = (seq_len + block - 1) / block;
+  a.scale = scale;
+  hipError_t e = calibatt::launch_block_mass(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "launching block mass");
+  return ok();
+}
+
+size_t calibatt_compile_ws_bytes(int P, int H, int nqb, int nkb) {
+  if (P < 1 || H < 1 || nqb < 1 || nkb < 1) return 0;
+  const size_t rows = (size_t)H * nqb;
+  const size_t keep = (rows * nkb + 15) / 16 * 16;
+  return keep + rows * sizeof(int32_t);
+}
+
+calibatt_status calibatt_compile_masks(const float* mass, int P, int H, int nqb, int nkb,
+                                       int nkb_valid, int keep_topk, int min_agree, int32_t* row_ptr,
+                                       int32_t* col_idx, int64_t nnz_cap, int64_t* nnz_out, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  if (!mass || !row_ptr || !nnz_out || !ws) return fail(CALIBATT_ERR_NULL, "mass, row_ptr, nnz_out and ws must be non-NULL");
+  if (P < 1 || H < 1 || nqb < 1 || nkb < 1) return fail(CALIBATT_ERR_SHAPE, "P, H, nqb and nkb must be >= 1");
+  if (nkb > calibatt::kMaxKeyBlocks) return fail(CALIBATT_ERR_UNSUPPORTED, "nkb=%d exceeds %d", nkb, calibatt::kMaxKeyBlocks);
+  if (nkb_valid < 0 || nkb_valid > nkb) return fail(CALIBATT_ERR_SHAPE, "nkb_valid=%d must be in [0, nkb=%d]", nkb_valid, nkb);
+  if (keep_topk < 0) return fail(CALIBATT_ERR_SHAPE, "keep_topk=%d must be >= 0", keep_topk);
+  if (min_agree < 0 || min_agree > P) return fail(CALIBATT_ERR_SHAPE, "min_agree=%d must be in [0, P=%d]", min_agree, P);
+  if (nnz_cap < 0) return fail(CALIBATT_ERR_SHAPE, "nnz_cap must be >= 0");
+  if (nnz_cap > 0 && !col_idx) return fail(CALIBATT_ERR_NULL, "col_idx must be non-NULL when nnz_cap > 0");
+  const long long rows = (long long)H * nqb;
+  if (rows * nkb >= (1LL << 31)) return fail(CALIBATT_ERR_SHAPE, "H*nqb*nkb must be < 2^31");
+  if ((long long)P * rows * nkb >= (1LL << 40)) return fail(CALIBATT_ERR_SHAPE, "P*H*nqb*nkb too large");
+  const size_t need = calibatt_compile_ws_bytes(P, H, nqb, nkb);
+  if (ws_bytes < need) return fail(CALIBATT_ERR_CAPACITY, "ws_bytes=%zu < %zu required", ws_bytes, need);
+  if (!aligned(ws, 16) || !aligned(mass, 4) || !aligned(row_ptr, 4) || (col_idx && !aligned(col_idx, 4)))
+    return fail(CALIBATT_ERR_ALIGN, "ws must be 16-byte aligned; mass, row_ptr, col_idx 4-byte aligned");
+
+  calibatt::CompileArgs a;
+  a.mass = mass;
+  a.P = P;
+  a.H = H;
+  a.nqb = nqb;
+  a.nkb = nkb;
+  a.nkb_valid = nkb_valid;
+  a.keep_topk = keep_topk;
+  a.min_agree = min_agree;
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.keep_ws = static_cast<uint8_t*>(ws);
+  a.count_ws = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + (rows * nkb + 15) / 16 * 16);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = calibatt::launch_compile_count(a, st);
+  if (e != hipSuccess) return hip_fail(e, "launching mask compile (count)");
+  int32_t total = 0;
+  e = hipMemcpyAsync(&total, row_ptr + rows, sizeof(int32_t), hipMemcpyDeviceToHost, st);
+  if (e != hipSuccess) return hip_fail(e, "reading the kept count");
+  e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "synchronising after mask compile (count)");
+  *nnz_out = total;
+  if (total > nnz_cap)
+    return fail(CALIBATT_ERR_CAPACITY, "kept blocks %d exceed nnz_cap=%lld", total, (long long)nnz_cap);
+  if (total > 0) {
+    e = calibatt::launch_compile_fill(a, st);
+    if (e != hipSuccess) return hip_fail(e, "launching mask compile (fill)");
+  }
+  return ok();
+}
+
+calibatt_status calibatt_build_schedule(const int32_t* row_ptr, int H, int nqb, int32_t* work_order,
+                                        void* stream) {
+  if (!row_ptr || !work_order) return fail(CALIBATT_ERR_NULL, "row_ptr and work_order must be non-NULL");
+  if (H < 1 || nqb < 1) return fail(CALIBATT_ERR_SHAPE, "H and nqb must be >= 1");
+  if (nqb > calibatt::kMaxKeyBlocks) return fail(CALIBATT_ERR_UNSUPPORTED, "nqb=%d exceeds %d", nqb, calibatt::kMaxKeyBlocks);
+  if (!aligned(row_ptr, 4) || !aligned(work_order, 4)) return fail(CALIBATT_ERR_ALIGN, "row_ptr and work_order must be 4-byte aligned");
+  hipError_t e = calibatt::launch_schedule(row_ptr, H, nqb, work_order, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "launching work-order build");
+  return ok();
+}
+
+calibatt_status calibatt_validate_csr(const int32_t* row_ptr, const int32_t* col_idx, int rows,
+                                      int nkb_valid, int64_t nnz) {
+  if (!row_ptr) return fail(CALIBATT_ERR_NULL, "row_ptr must be non-NULL");
+  if (rows < 0 || nkb_valid < 0 || nnz < 0) return fail(CALIBATT_ERR_SHAPE, "rows, nkb_valid and nnz must be >= 0");
+  if (nnz > 0 && !col_idx) return fail(CALIBATT_ERR_NULL, "col_idx must be non-NULL when nnz > 0");
+  if (row_ptr[0] != 0) return fail(CALIBATT_ERR_CSR, "row_ptr[0]=%d, expected 0", row_ptr[0]);
+  for (int r = 0; r < rows; ++r) {
+    const int32_t a = row_ptr[r], b = row_ptr[r + 1];
+    if (b < a) return fail(CALIBATT_ERR_CSR, "row_ptr decreases at row %d (%d -> %d)", r, a, b);
+    if (b > nnz) return fail(CALIBATT_ERR_CSR, "row_ptr[%d]=%d exceeds nnz=%lld", r + 1, b, (long long)nnz);
+    for (int32_t i = a; i < b; ++i) {
+      const int32_t kb = col_idx[i];
+      if (kb < 0 || kb >= nkb_valid) return fail(CALIBATT_ERR_CSR, "row %d: column %d outside [0, %d)", r, kb, nkb_valid);
+      if (i > a && kb <= col_idx[i - 1])
+        return fail(CALIBATT_ERR_CSR, "row %d: columns not strictly ascending (%d after %d)", r, kb, col_idx[i - 1]);
+    }
+  }
+  if (row_ptr[rows] != nnz) return fail(CALIBATT_ERR_CSR, "row_ptr[rows]=%d differs from nnz=%lld", row_ptr[rows], (long long)nnz);
+  return ok();
+}
+
+const char* calibatt_status_string(calibatt_status s) {
+  switch (s) {
+    case CALIBATT_OK: return "ok";
+    case CALIBATT_ERR_NULL: return "null pointer";
+    case CALIBATT_ERR_SHAPE: return "bad shape";
+    case CALIBATT_ERR_DTYPE: return "bad dtype";
+    case CALIBATT_ERR_ALIGN: return "misaligned pointer";
+    case CALIBATT_ERR_CSR: return "malformed kept-block list";
+    case CALIBATT_ERR_CAPACITY: return "output buffer too small";
+    case CALIBATT_ERR_UNSUPPORTED: return "unsupported combination";
+    case CALIBATT_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* calibatt_last_error(void) { return g_last_error.c_str(); }
+
+int calibatt_version(void) { return CALIBATT_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,180 @@
+// Mask compile and work order for gfx950.
+//
+// Per-prompt keep rule (Fig. 5(a) caption: the top key blocks of each query
+// block are kept): key block kb < nkb_valid of row (h, qb) is kept for prompt
+// p when fewer than K blocks precede it in the total order (mass descending,
+// kb ascending, NaN last).  The rank is counted exactly by comparing against
+// every block of the row held in LDS, so ties resolve the same way on every
+// run.  Agreement (Fig. 3(b) caption): a block enters the compiled list when
+// at least min_agree prompts keep it.  Lists are CSR rows r = h*nqb + qb with
+// ascending columns (the abstract compiles one pattern per layer, head and
+// timestep).
+//
+// Kernels: keep_agree (one workgroup per row: per-prompt ranks, counts,
+// agreed flags, kept count), row_offsets (one workgroup: exclusive scan of
+// the kept counts), fill_columns (one workgroup per row: ordered compaction
+// of the agreed flags), lpt_order (one workgroup per head: rank of each row
+// by kept count descending, index ascending).
+#include "tiles.h"
+#include "launch.h"
+
+namespace calibatt {
+
+// True when (a, ia) precedes (b, ib): non-NaN first, larger mass first, smaller index first.
+__device__ __forceinline__ bool precedes(float a, int ia, float b, int ib) {
+  const bool na = a != a, nb = b != b;
+  if (na != nb) return nb;
+  if (!na && a != b) return a > b;
+  return ia < ib;
+}
+
+constexpr int kRowThreads = 256;
+constexpr int kPerThread = kMaxKeyBlocks / kRowThreads;
+
+__global__ __launch_bounds__(kRowThreads) void keep_agree_kernel(
+    const float* __restrict__ mass, int P, int rows, int nkb, int nkb_valid, int K, int min_agree,
+    uint8_t* __restrict__ keep, int32_t* __restrict__ counts) {
+  __shared__ float m[kMaxKeyBlocks];
+  __shared__ int wsum[kRowThreads / 64];
+  const int r = blockIdx.x;
+  int cnt[kPerThread];
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) cnt[j] = 0;
+  for (int p = 0; p < P; ++p) {
+    __syncthreads();
+    const float* src = mass + ((size_t)p * rows + r) * nkb;
+    for (int kb = threadIdx.x; kb < nkb_valid; kb += kRowThreads) m[kb] = src[kb];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int kb = threadIdx.x + j * kRowThreads;
+      if (kb < nkb_valid) {
+        const float x = m[kb];
+        int rank = 0;
+        for (int o = 0; o < nkb_valid; ++o) rank += precedes(m[o], o, x, kb) ? 1 : 0;
+        cnt[j] += rank < K ? 1 : 0;
+      }
+    }
+  }
+  int kept = 0;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    const int kb = threadIdx.x + j * kRowThreads;
+    if (kb < nkb) {
+      const bool on = kb < nkb_valid && cnt[j] >= min_agree;
+      keep[(size_t)r * nkb + kb] = on ? 1 : 0;
+      kept += on ? 1 : 0;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) kept += __shfl_xor(kept, off);
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = kept;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int t = 0;
+    for (int i = 0; i < kRowThreads / 64; ++i) t += wsum[i];
+    counts[r] = t;
+  }
+}
+
+constexpr int kScanThreads = 1024;
+
+__global__ __launch_bounds__(kScanThreads) void row_offsets_kernel(const int32_t* __restrict__ counts,
+                                                                   int rows,
+                                                                   int32_t* __restrict__ row_ptr) {
+  __shared__ int part[kScanThreads];
+  const int per = (rows + kScanThreads - 1) / kScanThreads;
+  const int lo = threadIdx.x * per;
+  const int hi = min(lo + per, rows);
+  int s = 0;
+  for (int i = lo; i < hi; ++i) s += counts[i];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int off = 1; off < kScanThreads; off <<= 1) {
+    const int v = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int run = part[threadIdx.x] - s;   // exclusive prefix of this thread's chunk
+  if (threadIdx.x == 0) row_ptr[0] = 0;
+  for (int i = lo; i < hi; ++i) {
+    run += counts[i];
+    row_ptr[i + 1] = run;
+  }
+}
+
+__global__ __launch_bounds__(kRowThreads) void fill_columns_kernel(const uint8_t* __restrict__ keep,
+                                                                   int nkb,
+                                                                   const int32_t* __restrict__ row_ptr,
+                                                                   int32_t* __restrict__ col_idx) {
+  __shared__ int pre[kRowThreads];
+  const int r = blockIdx.x;
+  // thread t owns the contiguous key blocks [t*kPerThread, t*kPerThread + kPerThread)
+  const int kb0 = threadIdx.x * kPerThread;
+  bool on[kPerThread];
+  int n = 0;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    const int kb = kb0 + j;
+    on[j] = kb < nkb && keep[(size_t)r * nkb + kb] != 0;
+    n += on[j] ? 1 : 0;
+  }
+  pre[threadIdx.x] = n;
+  __syncthreads();
+  for (int off = 1; off < kRowThreads; off <<= 1) {
+    const int v = threadIdx.x >= off ? pre[threadIdx.x - off] : 0;
+    __syncthreads();
+    pre[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int pos = row_ptr[r] + pre[threadIdx.x] - n;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j)
+    if (on[j]) col_idx[pos++] = kb0 + j;
+}
+
+__global__ __launch_bounds__(kRowThreads) void lpt_order_kernel(const int32_t* __restrict__ row_ptr,
+                                                                int nqb,
+                                                                int32_t* __restrict__ work_order) {
+  __shared__ int cost[kMaxKeyBlocks];
+  const int h = blockIdx.x;
+  const int r0 = h * nqb;
+  for (int qb = threadIdx.x; qb < nqb; qb += kRowThreads) cost[qb] = row_ptr[r0 + qb + 1] - row_ptr[r0 + qb];
+  __syncthreads();
+  for (int qb = threadIdx.x; qb < nqb; qb += kRowThreads) {
+    const int cq = cost[qb];
+    int rank = 0;
+    for (int o = 0; o < nqb; ++o) {
+      const int co = cost[o];
+      rank += (co > cq || (co == cq && o < qb)) ? 1 : 0;
+    }
+    work_order[r0 + rank] = r0 + qb;
+  }
+}
+
+hipError_t launch_compile_count(const CompileArgs& a, hipStream_t st) {
+  const int rows = a.H * a.nqb;
+  hipLaunchKernelGGL(keep_agree_kernel, dim3(rows), dim3(kRowThreads), 0, st, a.mass, a.P, rows,
+                     a.nkb, a.nkb_valid, a.keep_topk, a.min_agree, a.keep_ws, a.count_ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(row_offsets_kernel, dim3(1), dim3(kScanThreads), 0, st, (const int32_t*)a.count_ws,
+                     rows, a.row_ptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_compile_fill(const CompileArgs& a, hipStream_t st) {
+  const int rows = a.H * a.nqb;
+  hipLaunchKernelGGL(fill_columns_kernel, dim3(rows), dim3(kRowThreads), 0, st,
+                     (const uint8_t*)a.keep_ws, a.nkb, (const int32_t*)a.row_ptr, a.col_idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_schedule(const int32_t* row_ptr, int H, int nqb, int32_t* work_order,
+                           hipStream_t st) {
+  hipLaunchKernelGGL(lpt_order_kernel, dim3(H), dim3(kRowThreads), 0, st, row_ptr, nqb, work_order);
+  return hipGetLastError();
+}
+
+}  // namespace calibatt

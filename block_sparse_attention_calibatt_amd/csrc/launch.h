@@ -1,0 +1,58 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+// Arguments arrive here already validated on the host.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace calibatt {
+
+struct AttnArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  const int32_t* row_ptr;      // unused by the dense kernel
+  const int32_t* col_idx;      // unused by the dense kernel
+  const int32_t* work_order;   // may be null
+  int32_t* queue;              // may be null (one workgroup per row)
+  int B, H, L, seq_len, d, block, nkb_valid;
+  float scale;
+  bool dtype_f32;
+  int num_cu;
+};
+
+hipError_t launch_attention(const AttnArgs& a, bool dense, hipStream_t st);
+
+struct MassArgs {
+  const void* Q;
+  const void* K;
+  float* lse;
+  float* mass;
+  int B, H, L, seq_len, d, block, nkb_valid;
+  float scale;
+};
+
+hipError_t launch_block_mass(const MassArgs& a, hipStream_t st);
+
+struct CompileArgs {
+  const float* mass;
+  int P, H, nqb, nkb, nkb_valid, keep_topk, min_agree;
+  int32_t* row_ptr;
+  int32_t* col_idx;
+  uint8_t* keep_ws;   // [H*nqb*nkb]
+  int32_t* count_ws;  // [H*nqb]
+};
+
+// Enqueues the per-row keep/agree pass and the row-offset scan.
+hipError_t launch_compile_count(const CompileArgs& a, hipStream_t st);
+// Enqueues the column fill (after the caller checked the kept count fits).
+hipError_t launch_compile_fill(const CompileArgs& a, hipStream_t st);
+
+hipError_t launch_schedule(const int32_t* row_ptr, int H, int nqb, int32_t* work_order,
+                           hipStream_t st);
+
+constexpr int kMaxKeyBlocks = 1024;   // calibration and compile kernels keep a row in LDS
+
+}  // namespace calibatt

@@ -1,0 +1,144 @@
+// Shared device helpers for the gfx950 (CDNA4) attention and calibration kernels.
+//
+// Matrix-core layouts (v_mfma_f32_32x32x16_bf16, wave of 64 lanes; lane l,
+// half g = l / 32, column c = l % 32):
+//   A operand (32 x 16): lane holds A[c][8g .. 8g+7]
+//   B operand (16 x 32): lane holds B[8g .. 8g+7][c]
+//   C/D       (32 x 32): lane holds D[8*(r/4) + 4g + r%4][c], r = 0..15
+//
+// Scores are computed transposed, S^T = K * Q^T, so that every lane owns one
+// query (column c) and the softmax over keys needs only lane-local work plus
+// one exchange with lane l^32.  The K rows fed to the A operand are permuted
+// (bits 2 and 3 of the row index swapped) so that lane half g ends up holding
+// keys 16*(r/8) + 8g + (r%8) of each 32-key slice: exactly the B-operand
+// layout the P*V product needs, with no data movement between the products.
+//
+// LDS tiles are rows of 16-byte chunks with an XOR swizzle on the chunk
+// index, so that the matrix-core operand reads (16 consecutive rows, one
+// chunk) and the transposed V writes (16 rows spaced 8 apart) both spread
+// over all bank groups.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace calibatt {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Chunk swizzle for a row of CH 16-byte chunks (CH = 16 or 8).
+template <int CH>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (CH == 16) {
+    return (row & 15) ^ ((row >> 4) & 7);
+  } else {
+    return ((row >> 1) & 7) ^ ((row >> 4) & 7);
+  }
+}
+
+template <int CH>
+__device__ __forceinline__ int chunk_index(int row, int chunk) {
+  return row * CH + (chunk ^ swz<CH>(row));
+}
+
+// Row of the K tile read by lane column c for the A operand: bits 2 and 3 swapped.
+__device__ __forceinline__ int qk_row_perm(int c) {
+  return (c & 0x13) | ((c & 4) << 1) | ((c & 8) >> 1);
+}
+
+// Key (within a 32-key slice) held in accumulator register r by lane half g.
+__device__ __forceinline__ int slice_key(int r, int g) { return 16 * (r >> 3) + 8 * g + (r & 7); }
+
+// K tile [BLK keys][D] bf16, row-major in HBM -> swizzled LDS.  NT threads.
+template <int D, int BLK, int NT>
+__device__ __forceinline__ void load_k_tile(const bf16* __restrict__ src, u32x4* __restrict__ lds) {
+  constexpr int CH = D / 8;
+  constexpr int PER = BLK * CH / NT;
+  static_assert(PER * NT == BLK * CH, "tile must split evenly over the threads");
+  u32x4 r[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int idx = threadIdx.x + i * NT;
+    r[i] = *reinterpret_cast<const u32x4*>(src + (idx / CH) * D + (idx % CH) * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int idx = threadIdx.x + i * NT;
+    lds[chunk_index<CH>(idx / CH, idx % CH)] = r[i];
+  }
+}
+
+// V tile [BLK keys][D] bf16 in HBM -> transposed Vt [D][BLK] in swizzled LDS.
+// Each thread moves 8x8 sub-blocks: 8 row loads of 16 bytes, a register
+// transpose with byte permutes, 8 row stores of 16 bytes.
+template <int D, int BLK, int NT>
+__device__ __forceinline__ void load_v_tile_t(const bf16* __restrict__ src, u32x4* __restrict__ lds) {
+  constexpr int DG = D / 8;
+  constexpr int KG = BLK / 8;
+  constexpr int CHV = BLK / 8;
+  for (int sb = threadIdx.x; sb < DG * KG; sb += NT) {
+    const int dg = sb % DG, kg = sb / DG;
+    u32x4 in[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      in[i] = *reinterpret_cast<const u32x4*>(src + (kg * 8 + i) * D + dg * 8);
+    u32x4 out[8];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t x = in[2 * j][e2], y = in[2 * j + 1][e2];
+        out[2 * e2][j] = __builtin_amdgcn_perm(y, x, 0x05040100u);
+        out[2 * e2 + 1][j] = __builtin_amdgcn_perm(y, x, 0x07060302u);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) lds[chunk_index<CHV>(dg * 8 + e, kg)] = out[e];
+  }
+}
+
+// S^T for one wave: BLK keys x 32 queries, as BLK/32 accumulators of 32x32.
+template <int D, int BLK>
+__device__ __forceinline__ void qk_tile(const u32x4* __restrict__ ldsK, const bf16x8* qreg,
+                                        f32x16* sacc, int g, int c) {
+  constexpr int CH = D / 8;
+  const int prow = qk_row_perm(c);
+#pragma unroll
+  for (int mt = 0; mt < BLK / 32; ++mt) {
+    f32x16 acc = {};
+    const int row = 32 * mt + prow;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const u32x4 a = ldsK[chunk_index<CH>(row, 2 * s + g)];
+      acc = mfma_bf16(__builtin_bit_cast(bf16x8, a), qreg[s], acc);
+    }
+    sacc[mt] = acc;
+  }
+}
+
+// Max with the partner lane l^32 (same query, other half of the keys).
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+}  // namespace calibatt

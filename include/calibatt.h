@@ -1,0 +1,200 @@
+/*
+ * calibatt.h - C ABI of the MI355X (gfx950) calibrated block-sparse attention library.
+ *
+ * The method is CalibAtt ("Accelerating Text-to-Video Generation with
+ * Calibrated Sparse Attention", arXiv 2603.05503).  Offline, calibration
+ * prompts are run through the model, the post-softmax attention maps are
+ * pooled to blocks, the top key blocks of every query block are kept per
+ * prompt, and blocks that enough prompts agree on form a mask per (layer,
+ * head, timestep).  At inference the kept blocks are computed densely and the
+ * rest are skipped, i.e. their keys are absent from the softmax.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers are DEVICE pointers unless the comment says (host).
+ * - Q, K, V, O are [B, H, L, d] row-major and contiguous (d fastest).  L is
+ *   the padded token count and must be a multiple of `block`; tokens
+ *   t >= seq_len are padding: they are never keys, and their output rows are
+ *   written as zero.
+ * - One block is `block` tokens; query blocks and key blocks have the same
+ *   size.  nqb = nkb = L / block; nkb_valid = ceil(seq_len / block).
+ * - A mask set is CSR over rows r = h * nqb + qb (h-major): the kept key
+ *   blocks of row r are col_idx[row_ptr[r] .. row_ptr[r+1]), ascending,
+ *   unique, each < nkb_valid.  row_ptr has H*nqb+1 int32 entries, row_ptr[0]
+ *   = 0.  One mask set serves every batch entry.
+ * - Ownership: the caller allocates and frees every buffer.  The library keeps
+ *   no pointer after a call returns and holds no global state besides a
+ *   per-device property cache and a thread-local error message.
+ * - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL is the
+ *   default stream) and the call returns after enqueueing, except where a
+ *   comment says it synchronises.
+ * - Errors: argument checks run on the host before anything is enqueued; on
+ *   an argument error nothing is written.  A failed HIP call returns
+ *   CALIBATT_ERR_HIP.  calibatt_last_error() gives the detail.  A malformed
+ *   CSR passed to a device entry point is undefined behaviour on the device:
+ *   check untrusted lists with calibatt_validate_csr first.
+ * - Supported shapes: d in {64, 128}; block in {64, 128}; bf16 or f32
+ *   inputs; Q/K/V/O 16-byte aligned; B, H >= 1; 0 < seq_len <= L;
+ *   B * H * L * d < 2^31.
+ */
+#ifndef CALIBATT_H
+#define CALIBATT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CALIBATT_VERSION 100 /* major * 100 + minor */
+
+typedef enum {
+  CALIBATT_OK = 0,
+  CALIBATT_ERR_NULL = 1,        /* a required pointer is NULL */
+  CALIBATT_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+  CALIBATT_ERR_DTYPE = 3,       /* unknown dtype code */
+  CALIBATT_ERR_ALIGN = 4,       /* a pointer is not aligned as required */
+  CALIBATT_ERR_CSR = 5,         /* a kept-block list is malformed */
+  CALIBATT_ERR_CAPACITY = 6,    /* an output buffer is too small */
+  CALIBATT_ERR_UNSUPPORTED = 7, /* a valid but unimplemented combination */
+  CALIBATT_ERR_HIP = 8          /* the HIP runtime reported an error */
+} calibatt_status;
+
+typedef enum { CALIBATT_BF16 = 0, CALIBATT_F32 = 1 } calibatt_dtype;
+
+/*
+ * Block-sparse attention forward (inference step).
+ * Pages: abstract (selected connections computed densely, unselected ones
+ * skipped) and Fig. 5(b) caption (block masks loaded, unset blocks not
+ * computed).  For every batch entry b, head h and query token i < seq_len in
+ * query block qb (row r = h*nqb + qb), with J_i the valid tokens of the kept
+ * key blocks of row r:
+ *     O[b,h,i,:] = sum_{j in J_i} softmax_j(scale * Q[b,h,i,:] . K[b,h,j,:]) V[b,h,j,:]
+ * A row with no kept block, and every padded query row, is written as zero.
+ *
+ *   Q, K, V     [B, H, L, d] inputs of dtype `dt` (device).
+ *   O           [B, H, L, d] output of dtype `dt` (device); fully written.
+ *   row_ptr     [H*nqb + 1] int32 CSR row offsets (device).
+ *   col_idx     [row_ptr[H*nqb]] int32 kept key blocks (device).
+ *   block       tokens per block (64 or 128).
+ *   scale       softmax scale applied to q.k (usually 1/sqrt(d)).
+ *   work_order  optional [H*nqb] int32 permutation of rows giving the order
+ *               rows are started in (see calibatt_build_schedule); NULL =
+ *               natural order.  The result does not depend on it (each row
+ *               is reduced by one workgroup in col_idx order).
+ *   queue_ws    optional int32 workspace of >= 16 entries (device), 16-byte
+ *               aligned.  Non-NULL selects the persistent launch: one grid
+ *               that fills the GPU pulls rows from an atomic queue kept in
+ *               queue_ws (reset on `stream` by the call itself); NULL = one
+ *               workgroup per row.  Calls that share a queue_ws must not
+ *               overlap in time.
+ *   nnz         number of entries of col_idx (= row_ptr[H*nqb]); used only
+ *               for the host-side size check.
+ * The bf16 path computes q.k and p.v on bf16 matrix cores with float32
+ * accumulation and a float32 softmax; probabilities are rounded to bf16
+ * before the p.v product; O is rounded to bf16.  The f32 path is float32
+ * throughout.
+ */
+calibatt_status calibatt_sparse_attn_fwd(const void* Q, const void* K, const void* V, void* O,
+                                         const int32_t* row_ptr, const int32_t* col_idx,
+                                         int block, float scale, int B, int H, int L,
+                                         int seq_len, int d, calibatt_dtype dt,
+                                         const int32_t* work_order, int32_t* queue_ws,
+                                         int64_t nnz, void* stream);
+
+/*
+ * Dense attention forward: the same computation with every valid key block
+ * kept (the pages' dense baseline, Table 1 and Table S6).  Arguments as above.
+ */
+calibatt_status calibatt_dense_attn_fwd(const void* Q, const void* K, const void* V, void* O,
+                                        int block, float scale, int B, int H, int L, int seq_len,
+                                        int d, calibatt_dtype dt, void* stream);
+
+/*
+ * Calibration pooling: post-softmax attention mass per (query block, key
+ * block).  Pages: Fig. 2 caption (block-level view of post-softmax maps),
+ * Table S5 caption (block energies on the calibration prompts).  With the
+ * full softmax over the valid keys j < seq_len,
+ *     mass[b,h,qb,kb] = sum_{i in qb, i < seq_len} sum_{j in kb, j < seq_len}
+ *                       softmax_j(scale * Q[b,h,i,:] . K[b,h,j,:])
+ * so each valid query contributes 1 to its row of blocks.
+ *
+ *   Q, K     [B, H, L, d] inputs of dtype `dt` (device).
+ *   lse_ws   [B, H, L] float32 workspace (device); on return it holds
+ *            log(sum_{j < seq_len} exp(scale * q_i . k_j)) per query (natural
+ *            log; padded rows hold -inf).
+ *   mass     [B, H, nqb, nkb] float32 output (device); fully written.
+ * Two passes are enqueued: row log-sum-exp, then tile sums of exp(s - lse).
+ */
+calibatt_status calibatt_block_mass(const void* Q, const void* K, int B, int H, int L, int seq_len,
+                                    int d, calibatt_dtype dt, int block, float scale,
+                                    float* lse_ws, float* mass, void* stream);
+
+/*
+ * Mask compile: per-prompt top-K key blocks -> cross-prompt agreement -> CSR.
+ * Pages: Fig. 5(a) caption (top key blocks per query block, aggregated
+ * across prompts into a mask dictionary), Fig. 3(b) caption (per-block keep
+ * frequency across prompts, agreement threshold), abstract (patterns compiled
+ * per layer, head and timestep).
+ * For prompt p and row (h, qb) the key block kb < nkb_valid is kept when fewer
+ * than keep_topk blocks precede it in the order (mass descending, kb
+ * ascending; NaN last).  A block enters the CSR when at least min_agree
+ * prompts keep it.  Rows with no agreed block stay empty.
+ *
+ *   mass       [P, H, nqb, nkb] float32 (device), e.g. calibatt_block_mass
+ *              outputs of P prompts stacked.
+ *   nkb_valid  key blocks eligible (<= nkb; ceil(seq_len / block)).
+ *   keep_topk  K >= 0 (K >= nkb_valid keeps every eligible block).
+ *   min_agree  0 <= min_agree <= P (ceil(rho * P) for agreement rho).
+ *   row_ptr    [H*nqb + 1] int32 output (device).
+ *   col_idx    [nnz_cap] int32 output (device).
+ *   nnz_out    (host) int64: number of kept blocks, set on OK and on
+ *              CALIBATT_ERR_CAPACITY (then col_idx is not written; call
+ *              again with a larger buffer).  H*nqb*nkb_valid always suffices.
+ *   ws         device workspace of calibatt_compile_ws_bytes(...) bytes,
+ *              16-byte aligned.
+ * Synchronises `stream` once (to read the kept count back to the host).
+ */
+calibatt_status calibatt_compile_masks(const float* mass, int P, int H, int nqb, int nkb,
+                                       int nkb_valid, int keep_topk, int min_agree,
+                                       int32_t* row_ptr, int32_t* col_idx, int64_t nnz_cap,
+                                       int64_t* nnz_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes calibatt_compile_masks needs for these sizes (0 on bad sizes). */
+size_t calibatt_compile_ws_bytes(int P, int H, int nqb, int nkb);
+
+/*
+ * Work order for calibatt_sparse_attn_fwd.  The pages do not describe a
+ * scheduler; rows keep very different numbers of blocks (Fig. S9's
+ * skip-list row lengths), so rows start longest first: heads ascending,
+ * inside a head rows by kept count descending, ties by ascending qb.
+ *   row_ptr     [H*nqb + 1] int32 (device).
+ *   work_order  [H*nqb] int32 output (device): row indices h*nqb + qb.
+ */
+calibatt_status calibatt_build_schedule(const int32_t* row_ptr, int H, int nqb,
+                                        int32_t* work_order, void* stream);
+
+/*
+ * Host-side CSR check (no GPU use).  row_ptr (host) [rows + 1], col_idx
+ * (host) [nnz].  Returns CALIBATT_OK, or CALIBATT_ERR_CSR naming the first
+ * defect (row_ptr[0] != 0, decreasing offsets, row_ptr[rows] != nnz, a column
+ * out of [0, nkb_valid), columns not strictly ascending).
+ */
+calibatt_status calibatt_validate_csr(const int32_t* row_ptr, const int32_t* col_idx, int rows,
+                                      int nkb_valid, int64_t nnz);
+
+/* Static text for a status code. */
+const char* calibatt_status_string(calibatt_status s);
+
+/* Detail of the last non-OK status returned on this thread ("" if none). */
+const char* calibatt_last_error(void);
+
+/* CALIBATT_VERSION of the built library. */
+int calibatt_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CALIBATT_H */

@@ -1,0 +1,124 @@
+"""The C-ABI library loads, exports what include/calibatt.h declares, and
+rejects bad arguments on the host before any GPU work (no GPU needed)."""
+
+import ctypes
+import subprocess
+
+import numpy as np
+import pytest
+
+import block_sparse_attention_calibatt_amd as cal
+from block_sparse_attention_calibatt_amd import _lib
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return cal.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _lib.header_symbols()
+    assert len(names) == 10
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for n in names:
+        assert n in exported, f"{n} is declared but not exported"
+        getattr(lib, n)
+    assert set(_lib.SIGNATURES) == set(names), "binding and header disagree"
+
+
+def test_version_and_strings(lib):
+    assert cal.calibatt_version() == 100
+    for code, name in _lib.STATUS.items():
+        assert cal.calibatt_status_string(code) != "unknown status"
+    assert cal.calibatt_status_string(99) == "unknown status"
+
+
+V = ctypes.c_void_p
+P16, P32, P48, P64 = V(16), V(32), V(48), V(64)     # aligned fake addresses, never dereferenced
+
+
+def _sparse(lib, **kw):
+    a = dict(Q=P16, K=P32, V=P48, O=P64, row_ptr=V(128), col_idx=V(256), block=128, scale=0.1, B=1, H=2,
+             L=1024, seq_len=1000, d=128, dt=0, work_order=None, queue_ws=None, nnz=10, stream=None)
+    a.update(kw)
+    return lib.calibatt_sparse_attn_fwd(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Q=None), 1),
+    (dict(O=None), 1),
+    (dict(row_ptr=None), 1),
+    (dict(col_idx=None), 1),
+    (dict(Q=V(17)), 4),
+    (dict(row_ptr=V(130)), 4),
+    (dict(queue_ws=V(132)), 4),
+    (dict(dt=7), 3),
+    (dict(block=96), 7),
+    (dict(d=96), 7),
+    (dict(L=1000), 2),
+    (dict(seq_len=0), 2),
+    (dict(seq_len=1025), 2),
+    (dict(B=0), 2),
+    (dict(H=-1), 2),
+    (dict(B=1024, H=64, L=65536), 2),
+    (dict(nnz=-1), 5),
+    (dict(nnz=2 * 8 * 8 + 1), 5),
+])
+def test_sparse_rejects(lib, kw, status):
+    assert _sparse(lib, **kw) == status
+    assert cal.calibatt_last_error() != ""
+
+
+def test_dense_and_mass_reject(lib):
+    assert lib.calibatt_dense_attn_fwd(None, P32, P48, P64, 128, 0.1, 1, 1, 256, 256, 128, 0, None) == 1
+    assert lib.calibatt_dense_attn_fwd(P16, P32, P48, P64, 32, 0.1, 1, 1, 256, 256, 128, 0, None) == 7
+    assert lib.calibatt_block_mass(P16, P32, 1, 1, 256, 256, 128, 1, 128, 0.1, P48, P64, None) == 7, "f32 mass"
+    assert lib.calibatt_block_mass(P16, P32, 1, 1, 256, 300, 128, 0, 128, 0.1, P48, P64, None) == 2
+    assert lib.calibatt_block_mass(P16, None, 1, 1, 256, 256, 128, 0, 128, 0.1, P48, P64, None) == 1
+    assert lib.calibatt_block_mass(P16, P32, 1, 1, 128 * 2048, 256, 64, 0, 128, 0.1, P48, P64, None) == 7
+
+
+def test_compile_and_schedule_reject(lib):
+    n = ctypes.c_int64(0)
+    ws = lib.calibatt_compile_ws_bytes(8, 40, 256, 256)
+    assert ws == 40 * 256 * 256 + 40 * 256 * 4
+    assert lib.calibatt_compile_ws_bytes(0, 1, 1, 1) == 0
+    base = dict(mass=P16, P=8, H=40, nqb=256, nkb=256, nkb_valid=256, K=64, t=4, row_ptr=P32, col_idx=P48,
+                cap=10, nnz=ctypes.byref(n), ws=P64, ws_bytes=ws, stream=None)
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        return lib.calibatt_compile_masks(*a.values())
+    assert call(mass=None) == 1
+    assert call(P=0) == 2
+    assert call(t=9) == 2
+    assert call(t=-1) == 2
+    assert call(K=-1) == 2
+    assert call(nkb_valid=257) == 2
+    assert call(nkb=2048, nkb_valid=2048) == 7
+    assert call(ws_bytes=ws - 1) == 6
+    assert call(ws=V(72)) == 4
+    assert lib.calibatt_build_schedule(None, 1, 1, P16, None) == 1
+    assert lib.calibatt_build_schedule(P16, 0, 1, P32, None) == 2
+    assert lib.calibatt_build_schedule(P16, 1, 4096, P32, None) == 7
+
+
+def test_validate_csr(lib):
+    ok_rp = np.array([0, 2, 2, 5], np.int32)
+    ok_ci = np.array([0, 3, 1, 2, 7], np.int32)
+    cal.calibatt_validate_csr(ok_rp, ok_ci, 3, 8)
+    bad = [
+        (np.array([1, 2, 2, 5], np.int32), ok_ci),             # row_ptr[0] != 0
+        (np.array([0, 3, 2, 5], np.int32), ok_ci),             # decreasing
+        (ok_rp, np.array([0, 3, 1, 2, 8], np.int32)),          # column out of range
+        (ok_rp, np.array([0, 3, 2, 1, 7], np.int32)),          # not ascending
+        (ok_rp, np.array([0, 3, 1, 1, 7], np.int32)),          # duplicate
+        (ok_rp, np.array([0, -1, 1, 2, 7], np.int32)),         # negative
+        (ok_rp, ok_ci[:4]),                                    # nnz mismatch
+    ]
+    for rp, ci in bad:
+        with pytest.raises(cal.CalibattError) as e:
+            cal.calibatt_validate_csr(rp, ci, 3, 8)
+        assert e.value.status == 5 or e.value.status == 1

@@ -1,0 +1,207 @@
+"""GPU parity: block-sparse and dense attention forward vs the float64 oracle.
+
+Tolerances: max |O_gpu - O_oracle| <= 1e-4 for float32 inputs and <= 2e-2 for
+bfloat16 inputs (float32 accumulation; probabilities and O rounded to bf16)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import block_sparse_attention_calibatt_amd as cal
+from tests.gpu_util import say, to_dev, i32, small_cfg, inputs, err
+
+pytestmark = pytest.mark.gpu
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+TDT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def run_sparse(q, k, v, rp, ci, cfg, work_order=None, persistent=False):
+    dt = TDT[cfg.dtype]
+    Q, K, V = (to_dev(x, dt) for x in (q, k, v))
+    O = torch.full_like(Q, float("nan"))
+    RP, CI = i32(rp), i32(ci if len(ci) else np.zeros(1, np.int32))[: len(ci)]
+    WO = None if work_order is None else i32(work_order)
+    qws = torch.zeros(16, dtype=torch.int32, device="cuda:0") if persistent else None
+    cal.calibatt_sparse_attn_fwd(Q, K, V, O, RP, CI, cfg.block, cfg.scale, cfg.S, WO, qws)
+    torch.cuda.synchronize()
+    return O
+
+
+def run_dense(q, k, v, cfg):
+    dt = TDT[cfg.dtype]
+    Q, K, V = (to_dev(x, dt) for x in (q, k, v))
+    O = torch.full_like(Q, float("nan"))
+    cal.calibatt_dense_attn_fwd(Q, K, V, O, cfg.block, cfg.scale, cfg.S)
+    torch.cuda.synchronize()
+    return O
+
+
+def test_tiny_f32_config(gpu):
+    cfg = synth.get_config("tiny")
+    say("case: tiny f32 config", cfg)
+    q, k, v = inputs(cfg)
+    rp, ci = synth.csr_for_config(cfg)
+    ref = oracle.sparse_attention_gather(q, k, v, rp, ci, cfg.block, cfg.scale, cfg.S)
+    for persistent in (False, True):
+        O = run_sparse(q, k, v, rp, ci, cfg, persistent=persistent)
+        e = err(O, ref)
+        say(f"  persistent={persistent} max err {e:.3e}")
+        assert e <= TOL["f32"]
+
+
+SHAPES = [
+    # B, H, L, S, d, block, dtype
+    (1, 2, 1024, 1000, 128, 128, "bf16"),
+    (2, 1, 768, 700, 128, 128, "bf16"),
+    (1, 2, 512, 449, 64, 64, "bf16"),
+    (1, 2, 1024, 1000, 128, 64, "bf16"),
+    (1, 2, 1024, 1000, 64, 128, "bf16"),
+    (1, 2, 512, 449, 64, 64, "f32"),
+    (1, 1, 512, 500, 128, 128, "f32"),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_sparse_small(gpu, shape):
+    B, H, L, S, d, block, dtype = shape
+    cfg = small_cfg(B=B, H=H, L=L, S=S, d=d, block=block, dtype=dtype, grid=(4, 8, 16) if dtype == "bf16" else None)
+    say("case: sparse small", shape)
+    q, k, v = inputs(cfg)
+    rng = np.random.default_rng(sum(shape[:6]))
+    rp, ci = synth.random_csr(rng, H, L // block, cfg.nkb_valid, 0.4, empty_rows=1, full_rows=1)
+    ref = oracle.sparse_attention_gather(q, k, v, rp, ci, block, cfg.scale, S)
+    for persistent in (False, True):
+        O = run_sparse(q, k, v, rp, ci, cfg, persistent=persistent)
+        e = err(O, ref)
+        say(f"  persistent={persistent} max err {e:.3e}")
+        assert e <= TOL[dtype]
+
+
+@pytest.mark.parametrize("shape", SHAPES[:3] + SHAPES[5:6], ids=lambda s: "x".join(map(str, s)))
+def test_dense_small(gpu, shape):
+    B, H, L, S, d, block, dtype = shape
+    cfg = small_cfg(B=B, H=H, L=L, S=S, d=d, block=block, dtype=dtype)
+    say("case: dense small", shape)
+    q, k, v = inputs(cfg)
+    ref = oracle.dense_attention(q, k, v, cfg.scale, S)
+    O = run_dense(q, k, v, cfg)
+    e = err(O, ref)
+    say(f"  max err {e:.3e}")
+    assert e <= TOL[dtype]
+
+
+def test_all_kept_sparse_is_dense_bitwise(gpu):
+    cfg = small_cfg(H=3, L=1024, S=1000)
+    say("case: all-kept sparse vs dense, bitwise")
+    q, k, v = inputs(cfg)
+    nqb, nkv = cfg.nqb, cfg.nkb_valid
+    rp = (np.arange(cfg.rows + 1) * nkv).astype(np.int32)
+    ci = np.tile(np.arange(nkv), cfg.rows).astype(np.int32)
+    a = run_sparse(q, k, v, rp, ci, cfg)
+    b = run_dense(q, k, v, cfg)
+    assert torch.equal(a, b)
+
+
+def test_schedule_invariance_bitwise(gpu):
+    cfg = small_cfg(H=4, L=2048, S=2040)
+    say("case: work order / persistence invariance")
+    q, k, v = inputs(cfg)
+    rng = np.random.default_rng(9)
+    rp, ci = synth.random_csr(rng, cfg.H, cfg.nqb, cfg.nkb_valid, 0.3, empty_rows=2, full_rows=2)
+    base = run_sparse(q, k, v, rp, ci, cfg)
+    lpt = oracle.lpt_work_order(rp, cfg.H, cfg.nqb)
+    orders = [lpt, lpt[::-1].copy(), rng.permutation(cfg.rows).astype(np.int32)]
+    for wo in orders:
+        for persistent in (False, True):
+            o = run_sparse(q, k, v, rp, ci, cfg, work_order=wo, persistent=persistent)
+            assert torch.equal(o, base)
+    again = run_sparse(q, k, v, rp, ci, cfg)
+    assert torch.equal(again, base), "repeat run"
+
+
+def test_empty_mask(gpu):
+    cfg = small_cfg(H=1, L=512, S=512)
+    say("case: every row empty")
+    q, k, v = inputs(cfg)
+    rp = np.zeros(cfg.rows + 1, np.int32)
+    ci = np.zeros(0, np.int32)
+    O = run_sparse(q, k, v, rp, ci, cfg, persistent=True)
+    assert torch.count_nonzero(O.float()).item() == 0
+
+
+def test_lone_valid_key(gpu):
+    """S = 449, block 64: rows keeping only the last block return v[448]."""
+    cfg = small_cfg(H=1, L=512, S=449, d=64, block=64)
+    say("case: lone valid key")
+    q, k, v = inputs(cfg)
+    rp = np.arange(cfg.rows + 1).astype(np.int32)
+    ci = np.full(cfg.rows, 7, np.int32)
+    O = run_sparse(q, k, v, rp, ci, cfg)
+    want = torch.from_numpy(v[0, 0, 448]).to(torch.bfloat16)
+    got = O[0, 0, :449].cpu()
+    assert torch.equal(got, want.expand_as(got))
+    assert torch.count_nonzero(O[0, 0, 449:].float()).item() == 0
+
+
+def _sample_items(cfg, rng, n):
+    items = [(0, 0, 0), (0, cfg.H - 1, cfg.nqb - 1)]
+    while len(items) < n:
+        items.append((int(rng.integers(cfg.B)), int(rng.integers(cfg.H)), int(rng.integers(cfg.nqb))))
+    return items
+
+
+def _full_size_check(cfg, rp, ci, seed_items, n_items, tol=2e-2):
+    q, k, v = inputs(cfg)
+    wo = oracle.lpt_work_order(rp, cfg.H, cfg.nqb)
+    O = run_sparse(q, k, v, rp, ci, cfg, work_order=wo, persistent=True)
+    items = _sample_items(cfg, np.random.default_rng(seed_items), n_items)
+    ref = oracle.sparse_attention_rows(q, k, v, rp, ci, cfg.block, cfg.scale, cfg.S, items)
+    worst = 0.0
+    for (b, h, qb), rr in zip(items, ref):
+        g = O[b, h, qb * cfg.block:(qb + 1) * cfg.block].float().cpu().numpy()
+        worst = max(worst, float(np.max(np.abs(g - rr))))
+    say(f"  {len(items)} sampled query blocks, max err {worst:.3e}")
+    assert worst <= tol
+    tail = O[:, :, cfg.S:].float()
+    assert torch.count_nonzero(tail).item() == 0, "padded rows must be zero"
+    assert torch.isfinite(O.float()).all()
+
+
+def test_wan_full_size_sampled(gpu):
+    cfg = synth.get_config("wan")
+    say("case: Wan full size, persistent + longest-first order, sampled rows")
+    rp, ci = synth.csr_for_config(cfg)
+    _full_size_check(cfg, rp, ci, 11, 24)
+
+
+def test_mochi_full_size_sampled(gpu):
+    cfg = synth.get_config("mochi")
+    say("case: Mochi full size, sampled rows")
+    rp, ci = synth.csr_for_config(cfg)
+    _full_size_check(cfg, rp, ci, 21, 24)
+
+
+def test_imbalance_sets_sampled(gpu):
+    cfg = synth.get_config("imbalance")
+    for t in (0, 49):
+        say(f"case: imbalance set {t}, sampled rows")
+        rp, ci = synth.csr_for_config(cfg, t)
+        _full_size_check(cfg, rp, ci, 31 + t, 12)
+
+
+def test_mochi_dense_sampled(gpu):
+    cfg = synth.get_config("mochi")
+    say("case: Mochi dense, sampled rows")
+    q, k, v = inputs(cfg)
+    O = run_dense(q, k, v, cfg)
+    nkv = cfg.nkb_valid
+    rp = (np.arange(cfg.rows + 1) * nkv).astype(np.int32)
+    ci = np.tile(np.arange(nkv), cfg.rows).astype(np.int32)
+    items = _sample_items(cfg, np.random.default_rng(5), 6)
+    ref = oracle.sparse_attention_rows(q, k, v, rp, ci, cfg.block, cfg.scale, cfg.S, items)
+    worst = max(float(np.max(np.abs(O[b, h, qb * 128:(qb + 1) * 128].float().cpu().numpy() - rr)))
+                for (b, h, qb), rr in zip(items, ref))
+    say(f"  max err {worst:.3e}")
+    assert worst <= 2e-2
