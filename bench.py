@@ -1,0 +1,259 @@
+"""Benchmark: block-sparse attention forward at the Wan 2.1 14B attention shape.
+
+One step = one inference call of the hot path on the GPU: look up the mask
+set of the timestep in the resident bank and run the block-sparse forward
+(persistent launch, longest-row-first order).  Inputs are resident in HBM
+before the timed region starts.  The metric is effective kept-block
+throughput: 4 * block^2 * d FLOP per kept (query block, key block) tile,
+counting full tiles, divided by the step time.  Also reported: the dense
+forward on the same inputs (speedup = t_dense / t_sparse, the ratio the pages
+print), the offline calibration steps (block mass, compile, work order) and
+the float64 CPU oracle timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+       python bench.py --copy-probe 1024   (plain copy, for counter scaling)
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective kept-block TFLOPS (frac of bf16 MFMA peak) + speedup vs dense, Wan shape"
+PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 matrix peak (vendor figure)
+COUNTERS = os.path.join(ROOT, "profiles", "attn_sparse_wan_counters.json")
+KERNEL_SOURCES = ["block_sparse_attention_calibatt_amd/csrc/attn_fwd.hip",
+                  "block_sparse_attention_calibatt_amd/csrc/tiles.h"]
+
+
+def speedup(t_dense, t_method):
+    """Time ratio at equal shape, the definition behind every speedup the pages print."""
+    return t_dense / t_method
+
+
+def tile_flops(block, d):
+    return 4.0 * block * block * d
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(launch_flops):
+    """HBM bytes per launch from the committed counter summary, if it matches the current kernel."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def copy_probe(mb):
+    import torch
+    n = mb * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "launches": 3}))
+
+
+def cpu_baseline(q, k, v, rp, ci, cfg, budget_s):
+    """The float64 oracle on whole query blocks of the same inputs, until budget_s elapses."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    items, flops = [], 0.0
+    t0 = time.perf_counter()
+    h = 0
+    qb = 0
+    while time.perf_counter() - t0 < budget_s and h < cfg.H:
+        it = (0, h, qb)
+        oracle.sparse_attention_rows(q, k, v, rp, ci, cfg.block, cfg.scale, cfg.S, [it])
+        r = h * cfg.nqb + qb
+        flops += tile_flops(cfg.block, cfg.d) * int(rp[r + 1] - rp[r])
+        items.append(it)
+        qb += 1
+        if qb == cfg.nqb:
+            qb, h = 0, h + 1
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{len(items)} of {cfg.rows} query blocks (heads 0..{items[-1][1]}, in order) of the "
+                      f"same Wan inputs and mask, float64, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="wan", choices=["wan", "mochi", "imbalance"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-calib", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MB")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the block-sparse forward "
+              "shards by head with no exchange, see the design notes", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
+
+    import torch
+    import synth
+    import block_sparse_attention_calibatt_amd as cal
+
+    cal.load()
+    cfg = synth.get_config(args.config)
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    q, k, v = synth.gen_qkv(cfg)
+    sets = [synth.csr_for_config(cfg, t) for t in range(cfg.n_sets)]
+    Q, K, V = (torch.from_numpy(x).to(dev).to(torch.bfloat16).contiguous() for x in (q, k, v))
+    O = torch.empty_like(Q)
+    bank = cal.MaskBank(sets, cfg.H, cfg.nqb, cfg.nkb_valid, dev)
+    qws = torch.zeros(16, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    gen_s = time.perf_counter() - t_gen
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        rp, ci, wo, _ = bank.lookup(i % len(bank))
+        cal.calibatt_sparse_attn_fwd(Q, K, V, O, rp, ci, cfg.block, cfg.scale, cfg.S, wo, qws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step(i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    nnz_steps = [int(bank.nnz[i % len(bank)]) for i in range(args.steps)]
+    flops = tile_flops(cfg.block, cfg.d) * cfg.B * float(np.mean(nnz_steps))
+    value = flops / (ms * 1e-3) / 1e12
+    achieved = float(np.mean([tile_flops(cfg.block, cfg.d) * cfg.B * n / (t * 1e-3) / 1e12
+                              for n, t in zip(nnz_steps, launch_ms)]))
+    density = float(np.mean(bank.nnz)) / (cfg.rows * cfg.nkb_valid)
+
+    extra = {}
+    if not args.no_dense:
+        for _ in range(2):
+            cal.calibatt_dense_attn_fwd(Q, K, V, O, cfg.block, cfg.scale, cfg.S)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        nd = 5
+        e0.record(stream)
+        for _ in range(nd):
+            cal.calibatt_dense_attn_fwd(Q, K, V, O, cfg.block, cfg.scale, cfg.S)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = e0.elapsed_time(e1) / nd
+        dense_flops = tile_flops(cfg.block, cfg.d) * cfg.B * cfg.rows * cfg.nkb_valid
+        extra["dense_ms"] = round(dense_ms, 4)
+        extra["dense_tflops"] = round(dense_flops / (dense_ms * 1e-3) / 1e12, 2)
+        extra["speedup_vs_dense"] = round(speedup(dense_ms, ms), 3)
+
+    if not args.no_calib:
+        # offline calibration steps on one prompt at this shape, then compile of 8 prompts' masses
+        lse = torch.empty(cfg.B * cfg.H * cfg.L, dtype=torch.float32, device=dev)
+        mass = torch.empty((8, cfg.H, cfg.nqb, cfg.nkb), dtype=torch.float32, device=dev)
+        cal.calibatt_block_mass(Q, K, cfg.block, cfg.scale, lse, mass[0], cfg.S)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record(stream)
+        for p in range(8):
+            cal.calibatt_block_mass(Q, K, cfg.block, cfg.scale, lse, mass[p], cfg.S)
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        t_c = time.perf_counter()
+        rp, ci = cal.calibatt_compile_masks(mass, cfg.nkb // 4, 4, cfg.nkb_valid)
+        compile_s = time.perf_counter() - t_c
+        wo = torch.empty(cfg.rows, dtype=torch.int32, device=dev)
+        e[2].record(stream)
+        cal.calibatt_build_schedule(rp, cfg.H, cfg.nqb, wo)
+        e[3].record(stream)
+        torch.cuda.synchronize()
+        pool_ms = e[0].elapsed_time(e[1]) / 8
+        extra["calib"] = {
+            "block_mass_ms_per_prompt": round(pool_ms, 3),
+            "block_mass_qk_tflops": round(2 * 2.0 * cfg.B * cfg.H * cfg.S * cfg.S * cfg.d / (pool_ms * 1e-3) / 1e12, 2),
+            "compile_ms_8_prompts_incl_sync": round(compile_s * 1e3, 3),
+            "schedule_ms": round(e[2].elapsed_time(e[3]), 4),
+            "compiled_density": round(ci.numel() / (cfg.rows * cfg.nkb_valid), 4),
+        }
+
+    cpu = None
+    if not args.no_cpu:
+        rp0, ci0 = sets[0]
+        cpu = cpu_baseline(q, k, v, rp0, ci0, cfg, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: B={cfg.B} H={cfg.H} L={cfg.L} (valid {cfg.S}) d={cfg.d} "
+                        f"block={cfg.block}, {len(bank)} mask set(s), mean kept density {density:.4f}",
+            "global_batch": cfg.B,
+            "seq_len": cfg.S,
+            "parallelism": "single GPU",
+            "kept_blocks_per_step": float(np.mean(nnz_steps)),
+            "launch": "persistent grid, atomic row queue, longest-row-first order per head",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic_from_profile(flops),
+            "kernel": "attn_fwd_bf16_kernel<128,128,false>",
+            "avg_launch_ms": round(float(np.mean(launch_ms)), 4),
+        },
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 3),
+        "input_setup_s": round(gen_s, 2),
+    }
+    line.update(extra)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

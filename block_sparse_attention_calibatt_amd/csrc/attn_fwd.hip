@@ -22,26 +22,128 @@
 
 namespace calibatt {
 
+// Pipeline geometry of the bf16 kernel.  Keys are consumed in sub-tiles of
+// 64 (a 128-token kept block is two sub-tiles).  Two LDS buffers each hold a
+// K sub-tile (rows of 16-byte chunks, XOR-swizzled) and a transposed V
+// sub-tile.  While sub-tile j is computed from one buffer, sub-tile j+1 is in
+// flight: K goes straight from HBM into the other buffer by buffer-to-LDS
+// DMA (no registers), V comes into registers in 8-key x 4-d blocks (8 loads
+// of 8 bytes per thread) and is transposed with byte permutes and written
+// after the compute of sub-tile j.
+template <int D, int BLK>
+struct Pipe {
+  static constexpr int NT = BLK * 2;        // threads: BLK/32 waves of 64
+  static constexpr int NW = BLK / 32;
+  static constexpr int BN = 64;             // keys per sub-tile
+  static constexpr int SPB = BLK / BN;      // sub-tiles per kept block
+  static constexpr int CH = D / 8;          // 16-byte chunks per K row
+  static constexpr int CHV = BN / 8;        // 16-byte chunks per Vt row
+  static constexpr int KROWS_PER_LOAD = 64 / CH;            // rows one wave DMA covers
+  static constexpr int KLOADS = BN / KROWS_PER_LOAD / NW;   // DMA instructions per wave
+  static constexpr int DQ = D / 4;          // 4-wide d groups
+  static constexpr int VBLK = (BN / 8) * DQ;                // 8x4 V blocks per sub-tile
+  static constexpr int VPER = (VBLK + NT - 1) / NT;
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Per-lane byte offsets of the K DMA (one per DMA instruction), relative to the sub-tile start.
+template <int D, int BLK>
+__device__ __forceinline__ void k_dma_offsets(int w, int lane, int* koff) {
+  using P = Pipe<D, BLK>;
+#pragma unroll
+  for (int i = 0; i < P::KLOADS; ++i) {
+    const int row = (w * P::KLOADS + i) * P::KROWS_PER_LOAD + lane / P::CH;
+    const int chunk = (lane % P::CH) ^ swz<P::CH>(row);
+    koff[i] = (row * D + chunk * 8) * 2;
+  }
+}
+
+// K sub-tile starting at key k0 -> swizzled LDS buffer, by DMA.
+template <int D, int BLK>
+__device__ __forceinline__ void k_dma(__amdgpu_buffer_rsrc_t rk, int k0, u32x4* ldsK, int w, const int* koff) {
+  using P = Pipe<D, BLK>;
+#pragma unroll
+  for (int i = 0; i < P::KLOADS; ++i) {
+    const int r0 = (w * P::KLOADS + i) * P::KROWS_PER_LOAD;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(ldsK + r0 * P::CH), 16, koff[i], k0 * D * 2, 0, 0);
+  }
+}
+
+template <int D, int BLK>
+__device__ __forceinline__ void v_load(__amdgpu_buffer_rsrc_t rv, int k0, int voff, u32x2* st) {
+  using P = Pipe<D, BLK>;
+#pragma unroll
+  for (int j = 0; j < P::VPER; ++j) {
+    const int vb = threadIdx.x + j * P::NT;
+    if (P::VBLK % P::NT == 0 || vb < P::VBLK) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        st[8 * j + i] = __builtin_amdgcn_raw_buffer_load_b64(
+            rv, voff + j * (P::NT / P::DQ) * 8 * D * 2 + i * D * 2, k0 * D * 2, 0);
+    }
+  }
+}
+
+template <int D, int BLK>
+__device__ __forceinline__ void v_store(const u32x2* st, u32x4* ldsV) {
+  using P = Pipe<D, BLK>;
+#pragma unroll
+  for (int j = 0; j < P::VPER; ++j) {
+    const int vb = threadIdx.x + j * P::NT;
+    if (P::VBLK % P::NT == 0 || vb < P::VBLK) {
+      const int dq = vb % P::DQ, kg = vb / P::DQ;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t x = st[8 * j + 2 * q][e >> 1], y = st[8 * j + 2 * q + 1][e >> 1];
+          o[q] = __builtin_amdgcn_perm(y, x, (e & 1) ? 0x07060302u : 0x05040100u);
+        }
+        ldsV[chunk_index<P::CHV>(dq * 4 + e, kg)] = o;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <int I>
+struct Buf {
+  static constexpr int value = I;
+};
+
 template <int D, int BLK, bool DENSE>
-__global__ __launch_bounds__(BLK * 2) void attn_fwd_bf16_kernel(
+__global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     const int32_t* __restrict__ work_order, int32_t* __restrict__ queue, int items, int H, int L,
     int seq_len, int nkb_valid, float c2) {
-  constexpr int NT = BLK * 2;
-  constexpr int KT = BLK / 32;   // 32-key slices per block
+  using P = Pipe<D, BLK>;
   constexpr int DS = D / 16;     // k-steps of Q K^T
   constexpr int DT = D / 32;     // 32-row d tiles of O^T
-  constexpr int CH = D / 8;      // 16-byte chunks per K row
-  constexpr int CHV = BLK / 8;   // 16-byte chunks per Vt row
-  __shared__ u32x4 ldsK[BLK * CH];
-  __shared__ u32x4 ldsV[D * CHV];
+  // two buffers as separate LDS objects, so loads into one never alias reads of the other
+  __shared__ u32x4 ldsK0[P::BN * P::CH];
+  __shared__ u32x4 ldsK1[P::BN * P::CH];
+  __shared__ u32x4 ldsV0[D * P::CHV];
+  __shared__ u32x4 ldsV1[D * P::CHV];
   __shared__ int s_item;
 
   const int nqb = L / BLK;
   const int rows = H * nqb;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 5, c = lane & 31;
+  const int prow = qk_row_perm(c);
+  const uint32_t slab_bytes = (uint32_t)L * D * 2;
+
+  int koff[P::KLOADS];
+  k_dma_offsets<D, BLK>(w, lane, koff);
+  const int voff = (((threadIdx.x / P::DQ) * 8) * D + (threadIdx.x % P::DQ) * 4) * 2;
 
   int item = blockIdx.x;
   for (;;) {
@@ -56,15 +158,14 @@ __global__ __launch_bounds__(BLK * 2) void attn_fwd_bf16_kernel(
     const int r = work_order ? work_order[ri] : ri;
     const int h = r / nqb, qb = r - h * nqb;
     const size_t base = ((size_t)b * H + h) * (size_t)L * D;
-    const bf16* Qb = Q + base;
-    const bf16* Kb = K + base;
-    const bf16* Vb = V + base;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + base, slab_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + base, slab_bytes);
     const int q = qb * BLK + 32 * w + c;   // this lane's query
 
     bf16x8 qreg[DS];
 #pragma unroll
     for (int s = 0; s < DS; ++s)
-      qreg[s] = *reinterpret_cast<const bf16x8*>(Qb + (size_t)q * D + 16 * s + 8 * g);
+      qreg[s] = *reinterpret_cast<const bf16x8*>(Q + base + (size_t)q * D + 16 * s + 8 * g);
 
     f32x16 oacc[DT];
 #pragma unroll
@@ -72,22 +173,53 @@ __global__ __launch_bounds__(BLK * 2) void attn_fwd_bf16_kernel(
     float m_run = kNegInf, l_run = 0.f;
 
     const int beg = DENSE ? 0 : row_ptr[r];
-    const int end = DENSE ? nkb_valid : row_ptr[r + 1];
-    for (int it = beg; it < end; ++it) {
-      const int kb = DENSE ? it : col_idx[it];
-      const size_t koff = (size_t)kb * BLK * D;
-      __syncthreads();
-      load_k_tile<D, BLK, NT>(Kb + koff, ldsK);
-      load_v_tile_t<D, BLK, NT>(Vb + koff, ldsV);
-      __syncthreads();
+    const int nsub = ((DENSE ? nkb_valid : row_ptr[r + 1]) - beg) * P::SPB;
+    auto key0 = [&](int j) -> int {
+      const int kb = DENSE ? j / P::SPB : col_idx[beg + j / P::SPB];
+      return kb * BLK + (j % P::SPB) * P::BN;
+    };
 
-      f32x16 sacc[KT];
-      qk_tile<D, BLK>(ldsK, qreg, sacc, g, c);
+    u32x2 st[8 * P::VPER];
+    if (nsub > 0) {
+      const int k0 = key0(0);
+      k_dma<D, BLK>(rk, k0, ldsK0, w, koff);
+      v_load<D, BLK>(rv, k0, voff, st);
+      v_store<D, BLK>(st, ldsV0);
+    }
+    wait_vm();
+    __syncthreads();
 
-      const int k0 = kb * BLK;
-      if (k0 + BLK > seq_len) {
+    // one sub-tile: compute from buffer B while sub-tile j+1 streams into buffer 1-B
+    auto step = [&](int j, auto bufc) {
+      constexpr int B = decltype(bufc)::value;
+      u32x4* const kcur = B == 0 ? ldsK0 : ldsK1;
+      u32x4* const vcur = B == 0 ? ldsV0 : ldsV1;
+      u32x4* const knext = B == 0 ? ldsK1 : ldsK0;
+      u32x4* const vnext = B == 0 ? ldsV1 : ldsV0;
+      const int k0 = key0(j);
+      const bool more = j + 1 < nsub;
+      if (more) {
+        const int k1 = key0(j + 1);
+        k_dma<D, BLK>(rk, k1, knext, w, koff);
+        v_load<D, BLK>(rv, k1, voff, st);
+      }
+
+      // S^T for 64 keys x 32 queries: two 32x32 accumulators
+      f32x16 sacc[2];
 #pragma unroll
-        for (int mt = 0; mt < KT; ++mt)
+      for (int mt = 0; mt < 2; ++mt) {
+        const int row = 32 * mt + prow;
+        u32x4 a[DS];
+#pragma unroll
+        for (int s = 0; s < DS; ++s) a[s] = kcur[chunk_index<P::CH>(row, 2 * s + g)];
+        f32x16 acc = {};
+#pragma unroll
+        for (int s = 0; s < DS; ++s) acc = mfma_bf16(__builtin_bit_cast(bf16x8, a[s]), qreg[s], acc);
+        sacc[mt] = acc;
+      }
+      if (k0 + P::BN > seq_len) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr)
             if (k0 + 32 * mt + slice_key(rr, g) >= seq_len) sacc[mt][rr] = kNegInf;
@@ -95,45 +227,57 @@ __global__ __launch_bounds__(BLK * 2) void attn_fwd_bf16_kernel(
 
       float mx = kNegInf;
 #pragma unroll
-      for (int mt = 0; mt < KT; ++mt)
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, sacc[mt][rr]);
       mx = pair_max(mx);
       const float m_new = fmaxf(m_run, mx);
       const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = fast_exp2((m_run - m_use) * c2);
       const float mc = m_use * c2;
+      if (__any(m_new > m_run)) {
+        const float alpha = fast_exp2((m_run - m_use) * c2);
+        l_run *= alpha;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
+      }
       m_run = m_new;
 
-      float psum = 0.f;
-      bf16x8 pb[BLK / 16];
+      bf16x8 pb[4];
 #pragma unroll
-      for (int mt = 0; mt < KT; ++mt) {
+      for (int ks = 0; ks < 4; ++ks) {
+        bf16x8 v;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          bf16x8 v;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float p = fast_exp2(fmaf(sacc[mt][8 * half + e], c2, -mc));
-            psum += p;
-            v[e] = (bf16)p;
-          }
-          pb[2 * mt + half] = v;
-        }
+        for (int e = 0; e < 8; ++e) v[e] = (bf16)fast_exp2(fmaf(sacc[ks >> 1][8 * (ks & 1) + e], c2, -mc));
+        pb[ks] = v;
       }
-      l_run = l_run * alpha + psum;
+      // row sum of the rounded probabilities, the same values the P*V product uses
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      const bf16x2 one2 = {(bf16)1.f, (bf16)1.f};
 #pragma unroll
-      for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 pr = {pb[ks][e], pb[ks][e + 1]};
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, l_run, false);
+        }
 
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
         const int row = 32 * t + c;
+        u32x4 a[4];
 #pragma unroll
-        for (int ks = 0; ks < BLK / 16; ++ks) {
-          const u32x4 a = ldsV[chunk_index<CHV>(row, 2 * ks + g)];
-          oacc[t] = mfma_bf16(__builtin_bit_cast(bf16x8, a), pb[ks], oacc[t]);
-        }
+        for (int ks = 0; ks < 4; ++ks) a[ks] = vcur[chunk_index<P::CHV>(row, 2 * ks + g)];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) oacc[t] = mfma_bf16(__builtin_bit_cast(bf16x8, a[ks]), pb[ks], oacc[t]);
       }
+      if (more) v_store<D, BLK>(st, vnext);
+      wait_vm();
+      __syncthreads();
+    };
+
+    for (int j = 0; j < nsub; j += 2) {
+      step(j, Buf<0>{});
+      if (j + 1 < nsub) step(j + 1, Buf<1>{});
     }
 
     const float l_tot = pair_sum(l_run);

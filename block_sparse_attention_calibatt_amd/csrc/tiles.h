@@ -15,8 +15,7 @@
 //
 // LDS tiles are rows of 16-byte chunks with an XOR swizzle on the chunk
 // index, so that the matrix-core operand reads (16 consecutive rows, one
-// chunk) and the transposed V writes (16 rows spaced 8 apart) both spread
-// over all bank groups.
+// chunk) spread over all bank groups.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -40,13 +39,18 @@ __device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Chunk swizzle for a row of CH 16-byte chunks (CH = 16 or 8).
+// Chunk swizzle for a row of CH 16-byte chunks (CH = 16 or 8).  Reads of 16
+// consecutive rows at one chunk hit 16 distinct 16-byte bank groups; the
+// swizzle uses only row bits 0..4, so rows 32 apart share it and an operand
+// address advances by a constant between 32-row tiles.  For 8-chunk rows the
+// extra bit-4 term also spreads the transposed V writes (rows 4 apart) over 8
+// groups.
 template <int CH>
 __device__ __forceinline__ int swz(int row) {
   if constexpr (CH == 16) {
-    return (row & 15) ^ ((row >> 4) & 7);
+    return row & 15;
   } else {
-    return ((row >> 1) & 7) ^ ((row >> 4) & 7);
+    return ((row >> 1) & 7) ^ ((row >> 4) & 1);
   }
 }
 
@@ -79,35 +83,6 @@ __device__ __forceinline__ void load_k_tile(const bf16* __restrict__ src, u32x4*
   for (int i = 0; i < PER; ++i) {
     const int idx = threadIdx.x + i * NT;
     lds[chunk_index<CH>(idx / CH, idx % CH)] = r[i];
-  }
-}
-
-// V tile [BLK keys][D] bf16 in HBM -> transposed Vt [D][BLK] in swizzled LDS.
-// Each thread moves 8x8 sub-blocks: 8 row loads of 16 bytes, a register
-// transpose with byte permutes, 8 row stores of 16 bytes.
-template <int D, int BLK, int NT>
-__device__ __forceinline__ void load_v_tile_t(const bf16* __restrict__ src, u32x4* __restrict__ lds) {
-  constexpr int DG = D / 8;
-  constexpr int KG = BLK / 8;
-  constexpr int CHV = BLK / 8;
-  for (int sb = threadIdx.x; sb < DG * KG; sb += NT) {
-    const int dg = sb % DG, kg = sb / DG;
-    u32x4 in[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      in[i] = *reinterpret_cast<const u32x4*>(src + (kg * 8 + i) * D + dg * 8);
-    u32x4 out[8];
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t x = in[2 * j][e2], y = in[2 * j + 1][e2];
-        out[2 * e2][j] = __builtin_amdgcn_perm(y, x, 0x05040100u);
-        out[2 * e2 + 1][j] = __builtin_amdgcn_perm(y, x, 0x07060302u);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) lds[chunk_index<CHV>(dg * 8 + e, kg)] = out[e];
   }
 }
 
