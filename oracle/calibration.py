@@ -107,6 +107,12 @@ def to_csr(mask):
 
 
 def compile_masks(mass, keep_topk, min_agree, nkb_valid=None):
-    """mass [P, H, nqb, nkb] -> CSR of the blocks that >= min_agree prompts keep in their top K."""
+    """mass [P, H, nqb, nkb] -> CSR of the blocks that >= min_agree prompts keep in their top K.
+
+    Key blocks at or past nkb_valid hold no valid key: they are never kept,
+    whatever the agreement threshold (also when min_agree is 0)."""
     keep = topk_keep(mass, keep_topk, nkb_valid)
-    return to_csr(agreement(keep, min_agree))
+    agreed = agreement(keep, min_agree)
+    if nkb_valid is not None:
+        agreed[..., nkb_valid:] = False
+    return to_csr(agreed)

@@ -274,24 +274,29 @@ def pin_csr(to_csr_impl, seed=11):
 
 
 def pin_compile_brute(compile_impl, seed=12):
-    """Whole compile on a tiny bank of prompts, every step done by enumeration."""
+    """Whole compile on a tiny bank of prompts, every step done by enumeration.
+
+    Covers a key range shorter than the mass (nkb_valid < nkb) and the
+    thresholds 0 (every eligible block), 1 (union) and P (intersection)."""
     rng = _rng(seed)
-    P, H, nqb, nkb, K, t = 4, 2, 3, 6, 2, 2
+    P, H, nqb, nkb, K = 4, 2, 3, 6, 2
     mass = rng.integers(0, 3, size=(P, H, nqb, nkb)).astype(np.float32)
-    row_ptr, col_idx = compile_impl(mass, K, t)
-    want_rows = []
-    for h in range(H):
-        for qb in range(nqb):
-            cnt = [0] * nkb
-            for p in range(P):
-                row = mass[p, h, qb]
-                best = max(itertools.combinations(range(nkb), K),
-                           key=lambda s: (sum(float(row[i]) for i in s), [-i for i in s]))
-                for i in best:
-                    cnt[i] += 1
-            want_rows.append([kb for kb in range(nkb) if cnt[kb] >= t])
-    got_rows = [list(col_idx[row_ptr[r]:row_ptr[r + 1]]) for r in range(H * nqb)]
-    assert got_rows == want_rows, "compile by enumeration"
+    for nv in (6, 5):
+        for t in (0, 1, 2, 4):
+            row_ptr, col_idx = compile_impl(mass, K, t, nv)
+            want_rows = []
+            for h in range(H):
+                for qb in range(nqb):
+                    cnt = [0] * nkb
+                    for p in range(P):
+                        row = mass[p, h, qb]
+                        best = max(itertools.combinations(range(nv), K),
+                                   key=lambda s: (sum(float(row[i]) for i in s), [-i for i in s]))
+                        for i in best:
+                            cnt[i] += 1
+                    want_rows.append([kb for kb in range(nv) if cnt[kb] >= t])
+            got_rows = [list(col_idx[row_ptr[r]:row_ptr[r + 1]]) for r in range(H * nqb)]
+            assert got_rows == want_rows, f"compile by enumeration (nkb_valid={nv}, min_agree={t})"
 
 
 # ---------------------------------------------------------------- schedule
