@@ -134,7 +134,7 @@ def main():
     Q, K, V = (torch.from_numpy(x).to(dev).to(torch.bfloat16).contiguous() for x in (q, k, v))
     O = torch.empty_like(Q)
     bank = cal.MaskBank(sets, cfg.H, cfg.nqb, cfg.nkb_valid, dev)
-    qws = torch.zeros(16, dtype=torch.int32, device=dev)
+    qws = cal.new_queue(dev)
     torch.cuda.synchronize()
     gen_s = time.perf_counter() - t_gen
 
@@ -168,12 +168,12 @@ def main():
     extra = {}
     if not args.no_dense:
         for _ in range(2):
-            cal.calibatt_dense_attn_fwd(Q, K, V, O, cfg.block, cfg.scale, cfg.S)
+            cal.calibatt_dense_attn_fwd(Q, K, V, O, cfg.block, cfg.scale, cfg.S, qws)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         nd = 5
         e0.record(stream)
         for _ in range(nd):
-            cal.calibatt_dense_attn_fwd(Q, K, V, O, cfg.block, cfg.scale, cfg.S)
+            cal.calibatt_dense_attn_fwd(Q, K, V, O, cfg.block, cfg.scale, cfg.S, qws)
         e1.record(stream)
         torch.cuda.synchronize()
         dense_ms = e0.elapsed_time(e1) / nd
@@ -196,7 +196,7 @@ def main():
         t_c = time.perf_counter()
         rp, ci = cal.calibatt_compile_masks(mass, cfg.nkb // 4, 4, cfg.nkb_valid)
         compile_s = time.perf_counter() - t_c
-        wo = torch.empty(cfg.rows, dtype=torch.int32, device=dev)
+        wo = torch.empty(cfg.rows + 9, dtype=torch.int32, device=dev)
         e[2].record(stream)
         cal.calibatt_build_schedule(rp, cfg.H, cfg.nqb, wo)
         e[3].record(stream)
@@ -235,7 +235,7 @@ def main():
             "seq_len": cfg.S,
             "parallelism": "single GPU",
             "kept_blocks_per_step": float(np.mean(nnz_steps)),
-            "launch": "persistent grid, atomic row queue, longest-row-first order per head",
+            "launch": "persistent grid; heads spread over 8 per-XCD partitions longest first, rows longest first, atomic queue per partition with stealing",
         },
         "roofline": {
             "bound": "mfma",

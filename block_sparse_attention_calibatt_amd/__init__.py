@@ -9,6 +9,7 @@ timesteps on the GPU.  Build the library with
 
 from ._lib import CalibattError, LIB_PATH, load
 from .capi import (
+    new_queue,
     calibatt_sparse_attn_fwd,
     calibatt_dense_attn_fwd,
     calibatt_block_mass,
@@ -26,6 +27,7 @@ __all__ = [
     "CalibattError",
     "LIB_PATH",
     "load",
+    "new_queue",
     "calibatt_sparse_attn_fwd",
     "calibatt_dense_attn_fwd",
     "calibatt_block_mass",

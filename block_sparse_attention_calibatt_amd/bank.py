@@ -28,7 +28,7 @@ class MaskBank:
         ci_all = np.concatenate([np.asarray(ci, dtype=np.int32) for _, ci in sets] + [np.zeros(1, np.int32)])
         self.row_ptr = torch.from_numpy(rp_all).to(device)
         self.col_idx = torch.from_numpy(ci_all).to(device)
-        self.work_order = torch.empty((len(sets), rows), dtype=torch.int32, device=device)
+        self.work_order = torch.empty((len(sets), rows + 9), dtype=torch.int32, device=device)
         for t in range(len(sets)):
             calibatt_build_schedule(self.row_ptr[t], self.H, self.nqb, self.work_order[t])
 

@@ -38,6 +38,21 @@ def _dev_tensor(t, name, dtype=None):
         _need(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
 
 
+PARTS = 8            # work partitions (one per XCD)
+QUEUE_INTS = 128     # persistent-launch counters: 8 partitions x 16 int32
+
+
+def new_queue(device):
+    """A zeroed persistent-launch workspace for the attention entry points."""
+    return torch.zeros(QUEUE_INTS, dtype=torch.int32, device=device)
+
+
+def _queue(queue_ws):
+    if queue_ws is not None:
+        _dev_tensor(queue_ws, "queue_ws", torch.int32)
+        _need(queue_ws.numel() >= QUEUE_INTS, f"queue_ws needs >= {QUEUE_INTS} int32 entries")
+
+
 def _qkv(Q, K, V, O):
     for n, t in (("Q", Q), ("K", K), ("V", V), ("O", O)):
         _dev_tensor(t, n)
@@ -60,10 +75,8 @@ def calibatt_sparse_attn_fwd(Q, K, V, O, row_ptr, col_idx, block, scale, seq_len
     _need(row_ptr.numel() == rows + 1, f"row_ptr must have H*nqb+1 = {rows + 1} entries")
     if work_order is not None:
         _dev_tensor(work_order, "work_order", torch.int32)
-        _need(work_order.numel() == rows, f"work_order must have {rows} entries")
-    if queue_ws is not None:
-        _dev_tensor(queue_ws, "queue_ws", torch.int32)
-        _need(queue_ws.numel() >= 16, "queue_ws needs >= 16 int32 entries")
+        _need(work_order.numel() == rows + PARTS + 1, f"work_order must have H*nqb+9 = {rows + PARTS + 1} entries")
+    _queue(queue_ws)
     lib = load()
     check(lib.calibatt_sparse_attn_fwd(
         _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(row_ptr), _ptr(col_idx), int(block), float(scale),
@@ -72,12 +85,13 @@ def calibatt_sparse_attn_fwd(Q, K, V, O, row_ptr, col_idx, block, scale, seq_len
     return O
 
 
-def calibatt_dense_attn_fwd(Q, K, V, O, block, scale, seq_len=None):
+def calibatt_dense_attn_fwd(Q, K, V, O, block, scale, seq_len=None, queue_ws=None):
     B, H, L, d = _qkv(Q, K, V, O)
     seq_len = L if seq_len is None else int(seq_len)
+    _queue(queue_ws)
     lib = load()
     check(lib.calibatt_dense_attn_fwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), int(block), float(scale),
-                                      B, H, L, seq_len, d, _DT[Q.dtype], _stream(Q)))
+                                      B, H, L, seq_len, d, _DT[Q.dtype], _ptr(queue_ws), _stream(Q)))
     return O
 
 
@@ -136,9 +150,9 @@ def calibatt_build_schedule(row_ptr, H, nqb, work_order=None):
     _dev_tensor(row_ptr, "row_ptr", torch.int32)
     _need(row_ptr.numel() == H * nqb + 1, "row_ptr must have H*nqb+1 entries")
     if work_order is None:
-        work_order = torch.empty(H * nqb, dtype=torch.int32, device=row_ptr.device)
+        work_order = torch.empty(H * nqb + PARTS + 1, dtype=torch.int32, device=row_ptr.device)
     _dev_tensor(work_order, "work_order", torch.int32)
-    _need(work_order.numel() == H * nqb, "work_order must have H*nqb entries")
+    _need(work_order.numel() == H * nqb + PARTS + 1, "work_order must have H*nqb+9 entries")
     lib = load()
     check(lib.calibatt_build_schedule(_ptr(row_ptr), int(H), int(nqb), _ptr(work_order), _stream(row_ptr)))
     return work_order
@@ -170,6 +184,7 @@ def calibatt_version():
 
 __all__ = [
     "CalibattError",
+    "new_queue",
     "calibatt_sparse_attn_fwd",
     "calibatt_dense_attn_fwd",
     "calibatt_block_mass",

@@ -144,13 +144,14 @@ calibatt_status calibatt_sparse_attn_fwd(const void* Q, const void* K, const voi
 
 calibatt_status calibatt_dense_attn_fwd(const void* Q, const void* K, const void* V, void* O,
                                         int block, float scale, int B, int H, int L, int seq_len,
-                                        int d, calibatt_dtype dt, void* stream) {
+                                        int d, calibatt_dtype dt, int32_t* queue_ws, void* stream) {
   calibatt_status s = check_ptrs4(Q, K, V, O);
   if (s != CALIBATT_OK) return s;
   s = check_qkv_shape(B, H, L, seq_len, d, dt, block);
   if (s != CALIBATT_OK) return s;
+  if (queue_ws && !aligned(queue_ws, 16)) return fail(CALIBATT_ERR_ALIGN, "queue_ws must be 16-byte aligned");
   return run_attention(Q, K, V, O, nullptr, nullptr, block, scale, B, H, L, seq_len, d, dt, nullptr,
-                       nullptr, true, stream);
+                       queue_ws, true, stream);
 }
 
 calibatt_status calibatt_block_mass(const void* Q, const void* K, int B, int H, int L, int seq_len,
@@ -245,6 +246,7 @@ calibatt_status calibatt_build_schedule(const int32_t* row_ptr, int H, int nqb, 
   if (!row_ptr || !work_order) return fail(CALIBATT_ERR_NULL, "row_ptr and work_order must be non-NULL");
   if (H < 1 || nqb < 1) return fail(CALIBATT_ERR_SHAPE, "H and nqb must be >= 1");
   if (nqb > calibatt::kMaxKeyBlocks) return fail(CALIBATT_ERR_UNSUPPORTED, "nqb=%d exceeds %d", nqb, calibatt::kMaxKeyBlocks);
+  if (H > calibatt::kMaxHeads) return fail(CALIBATT_ERR_UNSUPPORTED, "H=%d exceeds %d", H, calibatt::kMaxHeads);
   if (!aligned(row_ptr, 4) || !aligned(work_order, 4)) return fail(CALIBATT_ERR_ALIGN, "row_ptr and work_order must be 4-byte aligned");
   hipError_t e = calibatt::launch_schedule(row_ptr, H, nqb, work_order, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "launching work-order build");

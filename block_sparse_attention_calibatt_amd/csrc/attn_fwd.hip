@@ -14,9 +14,11 @@
 // row are reduced in col_idx order by that one workgroup, so the result does
 // not depend on the order rows are scheduled in.
 //
-// Scheduling: with a queue pointer the grid is persistent and workgroups pop
-// row indices from an atomic counter; the optional work_order permutes rows
-// (longest first) so the tail of the launch holds the short rows.
+// Scheduling: with a queue pointer the grid is persistent; each workgroup
+// pops rows from the atomic counter of its XCD's partition of the work order
+// (heads spread over partitions, rows longest first), then helps the other
+// partitions.  Keeping a head's rows on one XCD keeps its K/V in that XCD's
+// L2; longest-first puts the short rows at the tail of the launch.
 #include "tiles.h"
 #include "launch.h"
 
@@ -113,6 +115,53 @@ __device__ __forceinline__ void v_store(const u32x2* st, u32x4* ldsV) {
 
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Where a workgroup's next row comes from.  With a work order, rows are
+// grouped into kParts partition lists (offsets after the rows); without one,
+// partition p holds heads p, p + kParts, ... in natural order.
+struct RowSource {
+  const int32_t* order;
+  int rows, nqb, H, B;
+  __device__ __forceinline__ int part_len(int p) const {
+    if (order) return order[rows + p + 1] - order[rows + p];
+    return ((H - p + kParts - 1) / kParts) * nqb;
+  }
+  __device__ __forceinline__ int part_row(int p, int k) const {
+    if (order) return order[order[rows + p] + k];
+    return (p + kParts * (k / nqb)) * nqb + k % nqb;
+  }
+};
+
+// Persistent scheduling: serve partition blockIdx.x % kParts (the XCD this
+// workgroup runs on) until its counter passes its length, then move to the
+// next partition; every workgroup visits every partition once, so the grid
+// always drains.  Without a queue, workgroup i takes row i of the order.
+template <typename Body>
+__device__ __forceinline__ void for_each_row(const RowSource& src, int32_t* queue, int* s_item, Body body) {
+  if (queue) {
+    int p = blockIdx.x % kParts;
+    for (int tries = 0; tries < kParts;) {
+      if (threadIdx.x == 0) *s_item = atomicAdd(queue + p * kQueueStride, 1);
+      __syncthreads();
+      const int k = *s_item;
+      __syncthreads();
+      const int len = src.part_len(p);
+      if (k >= src.B * len) {
+        p = (p + 1) % kParts;
+        ++tries;
+        continue;
+      }
+      const int b = k / len;
+      body(b, src.part_row(p, k - b * len));
+    }
+  } else {
+    const int item = blockIdx.x;
+    const int b = item / src.rows, j = item - b * src.rows;
+    body(b, src.order ? src.order[j] : j);
+  }
+}
+
+constexpr float kLazyLog2 = 8.f;
+
 template <int I>
 struct Buf {
   static constexpr int value = I;
@@ -140,22 +189,14 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(
   const int g = lane >> 5, c = lane & 31;
   const int prow = qk_row_perm(c);
   const uint32_t slab_bytes = (uint32_t)L * D * 2;
+  const float lazy_thr = kLazyLog2 / c2;   // in raw score units
 
   int koff[P::KLOADS];
   k_dma_offsets<D, BLK>(w, lane, koff);
   const int voff = (((threadIdx.x / P::DQ) * 8) * D + (threadIdx.x % P::DQ) * 4) * 2;
 
-  int item = blockIdx.x;
-  for (;;) {
-    if (queue) {
-      if (threadIdx.x == 0) s_item = atomicAdd(queue, 1);
-      __syncthreads();
-      item = s_item;
-      __syncthreads();
-    }
-    if (item >= items) break;
-    const int b = item / rows, ri = item - b * rows;
-    const int r = work_order ? work_order[ri] : ri;
+  const RowSource src{work_order, rows, nqb, H, items / rows};
+  for_each_row(src, queue, &s_item, [&](int b, int r) {
     const int h = r / nqb, qb = r - h * nqb;
     const size_t base = ((size_t)b * H + h) * (size_t)L * D;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + base, slab_bytes);
@@ -231,16 +272,19 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, sacc[mt][rr]);
       mx = pair_max(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float mc = m_use * c2;
-      if (__any(m_new > m_run)) {
-        const float alpha = fast_exp2((m_run - m_use) * c2);
+      // Lazy rescale: the reference maximum moves only when a score passes it
+      // by more than kLazyLog2 in log2 units, so probabilities stay below
+      // 2^kLazyLog2 and O and l are rescaled a few times per row instead of
+      // on most sub-tiles.  O = acc / l is the same for any reference.
+      if (__any(mx > m_run + lazy_thr)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_run - m_new) * c2);
         l_run *= alpha;
 #pragma unroll
         for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
+        m_run = m_new;
       }
-      m_run = m_new;
+      const float mc = (m_run == kNegInf ? 0.f : m_run) * c2;
 
       bf16x8 pb[4];
 #pragma unroll
@@ -295,8 +339,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(
         *reinterpret_cast<bf16x4*>(Ob + d0) = o;
       }
     }
-    if (!queue) break;
-  }
+  });
 }
 
 // float32 path: 32-key slices, fp32 matrix cores (32x32x2), P kept in float32.
@@ -322,17 +365,8 @@ __global__ __launch_bounds__(BLK * 2) void attn_fwd_f32_kernel(
   // slice row fed by lane column c: key 2*(i without bit 2) + bit 2
   const int krow = ((c >> 3) << 3) | ((c & 3) << 1) | ((c >> 2) & 1);
 
-  int item = blockIdx.x;
-  for (;;) {
-    if (queue) {
-      if (threadIdx.x == 0) s_item = atomicAdd(queue, 1);
-      __syncthreads();
-      item = s_item;
-      __syncthreads();
-    }
-    if (item >= items) break;
-    const int b = item / rows, ri = item - b * rows;
-    const int r = work_order ? work_order[ri] : ri;
+  const RowSource src{work_order, rows, nqb, H, items / rows};
+  for_each_row(src, queue, &s_item, [&](int b, int r) {
     const int h = r / nqb, qb = r - h * nqb;
     const size_t base = ((size_t)b * H + h) * (size_t)L * D;
     const int q = qb * BLK + 32 * w + c;
@@ -402,8 +436,7 @@ __global__ __launch_bounds__(BLK * 2) void attn_fwd_f32_kernel(
     for (int t = 0; t < DT; ++t)
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) Ob[32 * t + 8 * (rr >> 2) + 4 * g + (rr & 3)] = oacc[t][rr] * inv;
-    if (!queue) break;
-  }
+  });
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int n, int32_t v) {
@@ -424,7 +457,7 @@ static hipError_t launch_typed(const AttnArgs& a, hipStream_t st) {
   if (items == 0) return hipSuccess;
   int grid = items;
   if (a.queue) {
-    hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, st, a.queue, 16, 0);
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(kQueueInts), 0, st, a.queue, kQueueInts, 0);
     int per_cu = 1;
     hipError_t e = a.dtype_f32
         ? occupancy(attn_fwd_f32_kernel<D, BLK, DENSE>, threads, &per_cu)

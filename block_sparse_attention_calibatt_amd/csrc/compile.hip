@@ -13,8 +13,8 @@
 // Kernels: keep_agree (one workgroup per row: per-prompt ranks, counts,
 // agreed flags, kept count), row_offsets (one workgroup: exclusive scan of
 // the kept counts), fill_columns (one workgroup per row: ordered compaction
-// of the agreed flags), lpt_order (one workgroup per head: rank of each row
-// by kept count descending, index ascending).
+// of the agreed flags), lpt_schedule (one workgroup per head: the head's
+// partition, then each row's rank by kept count descending, index ascending).
 #include "tiles.h"
 #include "launch.h"
 
@@ -134,11 +134,53 @@ __global__ __launch_bounds__(kRowThreads) void fill_columns_kernel(const uint8_t
     if (on[j]) col_idx[pos++] = kb0 + j;
 }
 
-__global__ __launch_bounds__(kRowThreads) void lpt_order_kernel(const int32_t* __restrict__ row_ptr,
-                                                                int nqb,
-                                                                int32_t* __restrict__ work_order) {
+// Work order: heads go to kParts partitions longest first (greedy, ties to
+// the lowest partition); a partition lists its heads in that order and each
+// head's rows by kept count descending, ties by query block.  Output: the
+// concatenated lists, then the kParts+1 list offsets.  Every workgroup (one
+// per head) recomputes the small head assignment itself, so no scratch
+// memory is needed.
+__global__ __launch_bounds__(kRowThreads) void lpt_schedule_kernel(const int32_t* __restrict__ row_ptr,
+                                                                   int H, int nqb,
+                                                                   int32_t* __restrict__ out) {
+  __shared__ int hcost[kMaxHeads];
+  __shared__ int hsorted[kMaxHeads];
   __shared__ int cost[kMaxKeyBlocks];
+  __shared__ int s_off[kParts + 1];
+  __shared__ int s_start;
   const int h = blockIdx.x;
+  const int rows = H * nqb;
+  for (int i = threadIdx.x; i < H; i += kRowThreads) hcost[i] = row_ptr[(i + 1) * nqb] - row_ptr[i * nqb];
+  __syncthreads();
+  for (int i = threadIdx.x; i < H; i += kRowThreads) {
+    const int ci = hcost[i];
+    int rank = 0;
+    for (int o = 0; o < H; ++o) rank += (hcost[o] > ci || (hcost[o] == ci && o < i)) ? 1 : 0;
+    hsorted[rank] = i;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    long long load[kParts];
+    int cnt[kParts];
+    for (int p = 0; p < kParts; ++p) load[p] = 0, cnt[p] = 0;
+    int mine = 0, pos = 0;
+    for (int k = 0; k < H; ++k) {
+      const int hh = hsorted[k];
+      int p = 0;
+      for (int i = 1; i < kParts; ++i)
+        if (load[i] < load[p]) p = i;
+      if (hh == h) mine = p, pos = cnt[p];
+      load[p] += hcost[hh];
+      cnt[p] += 1;
+    }
+    int off = 0;
+    for (int p = 0; p < kParts; ++p) {
+      s_off[p] = off;
+      off += cnt[p] * nqb;
+    }
+    s_off[kParts] = off;
+    s_start = s_off[mine] + pos * nqb;
+  }
   const int r0 = h * nqb;
   for (int qb = threadIdx.x; qb < nqb; qb += kRowThreads) cost[qb] = row_ptr[r0 + qb + 1] - row_ptr[r0 + qb];
   __syncthreads();
@@ -149,8 +191,9 @@ __global__ __launch_bounds__(kRowThreads) void lpt_order_kernel(const int32_t* _
       const int co = cost[o];
       rank += (co > cq || (co == cq && o < qb)) ? 1 : 0;
     }
-    work_order[r0 + rank] = r0 + qb;
+    out[s_start + rank] = r0 + qb;
   }
+  if (h == 0 && threadIdx.x <= kParts) out[rows + threadIdx.x] = s_off[threadIdx.x];
 }
 
 hipError_t launch_compile_count(const CompileArgs& a, hipStream_t st) {
@@ -173,7 +216,7 @@ hipError_t launch_compile_fill(const CompileArgs& a, hipStream_t st) {
 
 hipError_t launch_schedule(const int32_t* row_ptr, int H, int nqb, int32_t* work_order,
                            hipStream_t st) {
-  hipLaunchKernelGGL(lpt_order_kernel, dim3(H), dim3(kRowThreads), 0, st, row_ptr, nqb, work_order);
+  hipLaunchKernelGGL(lpt_schedule_kernel, dim3(H), dim3(kRowThreads), 0, st, row_ptr, H, nqb, work_order);
   return hipGetLastError();
 }
 

@@ -15,8 +15,8 @@ struct AttnArgs {
   void* O;
   const int32_t* row_ptr;      // unused by the dense kernel
   const int32_t* col_idx;      // unused by the dense kernel
-  const int32_t* work_order;   // may be null
-  int32_t* queue;              // may be null (one workgroup per row)
+  const int32_t* work_order;   // [rows + kParts + 1] or null
+  int32_t* queue;              // [kQueueInts] or null (one workgroup per row)
   int B, H, L, seq_len, d, block, nkb_valid;
   float scale;
   bool dtype_f32;
@@ -54,5 +54,11 @@ hipError_t launch_schedule(const int32_t* row_ptr, int H, int nqb, int32_t* work
                            hipStream_t st);
 
 constexpr int kMaxKeyBlocks = 1024;   // calibration and compile kernels keep a row in LDS
+constexpr int kMaxHeads = 1024;       // the work-order kernel keeps all head costs in LDS
+// Work partitions: MI355X has 8 XCDs and places workgroup i of a launch on XCD
+// i % 8, so a persistent workgroup serves partition blockIdx.x % 8 first.
+constexpr int kParts = 8;
+constexpr int kQueueStride = 16;      // int32 between partition counters (64 bytes)
+constexpr int kQueueInts = kParts * kQueueStride;
 
 }  // namespace calibatt

@@ -79,16 +79,19 @@ typedef enum { CALIBATT_BF16 = 0, CALIBATT_F32 = 1 } calibatt_dtype;
  *   col_idx     [row_ptr[H*nqb]] int32 kept key blocks (device).
  *   block       tokens per block (64 or 128).
  *   scale       softmax scale applied to q.k (usually 1/sqrt(d)).
- *   work_order  optional [H*nqb] int32 permutation of rows giving the order
- *               rows are started in (see calibatt_build_schedule); NULL =
- *               natural order.  The result does not depend on it (each row
- *               is reduced by one workgroup in col_idx order).
- *   queue_ws    optional int32 workspace of >= 16 entries (device), 16-byte
+ *   work_order  optional [H*nqb + 9] int32 from calibatt_build_schedule: a
+ *               permutation of the rows split into 8 partition lists,
+ *               followed by the 9 list offsets (0, ..., H*nqb).  NULL =
+ *               partition p holds heads p, p+8, ... in natural order.  The
+ *               result does not depend on it (each row is reduced by one
+ *               workgroup in col_idx order).
+ *   queue_ws    optional int32 workspace of >= 128 entries (device), 16-byte
  *               aligned.  Non-NULL selects the persistent launch: one grid
- *               that fills the GPU pulls rows from an atomic queue kept in
- *               queue_ws (reset on `stream` by the call itself); NULL = one
- *               workgroup per row.  Calls that share a queue_ws must not
- *               overlap in time.
+ *               that fills the GPU; workgroup i serves partition i % 8 (the
+ *               XCD it runs on) from an atomic counter in queue_ws, then the
+ *               other partitions.  The call resets the counters on `stream`
+ *               itself.  NULL = one workgroup per row.  Calls that share a
+ *               queue_ws must not overlap in time.
  *   nnz         number of entries of col_idx (= row_ptr[H*nqb]); used only
  *               for the host-side size check.
  * The bf16 path computes q.k and p.v on bf16 matrix cores with float32
@@ -105,11 +108,13 @@ calibatt_status calibatt_sparse_attn_fwd(const void* Q, const void* K, const voi
 
 /*
  * Dense attention forward: the same computation with every valid key block
- * kept (the pages' dense baseline, Table 1 and Table S6).  Arguments as above.
+ * kept (the pages' dense baseline, Table 1 and Table S6).  Arguments as above;
+ * queue_ws (optional, >= 128 int32) selects the persistent launch with the
+ * natural head partition.
  */
 calibatt_status calibatt_dense_attn_fwd(const void* Q, const void* K, const void* V, void* O,
                                         int block, float scale, int B, int H, int L, int seq_len,
-                                        int d, calibatt_dtype dt, void* stream);
+                                        int d, calibatt_dtype dt, int32_t* queue_ws, void* stream);
 
 /*
  * Calibration pooling: post-softmax attention mass per (query block, key
@@ -167,10 +172,14 @@ size_t calibatt_compile_ws_bytes(int P, int H, int nqb, int nkb);
 /*
  * Work order for calibatt_sparse_attn_fwd.  The pages do not describe a
  * scheduler; rows keep very different numbers of blocks (Fig. S9's
- * skip-list row lengths), so rows start longest first: heads ascending,
- * inside a head rows by kept count descending, ties by ascending qb.
- *   row_ptr     [H*nqb + 1] int32 (device).
- *   work_order  [H*nqb] int32 output (device): row indices h*nqb + qb.
+ * skip-list row lengths).  Heads (cost = kept blocks) are given, longest
+ * first, to the least-loaded of 8 partitions (ties: lowest partition), one
+ * partition per XCD so a head's K/V stays in one L2; a partition lists its
+ * heads in that order and each head's rows by kept count descending, ties by
+ * ascending qb.
+ *   row_ptr     [H*nqb + 1] int32 (device).  H <= 1024, nqb <= 1024.
+ *   work_order  [H*nqb + 9] int32 output (device): row indices h*nqb + qb of
+ *               the 8 lists, then the 9 list offsets.
  */
 calibatt_status calibatt_build_schedule(const int32_t* row_ptr, int H, int nqb,
                                         int32_t* work_order, void* stream);

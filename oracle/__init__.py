@@ -16,7 +16,8 @@ What it computes (each function cites the passage it follows):
   with a threshold (Fig. 3(b) caption, Fig. 7 caption), and the kept lists as
   CSR rows keyed by (head, query block) (abstract: per layer, head and
   timestep).
-* ``schedule``    - the longest-row-first work order within each head.
+* ``schedule``    - the work order: heads spread over 8 partitions longest
+  first, rows inside a head longest first.
 
 Pins: every function is checked by ``tests/test_oracle_*.py`` against facts
 that do not come from this code (library routines on the special cases they

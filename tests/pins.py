@@ -303,14 +303,32 @@ def pin_compile_brute(compile_impl, seed=12):
 
 def pin_lpt(lpt_impl, seed=13):
     rng = _rng(seed)
-    H, nqb = 3, 9
+    H, nqb = 11, 9
     counts = rng.integers(0, 5, size=H * nqb)
     row_ptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
-    order = lpt_impl(row_ptr, H, nqb)
-    assert sorted(order.tolist()) == list(range(H * nqb)), "a permutation"
-    for h in range(H):
-        seg = order[h * nqb:(h + 1) * nqb]
-        assert np.all(seg // nqb == h), "head-major"
-        c = counts[seg]
-        for a, b_ in zip(range(nqb - 1), range(1, nqb)):
-            assert c[a] > c[b_] or (c[a] == c[b_] and seg[a] < seg[b_]), "longest first, ties by index"
+    out = lpt_impl(row_ptr, H, nqb)
+    rows = H * nqb
+    order, off = out[:rows], out[rows:]
+    assert len(out) == rows + 9 and off[0] == 0 and off[-1] == rows and np.all(np.diff(off) >= 0)
+    assert sorted(order.tolist()) == list(range(rows)), "a permutation"
+    for p in range(8):
+        seg = order[off[p]:off[p + 1]]
+        assert len(seg) % nqb == 0, "whole heads per partition"
+        for i in range(0, len(seg), nqb):
+            hs = seg[i:i + nqb]
+            assert np.all(hs // nqb == hs[0] // nqb), "a head's rows are contiguous"
+            c = counts[hs]
+            for a in range(nqb - 1):
+                assert c[a] > c[a + 1] or (c[a] == c[a + 1] and hs[a] < hs[a + 1]), "longest first, ties by index"
+    # hand-worked greedy: 9 heads of one row with costs 9..1 over 8 partitions:
+    # heads 0..7 (costs 9..2) open partitions 0..7, head 8 (cost 1) joins the
+    # lightest, partition 7 (cost 2), after head 7.
+    rp = np.concatenate([[0], np.cumsum(np.arange(9, 0, -1))]).astype(np.int32)
+    out = lpt_impl(rp, 9, 1)
+    assert out[:9].tolist() == [0, 1, 2, 3, 4, 5, 6, 7, 8]
+    assert out[9:].tolist() == [0, 1, 2, 3, 4, 5, 6, 7, 9]
+    # equal heads spread evenly, then by index: 16 equal heads -> two per partition
+    rp = (np.arange(17) * 3).astype(np.int32)
+    out = lpt_impl(rp, 16, 1)
+    assert out[:16].tolist() == [0, 8, 1, 9, 2, 10, 3, 11, 4, 12, 5, 13, 6, 14, 7, 15]
+    assert out[16:].tolist() == [0, 2, 4, 6, 8, 10, 12, 14, 16]

@@ -71,8 +71,9 @@ def test_sparse_rejects(lib, kw, status):
 
 
 def test_dense_and_mass_reject(lib):
-    assert lib.calibatt_dense_attn_fwd(None, P32, P48, P64, 128, 0.1, 1, 1, 256, 256, 128, 0, None) == 1
-    assert lib.calibatt_dense_attn_fwd(P16, P32, P48, P64, 32, 0.1, 1, 1, 256, 256, 128, 0, None) == 7
+    assert lib.calibatt_dense_attn_fwd(None, P32, P48, P64, 128, 0.1, 1, 1, 256, 256, 128, 0, None, None) == 1
+    assert lib.calibatt_dense_attn_fwd(P16, P32, P48, P64, 32, 0.1, 1, 1, 256, 256, 128, 0, None, None) == 7
+    assert lib.calibatt_dense_attn_fwd(P16, P32, P48, P64, 128, 0.1, 1, 1, 256, 256, 128, 0, V(132), None) == 4
     assert lib.calibatt_block_mass(P16, P32, 1, 1, 256, 256, 128, 1, 128, 0.1, P48, P64, None) == 7, "f32 mass"
     assert lib.calibatt_block_mass(P16, P32, 1, 1, 256, 300, 128, 0, 128, 0.1, P48, P64, None) == 2
     assert lib.calibatt_block_mass(P16, None, 1, 1, 256, 256, 128, 0, 128, 0.1, P48, P64, None) == 1
@@ -103,6 +104,7 @@ def test_compile_and_schedule_reject(lib):
     assert lib.calibatt_build_schedule(None, 1, 1, P16, None) == 1
     assert lib.calibatt_build_schedule(P16, 0, 1, P32, None) == 2
     assert lib.calibatt_build_schedule(P16, 1, 4096, P32, None) == 7
+    assert lib.calibatt_build_schedule(P16, 2048, 8, P32, None) == 7
 
 
 def test_validate_csr(lib):

@@ -23,17 +23,24 @@ def run_sparse(q, k, v, rp, ci, cfg, work_order=None, persistent=False):
     O = torch.full_like(Q, float("nan"))
     RP, CI = i32(rp), i32(ci if len(ci) else np.zeros(1, np.int32))[: len(ci)]
     WO = None if work_order is None else i32(work_order)
-    qws = torch.zeros(16, dtype=torch.int32, device="cuda:0") if persistent else None
+    qws = cal.new_queue("cuda:0") if persistent else None
     cal.calibatt_sparse_attn_fwd(Q, K, V, O, RP, CI, cfg.block, cfg.scale, cfg.S, WO, qws)
     torch.cuda.synchronize()
     return O
 
 
-def run_dense(q, k, v, cfg):
+def as_order(perm):
+    """A row permutation with an even 8-way split, in the work-order format."""
+    rows = len(perm)
+    return np.concatenate([perm, np.linspace(0, rows, 9).astype(np.int64)]).astype(np.int32)
+
+
+def run_dense(q, k, v, cfg, persistent=False):
     dt = TDT[cfg.dtype]
     Q, K, V = (to_dev(x, dt) for x in (q, k, v))
     O = torch.full_like(Q, float("nan"))
-    cal.calibatt_dense_attn_fwd(Q, K, V, O, cfg.block, cfg.scale, cfg.S)
+    cal.calibatt_dense_attn_fwd(Q, K, V, O, cfg.block, cfg.scale, cfg.S,
+                                cal.new_queue("cuda:0") if persistent else None)
     torch.cuda.synchronize()
     return O
 
@@ -86,10 +93,11 @@ def test_dense_small(gpu, shape):
     say("case: dense small", shape)
     q, k, v = inputs(cfg)
     ref = oracle.dense_attention(q, k, v, cfg.scale, S)
-    O = run_dense(q, k, v, cfg)
-    e = err(O, ref)
-    say(f"  max err {e:.3e}")
-    assert e <= TOL[dtype]
+    for persistent in (False, True):
+        O = run_dense(q, k, v, cfg, persistent)
+        e = err(O, ref)
+        say(f"  persistent={persistent} max err {e:.3e}")
+        assert e <= TOL[dtype]
 
 
 def test_all_kept_sparse_is_dense_bitwise(gpu):
@@ -101,7 +109,8 @@ def test_all_kept_sparse_is_dense_bitwise(gpu):
     ci = np.tile(np.arange(nkv), cfg.rows).astype(np.int32)
     a = run_sparse(q, k, v, rp, ci, cfg)
     b = run_dense(q, k, v, cfg)
-    assert torch.equal(a, b)
+    c = run_dense(q, k, v, cfg, persistent=True)
+    assert torch.equal(a, b) and torch.equal(a, c)
 
 
 def test_schedule_invariance_bitwise(gpu):
@@ -112,7 +121,7 @@ def test_schedule_invariance_bitwise(gpu):
     rp, ci = synth.random_csr(rng, cfg.H, cfg.nqb, cfg.nkb_valid, 0.3, empty_rows=2, full_rows=2)
     base = run_sparse(q, k, v, rp, ci, cfg)
     lpt = oracle.lpt_work_order(rp, cfg.H, cfg.nqb)
-    orders = [lpt, lpt[::-1].copy(), rng.permutation(cfg.rows).astype(np.int32)]
+    orders = [lpt, as_order(lpt[:cfg.rows][::-1]), as_order(rng.permutation(cfg.rows))]
     for wo in orders:
         for persistent in (False, True):
             o = run_sparse(q, k, v, rp, ci, cfg, work_order=wo, persistent=persistent)
@@ -195,7 +204,7 @@ def test_mochi_dense_sampled(gpu):
     cfg = synth.get_config("mochi")
     say("case: Mochi dense, sampled rows")
     q, k, v = inputs(cfg)
-    O = run_dense(q, k, v, cfg)
+    O = run_dense(q, k, v, cfg, persistent=True)
     nkv = cfg.nkb_valid
     rp = (np.arange(cfg.rows + 1) * nkv).astype(np.int32)
     ci = np.tile(np.arange(nkv), cfg.rows).astype(np.int32)

@@ -142,7 +142,7 @@ def test_mask_bank_lookup(gpu):
     bank = cal.MaskBank(sets, cfg.H, cfg.nqb, cfg.nkb_valid, torch.device("cuda:0"))
     q, k, v = synth.gen_qkv(cfg)
     Q, K, V = (to_dev(x, torch.bfloat16) for x in (q, k, v))
-    qws = torch.zeros(16, dtype=torch.int32, device="cuda:0")
+    qws = cal.new_queue("cuda:0")
     for t in (0, 3, 5):
         rp, ci, wo, nnz = bank.lookup(t)
         assert nnz == len(sets[t][1])
@@ -202,7 +202,7 @@ def _pipeline(cfg, prompt_seeds, infer_seed, check_rows, tag):
     q, k, v = synth.gen_qkv(cfg, infer_seed)
     Q, Kt, V = (to_dev(x, torch.bfloat16) for x in (q, k, v))
     O = torch.empty_like(Q)
-    qws = torch.zeros(16, dtype=torch.int32, device=dev)
+    qws = cal.new_queue(dev)
     cal.calibatt_sparse_attn_fwd(Q, Kt, V, O, rp, ci, cfg.block, cfg.scale, cfg.S, wo, qws)
     torch.cuda.synchronize()
 

@@ -161,6 +161,18 @@ def test_csr_and_schedule_mutants_are_caught():
     assert _trips(desc_cols, [pins.pin_csr])
 
     def shortest_first(row_ptr, H, nqb):
-        o = oracle.lpt_work_order(row_ptr, H, nqb)
-        return np.concatenate([o[h * nqb:(h + 1) * nqb][::-1] for h in range(H)])
+        o = oracle.lpt_work_order(row_ptr, H, nqb).copy()
+        for i in range(0, H * nqb, nqb):
+            o[i:i + nqb] = o[i:i + nqb][::-1]
+        return o
     assert _trips(shortest_first, [pins.pin_lpt])
+
+    def heads_in_index_order(row_ptr, H, nqb):
+        from oracle import schedule as sc
+        orig = sc.head_partitions
+        sc.head_partitions = lambda rp, H_, n: [list(range(p, H_, 8)) for p in range(8)]
+        try:
+            return sc.lpt_work_order(row_ptr, H, nqb)
+        finally:
+            sc.head_partitions = orig
+    assert _trips(heads_in_index_order, [pins.pin_lpt])
