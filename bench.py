@@ -1,9 +1,11 @@
 """Benchmark: block-sparse attention forward at the Wan 2.1 14B attention shape.
 
 One step = one inference call of the hot path on the GPU: look up the mask
-set of the timestep in the resident bank and run the block-sparse forward
-(persistent launch, longest-row-first order).  Inputs are resident in HBM
-before the timed region starts.  The metric is effective kept-block
+set of the timestep in the resident bank, lay V out as V^T in a preallocated
+workspace (the attention kernel reads V transposed) and run the block-sparse
+forward (persistent launch, longest-row-first order).  Inputs are resident
+in HBM before the timed region starts.  The roofline figures are for the
+attention kernel alone, timed with events on the launch stream around it.  The metric is effective kept-block
 throughput: 4 * block^2 * d FLOP per kept (query block, key block) tile,
 counting full tiles, divided by the step time.  Also reported: the dense
 forward on the same inputs (speedup = t_dense / t_sparse, the ratio the pages
@@ -135,28 +137,35 @@ def main():
     O = torch.empty_like(Q)
     bank = cal.MaskBank(sets, cfg.H, cfg.nqb, cfg.nkb_valid, dev)
     qws = cal.new_queue(dev)
+    VT = cal.new_vt(Q)
     torch.cuda.synchronize()
     gen_s = time.perf_counter() - t_gen
 
     stream = torch.cuda.current_stream(dev)
 
-    def step(i):
+    def step(i, mid=None):
         rp, ci, wo, _ = bank.lookup(i % len(bank))
-        cal.calibatt_sparse_attn_fwd(Q, K, V, O, rp, ci, cfg.block, cfg.scale, cfg.S, wo, qws)
+        cal.calibatt_transpose_v(V, VT, cfg.S)
+        if mid is not None:
+            mid.record(stream)
+        cal.calibatt_sparse_attn_fwd(Q, K, VT, O, rp, ci, cfg.block, cfg.scale, cfg.S, wo, qws,
+                                     v_transposed=True)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    mid = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev[0].record(stream)
     for i in range(args.steps):
-        step(i)
+        step(i, mid[i])
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    launch_ms = [mid[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    transpose_ms = [ev[i].elapsed_time(mid[i]) for i in range(args.steps)]
     ms = ev[0].elapsed_time(ev[-1]) / args.steps
     nnz_steps = [int(bank.nnz[i % len(bank)]) for i in range(args.steps)]
     flops = tile_flops(cfg.block, cfg.d) * cfg.B * float(np.mean(nnz_steps))
@@ -168,12 +177,12 @@ def main():
     extra = {}
     if not args.no_dense:
         for _ in range(2):
-            cal.calibatt_dense_attn_fwd(Q, K, V, O, cfg.block, cfg.scale, cfg.S, qws)
+            cal.calibatt_dense_attn_fwd(Q, K, V, O, cfg.block, cfg.scale, cfg.S, qws, vt_ws=VT)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         nd = 5
         e0.record(stream)
         for _ in range(nd):
-            cal.calibatt_dense_attn_fwd(Q, K, V, O, cfg.block, cfg.scale, cfg.S, qws)
+            cal.calibatt_dense_attn_fwd(Q, K, V, O, cfg.block, cfg.scale, cfg.S, qws, vt_ws=VT)
         e1.record(stream)
         torch.cuda.synchronize()
         dense_ms = e0.elapsed_time(e1) / nd
@@ -246,6 +255,10 @@ def main():
             "traffic": traffic_from_profile(flops),
             "kernel": "attn_fwd_bf16_kernel<128,128,false>",
             "avg_launch_ms": round(float(np.mean(launch_ms)), 4),
+        },
+        "transpose_v": {
+            "avg_ms": round(float(np.mean(transpose_ms)), 4),
+            "GB/s": round(2 * V.numel() * 2 / (float(np.mean(transpose_ms)) * 1e-3) / 1e9, 1),
         },
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),

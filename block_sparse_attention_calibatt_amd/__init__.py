@@ -10,6 +10,8 @@ timesteps on the GPU.  Build the library with
 from ._lib import CalibattError, LIB_PATH, load
 from .capi import (
     new_queue,
+    new_vt,
+    calibatt_transpose_v,
     calibatt_sparse_attn_fwd,
     calibatt_dense_attn_fwd,
     calibatt_block_mass,
@@ -28,6 +30,8 @@ __all__ = [
     "LIB_PATH",
     "load",
     "new_queue",
+    "new_vt",
+    "calibatt_transpose_v",
     "calibatt_sparse_attn_fwd",
     "calibatt_dense_attn_fwd",
     "calibatt_block_mass",

@@ -24,6 +24,7 @@ STATUS = {
     8: "CALIBATT_ERR_HIP",
 }
 BF16, F32 = 0, 1
+V_BHLD, V_BHDL = 0, 1
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int
@@ -33,9 +34,10 @@ _sz = ctypes.c_size_t
 
 SIGNATURES = {
     "calibatt_sparse_attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _f32, _i32, _i32, _i32,
-                                        _i32, _i32, _i32, _vp, _vp, _i64, _vp]),
+                                        _i32, _i32, _i32, _vp, _vp, _i64, _i32, _vp, _vp]),
     "calibatt_dense_attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _i32, _f32, _i32, _i32, _i32, _i32, _i32,
-                                       _i32, _vp, _vp]),
+                                       _i32, _vp, _i32, _vp, _vp]),
+    "calibatt_transpose_v": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "calibatt_block_mass": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp,
                                    _vp]),
     "calibatt_compile_masks": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i64,

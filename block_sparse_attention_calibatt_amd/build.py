@@ -3,9 +3,11 @@
 Usage: python -m block_sparse_attention_calibatt_amd.build [--verbose]
 """
 
+import concurrent.futures
 import os
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
@@ -32,16 +34,39 @@ def hipcc():
     return "hipcc"
 
 
+# The attention kernel keeps Q in accumulation registers (the matrix cores
+# read it from there) and everything else in vector registers, which needs
+# the vector-register form of the matrix instructions.
+PER_FILE_FLAGS = {"attn_fwd.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
+
+
 def build(verbose=False, extra=()):
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    """Compile every source to an object (in parallel), then link the library."""
     tmp = LIB + ".tmp"
-    cmd = [hipcc()] + FLAGS + list(extra) + srcs + ["-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+    with tempfile.TemporaryDirectory(prefix="calibatt_build_") as tdir:
+        def compile_one(src):
+            obj = os.path.join(tdir, src + ".o")
+            flags = [f for f in FLAGS if f != "-shared"]
+            cmd = [hipcc()] + flags + PER_FILE_FLAGS.get(src, []) + list(extra) + [
+                "-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            res = subprocess.run(cmd, capture_output=True, text=True)
+            return src, obj, res
+
+        with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+            results = list(ex.map(compile_one, SOURCES))
+        for src, _, res in results:
+            if res.returncode != 0:
+                sys.stderr.write(res.stdout + res.stderr)
+                raise RuntimeError(f"hipcc failed on {src} with exit code {res.returncode}")
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + [o for _, o, _ in results] + ["-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError(f"linking failed with exit code {res.returncode}")
     os.replace(tmp, LIB)
     return LIB
 

@@ -12,7 +12,7 @@ import ctypes
 import numpy as np
 import torch
 
-from ._lib import BF16, F32, CalibattError, check, load
+from ._lib import BF16, F32, V_BHDL, V_BHLD, CalibattError, check, load
 
 _DT = {torch.bfloat16: BF16, torch.float32: F32}
 
@@ -53,20 +53,42 @@ def _queue(queue_ws):
         _need(queue_ws.numel() >= QUEUE_INTS, f"queue_ws needs >= {QUEUE_INTS} int32 entries")
 
 
-def _qkv(Q, K, V, O):
+def _qkv(Q, K, V, O, v_transposed=False):
     for n, t in (("Q", Q), ("K", K), ("V", V), ("O", O)):
         _dev_tensor(t, n)
     _need(Q.dim() == 4, "Q must be [B, H, L, d]")
-    for n, t in (("K", K), ("V", V), ("O", O)):
+    for n, t in (("K", K), ("O", O)):
         _need(t.shape == Q.shape and t.dtype == Q.dtype and t.device == Q.device,
               f"{n} must match Q in shape, dtype and device")
+    B, H, L, d = Q.shape
+    vshape = (B, H, d, L) if v_transposed else (B, H, L, d)
+    _need(tuple(V.shape) == vshape and V.dtype == Q.dtype and V.device == Q.device,
+          f"V must be {list(vshape)} of Q's dtype on Q's device")
     _need(Q.dtype in _DT, f"unsupported dtype {Q.dtype} (bfloat16 or float32)")
     return Q.shape
 
 
+def new_vt(Q):
+    """A V^T workspace [B, H, d, L] for the attention entry points (V given as [B, H, L, d])."""
+    B, H, L, d = Q.shape
+    return torch.empty((B, H, d, L), dtype=Q.dtype, device=Q.device)
+
+
+def _vt_args(Q, v_transposed, vt_ws):
+    """(layout code, workspace) for the C call; allocates the workspace if none is given."""
+    if v_transposed:
+        return V_BHDL, None
+    if vt_ws is None:
+        vt_ws = new_vt(Q)
+    _dev_tensor(vt_ws, "vt_ws", Q.dtype)
+    _need(vt_ws.numel() == Q.numel() and vt_ws.device == Q.device, "vt_ws must hold B*H*d*L elements on Q's device")
+    return V_BHLD, vt_ws
+
+
 def calibatt_sparse_attn_fwd(Q, K, V, O, row_ptr, col_idx, block, scale, seq_len=None,
-                             work_order=None, queue_ws=None):
-    B, H, L, d = _qkv(Q, K, V, O)
+                             work_order=None, queue_ws=None, v_transposed=False, vt_ws=None):
+    """V is [B, H, L, d], or V^T [B, H, d, L] with v_transposed=True; vt_ws receives V^T."""
+    B, H, L, d = _qkv(Q, K, V, O, v_transposed)
     seq_len = L if seq_len is None else int(seq_len)
     _dev_tensor(row_ptr, "row_ptr", torch.int32)
     _dev_tensor(col_idx, "col_idx", torch.int32)
@@ -77,22 +99,41 @@ def calibatt_sparse_attn_fwd(Q, K, V, O, row_ptr, col_idx, block, scale, seq_len
         _dev_tensor(work_order, "work_order", torch.int32)
         _need(work_order.numel() == rows + PARTS + 1, f"work_order must have H*nqb+9 = {rows + PARTS + 1} entries")
     _queue(queue_ws)
+    layout, vt_ws = _vt_args(Q, v_transposed, vt_ws)
     lib = load()
     check(lib.calibatt_sparse_attn_fwd(
         _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(row_ptr), _ptr(col_idx), int(block), float(scale),
         B, H, L, seq_len, d, _DT[Q.dtype], _ptr(work_order), _ptr(queue_ws), col_idx.numel(),
-        _stream(Q)))
+        layout, _ptr(vt_ws), _stream(Q)))
     return O
 
 
-def calibatt_dense_attn_fwd(Q, K, V, O, block, scale, seq_len=None, queue_ws=None):
-    B, H, L, d = _qkv(Q, K, V, O)
+def calibatt_dense_attn_fwd(Q, K, V, O, block, scale, seq_len=None, queue_ws=None, v_transposed=False,
+                            vt_ws=None):
+    B, H, L, d = _qkv(Q, K, V, O, v_transposed)
     seq_len = L if seq_len is None else int(seq_len)
     _queue(queue_ws)
+    layout, vt_ws = _vt_args(Q, v_transposed, vt_ws)
     lib = load()
     check(lib.calibatt_dense_attn_fwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), int(block), float(scale),
-                                      B, H, L, seq_len, d, _DT[Q.dtype], _ptr(queue_ws), _stream(Q)))
+                                      B, H, L, seq_len, d, _DT[Q.dtype], _ptr(queue_ws), layout,
+                                      _ptr(vt_ws), _stream(Q)))
     return O
+
+
+def calibatt_transpose_v(V, Vt=None, seq_len=None):
+    """V [B, H, L, d] -> V^T [B, H, d, L] (keys >= seq_len written as 0)."""
+    _dev_tensor(V, "V")
+    _need(V.dim() == 4 and V.dtype in _DT, "V must be [B, H, L, d], bfloat16 or float32")
+    B, H, L, d = V.shape
+    seq_len = L if seq_len is None else int(seq_len)
+    if Vt is None:
+        Vt = torch.empty((B, H, d, L), dtype=V.dtype, device=V.device)
+    _dev_tensor(Vt, "Vt", V.dtype)
+    _need(tuple(Vt.shape) == (B, H, d, L) and Vt.device == V.device, "Vt must be [B, H, d, L] on V's device")
+    lib = load()
+    check(lib.calibatt_transpose_v(_ptr(V), _ptr(Vt), B, H, L, seq_len, d, _DT[V.dtype], _stream(V)))
+    return Vt
 
 
 def calibatt_block_mass(Q, K, block, scale, lse_ws, mass, seq_len=None):
@@ -185,6 +226,8 @@ def calibatt_version():
 __all__ = [
     "CalibattError",
     "new_queue",
+    "new_vt",
+    "calibatt_transpose_v",
     "calibatt_sparse_attn_fwd",
     "calibatt_dense_attn_fwd",
     "calibatt_block_mass",

@@ -81,20 +81,67 @@ calibatt_status check_ptrs4(const void* Q, const void* K, const void* V, const v
   return CALIBATT_OK;
 }
 
+// V layout: with CALIBATT_V_BHLD the kernels need V^T, which is written into
+// vt_ws first; with CALIBATT_V_BHDL V already is V^T.
+// Two [B, H, L, d] tensors of `bytes` bytes each share memory.
+bool overlap(const void* p, const void* q, uintptr_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return a < b + bytes && b < a + bytes;
+}
+
+uintptr_t tensor_bytes(int B, int H, int L, int d, calibatt_dtype dt) {
+  return (uintptr_t)B * H * L * d * (dt == CALIBATT_F32 ? 4 : 2);
+}
+
+calibatt_status check_v_layout(calibatt_vlayout v_layout, const void* Q, const void* K, const void* V,
+                               const void* O, const void* vt_ws, int B, int H, int L, int d,
+                               calibatt_dtype dt) {
+  if (v_layout == CALIBATT_V_BHDL) return CALIBATT_OK;
+  if (v_layout != CALIBATT_V_BHLD) return fail(CALIBATT_ERR_SHAPE, "unknown v_layout code %d", (int)v_layout);
+  if (!vt_ws) return fail(CALIBATT_ERR_NULL, "vt_ws must be non-NULL when V is [B, H, L, d]");
+  if (!aligned(vt_ws, 16)) return fail(CALIBATT_ERR_ALIGN, "vt_ws must be 16-byte aligned");
+  const uintptr_t bytes = tensor_bytes(B, H, L, d, dt);
+  if (overlap(vt_ws, Q, bytes) || overlap(vt_ws, K, bytes) || overlap(vt_ws, V, bytes) || overlap(vt_ws, O, bytes))
+    return fail(CALIBATT_ERR_SHAPE, "vt_ws must not overlap Q, K, V or O");
+  return CALIBATT_OK;
+}
+
+calibatt_status enqueue_transpose(const void* V, void* Vt, int B, int H, int L, int seq_len, int d,
+                                  calibatt_dtype dt, void* stream) {
+  calibatt::TransposeArgs t;
+  t.V = V;
+  t.Vt = Vt;
+  t.B = B;
+  t.H = H;
+  t.L = L;
+  t.seq_len = seq_len;
+  t.d = d;
+  t.dtype_f32 = dt == CALIBATT_F32;
+  hipError_t e = calibatt::launch_transpose_v(t, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "launching the V transpose");
+  return CALIBATT_OK;
+}
+
 calibatt_status run_attention(const void* Q, const void* K, const void* V, void* O,
                               const int32_t* row_ptr, const int32_t* col_idx, int block, float scale,
                               int B, int H, int L, int seq_len, int d, calibatt_dtype dt,
-                              const int32_t* work_order, int32_t* queue_ws, bool dense,
-                              void* stream) {
+                              const int32_t* work_order, int32_t* queue_ws, calibatt_vlayout v_layout,
+                              void* vt_ws, bool dense, void* stream) {
   int ncu = 256;
   if (queue_ws) {
     hipError_t e = cu_count(&ncu);
     if (e != hipSuccess) return hip_fail(e, "querying the compute-unit count");
   }
+  const void* Vt = V;
+  if (v_layout == CALIBATT_V_BHLD) {
+    calibatt_status s = enqueue_transpose(V, vt_ws, B, H, L, seq_len, d, dt, stream);
+    if (s != CALIBATT_OK) return s;
+    Vt = vt_ws;
+  }
   calibatt::AttnArgs a;
   a.Q = Q;
   a.K = K;
-  a.V = V;
+  a.Vt = Vt;
   a.O = O;
   a.row_ptr = row_ptr;
   a.col_idx = col_idx;
@@ -123,10 +170,13 @@ calibatt_status calibatt_sparse_attn_fwd(const void* Q, const void* K, const voi
                                          const int32_t* row_ptr, const int32_t* col_idx, int block,
                                          float scale, int B, int H, int L, int seq_len, int d,
                                          calibatt_dtype dt, const int32_t* work_order,
-                                         int32_t* queue_ws, int64_t nnz, void* stream) {
+                                         int32_t* queue_ws, int64_t nnz, calibatt_vlayout v_layout,
+                                         void* vt_ws, void* stream) {
   calibatt_status s = check_ptrs4(Q, K, V, O);
   if (s != CALIBATT_OK) return s;
   s = check_qkv_shape(B, H, L, seq_len, d, dt, block);
+  if (s != CALIBATT_OK) return s;
+  s = check_v_layout(v_layout, Q, K, V, O, vt_ws, B, H, L, d, dt);
   if (s != CALIBATT_OK) return s;
   if (!row_ptr) return fail(CALIBATT_ERR_NULL, "row_ptr must be non-NULL");
   if (nnz < 0) return fail(CALIBATT_ERR_CSR, "nnz=%lld must be >= 0", (long long)nnz);
@@ -139,19 +189,35 @@ calibatt_status calibatt_sparse_attn_fwd(const void* Q, const void* K, const voi
     return fail(CALIBATT_ERR_ALIGN, "row_ptr, col_idx and work_order must be 4-byte aligned");
   if (queue_ws && !aligned(queue_ws, 16)) return fail(CALIBATT_ERR_ALIGN, "queue_ws must be 16-byte aligned");
   return run_attention(Q, K, V, O, row_ptr, col_idx, block, scale, B, H, L, seq_len, d, dt, work_order,
-                       queue_ws, false, stream);
+                       queue_ws, v_layout, vt_ws, false, stream);
 }
 
 calibatt_status calibatt_dense_attn_fwd(const void* Q, const void* K, const void* V, void* O,
                                         int block, float scale, int B, int H, int L, int seq_len,
-                                        int d, calibatt_dtype dt, int32_t* queue_ws, void* stream) {
+                                        int d, calibatt_dtype dt, int32_t* queue_ws,
+                                        calibatt_vlayout v_layout, void* vt_ws, void* stream) {
   calibatt_status s = check_ptrs4(Q, K, V, O);
   if (s != CALIBATT_OK) return s;
   s = check_qkv_shape(B, H, L, seq_len, d, dt, block);
   if (s != CALIBATT_OK) return s;
+  s = check_v_layout(v_layout, Q, K, V, O, vt_ws, B, H, L, d, dt);
+  if (s != CALIBATT_OK) return s;
   if (queue_ws && !aligned(queue_ws, 16)) return fail(CALIBATT_ERR_ALIGN, "queue_ws must be 16-byte aligned");
   return run_attention(Q, K, V, O, nullptr, nullptr, block, scale, B, H, L, seq_len, d, dt, nullptr,
-                       queue_ws, true, stream);
+                       queue_ws, v_layout, vt_ws, true, stream);
+}
+
+calibatt_status calibatt_transpose_v(const void* V, void* Vt, int B, int H, int L, int seq_len, int d,
+                                     calibatt_dtype dt, void* stream) {
+  if (!V || !Vt) return fail(CALIBATT_ERR_NULL, "V and Vt must be non-NULL");
+  if (!aligned(V, 16) || !aligned(Vt, 16)) return fail(CALIBATT_ERR_ALIGN, "V and Vt must be 16-byte aligned");
+  calibatt_status s = check_qkv_shape(B, H, L, seq_len, d, dt, 64);
+  if (s != CALIBATT_OK) return s;
+  if (overlap(V, Vt, tensor_bytes(B, H, L, d, dt)))
+    return fail(CALIBATT_ERR_SHAPE, "the transpose is out of place: V and Vt must not overlap");
+  s = enqueue_transpose(V, Vt, B, H, L, seq_len, d, dt, stream);
+  if (s != CALIBATT_OK) return s;
+  return ok();
 }
 
 calibatt_status calibatt_block_mass(const void* Q, const void* K, int B, int H, int L, int seq_len,

@@ -6,13 +6,20 @@
 // Fig. 5(b) caption).  The dense kernel is the same code with every valid key
 // block kept.
 //
-// bf16 kernel: one workgroup per query block of BLK tokens, BLK/32 waves,
-// each wave owning 32 queries.  Per kept key block: K tile -> LDS, V tile ->
-// transposed LDS, S^T = K Q^T on the matrix cores (Q held in registers),
-// online softmax in float32 with exp2 and the scale folded into one FMA,
-// P rounded to bf16, O^T += V^T P^T on the matrix cores.  The key blocks of a
-// row are reduced in col_idx order by that one workgroup, so the result does
-// not depend on the order rows are scheduled in.
+// V is read transposed, as V^T [B, H, d, L]: the P*V product contracts over
+// keys, and the matrix cores want the contracted index contiguous in each
+// lane's operand, so a V^T tile can go from HBM to LDS by DMA unchanged.
+// transpose_v_kernel makes V^T from V [B, H, L, d] when the caller has only
+// the latter (one HBM-bound pass over V).
+//
+// bf16 kernel: one workgroup per query block of BLK tokens, BLK/32 waves of
+// 32 queries each, two workgroups per CU.  Per 64-key sub-tile of a kept key
+// block: K tile and V^T tile -> LDS by DMA (the next sub-tile's DMA runs
+// while this one is computed), S^T = K Q^T on the matrix cores (Q held in
+// registers), online softmax in float32 with exp2 and the scale folded into
+// one FMA, P rounded to bf16, O^T += V^T P^T on the matrix cores.  The key
+// blocks of a row are reduced in col_idx order by that one workgroup, so the
+// result does not depend on the order rows are scheduled in.
 //
 // Scheduling: with a queue pointer the grid is persistent; each workgroup
 // pops rows from the atomic counter of its XCD's partition of the work order
@@ -24,96 +31,33 @@
 
 namespace calibatt {
 
-// Pipeline geometry of the bf16 kernel.  Keys are consumed in sub-tiles of
-// 64 (a 128-token kept block is two sub-tiles).  Two LDS buffers each hold a
-// K sub-tile (rows of 16-byte chunks, XOR-swizzled) and a transposed V
-// sub-tile.  While sub-tile j is computed from one buffer, sub-tile j+1 is in
-// flight: K goes straight from HBM into the other buffer by buffer-to-LDS
-// DMA (no registers), V comes into registers in 8-key x 4-d blocks (8 loads
-// of 8 bytes per thread) and is transposed with byte permutes and written
-// after the compute of sub-tile j.
-template <int D, int BLK>
-struct Pipe {
-  static constexpr int NT = BLK * 2;        // threads: BLK/32 waves of 64
-  static constexpr int NW = BLK / 32;
-  static constexpr int BN = 64;             // keys per sub-tile
-  static constexpr int SPB = BLK / BN;      // sub-tiles per kept block
-  static constexpr int CH = D / 8;          // 16-byte chunks per K row
-  static constexpr int CHV = BN / 8;        // 16-byte chunks per Vt row
-  static constexpr int KROWS_PER_LOAD = 64 / CH;            // rows one wave DMA covers
-  static constexpr int KLOADS = BN / KROWS_PER_LOAD / NW;   // DMA instructions per wave
-  static constexpr int DQ = D / 4;          // 4-wide d groups
-  static constexpr int VBLK = (BN / 8) * DQ;                // 8x4 V blocks per sub-tile
-  static constexpr int VPER = (VBLK + NT - 1) / NT;
-};
-
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Per-lane byte offsets of the K DMA (one per DMA instruction), relative to the sub-tile start.
-template <int D, int BLK>
-__device__ __forceinline__ void k_dma_offsets(int w, int lane, int* koff) {
-  using P = Pipe<D, BLK>;
-#pragma unroll
-  for (int i = 0; i < P::KLOADS; ++i) {
-    const int row = (w * P::KLOADS + i) * P::KROWS_PER_LOAD + lane / P::CH;
-    const int chunk = (lane % P::CH) ^ swz<P::CH>(row);
-    koff[i] = (row * D + chunk * 8) * 2;
-  }
+// s_waitcnt immediate (gfx9 encoding) for vmcnt(N) with expcnt and lgkmcnt
+// left unconstrained.  Written with the builtin rather than inline asm so that
+// the compiler's own wait insertion knows which DMA has landed.
+template <int N>
+constexpr int vmcnt_imm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  return (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
 }
 
-// K sub-tile starting at key k0 -> swizzled LDS buffer, by DMA.
-template <int D, int BLK>
-__device__ __forceinline__ void k_dma(__amdgpu_buffer_rsrc_t rk, int k0, u32x4* ldsK, int w, const int* koff) {
-  using P = Pipe<D, BLK>;
-#pragma unroll
-  for (int i = 0; i < P::KLOADS; ++i) {
-    const int r0 = (w * P::KLOADS + i) * P::KROWS_PER_LOAD;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(ldsK + r0 * P::CH), 16, koff[i], k0 * D * 2, 0, 0);
-  }
-}
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>()); }
 
-template <int D, int BLK>
-__device__ __forceinline__ void v_load(__amdgpu_buffer_rsrc_t rv, int k0, int voff, u32x2* st) {
-  using P = Pipe<D, BLK>;
-#pragma unroll
-  for (int j = 0; j < P::VPER; ++j) {
-    const int vb = threadIdx.x + j * P::NT;
-    if (P::VBLK % P::NT == 0 || vb < P::VBLK) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        st[8 * j + i] = __builtin_amdgcn_raw_buffer_load_b64(
-            rv, voff + j * (P::NT / P::DQ) * 8 * D * 2 + i * D * 2, k0 * D * 2, 0);
-    }
-  }
+// Workgroup barrier for the DMA pipeline.  Every wave first waits (s_waitcnt
+// vmcnt) for its own DMA writes that the next reads need; once it has, they
+// are in LDS, so the barrier itself needs no wait for memory traffic.  The
+// empty asm statements keep the compiler from moving LDS accesses across it;
+// LDS reads and writes of the wave itself complete in order.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
-
-template <int D, int BLK>
-__device__ __forceinline__ void v_store(const u32x2* st, u32x4* ldsV) {
-  using P = Pipe<D, BLK>;
-#pragma unroll
-  for (int j = 0; j < P::VPER; ++j) {
-    const int vb = threadIdx.x + j * P::NT;
-    if (P::VBLK % P::NT == 0 || vb < P::VBLK) {
-      const int dq = vb % P::DQ, kg = vb / P::DQ;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        u32x4 o;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t x = st[8 * j + 2 * q][e >> 1], y = st[8 * j + 2 * q + 1][e >> 1];
-          o[q] = __builtin_amdgcn_perm(y, x, (e & 1) ? 0x07060302u : 0x05040100u);
-        }
-        ldsV[chunk_index<P::CHV>(dq * 4 + e, kg)] = o;
-      }
-    }
-  }
-}
-
-__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Where a workgroup's next row comes from.  With a work order, rows are
 // grouped into kParts partition lists (offsets after the rows); without one,
@@ -142,7 +86,7 @@ __device__ __forceinline__ void for_each_row(const RowSource& src, int32_t* queu
     for (int tries = 0; tries < kParts;) {
       if (threadIdx.x == 0) *s_item = atomicAdd(queue + p * kQueueStride, 1);
       __syncthreads();
-      const int k = *s_item;
+      const int k = __builtin_amdgcn_readfirstlane(*s_item);
       __syncthreads();
       const int len = src.part_len(p);
       if (k >= src.B * len) {
@@ -160,48 +104,141 @@ __device__ __forceinline__ void for_each_row(const RowSource& src, int32_t* queu
   }
 }
 
+// Lazy rescale: the reference maximum of a query moves only when a score
+// passes it by more than kLazyLog2 in log2 units, so probabilities stay below
+// 2^kLazyLog2 and O and l are rescaled a few times per row instead of on
+// most sub-tiles.  O = acc / l is the same for any reference.
 constexpr float kLazyLog2 = 8.f;
 
 template <int I>
-struct Buf {
+struct Cst {
   static constexpr int value = I;
 };
 
+// Geometry of the 32-queries-per-wave bf16 kernel: BLK/32 waves, each owning
+// 32 queries, keys in sub-tiles of 64 (a kept block of 128 is two), two LDS
+// stages that each hold a K sub-tile (64 rows of D/8 16-byte units) and a
+// V^T sub-tile (D rows of 8 units), both filled by DMA.
+template <int D, int BLK>
+struct Geo {
+  static constexpr int NW = BLK / 32;
+  static constexpr int NT = NW * 64;
+  static constexpr int BN = 64;
+  static constexpr int SPB = BLK / BN;
+  static constexpr int CH = D / 8;
+  static constexpr int DS = D / 16;
+  static constexpr int DT = D / 32;
+  static constexpr int KS = BN / 16;
+  static constexpr int KUNITS = BN * CH;
+  static constexpr int VUNITS = D * 8;
+  static constexpr int KPER = KUNITS / 64 / NW;
+  static constexpr int VPER = VUNITS / 64 / NW;
+  // DMA instruction m of a tile writes LDS units 64m .. 64m+63; the lane's
+  // source offset within them depends on m modulo 4 only (the swizzles use
+  // row bits 0..4), and wave w issues m = w, w + NW, ...
+  static constexpr int PAT = 4 / NW;
+};
+
+// K sub-tile (keys k0 .. k0+63) -> swizzled LDS, by DMA.
+template <int D, int BLK>
+__device__ __forceinline__ void k_dma(__amdgpu_buffer_rsrc_t rk, int k0, u32x4* lds, int w, const int* pat) {
+  using G = Geo<D, BLK>;
+#pragma unroll
+  for (int i = 0; i < G::KPER; ++i) {
+    const int m = w + G::NW * i;
+    const int voff = pat[i % G::PAT];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(lds + 64 * m), 16, voff, k0 * D * 2 + m * 1024, 0, 0);
+  }
+}
+
+// V^T sub-tile (D rows, keys k0 .. k0+63) -> swizzled LDS, by DMA.  Row d of
+// the tile is 128 contiguous bytes of V^T row d; instruction m covers rows
+// 8m .. 8m+7.
+template <int D, int BLK>
+__device__ __forceinline__ void v_dma(__amdgpu_buffer_rsrc_t rv, int k0, int L, u32x4* lds, int w, const int* pat) {
+  using G = Geo<D, BLK>;
+#pragma unroll
+  for (int i = 0; i < G::VPER; ++i) {
+    const int m = w + G::NW * i;
+    const int voff = pat[i % G::PAT];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(lds + 64 * m), 16, voff, k0 * 2 + m * 16 * L, 0, 0);
+  }
+}
+
+// bf16 kernel, 32 queries per wave.  Sub-tile j of a row is computed from
+// stage j%2 while the DMA of sub-tile j+1 fills the other stage:
+//   S^T = K Q^T (Q in registers) on the matrix cores; tail keys masked;
+//   row maxima and the lazy rescale; P = exp2(S c2 - m c2) rounded to bf16
+//   and added to the row sums; O^T += V^T P^T on the matrix cores;
+//   wait for the DMA, barrier.
+// Two waves per SIMD (two workgroups per CU) let one wave's softmax run
+// beside the other's products.
 template <int D, int BLK, bool DENSE>
 __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ Vt,
     bf16* __restrict__ O, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     const int32_t* __restrict__ work_order, int32_t* __restrict__ queue, int items, int H, int L,
     int seq_len, int nkb_valid, float c2) {
-  using P = Pipe<D, BLK>;
-  constexpr int DS = D / 16;     // k-steps of Q K^T
-  constexpr int DT = D / 32;     // 32-row d tiles of O^T
-  // two buffers as separate LDS objects, so loads into one never alias reads of the other
-  __shared__ u32x4 ldsK0[P::BN * P::CH];
-  __shared__ u32x4 ldsK1[P::BN * P::CH];
-  __shared__ u32x4 ldsV0[D * P::CHV];
-  __shared__ u32x4 ldsV1[D * P::CHV];
+  using G = Geo<D, BLK>;
+  constexpr int DS = G::DS, DT = G::DT, KS = G::KS, CH = G::CH;
+  // the two stages are separate LDS objects, so the DMA into one never
+  // aliases the operand reads of the other
+  __shared__ u32x4 st0[G::KUNITS + G::VUNITS];
+  __shared__ u32x4 st1[G::KUNITS + G::VUNITS];
   __shared__ int s_item;
 
   const int nqb = L / BLK;
   const int rows = H * nqb;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5, c = lane & 31;
   const int prow = qk_row_perm(c);
   const uint32_t slab_bytes = (uint32_t)L * D * 2;
   const float lazy_thr = kLazyLog2 / c2;   // in raw score units
 
-  int koff[P::KLOADS];
-  k_dma_offsets<D, BLK>(w, lane, koff);
-  const int voff = (((threadIdx.x / P::DQ) * 8) * D + (threadIdx.x % P::DQ) * 4) * 2;
+  int kpat[G::PAT], vpat[G::PAT];
+#pragma unroll
+  for (int i = 0; i < G::PAT; ++i) {
+    const int m = w + G::NW * i;
+    const int krow = m * (64 / CH) + lane / CH;
+    kpat[i] = (lane / CH) * D * 2 + (((lane % CH) ^ swz<CH>(krow)) * 16);
+    const int vrow = m * 8 + lane / 8;
+    vpat[i] = (lane / 8) * L * 2 + (((lane % 8) ^ swz<8>(vrow)) * 16);
+  }
+  // operand reads: K row 32*mt + prow, unit 2s+g; V^T row 32*t + c, unit
+  // 2ks+g.  The swizzles see row bits 0..4 only, so the unit is the lane's
+  // constant XOR the k-step.
+  const int kx = g ^ swz<CH>(prow);
+  const int vx = g ^ swz<8>(c);
+  auto kread = [&](const u32x4* t, int mt, int s) __attribute__((always_inline)) {
+    return t[(32 * mt + prow) * CH + ((2 * s) ^ kx)];
+  };
+  auto vread = [&](const u32x4* t, int dt, int ks) __attribute__((always_inline)) {
+    return t[G::KUNITS + (32 * dt + c) * 8 + ((2 * ks) ^ vx)];
+  };
+
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one2 = {(bf16)1.f, (bf16)1.f};
 
   const RowSource src{work_order, rows, nqb, H, items / rows};
   for_each_row(src, queue, &s_item, [&](int b, int r) {
     const int h = r / nqb, qb = r - h * nqb;
     const size_t base = ((size_t)b * H + h) * (size_t)L * D;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + base, slab_bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + base, slab_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vt + base, slab_bytes);
     const int q = qb * BLK + 32 * w + c;   // this lane's query
+
+    const int beg = DENSE ? 0 : row_ptr[r];
+    const int nsub = ((DENSE ? nkb_valid : row_ptr[r + 1]) - beg) * G::SPB;
+    auto key0 = [&](int j) __attribute__((always_inline)) -> int {
+      const int kb = DENSE ? j / G::SPB : col_idx[beg + j / G::SPB];
+      return kb * BLK + (j % G::SPB) * G::BN;
+    };
+    if (nsub > 0) {
+      const int k0 = key0(0);
+      k_dma<D, BLK>(rk, k0, st0, w, kpat);
+      v_dma<D, BLK>(rv, k0, L, st0 + G::KUNITS, w, vpat);
+    }
 
     bf16x8 qreg[DS];
 #pragma unroll
@@ -212,53 +249,32 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
     for (int t = 0; t < DT; ++t) oacc[t] = f32x16{};
     float m_run = kNegInf, l_run = 0.f;
-
-    const int beg = DENSE ? 0 : row_ptr[r];
-    const int nsub = ((DENSE ? nkb_valid : row_ptr[r + 1]) - beg) * P::SPB;
-    auto key0 = [&](int j) -> int {
-      const int kb = DENSE ? j / P::SPB : col_idx[beg + j / P::SPB];
-      return kb * BLK + (j % P::SPB) * P::BN;
-    };
-
-    u32x2 st[8 * P::VPER];
-    if (nsub > 0) {
-      const int k0 = key0(0);
-      k_dma<D, BLK>(rk, k0, ldsK0, w, koff);
-      v_load<D, BLK>(rv, k0, voff, st);
-      v_store<D, BLK>(st, ldsV0);
-    }
     wait_vm();
-    __syncthreads();
+    lds_barrier();
 
-    // one sub-tile: compute from buffer B while sub-tile j+1 streams into buffer 1-B
-    auto step = [&](int j, auto bufc) {
+    auto step = [&](int j, auto bufc) __attribute__((always_inline)) {
       constexpr int B = decltype(bufc)::value;
-      u32x4* const kcur = B == 0 ? ldsK0 : ldsK1;
-      u32x4* const vcur = B == 0 ? ldsV0 : ldsV1;
-      u32x4* const knext = B == 0 ? ldsK1 : ldsK0;
-      u32x4* const vnext = B == 0 ? ldsV1 : ldsV0;
+      const u32x4* const cur = B == 0 ? st0 : st1;
+      u32x4* const nxt = B == 0 ? st1 : st0;
       const int k0 = key0(j);
-      const bool more = j + 1 < nsub;
-      if (more) {
+      if (j + 1 < nsub) {
         const int k1 = key0(j + 1);
-        k_dma<D, BLK>(rk, k1, knext, w, koff);
-        v_load<D, BLK>(rv, k1, voff, st);
+        k_dma<D, BLK>(rk, k1, nxt, w, kpat);
+        v_dma<D, BLK>(rv, k1, L, nxt + G::KUNITS, w, vpat);
       }
 
-      // S^T for 64 keys x 32 queries: two 32x32 accumulators
       f32x16 sacc[2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        const int row = 32 * mt + prow;
         u32x4 a[DS];
 #pragma unroll
-        for (int s = 0; s < DS; ++s) a[s] = kcur[chunk_index<P::CH>(row, 2 * s + g)];
+        for (int s = 0; s < DS; ++s) a[s] = kread(cur, mt, s);
         f32x16 acc = {};
 #pragma unroll
         for (int s = 0; s < DS; ++s) acc = mfma_bf16(__builtin_bit_cast(bf16x8, a[s]), qreg[s], acc);
         sacc[mt] = acc;
       }
-      if (k0 + P::BN > seq_len) {
+      if (k0 + G::BN > seq_len) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -272,10 +288,6 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, sacc[mt][rr]);
       mx = pair_max(mx);
-      // Lazy rescale: the reference maximum moves only when a score passes it
-      // by more than kLazyLog2 in log2 units, so probabilities stay below
-      // 2^kLazyLog2 and O and l are rescaled a few times per row instead of
-      // on most sub-tiles.  O = acc / l is the same for any reference.
       if (__any(mx > m_run + lazy_thr)) {
         const float m_new = fmaxf(m_run, mx);
         const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_run - m_new) * c2);
@@ -286,19 +298,16 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(
       }
       const float mc = (m_run == kNegInf ? 0.f : m_run) * c2;
 
-      bf16x8 pb[4];
+      bf16x8 pb[KS];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 0; ks < KS; ++ks) {
         bf16x8 v;
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = (bf16)fast_exp2(fmaf(sacc[ks >> 1][8 * (ks & 1) + e], c2, -mc));
         pb[ks] = v;
       }
-      // row sum of the rounded probabilities, the same values the P*V product uses
-      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-      const bf16x2 one2 = {(bf16)1.f, (bf16)1.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const bf16x2 pr = {pb[ks][e], pb[ks][e + 1]};
@@ -307,21 +316,19 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(
 
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
-        const int row = 32 * t + c;
-        u32x4 a[4];
+        u32x4 a[KS];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) a[ks] = vcur[chunk_index<P::CHV>(row, 2 * ks + g)];
+        for (int ks = 0; ks < KS; ++ks) a[ks] = vread(cur, t, ks);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) oacc[t] = mfma_bf16(__builtin_bit_cast(bf16x8, a[ks]), pb[ks], oacc[t]);
+        for (int ks = 0; ks < KS; ++ks) oacc[t] = mfma_bf16(__builtin_bit_cast(bf16x8, a[ks]), pb[ks], oacc[t]);
       }
-      if (more) v_store<D, BLK>(st, vnext);
       wait_vm();
-      __syncthreads();
+      lds_barrier();
     };
 
     for (int j = 0; j < nsub; j += 2) {
-      step(j, Buf<0>{});
-      if (j + 1 < nsub) step(j + 1, Buf<1>{});
+      step(j, Cst<0>{});
+      if (j + 1 < nsub) step(j + 1, Cst<1>{});
     }
 
     const float l_tot = pair_sum(l_run);
@@ -347,15 +354,15 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(
 // the K slice are fed in that order), which is the B layout of P^T.
 template <int D, int BLK, bool DENSE>
 __global__ __launch_bounds__(BLK * 2) void attn_fwd_f32_kernel(
-    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ Vt,
     float* __restrict__ O, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     const int32_t* __restrict__ work_order, int32_t* __restrict__ queue, int items, int H, int L,
     int seq_len, int nkb_valid, float c2) {
   constexpr int NT = BLK * 2;
-  constexpr int KP = D + 1;   // padded K row (floats)
+  constexpr int KP = D + 1;   // padded K and V rows (floats)
   constexpr int DT = D / 32;
   __shared__ float ldsK[32 * KP];
-  __shared__ float ldsV[32 * D];
+  __shared__ float ldsV[32 * KP];
   __shared__ int s_item;
 
   const int nqb = L / BLK;
@@ -390,7 +397,8 @@ __global__ __launch_bounds__(BLK * 2) void attn_fwd_f32_kernel(
         for (int i = threadIdx.x; i < 32 * D; i += NT) {
           const int kr = i / D, dd = i % D;
           ldsK[kr * KP + dd] = K[base + (size_t)(k0 + kr) * D + dd];
-          ldsV[kr * D + dd] = V[base + (size_t)(k0 + kr) * D + dd];
+          const int vk = i % 32, vd = i / 32;   // V^T row vd, 32 consecutive keys
+          ldsV[vk * KP + vd] = Vt[base + (size_t)vd * L + k0 + vk];
         }
         __syncthreads();
         f32x16 sacc = {};
@@ -424,7 +432,7 @@ __global__ __launch_bounds__(BLK * 2) void attn_fwd_f32_kernel(
           oacc[t] *= alpha;
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr)
-            oacc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(ldsV[(2 * rr + g) * D + 32 * t + c], p[rr],
+            oacc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(ldsV[(2 * rr + g) * KP + 32 * t + c], p[rr],
                                                            oacc[t], 0, 0, 0);
         }
       }
@@ -437,6 +445,38 @@ __global__ __launch_bounds__(BLK * 2) void attn_fwd_f32_kernel(
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) Ob[32 * t + 8 * (rr >> 2) + 4 * g + (rr & 3)] = oacc[t][rr] * inv;
   });
+}
+
+// V [B, H, L, d] -> V^T [B, H, d, L], keys at or past seq_len written as 0
+// (so that the zero probabilities of masked keys never meet a non-finite V).
+// One workgroup per 64 keys of one head; elements are moved as raw bits.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void transpose_v_kernel(const T* __restrict__ V, T* __restrict__ Vt, int L,
+                                                           int seq_len) {
+  constexpr int KB = 64;
+  constexpr int VEC = 16 / sizeof(T);      // elements per 16-byte access
+  constexpr int RS = D + 4 / sizeof(T);    // padded LDS row (elements): rows shift by one bank
+  __shared__ T tile[KB * RS];
+  const int tiles_per_head = L / KB;
+  const int bh = blockIdx.x / tiles_per_head;
+  const int k0 = (blockIdx.x - bh * tiles_per_head) * KB;
+  const T* src = V + (size_t)bh * L * D + (size_t)k0 * D;
+  T* dst = Vt + (size_t)bh * D * L + k0;
+  for (int i = threadIdx.x; i < KB * D / VEC; i += 256) {
+    const int kr = i / (D / VEC), dv = (i % (D / VEC)) * VEC;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(src + (size_t)kr * D + dv);
+#pragma unroll
+    for (int x = 0; x < VEC; ++x) tile[kr * RS + dv + x] = reinterpret_cast<const T*>(&v)[x];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < D * KB / VEC; i += 256) {
+    const int d = i / (KB / VEC), kk = (i % (KB / VEC)) * VEC;
+    u32x4 v;
+#pragma unroll
+    for (int x = 0; x < VEC; ++x)
+      reinterpret_cast<T*>(&v)[x] = (k0 + kk + x < seq_len) ? tile[(kk + x) * RS + d] : T(0);
+    *reinterpret_cast<u32x4*>(dst + (size_t)d * L + kk) = v;
+  }
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int n, int32_t v) {
@@ -468,12 +508,12 @@ static hipError_t launch_typed(const AttnArgs& a, hipStream_t st) {
   }
   if (a.dtype_f32) {
     hipLaunchKernelGGL((attn_fwd_f32_kernel<D, BLK, DENSE>), dim3(grid), dim3(threads), 0, st,
-                       (const float*)a.Q, (const float*)a.K, (const float*)a.V, (float*)a.O,
+                       (const float*)a.Q, (const float*)a.K, (const float*)a.Vt, (float*)a.O,
                        a.row_ptr, a.col_idx, a.work_order, a.queue, items, a.H, a.L, a.seq_len,
                        a.nkb_valid, c2);
   } else {
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, BLK, DENSE>), dim3(grid), dim3(threads), 0, st,
-                       (const bf16*)a.Q, (const bf16*)a.K, (const bf16*)a.V, (bf16*)a.O, a.row_ptr,
+                       (const bf16*)a.Q, (const bf16*)a.K, (const bf16*)a.Vt, (bf16*)a.O, a.row_ptr,
                        a.col_idx, a.work_order, a.queue, items, a.H, a.L, a.seq_len, a.nkb_valid, c2);
   }
   return hipGetLastError();
@@ -489,6 +529,23 @@ static hipError_t dispatch(const AttnArgs& a, hipStream_t st) {
 
 hipError_t launch_attention(const AttnArgs& a, bool dense, hipStream_t st) {
   return dense ? dispatch<true>(a, st) : dispatch<false>(a, st);
+}
+
+template <typename T>
+static hipError_t transpose_typed(const TransposeArgs& a, hipStream_t st) {
+  const int grid = a.B * a.H * (a.L / 64);
+  if (grid == 0) return hipSuccess;
+  if (a.d == 128)
+    hipLaunchKernelGGL((transpose_v_kernel<T, 128>), dim3(grid), dim3(256), 0, st, (const T*)a.V, (T*)a.Vt, a.L,
+                       a.seq_len);
+  else
+    hipLaunchKernelGGL((transpose_v_kernel<T, 64>), dim3(grid), dim3(256), 0, st, (const T*)a.V, (T*)a.Vt, a.L,
+                       a.seq_len);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_v(const TransposeArgs& a, hipStream_t st) {
+  return a.dtype_f32 ? transpose_typed<uint32_t>(a, st) : transpose_typed<uint16_t>(a, st);
 }
 
 }  // namespace calibatt

@@ -11,7 +11,7 @@ namespace calibatt {
 struct AttnArgs {
   const void* Q;
   const void* K;
-  const void* V;
+  const void* Vt;              // V^T [B, H, d, L]
   void* O;
   const int32_t* row_ptr;      // unused by the dense kernel
   const int32_t* col_idx;      // unused by the dense kernel
@@ -24,6 +24,15 @@ struct AttnArgs {
 };
 
 hipError_t launch_attention(const AttnArgs& a, bool dense, hipStream_t st);
+
+struct TransposeArgs {
+  const void* V;   // [B, H, L, d]
+  void* Vt;        // [B, H, d, L]
+  int B, H, L, seq_len, d;
+  bool dtype_f32;
+};
+
+hipError_t launch_transpose_v(const TransposeArgs& a, hipStream_t st);
 
 struct MassArgs {
   const void* Q;

@@ -15,7 +15,9 @@
  * - Q, K, V, O are [B, H, L, d] row-major and contiguous (d fastest).  L is
  *   the padded token count and must be a multiple of `block`; tokens
  *   t >= seq_len are padding: they are never keys, and their output rows are
- *   written as zero.
+ *   written as zero.  The attention entry points also accept V transposed,
+ *   as V^T [B, H, d, L] (CALIBATT_V_BHDL): the kernels read V^T, and given V
+ *   they first write V^T into a caller workspace.
  * - One block is `block` tokens; query blocks and key blocks have the same
  *   size.  nqb = nkb = L / block; nkb_valid = ceil(seq_len / block).
  * - A mask set is CSR over rows r = h * nqb + qb (h-major): the kept key
@@ -47,7 +49,7 @@
 extern "C" {
 #endif
 
-#define CALIBATT_VERSION 100 /* major * 100 + minor */
+#define CALIBATT_VERSION 200 /* major * 100 + minor */
 
 typedef enum {
   CALIBATT_OK = 0,
@@ -63,6 +65,12 @@ typedef enum {
 
 typedef enum { CALIBATT_BF16 = 0, CALIBATT_F32 = 1 } calibatt_dtype;
 
+/* Layout of the V argument of the attention entry points. */
+typedef enum {
+  CALIBATT_V_BHLD = 0, /* V [B, H, L, d]; the call transposes it into vt_ws first */
+  CALIBATT_V_BHDL = 1  /* V^T [B, H, d, L] (V[b,h,j,:] is column j); vt_ws unused */
+} calibatt_vlayout;
+
 /*
  * Block-sparse attention forward (inference step).
  * Pages: abstract (selected connections computed densely, unselected ones
@@ -73,7 +81,10 @@ typedef enum { CALIBATT_BF16 = 0, CALIBATT_F32 = 1 } calibatt_dtype;
  *     O[b,h,i,:] = sum_{j in J_i} softmax_j(scale * Q[b,h,i,:] . K[b,h,j,:]) V[b,h,j,:]
  * A row with no kept block, and every padded query row, is written as zero.
  *
- *   Q, K, V     [B, H, L, d] inputs of dtype `dt` (device).
+ *   Q, K        [B, H, L, d] inputs of dtype `dt` (device).
+ *   V           input of dtype `dt` (device) in the layout `v_layout` names.
+ *               With CALIBATT_V_BHDL its entries for keys >= seq_len must be
+ *               finite (they are multiplied by zero probabilities).
  *   O           [B, H, L, d] output of dtype `dt` (device); fully written.
  *   row_ptr     [H*nqb + 1] int32 CSR row offsets (device).
  *   col_idx     [row_ptr[H*nqb]] int32 kept key blocks (device).
@@ -94,6 +105,11 @@ typedef enum { CALIBATT_BF16 = 0, CALIBATT_F32 = 1 } calibatt_dtype;
  *               queue_ws must not overlap in time.
  *   nnz         number of entries of col_idx (= row_ptr[H*nqb]); used only
  *               for the host-side size check.
+ *   v_layout    CALIBATT_V_BHLD or CALIBATT_V_BHDL (see V).
+ *   vt_ws       with CALIBATT_V_BHLD: workspace of B*H*d*L elements of `dt`
+ *               (device), 16-byte aligned, not overlapping Q, K, V or O; on
+ *               return (once the stream reaches it) it holds V^T, as written
+ *               by calibatt_transpose_v.  Ignored with CALIBATT_V_BHDL.
  * The bf16 path computes q.k and p.v on bf16 matrix cores with float32
  * accumulation and a float32 softmax; probabilities are rounded to bf16
  * before the p.v product; O is rounded to bf16.  The f32 path is float32
@@ -104,7 +120,8 @@ calibatt_status calibatt_sparse_attn_fwd(const void* Q, const void* K, const voi
                                          int block, float scale, int B, int H, int L,
                                          int seq_len, int d, calibatt_dtype dt,
                                          const int32_t* work_order, int32_t* queue_ws,
-                                         int64_t nnz, void* stream);
+                                         int64_t nnz, calibatt_vlayout v_layout, void* vt_ws,
+                                         void* stream);
 
 /*
  * Dense attention forward: the same computation with every valid key block
@@ -114,7 +131,19 @@ calibatt_status calibatt_sparse_attn_fwd(const void* Q, const void* K, const voi
  */
 calibatt_status calibatt_dense_attn_fwd(const void* Q, const void* K, const void* V, void* O,
                                         int block, float scale, int B, int H, int L, int seq_len,
-                                        int d, calibatt_dtype dt, int32_t* queue_ws, void* stream);
+                                        int d, calibatt_dtype dt, int32_t* queue_ws,
+                                        calibatt_vlayout v_layout, void* vt_ws, void* stream);
+
+/*
+ * V [B, H, L, d] -> V^T [B, H, d, L]: Vt[b,h,c,j] = V[b,h,j,c] for j <
+ * seq_len and 0 for the padded keys j >= seq_len.  A layout change only (the
+ * attention kernels contract P*V over keys and read V^T tiles as they lie);
+ * the attention entry points call it themselves for CALIBATT_V_BHLD.
+ *   V, Vt   inputs/outputs of dtype `dt` (device), 16-byte aligned, not
+ *           overlapping.  L must be a multiple of 64; d in {64, 128}.
+ */
+calibatt_status calibatt_transpose_v(const void* V, void* Vt, int B, int H, int L, int seq_len, int d,
+                                     calibatt_dtype dt, void* stream);
 
 /*
  * Calibration pooling: post-softmax attention mass per (query block, key

@@ -18,7 +18,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _lib.header_symbols()
-    assert len(names) == 10
+    assert len(names) == 11
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     for n in names:
@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert cal.calibatt_version() == 100
+    assert cal.calibatt_version() == 200
     for code, name in _lib.STATUS.items():
         assert cal.calibatt_status_string(code) != "unknown status"
     assert cal.calibatt_status_string(99) == "unknown status"
@@ -40,7 +40,8 @@ P16, P32, P48, P64 = V(16), V(32), V(48), V(64)     # aligned fake addresses, ne
 
 def _sparse(lib, **kw):
     a = dict(Q=P16, K=P32, V=P48, O=P64, row_ptr=V(128), col_idx=V(256), block=128, scale=0.1, B=1, H=2,
-             L=1024, seq_len=1000, d=128, dt=0, work_order=None, queue_ws=None, nnz=10, stream=None)
+             L=1024, seq_len=1000, d=128, dt=0, work_order=None, queue_ws=None, nnz=10, v_layout=1, vt_ws=None,
+             stream=None)
     a.update(kw)
     return lib.calibatt_sparse_attn_fwd(*a.values())
 
@@ -64,6 +65,10 @@ def _sparse(lib, **kw):
     (dict(B=1024, H=64, L=65536), 2),
     (dict(nnz=-1), 5),
     (dict(nnz=2 * 8 * 8 + 1), 5),
+    (dict(v_layout=0), 1),                       # V given as [B, H, L, d] needs vt_ws
+    (dict(v_layout=0, vt_ws=V((1 << 30) + 8)), 4),
+    (dict(v_layout=0, vt_ws=V(16 + 4096)), 2),   # overlaps Q
+    (dict(v_layout=2), 2),
 ])
 def test_sparse_rejects(lib, kw, status):
     assert _sparse(lib, **kw) == status
@@ -71,13 +76,31 @@ def test_sparse_rejects(lib, kw, status):
 
 
 def test_dense_and_mass_reject(lib):
-    assert lib.calibatt_dense_attn_fwd(None, P32, P48, P64, 128, 0.1, 1, 1, 256, 256, 128, 0, None, None) == 1
-    assert lib.calibatt_dense_attn_fwd(P16, P32, P48, P64, 32, 0.1, 1, 1, 256, 256, 128, 0, None, None) == 7
-    assert lib.calibatt_dense_attn_fwd(P16, P32, P48, P64, 128, 0.1, 1, 1, 256, 256, 128, 0, V(132), None) == 4
+    def dense(*a, layout=1, vt=None):
+        return lib.calibatt_dense_attn_fwd(*a, layout, vt, None)
+    assert dense(None, P32, P48, P64, 128, 0.1, 1, 1, 256, 256, 128, 0, None) == 1
+    assert dense(P16, P32, P48, P64, 32, 0.1, 1, 1, 256, 256, 128, 0, None) == 7
+    assert dense(P16, P32, P48, P64, 128, 0.1, 1, 1, 256, 256, 128, 0, V(132)) == 4
+    assert dense(P16, P32, P48, P64, 128, 0.1, 1, 1, 256, 256, 128, 0, None, layout=0) == 1
+    assert dense(P16, P32, P48, P64, 128, 0.1, 1, 1, 256, 256, 128, 0, None, layout=0, vt=V(48)) == 2
     assert lib.calibatt_block_mass(P16, P32, 1, 1, 256, 256, 128, 1, 128, 0.1, P48, P64, None) == 7, "f32 mass"
     assert lib.calibatt_block_mass(P16, P32, 1, 1, 256, 300, 128, 0, 128, 0.1, P48, P64, None) == 2
     assert lib.calibatt_block_mass(P16, None, 1, 1, 256, 256, 128, 0, 128, 0.1, P48, P64, None) == 1
     assert lib.calibatt_block_mass(P16, P32, 1, 1, 128 * 2048, 256, 64, 0, 128, 0.1, P48, P64, None) == 7
+
+
+def test_transpose_rejects(lib):
+    def tr(V_, Vt, B=1, H=2, L=1024, S=1000, d=128, dt=0):
+        return lib.calibatt_transpose_v(V_, Vt, B, H, L, S, d, dt, None)
+    assert tr(None, P32) == 1
+    assert tr(P16, None) == 1
+    assert tr(V(17), P32) == 4
+    assert tr(P16, V(1 << 30), L=1000) == 2
+    assert tr(P16, V(1 << 30), d=96) == 7
+    assert tr(P16, V(1 << 30), dt=5) == 3
+    assert tr(P16, V(1 << 30), S=1025) == 2
+    assert tr(P16, V(16 + 1024)) == 2        # in place / overlapping
+    assert cal.calibatt_last_error() != ""
 
 
 def test_compile_and_schedule_reject(lib):

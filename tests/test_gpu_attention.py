@@ -130,6 +130,61 @@ def test_schedule_invariance_bitwise(gpu):
     assert torch.equal(again, base), "repeat run"
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_transpose_v_exact(gpu, dtype, d):
+    """V [B,H,L,d] -> V^T [B,H,d,L]: a pure layout change, keys >= seq_len zeroed."""
+    cfg = small_cfg(B=2, H=3, L=640, S=601, d=d, block=64, dtype=dtype)
+    say("case: V transpose", dtype, d)
+    _, _, v = inputs(cfg)
+    V = to_dev(v, TDT[dtype])
+    Vt = cal.calibatt_transpose_v(V, seq_len=cfg.S)
+    torch.cuda.synchronize()
+    want = np.swapaxes(V.float().cpu().numpy(), 2, 3).copy()
+    want[:, :, :, cfg.S:] = 0.0
+    assert np.array_equal(Vt.float().cpu().numpy(), want)
+
+
+def test_v_transposed_input_bitwise(gpu):
+    """Passing V^T directly gives the same bits as passing V."""
+    cfg = small_cfg(H=3, L=1024, S=1000)
+    say("case: V^T input == V input, bitwise")
+    q, k, v = inputs(cfg)
+    rng = np.random.default_rng(17)
+    rp, ci = synth.random_csr(rng, cfg.H, cfg.nqb, cfg.nkb_valid, 0.5, empty_rows=1, full_rows=1)
+    Q, K, V = (to_dev(x, torch.bfloat16) for x in (q, k, v))
+    RP, CI = i32(rp), i32(ci)
+    O1, O2 = torch.empty_like(Q), torch.empty_like(Q)
+    vt = cal.new_vt(Q)
+    cal.calibatt_sparse_attn_fwd(Q, K, V, O1, RP, CI, cfg.block, cfg.scale, cfg.S, vt_ws=vt)
+    Vt = cal.calibatt_transpose_v(V, seq_len=cfg.S)
+    cal.calibatt_sparse_attn_fwd(Q, K, Vt, O2, RP, CI, cfg.block, cfg.scale, cfg.S, v_transposed=True)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2)
+    assert torch.equal(vt, Vt), "the workspace holds V^T after the call"
+
+
+def test_row_lengths_one_to_nine_blocks(gpu):
+    """Rows of 0..9 kept blocks: every remainder of the sub-tile pipeline."""
+    cfg = small_cfg(H=2, L=2048, S=2000)
+    say("case: row lengths 0..9 blocks")
+    q, k, v = inputs(cfg)
+    rng = np.random.default_rng(23)
+    rows, counts = [], []
+    for r in range(cfg.rows):
+        c = r % 10
+        counts.append(c)
+        rows.append(np.sort(rng.choice(cfg.nkb_valid, size=c, replace=False)))
+    rp = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    ci = np.concatenate(rows).astype(np.int32)
+    ref = oracle.sparse_attention_gather(q, k, v, rp, ci, cfg.block, cfg.scale, cfg.S)
+    for persistent in (False, True):
+        O = run_sparse(q, k, v, rp, ci, cfg, persistent=persistent)
+        e = err(O, ref)
+        say(f"  persistent={persistent} max err {e:.3e}")
+        assert e <= TOL["bf16"]
+
+
 def test_empty_mask(gpu):
     cfg = small_cfg(H=1, L=512, S=512)
     say("case: every row empty")
