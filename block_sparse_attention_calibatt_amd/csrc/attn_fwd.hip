@@ -104,11 +104,12 @@ __device__ __forceinline__ void for_each_row(const RowSource& src, int32_t* queu
   }
 }
 
-// Lazy rescale: the reference maximum of a query moves only when a score
-// passes it by more than kLazyLog2 in log2 units, so probabilities stay below
-// 2^kLazyLog2 and O and l are rescaled a few times per row instead of on
-// most sub-tiles.  O = acc / l is the same for any reference.
-constexpr float kLazyLog2 = 8.f;
+// Lazy rescale: the reference of a query's probabilities moves (to the
+// running maximum) only when a sub-tile's probabilities sum past kSumCap, so
+// O and l are rescaled a few times per row, and the row maxima are computed
+// only then.  Probabilities stay at most kSumCap; O = acc / l is the same for
+// any reference.
+constexpr float kSumCap = 4096.f;
 
 template <int I>
 struct Cst {
@@ -139,40 +140,40 @@ struct Geo {
   static constexpr int PAT = 4 / NW;
 };
 
-// K sub-tile (keys k0 .. k0+63) -> swizzled LDS, by DMA.
+// DMA instruction i (0 .. KPER+VPER-1) of this wave for the sub-tile at key
+// k0: i < KPER moves part of the K sub-tile (keys k0 .. k0+63, rows of D/8
+// units), the rest part of the V^T sub-tile (D rows of 128 contiguous bytes
+// of V^T, instruction m covering rows 8m .. 8m+7), each into its swizzled
+// LDS tile of the stage.
 template <int D, int BLK>
-__device__ __forceinline__ void k_dma(__amdgpu_buffer_rsrc_t rk, int k0, u32x4* lds, int w, const int* pat) {
+__device__ __forceinline__ void tile_dma(int i, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int k0,
+                                         int L, u32x4* stage, int w, const int* kpat, const int* vpat) {
   using G = Geo<D, BLK>;
-#pragma unroll
-  for (int i = 0; i < G::KPER; ++i) {
+  if (i < G::KPER) {
     const int m = w + G::NW * i;
-    const int voff = pat[i % G::PAT];
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(lds + 64 * m), 16, voff, k0 * D * 2 + m * 1024, 0, 0);
-  }
-}
-
-// V^T sub-tile (D rows, keys k0 .. k0+63) -> swizzled LDS, by DMA.  Row d of
-// the tile is 128 contiguous bytes of V^T row d; instruction m covers rows
-// 8m .. 8m+7.
-template <int D, int BLK>
-__device__ __forceinline__ void v_dma(__amdgpu_buffer_rsrc_t rv, int k0, int L, u32x4* lds, int w, const int* pat) {
-  using G = Geo<D, BLK>;
-#pragma unroll
-  for (int i = 0; i < G::VPER; ++i) {
-    const int m = w + G::NW * i;
-    const int voff = pat[i % G::PAT];
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(lds + 64 * m), 16, voff, k0 * 2 + m * 16 * L, 0, 0);
+    const int voff = kpat[i % G::PAT];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(stage + 64 * m), 16, voff, k0 * D * 2 + m * 1024, 0, 0);
+  } else {
+    const int m = w + G::NW * (i - G::KPER);
+    const int voff = vpat[(i - G::KPER) % G::PAT];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(stage + G::KUNITS + 64 * m), 16, voff,
+                                             k0 * 2 + m * 16 * L, 0, 0);
   }
 }
 
 // bf16 kernel, 32 queries per wave.  Sub-tile j of a row is computed from
 // stage j%2 while the DMA of sub-tile j+1 fills the other stage:
-//   S^T = K Q^T (Q in registers) on the matrix cores; tail keys masked;
-//   row maxima and the lazy rescale; P = exp2(S c2 - m c2) rounded to bf16
-//   and added to the row sums; O^T += V^T P^T on the matrix cores;
-//   wait for the DMA, barrier.
-// Two waves per SIMD (two workgroups per CU) let one wave's softmax run
-// beside the other's products.
+//   S^T = K Q^T (Q in registers) on the matrix cores, the two 32-key halves
+//   interleaved, with this wave's DMA instructions for sub-tile j+1 spread
+//   between the products (issued in one burst right after the barrier they
+//   queue behind the other waves' and stall the wave); tail keys masked;
+//   P = exp2(S c2 - mc) rounded to bf16 and its row sums; the lazy rescale;
+//   O^T += V^T P^T on the matrix cores; wait for the DMA, barrier.
+// The key-block indices of a row are read two blocks ahead, so their scalar
+// loads have returned when a DMA needs them.  Past the row's last sub-tile
+// the DMA loads that sub-tile again into the free stage, so every step has
+// the same shape.  Two waves per SIMD (two workgroups per CU) let one wave's
+// softmax run beside the other's products.
 template <int D, int BLK, bool DENSE>
 __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ Vt,
@@ -194,7 +195,6 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(
   const int g = lane >> 5, c = lane & 31;
   const int prow = qk_row_perm(c);
   const uint32_t slab_bytes = (uint32_t)L * D * 2;
-  const float lazy_thr = kLazyLog2 / c2;   // in raw score units
 
   int kpat[G::PAT], vpat[G::PAT];
 #pragma unroll
@@ -208,13 +208,25 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(
   // operand reads: K row 32*mt + prow, unit 2s+g; V^T row 32*t + c, unit
   // 2ks+g.  The swizzles see row bits 0..4 only, so the unit is the lane's
   // constant XOR the k-step.
+  // The byte offsets of the DS + KS operand reads are kept in registers for
+  // the whole kernel, so that a read costs no address arithmetic: the stage
+  // and the 32-row tile are added as the instruction's immediate offset.
   const int kx = g ^ swz<CH>(prow);
   const int vx = g ^ swz<8>(c);
+  int koffs[DS], voffs[KS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) koffs[s] = (prow * CH + ((2 * s) ^ kx)) * 16;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) voffs[ks] = (G::KUNITS + c * 8 + ((2 * ks) ^ vx)) * 16;
+#pragma unroll
+  for (int s = 0; s < DS; ++s) asm volatile("" : "+v"(koffs[s]));
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(voffs[ks]));
   auto kread = [&](const u32x4* t, int mt, int s) __attribute__((always_inline)) {
-    return t[(32 * mt + prow) * CH + ((2 * s) ^ kx)];
+    return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(t) + mt * 32 * CH * 16 + koffs[s]);
   };
   auto vread = [&](const u32x4* t, int dt, int ks) __attribute__((always_inline)) {
-    return t[G::KUNITS + (32 * dt + c) * 8 + ((2 * ks) ^ vx)];
+    return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(t) + dt * 32 * 8 * 16 + voffs[ks]);
   };
 
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -229,15 +241,21 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(
     const int q = qb * BLK + 32 * w + c;   // this lane's query
 
     const int beg = DENSE ? 0 : row_ptr[r];
-    const int nsub = ((DENSE ? nkb_valid : row_ptr[r + 1]) - beg) * G::SPB;
-    auto key0 = [&](int j) __attribute__((always_inline)) -> int {
-      const int kb = DENSE ? j / G::SPB : col_idx[beg + j / G::SPB];
-      return kb * BLK + (j % G::SPB) * G::BN;
+    const int nblk = (DENSE ? nkb_valid : row_ptr[r + 1]) - beg;
+    const int nsub = nblk * G::SPB;
+    // key blocks: kb0 holds the current sub-tile's, kb1 the next block's,
+    // kb2 the one after (its load is in flight for a whole block)
+    auto blk = [&](int i) __attribute__((always_inline)) -> int {
+      i = i < nblk ? i : nblk - 1;
+      return DENSE ? i : col_idx[beg + i];
     };
+    int kb0 = 0, kb1 = 0, kb2 = 0;
     if (nsub > 0) {
-      const int k0 = key0(0);
-      k_dma<D, BLK>(rk, k0, st0, w, kpat);
-      v_dma<D, BLK>(rv, k0, L, st0 + G::KUNITS, w, vpat);
+      kb0 = blk(0);
+      kb1 = blk(1);
+      kb2 = blk(2);
+#pragma unroll
+      for (int i = 0; i < G::KPER + G::VPER; ++i) tile_dma<D, BLK>(i, rk, rv, kb0 * BLK, L, st0, w, kpat, vpat);
     }
 
     bf16x8 qreg[DS];
@@ -248,31 +266,44 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(
     f32x16 oacc[DT];
 #pragma unroll
     for (int t = 0; t < DT; ++t) oacc[t] = f32x16{};
-    float m_run = kNegInf, l_run = 0.f;
+    float mc = kNegInf, l_run = 0.f;   // reference of P (log2 units) and row sum
     wait_vm();
     lds_barrier();
 
-    auto step = [&](int j, auto bufc) __attribute__((always_inline)) {
+    // sub-tile j (part p of its block kb0): S from stage B, DMA of sub-tile
+    // j+1 (clamped to the last) into the other stage
+    auto step = [&](int j, auto bufc, int p) __attribute__((always_inline)) {
       constexpr int B = decltype(bufc)::value;
+      constexpr int NDMA = G::KPER + G::VPER;
       const u32x4* const cur = B == 0 ? st0 : st1;
       u32x4* const nxt = B == 0 ? st1 : st0;
-      const int k0 = key0(j);
-      if (j + 1 < nsub) {
-        const int k1 = key0(j + 1);
-        k_dma<D, BLK>(rk, k1, nxt, w, kpat);
-        v_dma<D, BLK>(rv, k1, L, nxt + G::KUNITS, w, vpat);
-      }
+      const int k0 = kb0 * BLK + p * G::BN;
+      const int kd = j + 1 >= nsub ? k0 : (p + 1 < G::SPB ? k0 + G::BN : kb1 * BLK);
 
+      // slot s: operand reads two slots ahead, the products of both 32-key
+      // halves at k-step s, then this slot's share of the DMA
       f32x16 sacc[2];
+      {
+        u32x4 ra[3][2];
+        ra[0][0] = kread(cur, 0, 0);
+        ra[0][1] = kread(cur, 1, 0);
+        if (DS > 1) {
+          ra[1][0] = kread(cur, 0, 1);
+          ra[1][1] = kread(cur, 1, 1);
+        }
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        u32x4 a[DS];
+        for (int s = 0; s < DS; ++s) {
+          if (s + 2 < DS) {
+            ra[(s + 2) % 3][0] = kread(cur, 0, s + 2);
+            ra[(s + 2) % 3][1] = kread(cur, 1, s + 2);
+          }
+          sacc[0] = mfma_bf16(__builtin_bit_cast(bf16x8, ra[s % 3][0]), qreg[s], s == 0 ? f32x16{} : sacc[0]);
+          sacc[1] = mfma_bf16(__builtin_bit_cast(bf16x8, ra[s % 3][1]), qreg[s], s == 0 ? f32x16{} : sacc[1]);
 #pragma unroll
-        for (int s = 0; s < DS; ++s) a[s] = kread(cur, mt, s);
-        f32x16 acc = {};
-#pragma unroll
-        for (int s = 0; s < DS; ++s) acc = mfma_bf16(__builtin_bit_cast(bf16x8, a[s]), qreg[s], acc);
-        sacc[mt] = acc;
+          for (int i = s * NDMA / DS; i < (s + 1) * NDMA / DS; ++i)
+            tile_dma<D, BLK>(i, rk, rv, kd, L, nxt, w, kpat, vpat);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       if (k0 + G::BN > seq_len) {
 #pragma unroll
@@ -282,37 +313,49 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(
             if (k0 + 32 * mt + slice_key(rr, g) >= seq_len) sacc[mt][rr] = kNegInf;
       }
 
-      float mx = kNegInf;
+      // P = exp2(S c2 - mc) against the current reference, and its row sums
+      // (of the rounded values, the ones P*V uses) in two chains
+      bf16x8 pb[KS];
+      float ls[2];
+      auto probs = [&]() __attribute__((always_inline)) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+        for (int ks = 0; ks < KS; ++ks) {
+          bf16x8 v;
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, sacc[mt][rr]);
-      mx = pair_max(mx);
-      if (__any(mx > m_run + lazy_thr)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_run - m_new) * c2);
+          for (int e = 0; e < 8; ++e) v[e] = (bf16)fast_exp2(fmaf(sacc[ks >> 1][8 * (ks & 1) + e], c2, -mc));
+          pb[ks] = v;
+        }
+        ls[0] = ls[1] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const bf16x2 pr = {pb[ks][e], pb[ks][e + 1]};
+            ls[(e >> 1) & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ls[(e >> 1) & 1], false);
+          }
+      };
+      probs();
+      // The reference moves only when a lane's sum passes kSumCap (or is not
+      // finite: the first sub-tile, whose reference is -inf): then to the row
+      // maximum, with O and l rescaled and P recomputed.  Every probability
+      // stays at most kSumCap, and O = acc / l does not depend on the
+      // reference.
+      if (__any(!(ls[0] + ls[1] <= kSumCap))) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, sacc[mt][rr]);
+        float mc_new = fmaxf(mc, pair_max(mx) * c2);
+        if (mc_new == kNegInf) mc_new = 0.f;   // every key so far masked
+        const float alpha = fast_exp2(mc - mc_new);
         l_run *= alpha;
 #pragma unroll
         for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
-        m_run = m_new;
+        mc = mc_new;
+        probs();
       }
-      const float mc = (m_run == kNegInf ? 0.f : m_run) * c2;
-
-      bf16x8 pb[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 v;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (bf16)fast_exp2(fmaf(sacc[ks >> 1][8 * (ks & 1) + e], c2, -mc));
-        pb[ks] = v;
-      }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const bf16x2 pr = {pb[ks][e], pb[ks][e + 1]};
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, l_run, false);
-        }
+      l_run += ls[0] + ls[1];
 
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
@@ -326,9 +369,18 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(
       lds_barrier();
     };
 
+    // after the last sub-tile of a block the window moves on one block
+    int nb = 3;   // next block index to load
+    auto shift = [&]() __attribute__((always_inline)) {
+      kb0 = kb1;
+      kb1 = kb2;
+      kb2 = blk(nb++);
+    };
     for (int j = 0; j < nsub; j += 2) {
-      step(j, Cst<0>{});
-      if (j + 1 < nsub) step(j + 1, Cst<1>{});
+      step(j, Cst<0>{}, 0);
+      if (G::SPB == 1) shift();
+      if (j + 1 < nsub) step(j + 1, Cst<1>{}, G::SPB == 1 ? 0 : 1);
+      shift();
     }
 
     const float l_tot = pair_sum(l_run);
