@@ -253,7 +253,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic_from_profile(flops),
-            "kernel": "attn_fwd_bf16_kernel<128,128,false>",
+            "kernel": "attn_fwd_pp_kernel<128,false>",
             "avg_launch_ms": round(float(np.mean(launch_ms)), 4),
         },
         "transpose_v": {

@@ -140,25 +140,39 @@ struct Geo {
   static constexpr int PAT = 4 / NW;
 };
 
+// K DMA instruction i (0 .. KPER-1) of wave w for the K sub-tile at key k0
+// (keys k0 .. k0+63, rows of D/8 units) into its swizzled LDS tile.
+template <int D, int BLK>
+__device__ __forceinline__ void k_dma_one(int i, __amdgpu_buffer_rsrc_t rk, int k0, u32x4* kt, int w,
+                                          const int* kpat) {
+  using G = Geo<D, BLK>;
+  const int m = w + G::NW * i;
+  const int voff = kpat[i % G::PAT];
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kt + 64 * m), 16, voff, k0 * D * 2 + m * 1024, 0, 0);
+}
+
+// V^T DMA instruction i (0 .. VPER-1) of wave w for the V^T sub-tile at key
+// k0 (D rows of 128 contiguous bytes of V^T; instruction m covers rows
+// 8m .. 8m+7) into its swizzled LDS tile.
+template <int D, int BLK>
+__device__ __forceinline__ void v_dma_one(int i, __amdgpu_buffer_rsrc_t rv, int k0, int L, u32x4* vt, int w,
+                                          const int* vpat) {
+  using G = Geo<D, BLK>;
+  const int m = w + G::NW * i;
+  const int voff = vpat[i % G::PAT];
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vt + 64 * m), 16, voff, k0 * 2 + m * 16 * L, 0, 0);
+}
+
 // DMA instruction i (0 .. KPER+VPER-1) of this wave for the sub-tile at key
-// k0: i < KPER moves part of the K sub-tile (keys k0 .. k0+63, rows of D/8
-// units), the rest part of the V^T sub-tile (D rows of 128 contiguous bytes
-// of V^T, instruction m covering rows 8m .. 8m+7), each into its swizzled
-// LDS tile of the stage.
+// k0, into a stage that holds the K tile followed by the V^T tile.
 template <int D, int BLK>
 __device__ __forceinline__ void tile_dma(int i, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int k0,
                                          int L, u32x4* stage, int w, const int* kpat, const int* vpat) {
   using G = Geo<D, BLK>;
-  if (i < G::KPER) {
-    const int m = w + G::NW * i;
-    const int voff = kpat[i % G::PAT];
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(stage + 64 * m), 16, voff, k0 * D * 2 + m * 1024, 0, 0);
-  } else {
-    const int m = w + G::NW * (i - G::KPER);
-    const int voff = vpat[(i - G::KPER) % G::PAT];
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(stage + G::KUNITS + 64 * m), 16, voff,
-                                             k0 * 2 + m * 16 * L, 0, 0);
-  }
+  if (i < G::KPER)
+    k_dma_one<D, BLK>(i, rk, k0, stage, w, kpat);
+  else
+    v_dma_one<D, BLK>(i - G::KPER, rv, k0, L, stage + G::KUNITS, w, vpat);
 }
 
 // bf16 kernel, 32 queries per wave.  Sub-tile j of a row is computed from
@@ -401,6 +415,363 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(
   });
 }
 
+// bf16 kernel for 128-token blocks in ping-pong form.  One workgroup of 8
+// waves per CU serves one row: wave group A (waves 0-3) takes the even
+// 64-key sub-tiles of the row and group B (waves 4-7) the odd ones, each
+// wave the same 32 queries as its partner w ^ 4, which shares its SIMD.
+// Each group keeps its own reference, row sums and O; at the end of the row
+// B hands its state to A through LDS and A writes the combined result (a
+// fixed split, so the result does not depend on scheduling).
+//
+// Time is cut into barrier-separated phases t = 0 .. n+1 (n sub-tiles).  In
+// phase t the group of parity t does only matrix-core work and the other
+// only vector work, so the two waves of a SIMD always hold complementary
+// work:
+//   matrix phase  S(t) = K(t) Q^T, with this wave's share of the DMA of
+//                 K(t+2) and V^T(t) spread between the products; then
+//                 O^T += V^T(t-2) P(t-2)^T
+//   vector phase  P(t-1) = exp2(S(t-1) c2 - mc) rounded to bf16, its row
+//                 sums and the lazy rescale; then wait for this wave's DMA
+//                 of the phase before
+// A DMA issued in phase t has landed by the end of phase t+1, so K(x) is
+// issued two phases before S(x) reads it and V^T(x) two phases before
+// P*V(x).  K and V^T rotate through three LDS stages each.
+template <int D, bool DENSE>
+__global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ Vt,
+    bf16* __restrict__ O, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+    const int32_t* __restrict__ work_order, int32_t* __restrict__ queue, int items, int H, int L,
+    int seq_len, int nkb_valid, float c2) {
+  constexpr int BLK = 128;
+  using G = Geo<D, BLK>;   // one wave group: NW = 4 waves of 32 queries
+  constexpr int DS = G::DS, DT = G::DT, KS = G::KS, CH = G::CH;
+  constexpr int NDMA = G::KPER + G::VPER;
+  static_assert(G::KUNITS == G::VUNITS, "K and V^T stages have one size");
+  constexpr int OBJ = G::KUNITS * 16;   // bytes of one stage
+  __shared__ u32x4 ks0[G::KUNITS], ks1[G::KUNITS], ks2[G::KUNITS];
+  __shared__ u32x4 vs0[G::VUNITS], vs1[G::VUNITS], vs2[G::VUNITS];
+  __shared__ int s_item;
+  u32x4* const kst[3] = {ks0, ks1, ks2};
+  u32x4* const vst[3] = {vs0, vs1, vs2};
+
+  const int nqb = L / BLK;
+  const int rows = H * nqb;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wv >> 2;   // 0: even sub-tiles, 1: odd
+  const int w = wv & 3;      // query slice of the block
+  const int g = lane >> 5, c = lane & 31;
+  const int prow = qk_row_perm(c);
+  const uint32_t slab_bytes = (uint32_t)L * D * 2;
+
+  int kpat[G::PAT], vpat[G::PAT];
+#pragma unroll
+  for (int i = 0; i < G::PAT; ++i) {
+    const int m = w + G::NW * i;
+    const int krow = m * (64 / CH) + lane / CH;
+    kpat[i] = (lane / CH) * D * 2 + (((lane % CH) ^ swz<CH>(krow)) * 16);
+    const int vrow = m * 8 + lane / 8;
+    vpat[i] = (lane / 8) * L * 2 + (((lane % 8) ^ swz<8>(vrow)) * 16);
+  }
+  // operand read offsets, kept in registers (see the 4-wave kernel)
+  const int kx = g ^ swz<CH>(prow);
+  const int vx = g ^ swz<8>(c);
+  int koffs[DS], voffs[KS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) koffs[s] = (prow * CH + ((2 * s) ^ kx)) * 16;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) voffs[ks] = (c * 8 + ((2 * ks) ^ vx)) * 16;
+#pragma unroll
+  for (int s = 0; s < DS; ++s) asm volatile("" : "+v"(koffs[s]));
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(voffs[ks]));
+  auto kread = [&](const u32x4* t, int mt, int s) __attribute__((always_inline)) {
+    return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(t) + mt * 32 * CH * 16 + koffs[s]);
+  };
+  auto vread = [&](const u32x4* t, int dt, int ks) __attribute__((always_inline)) {
+    return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(t) + dt * 32 * 8 * 16 + voffs[ks]);
+  };
+
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one2 = {(bf16)1.f, (bf16)1.f};
+
+  const RowSource src{work_order, rows, nqb, H, items / rows};
+  for_each_row(src, queue, &s_item, [&](int b, int r) {
+    const int h = r / nqb, qb = r - h * nqb;
+    const size_t base = ((size_t)b * H + h) * (size_t)L * D;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + base, slab_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vt + base, slab_bytes);
+    const int q = qb * BLK + 32 * w + c;   // this lane's query
+
+    const int beg = DENSE ? 0 : row_ptr[r];
+    const int nblk = (DENSE ? nkb_valid : row_ptr[r + 1]) - beg;
+    const int n = nblk * 2;   // sub-tiles
+    auto blk = [&](int i) __attribute__((always_inline)) -> int {
+      i = i < nblk ? i : nblk - 1;
+      i = i < 0 ? 0 : i;
+      return DENSE ? i : col_idx[beg + i];
+    };
+    // key blocks around phase t (block b = t/2): kbm = b-1, kb0 = b, kb1 =
+    // b+1; kb2 (b+2) is loaded a block ahead
+    int kbm = 0, kb0 = 0, kb1 = 0, kb2 = 0;
+    if (n > 0) {
+      kb0 = blk(0);
+      kb1 = blk(1);
+      kb2 = blk(2);
+      // K(0) by group A, K(1) by group B
+#pragma unroll
+      for (int i = 0; i < G::KPER; ++i)
+        k_dma_one<D, BLK>(i, rk, kb0 * BLK + grp * G::BN, grp == 0 ? ks0 : ks1, w, kpat);
+    }
+
+    // Q is scaled by c2 (the softmax scale in log2 units) on loading and
+    // rounded to bf16, so that the products give scores in log2 units and,
+    // with the accumulators started at -ref, exp2 needs no vector arithmetic
+    // before it
+    bf16x8 qreg[DS];
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      const bf16x8 qv = *reinterpret_cast<const bf16x8*>(Q + base + (size_t)q * D + 16 * s + 8 * g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qreg[s][e] = (bf16)((float)qv[e] * c2);
+    }
+
+    f32x16 oacc[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t) oacc[t] = f32x16{};
+    // this group's reference (log2 units) and row sum; fresh until the
+    // reference has been set from the maximum of a sub-tile with valid keys
+    float ref = 0.f, l_run = 0.f;
+    bool fresh = true;
+    f32x16 cneg = {};   // -ref in every accumulator register
+    f32x16 sacc[2];
+    bf16x8 pb[KS];
+    bool rescale = false;   // O *= alpha is due before the next P*V
+    float alpha = 1.f;
+    wait_vm();
+    lds_barrier();
+
+    // after a phase of odd t the next phase is in the next block
+    auto shift = [&](int t) __attribute__((always_inline)) {
+      kbm = kb0;
+      kb0 = kb1;
+      kb1 = kb2;
+      kb2 = blk((t + 1) / 2 + 2);
+    };
+    // matrix phase t, with TM = t % 6 fixing the stages
+    auto mphase = [&](int t, auto tmc) __attribute__((always_inline)) {
+      constexpr int TM = decltype(tmc)::value;
+      constexpr int KST = TM % 3, KDST = (TM + 2) % 3, VST = (TM + 1) % 3, VDST = TM % 3;
+      // the wave index, re-read in every phase so that the DMA destinations
+      // (one per stage and instruction) are formed where they are used
+      // instead of all being kept in scalar registers
+      int wq;
+      asm volatile("s_mov_b32 %0, %1" : "=s"(wq) : "s"(w));
+      {
+        if (t < n) {
+          const int kd = kb1 * BLK + (TM & 1) * G::BN;          // K(t+2), clamped by blk()
+          const int vd = kb0 * BLK + (TM & 1) * G::BN;          // V^T(t)
+          const u32x4* const kc = kst[KST];
+          u32x4 ra[3][2];
+          ra[0][0] = kread(kc, 0, 0);
+          ra[0][1] = kread(kc, 1, 0);
+          if (DS > 1) {
+            ra[1][0] = kread(kc, 0, 1);
+            ra[1][1] = kread(kc, 1, 1);
+          }
+#pragma unroll
+          for (int s = 0; s < DS; ++s) {
+            if (s + 2 < DS) {
+              ra[(s + 2) % 3][0] = kread(kc, 0, s + 2);
+              ra[(s + 2) % 3][1] = kread(kc, 1, s + 2);
+            }
+            sacc[0] = mfma_bf16(__builtin_bit_cast(bf16x8, ra[s % 3][0]), qreg[s], s == 0 ? cneg : sacc[0]);
+            sacc[1] = mfma_bf16(__builtin_bit_cast(bf16x8, ra[s % 3][1]), qreg[s], s == 0 ? cneg : sacc[1]);
+#pragma unroll
+            for (int i = s * NDMA / DS; i < (s + 1) * NDMA / DS; ++i) {
+              if (i < G::KPER)
+                k_dma_one<D, BLK>(i, rk, kd, kst[KDST], wq, kpat);
+              else
+                v_dma_one<D, BLK>(i - G::KPER, rv, vd, L, vst[VDST], wq, vpat);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        if (t >= 2 && t < n + 2) {
+          // O moves to the reference P(t-2) was computed against
+          if (rescale) {
+#pragma unroll
+            for (int tt = 0; tt < DT; ++tt) oacc[tt] *= alpha;
+            rescale = false;
+          }
+          const u32x4* const vc = vst[VST];
+          constexpr int NP = DT * KS;   // products, i -> ks = i / DT, dt = i % DT
+          u32x4 ra[3];
+          ra[0] = vread(vc, 0, 0);
+          if (NP > 1) ra[1] = vread(vc, 1 % DT, 1 / DT);
+#pragma unroll
+          for (int i = 0; i < NP; ++i) {
+            if (i + 2 < NP) ra[(i + 2) % 3] = vread(vc, (i + 2) % DT, (i + 2) / DT);
+            oacc[i % DT] = mfma_bf16(__builtin_bit_cast(bf16x8, ra[i % 3]), pb[i / DT], oacc[i % DT]);
+            if (i & 1) __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+      lds_barrier();
+      if (TM & 1) shift(t);
+    };
+    // vector phase t: P(t-1); then this wave's DMA of the phase before, which
+    // the next phase reads, must have landed
+    auto vphase = [&](int t, auto tmc) __attribute__((always_inline)) {
+      constexpr int TM = decltype(tmc)::value;
+      {
+        const int x = t - 1;
+        if (x >= 0 && x < n) {
+          const int k0 = (TM & 1) ? kb0 * BLK : kbm * BLK + G::BN;
+          if (k0 + G::BN > seq_len) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+              for (int rr = 0; rr < 16; ++rr)
+                if (k0 + 32 * mt + slice_key(rr, g) >= seq_len) sacc[mt][rr] = kNegInf;
+          }
+          float ls[2];
+          auto probs = [&]() __attribute__((always_inline)) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+              bf16x8 v;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) v[e] = (bf16)fast_exp2(sacc[ks >> 1][8 * (ks & 1) + e]);
+              pb[ks] = v;
+            }
+            ls[0] = ls[1] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+              for (int e = 0; e < 8; e += 2) {
+                const bf16x2 pr = {pb[ks][e], pb[ks][e + 1]};
+                ls[(e >> 1) & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ls[(e >> 1) & 1], false);
+              }
+          };
+          probs();
+          // the reference moves to the row maximum on the first sub-tile
+          // with valid keys, and later only when a lane's sum passes kSumCap
+          const bool redo = (fresh && k0 < seq_len) || __any(!(ls[0] + ls[1] <= kSumCap));
+          if (redo) {
+            float mx = kNegInf;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+              for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, sacc[mt][rr]);
+            mx = pair_max(mx);   // relative to ref; finite (a valid key is in range)
+            const float delta = fresh ? mx : fmaxf(mx, 0.f);
+            if (!fresh) {
+              alpha = fast_exp2(-delta);
+              l_run *= alpha;
+              rescale = true;
+            }
+            fresh = false;
+            ref += delta;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+              for (int rr = 0; rr < 16; ++rr) {
+                sacc[mt][rr] -= delta;
+                cneg[rr] = -ref;
+              }
+          }
+          if (redo) probs();
+          l_run += ls[0] + ls[1];
+        }
+        wait_vm();
+      }
+      lds_barrier();
+      if (TM & 1) shift(t);
+    };
+
+    // each wave alternates matrix and vector phases, six to a loop turn with
+    // no phase skipped (a phase past the row's work only meets the barrier),
+    // so on every path a matrix phase follows the vector phase that waited
+    // for its DMA.  Both groups meet T + 1 barriers: group A runs phases
+    // 0 .. T-1 and one empty one, group B an empty vector phase 0 and then
+    // phases 1 .. T.
+    const int T = ((n + 2 + 5) / 6) * 6;
+    auto run = [&](auto gc) __attribute__((always_inline)) {
+      constexpr int GR = decltype(gc)::value;
+      if (GR == 1) vphase(0, Cst<0>{});
+      for (int t = GR; t < T + GR; t += 6) {
+        mphase(t, Cst<GR % 6>{});
+        vphase(t + 1, Cst<(GR + 1) % 6>{});
+        mphase(t + 2, Cst<(GR + 2) % 6>{});
+        vphase(t + 3, Cst<(GR + 3) % 6>{});
+        mphase(t + 4, Cst<(GR + 4) % 6>{});
+        vphase(t + 5, Cst<(GR + 5) % 6>{});
+      }
+      if (GR == 0) lds_barrier();
+    };
+    if (n > 0) {
+      if (grp == 0)
+        run(Cst<0>{});
+      else
+        run(Cst<1>{});
+    }
+
+    // group B hands O, mc and l to group A: 8-float chunks u = 0 .. 2*DT-1 of
+    // every lane, chunk u in stage object (u * 8 KiB) / OBJ, then mc and l
+    char* const objs[6] = {(char*)ks0, (char*)ks1, (char*)ks2, (char*)vs0, (char*)vs1, (char*)vs2};
+    auto chunk = [&](int u) __attribute__((always_inline)) -> float* {
+      return reinterpret_cast<float*>(objs[(u * 8192) / OBJ] + (u * 8192) % OBJ) + (w * 64 + lane) * 8;
+    };
+    float* const ml = reinterpret_cast<float*>(objs[4]) + (w * 64 + lane) * 2;
+    if (grp == 1) {
+#pragma unroll
+      for (int u = 0; u < 2 * DT; ++u) {
+        f32x4 lo, hi;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lo[e] = oacc[u >> 1][8 * (u & 1) + e];
+          hi[e] = oacc[u >> 1][8 * (u & 1) + 4 + e];
+        }
+        reinterpret_cast<f32x4*>(chunk(u))[0] = lo;
+        reinterpret_cast<f32x4*>(chunk(u))[1] = hi;
+      }
+      ml[0] = fresh ? kNegInf : ref;
+      ml[1] = l_run;
+    }
+    lds_barrier();
+    if (grp == 0) {
+      // a group that saw no valid key (fresh) holds nothing and is left out
+      const float mca = fresh ? kNegInf : ref;
+      const float mcb = ml[0], lb = ml[1];
+      float m = fmaxf(mca, mcb);
+      if (m == kNegInf) m = 0.f;
+      const float aa = fast_exp2(mca - m), ab = fast_exp2(mcb - m);
+      const float l_tot = pair_sum(l_run * aa + lb * ab);
+      const float inv = (q < seq_len && l_tot > 0.f) ? 1.f / l_tot : 0.f;
+      const float fa = aa * inv, fb = ab * inv;
+      bf16* Ob = O + base + (size_t)q * D;
+#pragma unroll
+      for (int u = 0; u < 2 * DT; ++u) {
+        const f32x4 lo = reinterpret_cast<const f32x4*>(chunk(u))[0];
+        const f32x4 hi = reinterpret_cast<const f32x4*>(chunk(u))[1];
+        const int t = u >> 1;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int rq = 2 * (u & 1) + half;   // register quad: rows 4*rq .. 4*rq+3 of the tile
+          const f32x4 ob = half ? hi : lo;
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          bf16x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = (bf16)(oacc[t][4 * rq + e] * fa + ob[e] * fb);
+          *reinterpret_cast<bf16x4*>(Ob + 32 * t + 8 * rq + 4 * g) = o;
+        }
+      }
+    }
+    // the stages are free again for the next row's DMA
+    lds_barrier();
+  });
+}
+
 // float32 path: 32-key slices, fp32 matrix cores (32x32x2), P kept in float32.
 // Lane (g, c) holds, for slice accumulator register r, key 2r + g (rows of
 // the K slice are fed in that order), which is the B layout of P^T.
@@ -541,8 +912,29 @@ static hipError_t occupancy(Kern k, int threads, int* blocks_per_cu) {
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, k, threads, 0);
 }
 
+template <int D, bool DENSE>
+static hipError_t launch_pp(const AttnArgs& a, hipStream_t st) {
+  const int items = a.B * a.H * (a.L / 128);
+  const float c2 = a.scale * kLog2e;
+  if (items == 0) return hipSuccess;
+  int grid = items;
+  if (a.queue) {
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(kQueueInts), 0, st, a.queue, kQueueInts, 0);
+    int per_cu = 1;
+    hipError_t e = occupancy(attn_fwd_pp_kernel<D, DENSE>, 512, &per_cu);
+    if (e != hipSuccess) return e;
+    const long long cap = (long long)a.num_cu * (per_cu > 0 ? per_cu : 1);
+    grid = (int)(cap < items ? cap : items);
+  }
+  hipLaunchKernelGGL((attn_fwd_pp_kernel<D, DENSE>), dim3(grid), dim3(512), 0, st, (const bf16*)a.Q,
+                     (const bf16*)a.K, (const bf16*)a.Vt, (bf16*)a.O, a.row_ptr, a.col_idx, a.work_order, a.queue,
+                     items, a.H, a.L, a.seq_len, a.nkb_valid, c2);
+  return hipGetLastError();
+}
+
 template <int D, int BLK, bool DENSE>
 static hipError_t launch_typed(const AttnArgs& a, hipStream_t st) {
+  if (BLK == 128 && !a.dtype_f32) return launch_pp<D, DENSE>(a, st);
   const int threads = BLK * 2;
   const int items = a.B * a.H * (a.L / BLK);
   const float c2 = a.scale * kLog2e;
