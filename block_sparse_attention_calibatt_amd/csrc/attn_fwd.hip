@@ -514,10 +514,25 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
     // key blocks around phase t (block b = t/2): kbm = b-1, kb0 = b, kb1 =
     // b+1; kb2 (b+2) is loaded a block ahead
     int kbm = 0, kb0 = 0, kb1 = 0, kb2 = 0;
+    // Inside the phase loop the indices come from two vector registers that
+    // hold 64 consecutive entries of the row's list each (lane l: entry
+    // 64*chunk + l), read with readlane: a scalar memory load there would
+    // make the next LDS wait also wait for it.  The next chunk is loaded 64
+    // blocks before it is read.
+    auto idx_chunk = [&](int cix) __attribute__((always_inline)) -> int {
+      int j = 64 * cix + lane;
+      j = j < nblk ? j : nblk - 1;
+      return DENSE ? j : col_idx[beg + j];
+    };
+    int cbase = 0, ck_cur = 0, ck_nxt = 0;
     if (n > 0) {
       kb0 = blk(0);
       kb1 = blk(1);
       kb2 = blk(2);
+      if (!DENSE) {
+        ck_cur = idx_chunk(0);
+        ck_nxt = idx_chunk(1);
+      }
       // K(0) by group A, K(1) by group B
 #pragma unroll
       for (int i = 0; i < G::KPER; ++i)
@@ -556,7 +571,19 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
       kbm = kb0;
       kb0 = kb1;
       kb1 = kb2;
-      kb2 = blk((t + 1) / 2 + 2);
+      int j = (t + 1) / 2 + 2;
+      j = j < nblk ? j : nblk - 1;
+      if (DENSE) {
+        kb2 = j;
+      } else {
+        const bool adv = (j >> 6) != cbase;   // j moves on by at most one per call
+        if (adv) {
+          ++cbase;
+          ck_cur = ck_nxt;
+        }
+        kb2 = __builtin_amdgcn_readlane(ck_cur, j & 63);
+        if (adv) ck_nxt = idx_chunk(cbase + 1);
+      }
     };
     // matrix phase t, with TM = t % 6 fixing the stages
     auto mphase = [&](int t, auto tmc) __attribute__((always_inline)) {
@@ -635,23 +662,25 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
               for (int rr = 0; rr < 16; ++rr)
                 if (k0 + 32 * mt + slice_key(rr, g) >= seq_len) sacc[mt][rr] = kNegInf;
           }
+          // P rounded to bf16 for the products; its row sums in fp32 from
+          // the unrounded values, in four chains (plain adds run beside the
+          // other wave's matrix products far better than dot2 does)
           float ls[2];
           auto probs = [&]() __attribute__((always_inline)) {
+            float ch[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
               bf16x8 v;
 #pragma unroll
-              for (int e = 0; e < 8; ++e) v[e] = (bf16)fast_exp2(sacc[ks >> 1][8 * (ks & 1) + e]);
+              for (int e = 0; e < 8; ++e) {
+                const float pe = fast_exp2(sacc[ks >> 1][8 * (ks & 1) + e]);
+                v[e] = (bf16)pe;
+                ch[e & 3] += pe;
+              }
               pb[ks] = v;
             }
-            ls[0] = ls[1] = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-              for (int e = 0; e < 8; e += 2) {
-                const bf16x2 pr = {pb[ks][e], pb[ks][e + 1]};
-                ls[(e >> 1) & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ls[(e >> 1) & 1], false);
-              }
+            ls[0] = ch[0] + ch[1];
+            ls[1] = ch[2] + ch[3];
           };
           probs();
           // the reference moves to the row maximum on the first sub-tile
