@@ -10,7 +10,11 @@ throughput: 4 * block^2 * d FLOP per kept (query block, key block) tile,
 counting full tiles, divided by the step time.  Also reported: the dense
 forward on the same inputs (speedup = t_dense / t_sparse, the ratio the pages
 print), the offline calibration steps (block mass, compile, work order) and
-the float64 CPU oracle timed on a bounded sample of the same workload.
+the float64 CPU oracle timed on a bounded sample of the same workload, and
+the sustained matrix-core rate this GPU reaches with zero and with random
+bf16 operands (the built `mfma_rate` probe, run after the timed work in its
+own process): under random operands the clock drops to stay within power,
+which bounds any matrix-core-bound kernel below the vendor figure.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
        python bench.py --copy-probe 1024   (plain copy, for counter scaling)
@@ -64,6 +68,19 @@ def traffic_from_profile(launch_flops):
     return c.get("hbm_bytes_per_launch")
 
 
+def mfma_rate():
+    """Sustained matrix-core rate with zero and with random bf16 operands (the built probe), or None."""
+    exe = os.path.join(ROOT, "block_sparse_attention_calibatt_amd", "mfma_rate")
+    if not os.path.exists(exe):
+        return None
+    import subprocess
+    try:
+        res = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+        return json.loads(res.stdout.strip().splitlines()[-1]) if res.returncode == 0 else None
+    except (subprocess.SubprocessError, ValueError, IndexError):
+        return None
+
+
 def copy_probe(mb):
     import torch
     n = mb * (1 << 20) // 4
@@ -112,6 +129,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-calib", action="store_true")
+    ap.add_argument("--no-peak-probe", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB")
     args = ap.parse_args()
 
@@ -219,6 +237,9 @@ def main():
             "compiled_density": round(ci.numel() / (cfg.rows * cfg.nkb_valid), 4),
         }
 
+    # the probe runs in its own process, after the timed work
+    peak_probe = None if args.no_peak_probe else mfma_rate()
+
     cpu = None
     if not args.no_cpu:
         rp0, ci0 = sets[0]
@@ -255,6 +276,9 @@ def main():
             "traffic": traffic_from_profile(flops),
             "kernel": "attn_fwd_pp_kernel<128,false>",
             "avg_launch_ms": round(float(np.mean(launch_ms)), 4),
+            "measured_mfma_rate": peak_probe,
+            "frac_of_random_operand_rate": (round(achieved / peak_probe["random_operands_tflops"], 4)
+                                            if peak_probe else None),
         },
         "transpose_v": {
             "avg_ms": round(float(np.mean(transpose_ms)), 4),

@@ -1,4 +1,5 @@
-"""Build libcalibatt.so (gfx950) in-tree with hipcc.
+"""Build libcalibatt.so (gfx950) in-tree with hipcc, and the matrix-core
+rate probe (`mfma_rate`, run by bench.py for the roofline).
 
 Usage: python -m block_sparse_attention_calibatt_amd.build [--verbose]
 """
@@ -12,6 +13,8 @@ import tempfile
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libcalibatt.so")
+PROBE_SRC = os.path.join(CSRC, "probes", "mfma_rate.hip")
+PROBE = os.path.join(PKG, "mfma_rate")
 SOURCES = ["api.hip", "attn_fwd.hip", "mass.hip", "compile.hip"]
 ARCH = os.environ.get("CALIBATT_ARCH", "gfx950")
 
@@ -34,9 +37,10 @@ def hipcc():
     return "hipcc"
 
 
-# The attention kernel keeps Q in accumulation registers (the matrix cores
-# read it from there) and everything else in vector registers, which needs
-# the vector-register form of the matrix instructions.
+# The attention kernels keep their matrix-core accumulators in ordinary
+# vector registers (mixing in accumulation registers splits the register
+# file in half at two waves per SIMD and spills), which needs the
+# vector-register form of the matrix instructions.
 PER_FILE_FLAGS = {"attn_fwd.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
 
 
@@ -54,8 +58,21 @@ def build(verbose=False, extra=()):
             res = subprocess.run(cmd, capture_output=True, text=True)
             return src, obj, res
 
-        with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        def build_probe():
+            flags = [f for f in FLAGS if f not in ("-shared", "-fPIC")]
+            cmd = [hipcc()] + flags + ["-mllvm", "--amdgpu-mfma-vgpr-form", PROBE_SRC, "-o", PROBE + ".tmp"]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            return subprocess.run(cmd, capture_output=True, text=True)
+
+        with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
+            probe = ex.submit(build_probe)
             results = list(ex.map(compile_one, SOURCES))
+            pres = probe.result()
+        if pres.returncode != 0:
+            sys.stderr.write(pres.stdout + pres.stderr)
+            raise RuntimeError(f"hipcc failed on {PROBE_SRC} with exit code {pres.returncode}")
+        os.replace(PROBE + ".tmp", PROBE)
         for src, _, res in results:
             if res.returncode != 0:
                 sys.stderr.write(res.stdout + res.stderr)

@@ -1,0 +1,127 @@
+// Sustained rate of v_mfma_f32_32x32x16_bf16 on this GPU, for the roofline
+// of the attention kernels.  One workgroup of 8 waves per CU (2 per SIMD,
+// the attention kernel's occupancy), each wave issuing products on four
+// independent accumulators from operands held in registers; the shader clock
+// over the run is read from s_memtime against the 100 MHz s_memrealtime.
+//
+// Two runs: operands all zero (the matrix cores' issue-rate limit) and
+// random N(0,1) bf16 operands (the data the attention kernel multiplies).
+// Under sustained random-operand products the GPU lowers its clock to stay
+// within its power limit, so the second rate, not the vendor figure, is what
+// a matrix-core-bound kernel can reach.  Prints one JSON line.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+#define CHECK(x)                                                              \
+  do {                                                                        \
+    hipError_t e_ = (x);                                                      \
+    if (e_ != hipSuccess) {                                                   \
+      fprintf(stderr, "mfma_rate: %s at line %d\n", hipGetErrorString(e_), __LINE__); \
+      exit(1);                                                                \
+    }                                                                         \
+  } while (0)
+
+constexpr int kThreads = 512;
+constexpr int kOperands = 16;   // bf16x8 operand registers per lane
+
+template <bool RANDOM>
+__global__ __launch_bounds__(kThreads) void mfma_rate_kernel(const bf16x8* __restrict__ in, float* __restrict__ out,
+                                                             unsigned long long* __restrict__ clk, int iters) {
+  bf16x8 a[8], b[8];
+  const size_t base = ((size_t)blockIdx.x * kThreads + threadIdx.x) * kOperands;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = RANDOM ? in[base + i] : bf16x8{};
+    b[i] = RANDOM ? in[base + 8 + i] : bf16x8{};
+  }
+  f32x16 acc[4] = {};
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], b[(j + t) & 7], acc[t], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(a[j]));
+  }
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  float r = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) r += acc[t][0] + acc[t][7];
+  out[(size_t)blockIdx.x * kThreads + threadIdx.x] = r;
+  if (threadIdx.x == 0 && blockIdx.x < 8) {
+    clk[blockIdx.x * 2] = t1 - t0;
+    clk[blockIdx.x * 2 + 1] = r1 - r0;
+  }
+}
+
+int main(int argc, char** argv) {
+  const int iters = argc > 1 ? atoi(argv[1]) : 40000;
+  int ncu = 0;
+  CHECK(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, 0));
+  const size_t lanes = (size_t)ncu * kThreads;
+  // N(0, 1) operands (Box-Muller on a 64-bit LCG), rounded to bf16: the
+  // distribution of the attention inputs
+  std::vector<unsigned short> h(lanes * kOperands * 8);
+  unsigned long long st = 0x9e3779b97f4a7c15ull;
+  auto uni = [&]() {
+    st = st * 6364136223846793005ull + 1442695040888963407ull;
+    return ((st >> 11) + 0.5) * (1.0 / 9007199254740992.0);
+  };
+  for (size_t i = 0; i < h.size(); i += 2) {
+    const double r = sqrt(-2.0 * log(uni())), th = 6.283185307179586 * uni();
+    const float v[2] = {(float)(r * cos(th)), (float)(r * sin(th))};
+    for (int k = 0; k < 2 && i + k < h.size(); ++k) {
+      unsigned u;
+      memcpy(&u, &v[k], 4);
+      u += 0x7fffu + ((u >> 16) & 1u);   // round to nearest even
+      h[i + k] = (unsigned short)(u >> 16);
+    }
+  }
+  bf16x8* in = nullptr;
+  float* out = nullptr;
+  unsigned long long* clk = nullptr;
+  CHECK(hipMalloc(&in, h.size() * 2));
+  CHECK(hipMalloc(&out, lanes * 4));
+  CHECK(hipMalloc(&clk, 16 * sizeof(unsigned long long)));
+  CHECK(hipMemcpy(in, h.data(), h.size() * 2, hipMemcpyHostToDevice));
+  hipEvent_t e0, e1;
+  CHECK(hipEventCreate(&e0));
+  CHECK(hipEventCreate(&e1));
+  double tf[2], ghz[2];
+  for (int mode = 0; mode < 2; ++mode) {
+    auto kern = mode ? mfma_rate_kernel<true> : mfma_rate_kernel<false>;
+    hipLaunchKernelGGL(kern, dim3(ncu), dim3(kThreads), 0, 0, in, out, clk, iters / 4);   // warm up
+    CHECK(hipGetLastError());
+    CHECK(hipDeviceSynchronize());
+    CHECK(hipEventRecord(e0));
+    hipLaunchKernelGGL(kern, dim3(ncu), dim3(kThreads), 0, 0, in, out, clk, iters);
+    CHECK(hipGetLastError());
+    CHECK(hipEventRecord(e1));
+    CHECK(hipEventSynchronize(e1));
+    float ms = 0.f;
+    CHECK(hipEventElapsedTime(&ms, e0, e1));
+    unsigned long long c[16];
+    CHECK(hipMemcpy(c, clk, sizeof(c), hipMemcpyDeviceToHost));
+    double g = 0.0;
+    for (int i = 0; i < 8; ++i) g += (double)c[2 * i] / ((double)c[2 * i + 1] / 1e8) / 1e9 / 8.0;
+    const double flops = (double)ncu * 8 * iters * 32 * (32.0 * 32 * 16 * 2);
+    tf[mode] = flops / (ms * 1e-3) / 1e12;
+    ghz[mode] = g;
+  }
+  printf("{\"zero_operands_tflops\": %.1f, \"zero_operands_clock_ghz\": %.3f, "
+         "\"random_operands_tflops\": %.1f, \"random_operands_clock_ghz\": %.3f, \"cus\": %d}\n",
+         tf[0], ghz[0], tf[1], ghz[1], ncu);
+  CHECK(hipFree(in));
+  CHECK(hipFree(out));
+  CHECK(hipFree(clk));
+  return 0;
+}
