@@ -447,10 +447,12 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
   constexpr int DS = G::DS, DT = G::DT, KS = G::KS, CH = G::CH;
   constexpr int NDMA = G::KPER + G::VPER;
   static_assert(G::KUNITS == G::VUNITS, "K and V^T stages have one size");
+  static_assert(DT * 2 * 8192 <= 4 * G::KUNITS * 16, "group B's O fits in K0, K1, K2 and V0");
   constexpr int OBJ = G::KUNITS * 16;   // bytes of one stage
   __shared__ u32x4 ks0[G::KUNITS], ks1[G::KUNITS], ks2[G::KUNITS];
   __shared__ u32x4 vs0[G::VUNITS], vs1[G::VUNITS], vs2[G::VUNITS];
   __shared__ int s_item;
+  __shared__ float s_ml[G::NW * 64 * 2];   // group B's reference and row sum, per lane
   u32x4* const kst[3] = {ks0, ks1, ks2};
   u32x4* const vst[3] = {vs0, vs1, vs2};
 
@@ -494,6 +496,11 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
 
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 one2 = {(bf16)1.f, (bf16)1.f};
+
+  // the V^T stages start as zeros, so that a product with zero
+  // probabilities never meets a non-finite LDS value
+  for (int u = threadIdx.x; u < G::VUNITS; u += 512) vs0[u] = vs1[u] = vs2[u] = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
 
   const RowSource src{work_order, rows, nqb, H, items / rows};
   for_each_row(src, queue, &s_item, [&](int b, int r) {
@@ -561,6 +568,8 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
     f32x16 cneg = {};   // -ref in every accumulator register
     f32x16 sacc[2];
     bf16x8 pb[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) pb[ks] = bf16x8{};   // P*V of phases 0 and 1 adds nothing
     bool rescale = false;   // O *= alpha is due before the next P*V
     float alpha = 1.f;
     wait_vm();
@@ -585,7 +594,14 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
         if (adv) ck_nxt = idx_chunk(cbase + 1);
       }
     };
-    // matrix phase t, with TM = t % 6 fixing the stages
+    // matrix phase t, with TM = t % 6 fixing the stages.  S(t) and
+    // P*V(t-2) run as one sequence of slots, each one pair of products and
+    // the operand reads of the slot PF ahead, so the P*V operands are in
+    // flight while the last scores are computed.  Every phase up to n+1 has
+    // this one shape: in phases 0 and 1 P is zero, so P*V adds nothing (the
+    // V^T stages always hold finite values: zeroed at the start, later only
+    // V^T tiles); in phases n and n+1 the scores come from a stale K stage
+    // and are never used; the DMA keys are clamped to the row.
     auto mphase = [&](int t, auto tmc) __attribute__((always_inline)) {
       constexpr int TM = decltype(tmc)::value;
       constexpr int KST = TM % 3, KDST = (TM + 2) % 3, VST = (TM + 1) % 3, VDST = TM % 3;
@@ -594,54 +610,62 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
       // instead of all being kept in scalar registers
       int wq;
       asm volatile("s_mov_b32 %0, %1" : "=s"(wq) : "s"(w));
-      {
-        if (t < n) {
-          const int kd = kb1 * BLK + (TM & 1) * G::BN;          // K(t+2), clamped by blk()
-          const int vd = kb0 * BLK + (TM & 1) * G::BN;          // V^T(t)
-          const u32x4* const kc = kst[KST];
-          u32x4 ra[3][2];
-          ra[0][0] = kread(kc, 0, 0);
-          ra[0][1] = kread(kc, 1, 0);
-          if (DS > 1) {
-            ra[1][0] = kread(kc, 0, 1);
-            ra[1][1] = kread(kc, 1, 1);
-          }
+      const int kd = kb1 * BLK + (TM & 1) * G::BN;   // K(t+2), clamped by blk()
+      const int vd = kb0 * BLK + (TM & 1) * G::BN;   // V^T(t)
+      const u32x4* const kc = kst[KST];
+      const u32x4* const vc = vst[VST];
+      auto dma_share = [&](int s) __attribute__((always_inline)) {
 #pragma unroll
-          for (int s = 0; s < DS; ++s) {
-            if (s + 2 < DS) {
-              ra[(s + 2) % 3][0] = kread(kc, 0, s + 2);
-              ra[(s + 2) % 3][1] = kread(kc, 1, s + 2);
-            }
-            sacc[0] = mfma_bf16(__builtin_bit_cast(bf16x8, ra[s % 3][0]), qreg[s], s == 0 ? cneg : sacc[0]);
-            sacc[1] = mfma_bf16(__builtin_bit_cast(bf16x8, ra[s % 3][1]), qreg[s], s == 0 ? cneg : sacc[1]);
-#pragma unroll
-            for (int i = s * NDMA / DS; i < (s + 1) * NDMA / DS; ++i) {
-              if (i < G::KPER)
-                k_dma_one<D, BLK>(i, rk, kd, kst[KDST], wq, kpat);
-              else
-                v_dma_one<D, BLK>(i - G::KPER, rv, vd, L, vst[VDST], wq, vpat);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-          }
+        for (int i = s * NDMA / DS; i < (s + 1) * NDMA / DS; ++i) {
+          if (i < G::KPER)
+            k_dma_one<D, BLK>(i, rk, kd, kst[KDST], wq, kpat);
+          else
+            v_dma_one<D, BLK>(i - G::KPER, rv, vd, L, vst[VDST], wq, vpat);
         }
-        if (t >= 2 && t < n + 2) {
-          // O moves to the reference P(t-2) was computed against
-          if (rescale) {
+      };
+      // O moves to the reference P(t-2) was computed against
+      auto apply_rescale = [&]() __attribute__((always_inline)) {
+        if (rescale) {
 #pragma unroll
-            for (int tt = 0; tt < DT; ++tt) oacc[tt] *= alpha;
-            rescale = false;
-          }
-          const u32x4* const vc = vst[VST];
-          constexpr int NP = DT * KS;   // products, i -> ks = i / DT, dt = i % DT
-          u32x4 ra[3];
-          ra[0] = vread(vc, 0, 0);
-          if (NP > 1) ra[1] = vread(vc, 1 % DT, 1 / DT);
+          for (int tt = 0; tt < DT; ++tt) oacc[tt] *= alpha;
+          rescale = false;
+        }
+      };
+      if (t < n + 2) {
+        apply_rescale();
+        constexpr int NSL = DS + DT * KS / 2;   // slots: DS of scores, then P*V
+        constexpr int PF = 2;                   // operand reads run PF slots ahead
+        // operand h of slot sl: K row tile h at k-step sl, or the V^T tile of
+        // P*V product 2 (sl - DS) + h (ks = i / DT, dt = i % DT)
+        auto rd = [&](int sl, int h) __attribute__((always_inline)) -> u32x4 {
+          if (sl < DS) return kread(kc, h, sl);
+          const int i = 2 * (sl - DS) + h;
+          return vread(vc, i % DT, i / DT);
+        };
+        u32x4 ra[PF + 1][2];
 #pragma unroll
-          for (int i = 0; i < NP; ++i) {
-            if (i + 2 < NP) ra[(i + 2) % 3] = vread(vc, (i + 2) % DT, (i + 2) / DT);
-            oacc[i % DT] = mfma_bf16(__builtin_bit_cast(bf16x8, ra[i % 3]), pb[i / DT], oacc[i % DT]);
-            if (i & 1) __builtin_amdgcn_sched_barrier(0);
+        for (int sl = 0; sl < PF; ++sl) {
+          ra[sl][0] = rd(sl, 0);
+          ra[sl][1] = rd(sl, 1);
+        }
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl) {
+          if (sl + PF < NSL) {
+            ra[(sl + PF) % (PF + 1)][0] = rd(sl + PF, 0);
+            ra[(sl + PF) % (PF + 1)][1] = rd(sl + PF, 1);
           }
+          const bf16x8 a0 = __builtin_bit_cast(bf16x8, ra[sl % (PF + 1)][0]);
+          const bf16x8 a1 = __builtin_bit_cast(bf16x8, ra[sl % (PF + 1)][1]);
+          if (sl < DS) {
+            sacc[0] = mfma_bf16(a0, qreg[sl], sl == 0 ? cneg : sacc[0]);
+            sacc[1] = mfma_bf16(a1, qreg[sl], sl == 0 ? cneg : sacc[1]);
+            dma_share(sl);
+          } else {
+            const int i0 = 2 * (sl - DS), i1 = i0 + 1;
+            oacc[i0 % DT] = mfma_bf16(a0, pb[i0 / DT], oacc[i0 % DT]);
+            oacc[i1 % DT] = mfma_bf16(a1, pb[i1 / DT], oacc[i1 % DT]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       lds_barrier();
@@ -745,13 +769,16 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
         run(Cst<1>{});
     }
 
-    // group B hands O, mc and l to group A: 8-float chunks u = 0 .. 2*DT-1 of
-    // every lane, chunk u in stage object (u * 8 KiB) / OBJ, then mc and l
-    char* const objs[6] = {(char*)ks0, (char*)ks1, (char*)ks2, (char*)vs0, (char*)vs1, (char*)vs2};
+    // group B hands O, ref and l to group A: O in 8-float chunks u = 0 ..
+    // 2*DT-1 of every lane, chunk u in stage object (u * 8 KiB) / OBJ of
+    // K0, K1, K2, V0 (never V1 or V2: the P*V of the next row's phases 0
+    // and 1 reads those with zero probabilities, so they may only hold V^T
+    // tiles or zeros), ref and l in s_ml
+    char* const objs[4] = {(char*)ks0, (char*)ks1, (char*)ks2, (char*)vs0};
     auto chunk = [&](int u) __attribute__((always_inline)) -> float* {
       return reinterpret_cast<float*>(objs[(u * 8192) / OBJ] + (u * 8192) % OBJ) + (w * 64 + lane) * 8;
     };
-    float* const ml = reinterpret_cast<float*>(objs[4]) + (w * 64 + lane) * 2;
+    float* const ml = s_ml + (w * 64 + lane) * 2;
     if (grp == 1) {
 #pragma unroll
       for (int u = 0; u < 2 * DT; ++u) {
