@@ -15,7 +15,8 @@ What it computes (each function cites the passage it follows):
   top key blocks per query block (Fig. 5(a) caption), cross-prompt agreement
   with a threshold (Fig. 3(b) caption, Fig. 7 caption), and the kept lists as
   CSR rows keyed by (head, query block) (abstract: per layer, head and
-  timestep).
+  timestep); the energy-threshold row rule (Fig. S8 caption) as the variant
+  of the top-K rule.
 * ``schedule``    - the work order: heads spread over 8 partitions longest
   first, rows inside a head longest first.
 
@@ -41,6 +42,9 @@ from .calibration import (
     min_agree_count,
     to_csr,
     compile_masks,
+    mass_fixed,
+    energy_keep,
+    compile_masks_energy,
 )
 from .schedule import lpt_work_order
 
@@ -57,5 +61,8 @@ __all__ = [
     "min_agree_count",
     "to_csr",
     "compile_masks",
+    "mass_fixed",
+    "energy_keep",
+    "compile_masks_energy",
     "lpt_work_order",
 ]

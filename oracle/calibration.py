@@ -18,6 +18,16 @@ Pages (CalibAtt, arXiv 2603.05503):
   Reading: keep iff count >= ceil(rho * P), computed in exact rationals.
 * Abstract: the kept patterns are compiled per layer, head and timestep.
   Encoding: CSR rows r = h * nqb + qb with ascending key-block indices.
+* Fig. S8 caption: an energy threshold epsilon, scheduled over the
+  normalised timestep, is the pages' own per-row rule; no formula or value
+  survives in the text.  Reading: keep the shortest prefix of the row's
+  (mass descending, index ascending, NaN last) order whose mass reaches
+  (1 - epsilon) of the row's mass, i.e. block b is kept when the mass of the
+  blocks before it is still short of that target.  Decided exactly: masses
+  become integers in units of 2^-40 (round half to even, NaN and negative
+  values 0, each capped at 128, the most a pooled 128-query row can hold)
+  and epsilon is read as a decimal fraction.  The schedule over timesteps is
+  the caller's: one epsilon per compile.
 """
 
 from fractions import Fraction
@@ -75,6 +85,72 @@ def topk_keep(mass, K, nkb_valid=None):
     keep = np.zeros(mass.shape, dtype=bool)
     keep[..., :nv] = rank < K
     return keep
+
+
+MASS_UNIT_BITS = 40          # fixed point of block mass: 2^-40
+MASS_CAP = 128.0             # a pooled row of 128 queries holds at most 128
+
+
+def mass_fixed(mass):
+    """float32 block mass -> integer multiples of 2^-40 (int64 array).
+
+    NaN and negative values count 0; values are capped at MASS_CAP; rounding
+    is to the nearest integer, halves to even.  m * 2^40 is exact in
+    float64, and so is its rounding (below 2^53)."""
+    m = np.asarray(mass, dtype=np.float32).astype(np.float64)
+    m = np.where(np.isnan(m), 0.0, m)
+    m = np.clip(m, 0.0, MASS_CAP)
+    return np.rint(np.ldexp(m, MASS_UNIT_BITS)).astype(np.int64)
+
+
+def as_fraction(x):
+    """A threshold as an exact fraction; a float is read as the decimal it prints as."""
+    if isinstance(x, float):
+        x = str(x)
+    return Fraction(x)
+
+
+def energy_keep(mass, eps, nkb_valid=None):
+    """Keep, per row (last axis), the shortest prefix of the (mass desc, index
+    asc, NaN last) order whose mass reaches (1 - eps) of the row's mass.
+
+    Block b is kept when the fixed-point mass of the blocks before it in that
+    order, times the denominator of eps, is below (den - num) times the
+    row's total: exact integer arithmetic.  Only the first ``nkb_valid``
+    blocks take part."""
+    e = as_fraction(eps)
+    if not (0 <= e <= 1):
+        raise ValueError("eps must lie in [0, 1]")
+    num, den = e.numerator, e.denominator
+    mass = np.asarray(mass, dtype=np.float32)
+    nkb = mass.shape[-1]
+    nv = nkb if nkb_valid is None else nkb_valid
+    flat = mass.reshape(-1, nkb)
+    keep = np.zeros(flat.shape, dtype=bool)
+    fx_all = mass_fixed(flat[:, :nv])
+    for r in range(flat.shape[0]):
+        row = flat[r, :nv].astype(np.float64)
+        order = sorted(range(nv), key=lambda i: (bool(np.isnan(row[i])),
+                                                 -(0.0 if np.isnan(row[i]) else row[i]), i))
+        fx = [int(v) for v in fx_all[r]]
+        total = sum(fx)
+        before = 0
+        for i in order:
+            if before * den < (den - num) * total:
+                keep[r, i] = True
+            before += fx[i]
+    return keep.reshape(mass.shape)
+
+
+def compile_masks_energy(mass, eps, min_agree, nkb_valid=None):
+    """mass [P, H, nqb, nkb] -> CSR of the blocks that >= min_agree prompts keep
+    under the energy rule with threshold eps (one epsilon per compile, the
+    caller's schedule)."""
+    keep = energy_keep(mass, eps, nkb_valid)
+    agreed = agreement(keep, min_agree)
+    if nkb_valid is not None:
+        agreed[..., nkb_valid:] = False
+    return to_csr(agreed)
 
 
 def min_agree_count(rho, P):

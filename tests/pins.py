@@ -332,3 +332,102 @@ def pin_lpt(lpt_impl, seed=13):
     out = lpt_impl(rp, 16, 1)
     assert out[:16].tolist() == [0, 8, 1, 9, 2, 10, 3, 11, 4, 12, 5, 13, 6, 14, 7, 15]
     assert out[16:].tolist() == [0, 2, 4, 6, 8, 10, 12, 14, 16]
+
+
+def _load_golden(name):
+    import json, os
+    with open(os.path.join(os.path.dirname(__file__), "golden", name)) as f:
+        return json.load(f)
+
+
+def pin_mass_fixed(fixed_impl):
+    """Block mass in units of 2^-40: exact for dyadic values, round half to even, NaN/negative 0, cap 128."""
+    got = fixed_impl(np.array([0.5, 0.25, 1.0, 128.0, 200.0, -1.0, np.nan, 0.0], np.float32))
+    want = [2 ** 39, 2 ** 38, 2 ** 40, 2 ** 47, 2 ** 47, 0, 0, 0]
+    assert [int(x) for x in got] == want, "fixed point of exact values"
+    x = np.float32(0.1)
+    exact = Fraction(float(x)) * 2 ** 40                    # float32 0.1 as a fraction
+    assert int(fixed_impl(np.array([x]))[0]) == round(exact), "nearest multiple of 2^-40"
+    tiny = np.float32(2.0 ** -41)                            # exactly half a unit: ties to even (0)
+    assert int(fixed_impl(np.array([tiny]))[0]) == 0
+    assert int(fixed_impl(np.array([np.float32(3 * 2.0 ** -41)]))[0]) == 2, "1.5 units -> 2"
+
+
+def pin_energy_golden(energy_impl):
+    for case in _load_golden("energy_rule.json")["cases"]:
+        m = np.array([case["mass"]], np.float32)
+        got = energy_impl(m, Fraction(case["eps"]))[0].astype(int).tolist()
+        assert got == case["keep"], f"energy rule {case['mass']} eps {case['eps']}: {got}"
+
+
+def pin_energy_brute(energy_impl, seed=14):
+    """The kept count is the smallest k for which some k blocks hold (1 - eps) of the
+    row's mass; the kept set is the lexicographically first heaviest such k-set."""
+    rng = _rng(seed)
+    for trial in range(250):
+        nkb = int(rng.integers(1, 8))
+        row = (rng.integers(0, 5, size=nkb) / 8.0).astype(np.float32)   # dyadic, many ties
+        eps = Fraction(int(rng.integers(0, 9)), 8)
+        total = sum(Fraction(float(v)) for v in row)
+        target = (1 - eps) * total
+        want = np.zeros(nkb, dtype=bool)
+        for k in range(0, nkb + 1):
+            best = max(itertools.combinations(range(nkb), k),
+                       key=lambda s: (sum(Fraction(float(row[i])) for i in s), [-i for i in s]))
+            if sum(Fraction(float(row[i])) for i in best) >= target:
+                want[list(best)] = True
+                break
+        if total == 0:
+            want[:] = False                       # nothing is short of a zero target
+        got = energy_impl(row[None, :], eps)[0]
+        assert np.array_equal(got, want), f"row {row} eps {eps}: {got} vs {want}"
+
+
+def pin_energy_special(energy_impl, seed=15):
+    rng = _rng(seed)
+    m = rng.random((6, 12)).astype(np.float32)
+    m[0, 3] = np.nan
+    m[1] = 0.0
+    m[2, :4] = 0.0
+    assert np.array_equal(energy_impl(m, 0), (np.nan_to_num(m) > 0)), "eps 0 keeps every block with mass"
+    assert not energy_impl(m, 1).any(), "eps 1 keeps nothing"
+    assert not energy_impl(m, Fraction(1, 7))[0, 3], "NaN is never kept"
+    assert not energy_impl(m, Fraction(1, 3))[1].any(), "an empty row keeps nothing"
+    k9 = energy_impl(m, Fraction(1, 3), 9)
+    assert not k9[:, 9:].any(), "nothing past nkb_valid"
+    prev = None
+    for e in [Fraction(i, 10) for i in range(11)]:
+        cur = energy_impl(m, e)
+        if prev is not None:
+            assert not (cur & ~prev).any(), "a larger eps keeps a subset"
+        prev = cur
+
+
+def pin_compile_energy_brute(compile_impl, seed=16):
+    """Energy compile on a tiny bank: per-prompt sets by enumeration, then the count rule."""
+    rng = _rng(seed)
+    P, H, nqb, nkb = 3, 2, 2, 5
+    mass = (rng.integers(0, 4, size=(P, H, nqb, nkb)) / 4.0).astype(np.float32)
+    for nv in (5, 4):
+        for eps in (Fraction(0), Fraction(1, 4), Fraction(1, 2)):
+            for t in (0, 1, 2, 3):
+                row_ptr, col_idx = compile_impl(mass, eps, t, nv)
+                want_rows = []
+                for h in range(H):
+                    for qb in range(nqb):
+                        cnt = [0] * nkb
+                        for p in range(P):
+                            row = mass[p, h, qb, :nv]
+                            total = sum(Fraction(float(v)) for v in row)
+                            for k in range(0, nv + 1):
+                                best = max(itertools.combinations(range(nv), k),
+                                           key=lambda s: (sum(Fraction(float(row[i])) for i in s), [-i for i in s]))
+                                if sum(Fraction(float(row[i])) for i in best) >= (1 - eps) * total:
+                                    break
+                            if total == 0:
+                                best = ()
+                            for i in best:
+                                cnt[i] += 1
+                        want_rows.append([kb for kb in range(nv) if cnt[kb] >= t])
+                got = [list(col_idx[row_ptr[r]:row_ptr[r + 1]]) for r in range(H * nqb)]
+                assert got == want_rows, f"energy compile (nkb_valid={nv}, eps={eps}, min_agree={t})"

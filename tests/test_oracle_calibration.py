@@ -61,3 +61,13 @@ def test_compile_decides_in_float32():
     m64 = np.array([[[[1.0, 1.0 + 1e-12, 0.5, 0.25]]]])
     rp, ci = oracle.compile_masks(m64, 1, 1)
     assert ci.tolist() == [0], "float32 rounding makes the two equal; index breaks the tie"
+
+
+def test_energy_rule_pins():
+    """Energy-threshold row rule (Fig. S8 caption): fixed point, hand-worked cases,
+    enumeration, special cases, and the whole compile by enumeration."""
+    pins.pin_mass_fixed(oracle.mass_fixed)
+    pins.pin_energy_golden(oracle.energy_keep)
+    pins.pin_energy_brute(oracle.energy_keep)
+    pins.pin_energy_special(oracle.energy_keep)
+    pins.pin_compile_energy_brute(oracle.compile_masks_energy)

@@ -176,3 +176,53 @@ def test_csr_and_schedule_mutants_are_caught():
         finally:
             sc.head_partitions = orig
     assert _trips(heads_in_index_order, [pins.pin_lpt])
+
+
+def _energy_generic(mass, eps, nkb_valid=None, *, mode="ok"):
+    """Energy rule with a planted mistake (see ENERGY_MUTANTS)."""
+    e = oracle.calibration.as_fraction(eps)
+    num, den = e.numerator, e.denominator
+    mass = np.asarray(mass, dtype=np.float32)
+    nkb = mass.shape[-1]
+    nv = nkb if nkb_valid is None else nkb_valid
+    flat = mass.reshape(-1, nkb)
+    keep = np.zeros(flat.shape, dtype=bool)
+    fx_all = oracle.mass_fixed(flat[:, :nv])
+    for r in range(flat.shape[0]):
+        row = np.nan_to_num(flat[r, :nv].astype(np.float64), nan=-1.0)
+        sign = 1.0 if mode == "ascending" else -1.0
+        order = sorted(range(nv), key=lambda i: (sign * row[i], i))
+        fx = [int(v) for v in fx_all[r]]
+        total = sum(fx)
+        before = 0
+        for i in order:
+            if mode == "excludes_crossing":
+                ok = (before + fx[i]) * den <= (den - num) * total and fx[i] > 0
+            elif mode == "le":
+                ok = before * den <= (den - num) * total
+            elif mode == "eps_is_kept_fraction":
+                ok = before * den < num * total
+            else:
+                ok = before * den < (den - num) * total
+            keep[r, i] = ok
+            before += fx[i]
+    return keep.reshape(mass.shape)
+
+
+ENERGY_MUTANTS = {
+    "excludes_crossing_block": lambda *a: _energy_generic(*a, mode="excludes_crossing"),
+    "keeps_at_equality": lambda *a: _energy_generic(*a, mode="le"),
+    "eps_is_kept_fraction": lambda *a: _energy_generic(*a, mode="eps_is_kept_fraction"),
+    "ascending_order": lambda *a: _energy_generic(*a, mode="ascending"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ENERGY_MUTANTS))
+def test_energy_mutant_is_caught(name):
+    assert _trips(ENERGY_MUTANTS[name], [pins.pin_energy_golden, pins.pin_energy_brute, pins.pin_energy_special])
+
+
+def test_energy_reference_passes_its_pins():
+    """The mutant harness itself, run without a mistake, passes (so a trip means the mistake)."""
+    ok = lambda *a: _energy_generic(*a, mode="ok")
+    assert not _trips(ok, [pins.pin_energy_golden, pins.pin_energy_brute])
