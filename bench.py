@@ -223,6 +223,9 @@ def main():
         t_c = time.perf_counter()
         rp, ci = cal.calibatt_compile_masks(mass, cfg.nkb // 4, 4, cfg.nkb_valid)
         compile_s = time.perf_counter() - t_c
+        t_c = time.perf_counter()
+        rp_e, ci_e = cal.calibatt_compile_masks_energy(mass, 0.05, 4, cfg.nkb_valid)
+        energy_s = time.perf_counter() - t_c
         wo = torch.empty(cfg.rows + 9, dtype=torch.int32, device=dev)
         e[2].record(stream)
         cal.calibatt_build_schedule(rp, cfg.H, cfg.nqb, wo)
@@ -235,6 +238,8 @@ def main():
             "compile_ms_8_prompts_incl_sync": round(compile_s * 1e3, 3),
             "schedule_ms": round(e[2].elapsed_time(e[3]), 4),
             "compiled_density": round(ci.numel() / (cfg.rows * cfg.nkb_valid), 4),
+            "energy_compile_ms_8_prompts_incl_sync": round(energy_s * 1e3, 3),
+            "energy_compiled_density_eps_0.05": round(ci_e.numel() / (cfg.rows * cfg.nkb_valid), 4),
         }
 
     # the probe runs in its own process, after the timed work

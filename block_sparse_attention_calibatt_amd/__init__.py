@@ -17,6 +17,7 @@ from .capi import (
     calibatt_block_mass,
     calibatt_compile_ws_bytes,
     calibatt_compile_masks,
+    calibatt_compile_masks_energy,
     calibatt_build_schedule,
     calibatt_validate_csr,
     calibatt_status_string,
@@ -37,6 +38,7 @@ __all__ = [
     "calibatt_block_mass",
     "calibatt_compile_ws_bytes",
     "calibatt_compile_masks",
+    "calibatt_compile_masks_energy",
     "calibatt_build_schedule",
     "calibatt_validate_csr",
     "calibatt_status_string",

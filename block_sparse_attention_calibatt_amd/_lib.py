@@ -42,6 +42,8 @@ SIGNATURES = {
                                    _vp]),
     "calibatt_compile_masks": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i64,
                                       ctypes.POINTER(_i64), _vp, _sz, _vp]),
+    "calibatt_compile_masks_energy": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _i64, _i64, _i32, _vp, _vp,
+                                             _i64, ctypes.POINTER(_i64), _vp, _sz, _vp]),
     "calibatt_compile_ws_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "calibatt_build_schedule": (_i32, [_vp, _i32, _i32, _vp, _vp]),
     "calibatt_validate_csr": (_i32, [_vp, _vp, _i32, _i32, _i64]),

@@ -187,6 +187,43 @@ def calibatt_compile_masks(mass, keep_topk, min_agree, nkb_valid=None, row_ptr=N
     return row_ptr, col_idx[: nnz.value]
 
 
+def _eps_fraction(eps):
+    """epsilon as (num, den); a float is read as the decimal it prints as."""
+    from fractions import Fraction
+    e = Fraction(str(eps)) if isinstance(eps, float) else Fraction(eps)
+    _need(0 <= e <= 1, "eps must lie in [0, 1]")
+    _need(e.denominator < 2 ** 31, "eps needs a denominator below 2^31")
+    return e.numerator, e.denominator
+
+
+def calibatt_compile_masks_energy(mass, eps, min_agree, nkb_valid=None, row_ptr=None, col_idx=None, ws=None):
+    """Energy-threshold compile: mass [P, H, nqb, nkb] float32 -> (row_ptr, col_idx) int32 device tensors."""
+    _dev_tensor(mass, "mass", torch.float32)
+    _need(mass.dim() == 4, "mass must be [P, H, nqb, nkb]")
+    P, H, nqb, nkb = mass.shape
+    nkb_valid = nkb if nkb_valid is None else int(nkb_valid)
+    num, den = _eps_fraction(eps)
+    rows = H * nqb
+    dev = mass.device
+    if row_ptr is None:
+        row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    _dev_tensor(row_ptr, "row_ptr", torch.int32)
+    _need(row_ptr.numel() == rows + 1, "row_ptr must have H*nqb+1 entries")
+    if col_idx is None:
+        col_idx = torch.empty(max(1, rows * nkb_valid), dtype=torch.int32, device=dev)
+    _dev_tensor(col_idx, "col_idx", torch.int32)
+    need = calibatt_compile_ws_bytes(P, H, nqb, nkb)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _dev_tensor(ws, "ws", torch.uint8)
+    nnz = ctypes.c_int64(0)
+    lib = load()
+    check(lib.calibatt_compile_masks_energy(_ptr(mass), P, H, nqb, nkb, nkb_valid, num, den, int(min_agree),
+                                            _ptr(row_ptr), _ptr(col_idx), col_idx.numel(), ctypes.byref(nnz),
+                                            _ptr(ws), ws.numel(), _stream(mass)))
+    return row_ptr, col_idx[: nnz.value]
+
+
 def calibatt_build_schedule(row_ptr, H, nqb, work_order=None):
     _dev_tensor(row_ptr, "row_ptr", torch.int32)
     _need(row_ptr.numel() == H * nqb + 1, "row_ptr must have H*nqb+1 entries")

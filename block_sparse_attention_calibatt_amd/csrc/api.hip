@@ -256,10 +256,10 @@ size_t calibatt_compile_ws_bytes(int P, int H, int nqb, int nkb) {
   return keep + rows * sizeof(int32_t);
 }
 
-calibatt_status calibatt_compile_masks(const float* mass, int P, int H, int nqb, int nkb,
-                                       int nkb_valid, int keep_topk, int min_agree, int32_t* row_ptr,
-                                       int32_t* col_idx, int64_t nnz_cap, int64_t* nnz_out, void* ws,
-                                       size_t ws_bytes, void* stream) {
+static calibatt_status compile_common(const float* mass, int P, int H, int nqb, int nkb, int nkb_valid,
+                                      int keep_topk, bool energy, long long eps_num, long long eps_den,
+                                      int min_agree, int32_t* row_ptr, int32_t* col_idx, int64_t nnz_cap,
+                                      int64_t* nnz_out, void* ws, size_t ws_bytes, void* stream) {
   if (!mass || !row_ptr || !nnz_out || !ws) return fail(CALIBATT_ERR_NULL, "mass, row_ptr, nnz_out and ws must be non-NULL");
   if (P < 1 || H < 1 || nqb < 1 || nkb < 1) return fail(CALIBATT_ERR_SHAPE, "P, H, nqb and nkb must be >= 1");
   if (nkb > calibatt::kMaxKeyBlocks) return fail(CALIBATT_ERR_UNSUPPORTED, "nkb=%d exceeds %d", nkb, calibatt::kMaxKeyBlocks);
@@ -285,6 +285,9 @@ calibatt_status calibatt_compile_masks(const float* mass, int P, int H, int nqb,
   a.nkb_valid = nkb_valid;
   a.keep_topk = keep_topk;
   a.min_agree = min_agree;
+  a.energy = energy;
+  a.eps_num = eps_num;
+  a.eps_den = eps_den;
   a.row_ptr = row_ptr;
   a.col_idx = col_idx;
   a.keep_ws = static_cast<uint8_t*>(ws);
@@ -305,6 +308,25 @@ calibatt_status calibatt_compile_masks(const float* mass, int P, int H, int nqb,
     if (e != hipSuccess) return hip_fail(e, "launching mask compile (fill)");
   }
   return ok();
+}
+
+calibatt_status calibatt_compile_masks(const float* mass, int P, int H, int nqb, int nkb,
+                                       int nkb_valid, int keep_topk, int min_agree, int32_t* row_ptr,
+                                       int32_t* col_idx, int64_t nnz_cap, int64_t* nnz_out, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  return compile_common(mass, P, H, nqb, nkb, nkb_valid, keep_topk, false, 0, 1, min_agree, row_ptr, col_idx,
+                        nnz_cap, nnz_out, ws, ws_bytes, stream);
+}
+
+calibatt_status calibatt_compile_masks_energy(const float* mass, int P, int H, int nqb, int nkb,
+                                              int nkb_valid, int64_t eps_num, int64_t eps_den, int min_agree,
+                                              int32_t* row_ptr, int32_t* col_idx, int64_t nnz_cap,
+                                              int64_t* nnz_out, void* ws, size_t ws_bytes, void* stream) {
+  if (eps_den < 1 || eps_den > 2147483647LL || eps_num < 0 || eps_num > eps_den)
+    return fail(CALIBATT_ERR_SHAPE, "eps = %lld/%lld must satisfy 0 <= eps_num <= eps_den, 1 <= eps_den < 2^31",
+                (long long)eps_num, (long long)eps_den);
+  return compile_common(mass, P, H, nqb, nkb, nkb_valid, 0, true, eps_num, eps_den, min_agree, row_ptr, col_idx,
+                        nnz_cap, nnz_out, ws, ws_bytes, stream);
 }
 
 calibatt_status calibatt_build_schedule(const int32_t* row_ptr, int H, int nqb, int32_t* work_order,

@@ -10,6 +10,14 @@
 // ascending columns (the abstract compiles one pattern per layer, head and
 // timestep).
 //
+// Energy rule (Fig. S8 caption: an energy threshold epsilon per row): the
+// variant of the top-K rule.  Block kb is kept for prompt p when the mass of
+// the blocks before it in the same order is still short of (1 - eps) of the
+// row's mass, decided in exact integers: masses in units of 2^-40 (round half
+// to even; NaN and negative values 0; capped at 128, the most a pooled
+// 128-query row holds), compared as before * den < (den - num) * total in
+// 128-bit products.
+//
 // Kernels: keep_agree (one workgroup per row: per-prompt ranks, counts,
 // agreed flags, kept count), row_offsets (one workgroup: exclusive scan of
 // the kept counts), fill_columns (one workgroup per row: ordered compaction
@@ -53,6 +61,77 @@ __global__ __launch_bounds__(kRowThreads) void keep_agree_kernel(
         int rank = 0;
         for (int o = 0; o < nkb_valid; ++o) rank += precedes(m[o], o, x, kb) ? 1 : 0;
         cnt[j] += rank < K ? 1 : 0;
+      }
+    }
+  }
+  int kept = 0;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    const int kb = threadIdx.x + j * kRowThreads;
+    if (kb < nkb) {
+      const bool on = kb < nkb_valid && cnt[j] >= min_agree;
+      keep[(size_t)r * nkb + kb] = on ? 1 : 0;
+      kept += on ? 1 : 0;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) kept += __shfl_xor(kept, off);
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = kept;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int t = 0;
+    for (int i = 0; i < kRowThreads / 64; ++i) t += wsum[i];
+    counts[r] = t;
+  }
+}
+
+// Block mass in units of 2^-40 (see the energy rule above).
+__device__ __forceinline__ unsigned long long mass_fixed(float x) {
+  double d = (double)x;
+  if (!(d > 0.0)) return 0ull;   // NaN, zero, negative
+  if (d > 128.0) d = 128.0;
+  return (unsigned long long)rint(d * 1099511627776.0);   // * 2^40, exact; rint: half to even
+}
+
+__global__ __launch_bounds__(kRowThreads) void keep_energy_kernel(
+    const float* __restrict__ mass, int P, int rows, int nkb, int nkb_valid, long long eps_num,
+    long long eps_den, int min_agree, uint8_t* __restrict__ keep, int32_t* __restrict__ counts) {
+  __shared__ float m[kMaxKeyBlocks];
+  __shared__ unsigned long long fx[kMaxKeyBlocks];
+  __shared__ unsigned long long wtot[kRowThreads / 64];
+  __shared__ int wsum[kRowThreads / 64];
+  const int r = blockIdx.x;
+  const unsigned __int128 den = (unsigned long long)eps_den;
+  const unsigned __int128 keepw = (unsigned long long)(eps_den - eps_num);
+  int cnt[kPerThread];
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) cnt[j] = 0;
+  for (int p = 0; p < P; ++p) {
+    __syncthreads();
+    const float* src = mass + ((size_t)p * rows + r) * nkb;
+    unsigned long long part = 0;
+    for (int kb = threadIdx.x; kb < nkb_valid; kb += kRowThreads) {
+      const float x = src[kb];
+      m[kb] = x;
+      fx[kb] = mass_fixed(x);
+      part += fx[kb];
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+    if ((threadIdx.x & 63) == 0) wtot[threadIdx.x >> 6] = part;
+    __syncthreads();
+    unsigned long long total = 0;
+#pragma unroll
+    for (int i = 0; i < kRowThreads / 64; ++i) total += wtot[i];
+    const unsigned __int128 target = keepw * total;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int kb = threadIdx.x + j * kRowThreads;
+      if (kb < nkb_valid) {
+        const float x = m[kb];
+        unsigned long long before = 0;
+        for (int o = 0; o < nkb_valid; ++o) before += precedes(m[o], o, x, kb) ? fx[o] : 0ull;
+        cnt[j] += ((unsigned __int128)before * den < target) ? 1 : 0;
       }
     }
   }
@@ -198,8 +277,12 @@ __global__ __launch_bounds__(kRowThreads) void lpt_schedule_kernel(const int32_t
 
 hipError_t launch_compile_count(const CompileArgs& a, hipStream_t st) {
   const int rows = a.H * a.nqb;
-  hipLaunchKernelGGL(keep_agree_kernel, dim3(rows), dim3(kRowThreads), 0, st, a.mass, a.P, rows,
-                     a.nkb, a.nkb_valid, a.keep_topk, a.min_agree, a.keep_ws, a.count_ws);
+  if (a.energy)
+    hipLaunchKernelGGL(keep_energy_kernel, dim3(rows), dim3(kRowThreads), 0, st, a.mass, a.P, rows, a.nkb,
+                       a.nkb_valid, a.eps_num, a.eps_den, a.min_agree, a.keep_ws, a.count_ws);
+  else
+    hipLaunchKernelGGL(keep_agree_kernel, dim3(rows), dim3(kRowThreads), 0, st, a.mass, a.P, rows,
+                       a.nkb, a.nkb_valid, a.keep_topk, a.min_agree, a.keep_ws, a.count_ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(row_offsets_kernel, dim3(1), dim3(kScanThreads), 0, st, (const int32_t*)a.count_ws,

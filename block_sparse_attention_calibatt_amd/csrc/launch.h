@@ -48,6 +48,10 @@ hipError_t launch_block_mass(const MassArgs& a, hipStream_t st);
 struct CompileArgs {
   const float* mass;
   int P, H, nqb, nkb, nkb_valid, keep_topk, min_agree;
+  // per-prompt row rule: top keep_topk blocks, or (energy) the shortest
+  // prefix holding (1 - eps_num/eps_den) of the row's mass
+  bool energy = false;
+  long long eps_num = 0, eps_den = 1;
   int32_t* row_ptr;
   int32_t* col_idx;
   uint8_t* keep_ws;   // [H*nqb*nkb]

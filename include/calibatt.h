@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define CALIBATT_VERSION 200 /* major * 100 + minor */
+#define CALIBATT_VERSION 210 /* major * 100 + minor */
 
 typedef enum {
   CALIBATT_OK = 0,
@@ -195,7 +195,31 @@ calibatt_status calibatt_compile_masks(const float* mass, int P, int H, int nqb,
                                        int32_t* row_ptr, int32_t* col_idx, int64_t nnz_cap,
                                        int64_t* nnz_out, void* ws, size_t ws_bytes, void* stream);
 
-/* Workspace bytes calibatt_compile_masks needs for these sizes (0 on bad sizes). */
+/*
+ * Mask compile with the energy-threshold row rule instead of a fixed count.
+ * Pages: Fig. S8 caption (an energy threshold epsilon per row, scheduled over
+ * the normalised timestep; the schedule is the caller's: one epsilon per
+ * call).  For prompt p and row (h, qb) the key block kb < nkb_valid is kept
+ * when the mass of the blocks before it in the order (mass descending, kb
+ * ascending; NaN last) is still short of (1 - epsilon) of the row's mass:
+ * the shortest prefix of that order holding (1 - epsilon) of the mass.
+ * Decided exactly: each mass becomes an integer number of 2^-40 units
+ * (round half to even; NaN and negative values 0; values capped at 128, the
+ * most a pooled row of 128 queries holds) and the test is
+ * before * eps_den < (eps_den - eps_num) * total in 128-bit integers.
+ * epsilon = 0 keeps every block with mass; epsilon = 1 keeps nothing.
+ * Agreement, outputs, workspace and synchronisation as calibatt_compile_masks.
+ *
+ *   eps_num, eps_den  epsilon = eps_num / eps_den, 0 <= eps_num <= eps_den,
+ *                     1 <= eps_den < 2^31 (a decimal 0.05 is 1 / 20).
+ */
+calibatt_status calibatt_compile_masks_energy(const float* mass, int P, int H, int nqb, int nkb,
+                                              int nkb_valid, int64_t eps_num, int64_t eps_den,
+                                              int min_agree, int32_t* row_ptr, int32_t* col_idx,
+                                              int64_t nnz_cap, int64_t* nnz_out, void* ws,
+                                              size_t ws_bytes, void* stream);
+
+/* Workspace bytes calibatt_compile_masks(_energy) needs for these sizes (0 on bad sizes). */
 size_t calibatt_compile_ws_bytes(int P, int H, int nqb, int nkb);
 
 /*

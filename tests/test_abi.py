@@ -18,7 +18,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _lib.header_symbols()
-    assert len(names) == 11
+    assert len(names) == 12
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     for n in names:
@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert cal.calibatt_version() == 200
+    assert cal.calibatt_version() == 210
     for code, name in _lib.STATUS.items():
         assert cal.calibatt_status_string(code) != "unknown status"
     assert cal.calibatt_status_string(99) == "unknown status"
@@ -124,6 +124,21 @@ def test_compile_and_schedule_reject(lib):
     assert call(nkb=2048, nkb_valid=2048) == 7
     assert call(ws_bytes=ws - 1) == 6
     assert call(ws=V(72)) == 4
+    ebase = dict(mass=P16, P=8, H=40, nqb=256, nkb=256, nkb_valid=256, num=1, den=20, t=4, row_ptr=P32,
+                 col_idx=P48, cap=10, nnz=ctypes.byref(n), ws=P64, ws_bytes=ws, stream=None)
+
+    def ecall(**kw):
+        a = dict(ebase)
+        a.update(kw)
+        return lib.calibatt_compile_masks_energy(*a.values())
+    assert ecall(mass=None) == 1
+    assert ecall(den=0) == 2
+    assert ecall(num=-1) == 2
+    assert ecall(num=21) == 2
+    assert ecall(den=1 << 31, num=0) == 2
+    assert ecall(t=9) == 2
+    assert ecall(nkb=2048, nkb_valid=2048) == 7
+    assert ecall(ws_bytes=ws - 1) == 6
     assert lib.calibatt_build_schedule(None, 1, 1, P16, None) == 1
     assert lib.calibatt_build_schedule(P16, 0, 1, P32, None) == 2
     assert lib.calibatt_build_schedule(P16, 1, 4096, P32, None) == 7

@@ -14,6 +14,8 @@ calibrate -> compile -> infer pipeline, against the float64 oracle.
 
 import math
 
+from fractions import Fraction
+
 import numpy as np
 import pytest
 import torch
@@ -115,6 +117,55 @@ def test_compile_bitexact(gpu, case):
     assert np.array_equal(rp.cpu().numpy(), want_rp)
     assert np.array_equal(ci.cpu().numpy(), want_ci)
     say(f"  nnz {len(want_ci)}")
+
+
+@pytest.mark.parametrize("case", [
+    dict(P=8, H=3, nqb=16, nkb=16, nv=16, eps="1/4", t=4, kind="ties"),
+    dict(P=8, H=3, nqb=16, nkb=16, nv=13, eps="1/10", t=4, kind="nan"),
+    dict(P=5, H=2, nqb=8, nkb=24, nv=24, eps="0", t=3, kind="rand"),
+    dict(P=5, H=2, nqb=8, nkb=24, nv=24, eps="1", t=0, kind="rand"),
+    dict(P=4, H=2, nqb=8, nkb=8, nv=7, eps="1/2", t=1, kind="big"),
+    dict(P=3, H=1, nqb=4, nkb=1024, nv=1000, eps="1/20", t=2, kind="ties"),
+    dict(P=8, H=4, nqb=64, nkb=256, nv=256, eps="1/20", t=4, kind="rand"),
+], ids=lambda c: "P{P}H{H}q{nqb}k{nkb}v{nv}e{eps}t{t}{kind}".format(**c).replace("/", "_"))
+def test_compile_energy_bitexact(gpu, case):
+    """Energy-threshold compile (Fig. S8 caption reading) against the oracle, bit-exact."""
+    say("case: energy compile", case)
+    rng = np.random.default_rng(case["P"] * 1000 + case["nkb"] + 7)
+    if case["kind"] == "big":
+        m = (rng.random((case["P"], case["H"], case["nqb"], case["nkb"])) * 300.0).astype(np.float32)
+    else:
+        m = _masses(rng, case["P"], case["H"], case["nqb"], case["nkb"], case["kind"])
+    eps = Fraction(case["eps"])
+    rp, ci = cal.calibatt_compile_masks_energy(torch.from_numpy(m).cuda(), eps, case["t"], case["nv"])
+    want_rp, want_ci = oracle.compile_masks_energy(m, eps, case["t"], case["nv"])
+    assert np.array_equal(rp.cpu().numpy(), want_rp)
+    assert np.array_equal(ci.cpu().numpy(), want_ci)
+    say(f"  nnz {len(want_ci)}")
+
+
+def test_compile_energy_pooled_masses_sampled(gpu):
+    """Energy compile at the Wan shape on pooled masses of 8 prompts (their row sums are the
+    query counts, the rule's intended input); rows sampled and checked against the oracle."""
+    cfg = synth.get_config("calib")
+    say("case: energy compile of 8 prompts' pooled masses at Wan size, eps 1/20, min_agree 4")
+    masses = []
+    for seed in cfg.prompt_seeds[:8]:
+        q, k = synth.gen_qk(cfg, seed)
+        mass, _ = gpu_mass(q, k, cfg)
+        masses.append(mass[0])
+    M = torch.stack(masses).contiguous()
+    rp, ci = cal.calibatt_compile_masks_energy(M, Fraction(1, 20), 4, cfg.nkb_valid)
+    rp_h, ci_h = rp.cpu().numpy(), ci.cpu().numpy()
+    m_h = M.cpu().numpy()
+    rng = np.random.default_rng(11)
+    rows = [0, cfg.H * cfg.nqb - 1] + [int(x) for x in rng.integers(0, cfg.H * cfg.nqb, size=10)]
+    for r in rows:
+        h, qb = divmod(r, cfg.nqb)
+        keep = oracle.energy_keep(m_h[:, h, qb], Fraction(1, 20), cfg.nkb_valid)
+        want = np.nonzero(oracle.agreement(keep, 4))[0]
+        assert np.array_equal(ci_h[rp_h[r]:rp_h[r + 1]], want), f"row {r}"
+    say(f"  {len(rows)} rows match; kept density {len(ci_h) / (cfg.H * cfg.nqb * cfg.nkb_valid):.4f}")
 
 
 def test_compile_capacity_error(gpu):
