@@ -17,6 +17,10 @@ What it computes (each function cites the passage it follows):
   CSR rows keyed by (head, query block) (abstract: per layer, head and
   timestep); the energy-threshold row rule (Fig. S8 caption) as the variant
   of the top-K rule.
+* ``sharing``     - timestep sharing: the IoU of two timesteps' skipped-block
+  masks averaged over heads (Fig. S11 caption), runs of consecutive
+  timesteps with pair-wise IoU >= tau (Table S3 caption), one shared mask
+  per run.
 * ``schedule``    - the work order: heads spread over 8 partitions longest
   first, rows inside a head longest first.
 
@@ -47,6 +51,13 @@ from .calibration import (
     compile_masks_energy,
 )
 from .schedule import lpt_work_order
+from .sharing import (
+    kept_from_csr_sets,
+    skipped_sets,
+    iou_matrix,
+    cluster_timesteps,
+    share_timesteps,
+)
 
 __all__ = [
     "dense_attention",
@@ -65,4 +76,9 @@ __all__ = [
     "energy_keep",
     "compile_masks_energy",
     "lpt_work_order",
+    "kept_from_csr_sets",
+    "skipped_sets",
+    "iou_matrix",
+    "cluster_timesteps",
+    "share_timesteps",
 ]

@@ -23,6 +23,7 @@ from .masks import (
     imbalance_csr,
     random_csr,
     csr_for_config,
+    drifting_sets,
 )
 
 __all__ = [
@@ -41,4 +42,5 @@ __all__ = [
     "imbalance_csr",
     "random_csr",
     "csr_for_config",
+    "drifting_sets",
 ]

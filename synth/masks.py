@@ -18,6 +18,8 @@ Recipes (each per head h, random draws from PCG64 seeded with
   structures that the pages' attention-map figures show (Fig. 2, Fig. 4).
 * mochi: band |qb - kb| <= 2 plus uniformly random blocks so that every row
   keeps exactly 26 of 128 blocks (20.3%).
+* drifting timestep sets (drifting_sets): the Wan mask, then per step a
+  shrinking fraction of each row's kept blocks swapped for others.
 * imbalance: per head a density rho_h ~ U(0.05, 0.90); row r gets weight
   1 / (1 + pi(r)) for a random permutation pi (Zipf, s = 1); counts are
   rho_h * nqb * nkb split by weight, capped at nkb with the excess
@@ -162,6 +164,43 @@ def random_csr(rng, H, nqb, nkb_valid, density, empty_rows=0, full_rows=0):
         flat[pick[:empty_rows]] = False
         flat[pick[empty_rows:]] = True
     return _pack_rows(_lists(m))
+
+
+def drifting_sets(cfg, T, drift=0.10):
+    """T timestep mask sets at the Wan shape whose later steps are more alike.
+
+    Set 0 is the Wan mask of ``cfg``.  Set t (t >= 1) takes set t-1 and, in
+    every row, swaps round(f_t * n_row) kept non-diagonal blocks for as many
+    blocks not kept, f_t = drift * (1 - t / T)^2 (row counts stay fixed): the
+    structure of Fig. S11, where late denoising steps differ least.  Draws per
+    (set, head) from PCG64 seeded with SeedSequence([mask_seed, 7000 + t, h])."""
+    nqb, nkv = cfg.nqb, cfg.nkb_valid
+    rp, ci = wan_csr(cfg, 0)
+    kept = np.zeros((cfg.H, nqb, nkv), dtype=bool)
+    for r in range(cfg.H * nqb):
+        kept[r // nqb, r % nqb, ci[rp[r]:rp[r + 1]]] = True
+    diag = np.zeros((nqb, nkv), dtype=bool)
+    idx = np.arange(min(nqb, nkv))
+    diag[idx, idx] = True
+    sets = [(rp, ci)]
+    for t in range(1, T):
+        f = drift * (1.0 - t / T) ** 2
+        nxt = kept.copy()
+        for h in range(cfg.H):
+            rng = _rng(cfg.mask_seed, 7000 + t, h)
+            k = kept[h]
+            n_swap = np.rint(f * k.sum(axis=1)).astype(np.int64)
+            n_swap = np.minimum(n_swap, np.minimum((k & ~diag).sum(axis=1), (~k).sum(axis=1)))
+            pri = np.where(k & ~diag, rng.random(k.shape), np.inf)
+            rank = np.argsort(np.argsort(pri, axis=1), axis=1)
+            drop = rank < n_swap[:, None]
+            pri2 = np.where(~k, rng.random(k.shape), np.inf)
+            rank2 = np.argsort(np.argsort(pri2, axis=1), axis=1)
+            add = rank2 < n_swap[:, None]
+            nxt[h] = (k & ~drop) | add
+        kept = nxt
+        sets.append(_pack_rows(_lists(kept)))
+    return sets
 
 
 def csr_for_config(cfg, set_index=0):

@@ -431,3 +431,84 @@ def pin_compile_energy_brute(compile_impl, seed=16):
                         want_rows.append([kb for kb in range(nv) if cnt[kb] >= t])
                 got = [list(col_idx[row_ptr[r]:row_ptr[r + 1]]) for r in range(H * nqb)]
                 assert got == want_rows, f"energy compile (nkb_valid={nv}, eps={eps}, min_agree={t})"
+
+
+def _golden_sharing():
+    g = _load_golden("timestep_sharing.json")
+    T = len(g["kept_head0"])
+    kept = np.zeros((T, 2, 1, 4), dtype=bool)
+    for t, ks in enumerate(g["kept_head0"]):
+        kept[t, 0, 0, ks] = True
+    kept[:, 1] = True
+    return g, kept
+
+
+def pin_sharing_golden(share_impl):
+    """share_impl(kept, tau, nkb_valid) -> (clusters, shared, iou)."""
+    g, kept = _golden_sharing()
+    for case in g["cases"]:
+        tau = float(Fraction(case["tau"]))
+        clusters, shared, iou = share_impl(kept, tau, 4)
+        want_iou = np.array([[float(Fraction(x)) for x in row] for row in g["iou_mean"]])
+        assert np.max(np.abs(np.asarray(iou) - want_iou)) < 1e-15, "golden IoU"
+        assert list(np.asarray(clusters)) == case["clusters"], f"clusters at tau {case['tau']}"
+        got = [sorted(np.nonzero(shared[c, 0, 0])[0].tolist()) for c in range(len(shared))]
+        assert got == case["shared_head0"], f"shared masks at tau {case['tau']}"
+        assert np.asarray(shared)[:, 1].all(), "head 1 keeps everything"
+
+
+def pin_iou_brute(iou_impl, seed=17):
+    """Mean-over-heads IoU of skipped sets by Python sets and exact fractions."""
+    rng = _rng(seed)
+    for trial in range(20):
+        T, H, nqb, nkb = int(rng.integers(1, 5)), int(rng.integers(1, 4)), 2, 6
+        nv = int(rng.integers(1, nkb + 1))
+        kept = rng.random((T, H, nqb, nkb)) < rng.random()
+        got = np.asarray(iou_impl(kept, nv))
+        for t1 in range(T):
+            for t2 in range(T):
+                acc = Fraction(0)
+                for h in range(H):
+                    s1 = {(q, k) for q in range(nqb) for k in range(nv) if not kept[t1, h, q, k]}
+                    s2 = {(q, k) for q in range(nqb) for k in range(nv) if not kept[t2, h, q, k]}
+                    acc += Fraction(1) if not (s1 | s2) else Fraction(len(s1 & s2), len(s1 | s2))
+                assert abs(got[t1, t2] - float(acc / H)) < 1e-12, "IoU by sets"
+        assert np.allclose(got, got.T) and np.all(np.diag(got) == 1.0)
+
+
+def pin_cluster_props(cluster_impl, seed=18):
+    """Runs of consecutive timesteps; every pair inside a run reaches tau; a run
+    starts only where some member of the previous run falls below tau."""
+    rng = _rng(seed)
+    for trial in range(60):
+        T = int(rng.integers(1, 12))
+        a = rng.random((T, T))
+        iou = (a + a.T) / 2
+        np.fill_diagonal(iou, 1.0)
+        tau = float(rng.random())
+        cl = np.asarray(cluster_impl(iou, tau))
+        assert cl[0] == 0 and np.all(np.diff(cl) >= 0) and np.all(np.diff(cl) <= 1), "consecutive runs"
+        for c in range(int(cl.max()) + 1):
+            mem = np.nonzero(cl == c)[0]
+            for i in mem:
+                for j in mem:
+                    assert iou[i, j] >= tau or i == j, "pair below tau inside a run"
+            if c > 0:
+                prev = np.nonzero(cl == c - 1)[0]
+                assert any(iou[u, mem[0]] < tau for u in prev), "run split without cause"
+        assert np.all(np.asarray(cluster_impl(iou, 0.0)) == 0), "tau 0: one run"
+        assert np.array_equal(np.asarray(cluster_impl(iou, 1.5)), np.arange(T)), "tau > 1: every step alone"
+
+
+def pin_shared_union(share_impl, seed=19):
+    rng = _rng(seed)
+    kept = rng.random((7, 2, 3, 8)) < 0.5
+    for tau in (0.0, 0.3, 0.6, 1.0):
+        cl, shared, _ = share_impl(kept, tau, 7)
+        cl = np.asarray(cl)
+        for c in range(len(shared)):
+            want = np.zeros(kept.shape[1:], dtype=bool)
+            for t in np.nonzero(cl == c)[0]:
+                want |= kept[t]
+            want[..., 7:] = False
+            assert np.array_equal(shared[c], want), "shared mask = union of the members' kept blocks"

@@ -226,3 +226,48 @@ def test_energy_reference_passes_its_pins():
     """The mutant harness itself, run without a mistake, passes (so a trip means the mistake)."""
     ok = lambda *a: _energy_generic(*a, mode="ok")
     assert not _trips(ok, [pins.pin_energy_golden, pins.pin_energy_brute])
+
+
+def _iou_kept_sets(kept, nkb_valid):
+    """Mistake: IoU of the kept sets instead of the skipped sets."""
+    valid = np.arange(np.asarray(kept).shape[-1]) < nkb_valid
+    return oracle.iou_matrix(~np.asarray(kept, dtype=bool) & valid, nkb_valid)
+
+
+def _iou_pooled(kept, nkb_valid):
+    """Mistake: IoU pooled over heads instead of averaged."""
+    s = oracle.skipped_sets(kept, nkb_valid)
+    T = s.shape[0]
+    out = np.ones((T, T))
+    for a in range(T):
+        for b in range(T):
+            u = np.count_nonzero(s[a] | s[b])
+            out[a, b] = 1.0 if u == 0 else np.count_nonzero(s[a] & s[b]) / u
+    return out
+
+
+def _cluster_chain(iou, tau):
+    """Mistake: compare a timestep only with the one before it."""
+    T = iou.shape[0]
+    cl = np.zeros(T, dtype=np.int32)
+    for t in range(1, T):
+        cl[t] = cl[t - 1] + (0 if iou[t - 1, t] >= tau else 1)
+    return cl
+
+
+def _share_intersection(kept, tau, nkb_valid):
+    """Mistake: a cluster keeps only what all members keep."""
+    cl, shared, iou = oracle.share_timesteps(kept, tau, nkb_valid)
+    kept = np.asarray(kept, dtype=bool)
+    out = np.ones_like(shared)
+    for t in range(len(cl)):
+        out[cl[t]] &= kept[t]
+    out[..., nkb_valid:] = False
+    return cl, out, iou
+
+
+def test_sharing_mutants_are_caught():
+    assert _trips(_iou_kept_sets, [pins.pin_iou_brute])
+    assert _trips(_iou_pooled, [pins.pin_iou_brute])
+    assert _trips(_cluster_chain, [pins.pin_cluster_props])
+    assert _trips(_share_intersection, [pins.pin_shared_union, pins.pin_sharing_golden])
