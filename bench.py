@@ -242,6 +242,19 @@ def main():
             "energy_compiled_density_eps_0.05": round(ci_e.numel() / (cfg.rows * cfg.nkb_valid), 4),
         }
 
+    if not args.no_calib:
+        # timestep sharing of 24 drifting Wan-shaped mask sets (IoU, runs, shared masks)
+        tsets = synth.drifting_sets(cfg if cfg.name == "wan" else synth.get_config("wan"), 24)
+        tbank = cal.MaskBank(tsets, cfg.H, cfg.nqb, cfg.nkb_valid, dev)
+        tbank.share(0.95, cfg.nkb)
+        torch.cuda.synchronize()
+        t_s = time.perf_counter()
+        sb = tbank.share(0.95, cfg.nkb)
+        share_s = time.perf_counter() - t_s
+        extra.setdefault("calib", {})["share_24_sets_tau_0.95"] = {
+            "ms_incl_syncs": round(share_s * 1e3, 3), "shared_sets": sb.n_sets,
+            "runs": [int(x) for x in sb.cluster_of]}
+
     # the probe runs in its own process, after the timed work
     peak_probe = None if args.no_peak_probe else mfma_rate()
 

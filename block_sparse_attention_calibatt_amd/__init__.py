@@ -3,7 +3,8 @@
 The compute lives in libcalibatt.so (HIP kernels behind a C ABI, declared in
 include/calibatt.h).  This package is the thin binding: ``capi`` mirrors the
 C entry points one to one, ``MaskBank`` keeps the compiled lists of many
-timesteps on the GPU.  Build the library with
+timesteps on the GPU (``SharedMaskBank``: one mask per run of alike
+timesteps).  Build the library with
 ``python -m block_sparse_attention_calibatt_amd.build``.
 """
 
@@ -19,12 +20,14 @@ from .capi import (
     calibatt_compile_masks,
     calibatt_compile_masks_energy,
     calibatt_build_schedule,
+    calibatt_share_ws_bytes,
+    calibatt_share_timesteps,
     calibatt_validate_csr,
     calibatt_status_string,
     calibatt_last_error,
     calibatt_version,
 )
-from .bank import MaskBank
+from .bank import MaskBank, SharedMaskBank
 
 __all__ = [
     "CalibattError",
@@ -40,9 +43,12 @@ __all__ = [
     "calibatt_compile_masks",
     "calibatt_compile_masks_energy",
     "calibatt_build_schedule",
+    "calibatt_share_ws_bytes",
+    "calibatt_share_timesteps",
     "calibatt_validate_csr",
     "calibatt_status_string",
     "calibatt_last_error",
     "calibatt_version",
     "MaskBank",
+    "SharedMaskBank",
 ]

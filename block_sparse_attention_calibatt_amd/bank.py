@@ -11,7 +11,7 @@ arithmetic: it returns views, nothing is copied or launched.
 import numpy as np
 import torch
 
-from .capi import calibatt_build_schedule, calibatt_validate_csr
+from .capi import calibatt_build_schedule, calibatt_share_timesteps, calibatt_validate_csr
 
 
 class MaskBank:
@@ -32,6 +32,32 @@ class MaskBank:
         for t in range(len(sets)):
             calibatt_build_schedule(self.row_ptr[t], self.H, self.nqb, self.work_order[t])
 
+    @classmethod
+    def from_device(cls, row_ptr, col_idx, offsets, H, nqb, nkb_valid):
+        """A bank over sets already on the GPU: row_ptr [T, H*nqb+1], col_idx (concatenated),
+        offsets [T+1] (host int64, where each set's columns start)."""
+        self = cls.__new__(cls)
+        self.H, self.nqb, self.nkb_valid = int(H), int(nqb), int(nkb_valid)
+        self.offsets = np.asarray(offsets, dtype=np.int64)
+        self.nnz = np.diff(self.offsets)
+        self.row_ptr = row_ptr
+        self.col_idx = torch.cat([col_idx, torch.zeros(1, dtype=torch.int32, device=col_idx.device)])
+        rows = self.H * self.nqb
+        self.work_order = torch.empty((len(self.nnz), rows + 9), dtype=torch.int32, device=row_ptr.device)
+        for t in range(len(self.nnz)):
+            calibatt_build_schedule(self.row_ptr[t], self.H, self.nqb, self.work_order[t])
+        return self
+
+    def share(self, tau, nkb=None):
+        """Timestep sharing (calibatt_share_timesteps): a SharedMaskBank serving every
+        timestep of this bank from one mask per run of alike timesteps."""
+        nkb = self.nkb_valid if nkb is None else int(nkb)
+        off = torch.from_numpy(self.offsets).to(self.row_ptr.device)
+        cluster_of, iou, rp, soff, ci = calibatt_share_timesteps(self.row_ptr, self.col_idx, off, self.H, self.nqb,
+                                                                 nkb, self.nkb_valid, tau)
+        shared = MaskBank.from_device(rp, ci, soff.cpu().numpy(), self.H, self.nqb, self.nkb_valid)
+        return SharedMaskBank(shared, cluster_of.cpu().numpy(), iou)
+
     def __len__(self):
         return len(self.nnz)
 
@@ -39,3 +65,23 @@ class MaskBank:
         """(row_ptr, col_idx, work_order, nnz) of set t: views into the bank."""
         a, b = int(self.offsets[t]), int(self.offsets[t + 1])
         return self.row_ptr[t], self.col_idx[a:b], self.work_order[t], b - a
+
+
+class SharedMaskBank:
+    """Timesteps mapped onto the shared masks of their runs (Table S3 caption's timestep
+    sharing): lookup(t) returns the shared set of t's run."""
+
+    def __init__(self, shared, cluster_of, iou):
+        self.shared = shared
+        self.cluster_of = np.asarray(cluster_of, dtype=np.int64)
+        self.iou = iou
+
+    def __len__(self):
+        return len(self.cluster_of)
+
+    @property
+    def n_sets(self):
+        return len(self.shared)
+
+    def lookup(self, t):
+        return self.shared.lookup(int(self.cluster_of[t]))

@@ -224,6 +224,40 @@ def calibatt_compile_masks_energy(mass, eps, min_agree, nkb_valid=None, row_ptr=
     return row_ptr, col_idx[: nnz.value]
 
 
+def calibatt_share_ws_bytes(T, H, nqb, nkb):
+    return int(load().calibatt_share_ws_bytes(int(T), int(H), int(nqb), int(nkb)))
+
+
+def calibatt_share_timesteps(row_ptr, col_idx, set_off, H, nqb, nkb, nkb_valid, tau, ws=None):
+    """Bank of T sets (row_ptr [T, H*nqb+1], col_idx, set_off [T+1] int64, device) ->
+    (cluster_of [T], iou [T, T], shared_row_ptr [C, H*nqb+1], shared_set_off [C+1], shared_col_idx)."""
+    _dev_tensor(row_ptr, "row_ptr", torch.int32)
+    _dev_tensor(col_idx, "col_idx", torch.int32)
+    _dev_tensor(set_off, "set_off", torch.int64)
+    _need(row_ptr.dim() == 2 and row_ptr.shape[1] == H * nqb + 1, "row_ptr must be [T, H*nqb+1]")
+    T = row_ptr.shape[0]
+    _need(set_off.numel() == T + 1, "set_off must have T+1 entries")
+    dev = row_ptr.device
+    iou = torch.empty((T, T), dtype=torch.float64, device=dev)
+    cluster_of = torch.empty(T, dtype=torch.int32, device=dev)
+    s_rp = torch.empty((T, H * nqb + 1), dtype=torch.int32, device=dev)
+    s_off = torch.empty(T + 1, dtype=torch.int64, device=dev)
+    s_ci = torch.empty(max(1, T * H * nqb * int(nkb_valid)), dtype=torch.int32, device=dev)
+    need = calibatt_share_ws_bytes(T, H, nqb, nkb)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _dev_tensor(ws, "ws", torch.uint8)
+    C = ctypes.c_int32(0)
+    nnz = ctypes.c_int64(0)
+    lib = load()
+    check(lib.calibatt_share_timesteps(_ptr(row_ptr), _ptr(col_idx), _ptr(set_off), T, int(H), int(nqb), int(nkb),
+                                       int(nkb_valid), float(tau), _ptr(iou), _ptr(cluster_of), _ptr(s_rp),
+                                       _ptr(s_off), _ptr(s_ci), s_ci.numel(), ctypes.byref(C), ctypes.byref(nnz),
+                                       _ptr(ws), ws.numel(), _stream(row_ptr)))
+    c = C.value
+    return cluster_of, iou, s_rp[:c], s_off[: c + 1], s_ci[: nnz.value]
+
+
 def calibatt_build_schedule(row_ptr, H, nqb, work_order=None):
     _dev_tensor(row_ptr, "row_ptr", torch.int32)
     _need(row_ptr.numel() == H * nqb + 1, "row_ptr must have H*nqb+1 entries")

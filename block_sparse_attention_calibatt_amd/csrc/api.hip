@@ -329,6 +329,93 @@ calibatt_status calibatt_compile_masks_energy(const float* mass, int P, int H, i
                         nnz_cap, nnz_out, ws, ws_bytes, stream);
 }
 
+size_t calibatt_share_ws_bytes(int T, int H, int nqb, int nkb) {
+  if (T < 1 || H < 1 || nqb < 1 || nkb < 1) return 0;
+  const size_t rows = (size_t)H * nqb;
+  const size_t W = ((size_t)nkb + 31) / 32;
+  const size_t bits = (size_t)T * rows * W * 4;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  return 2 * up(bits) + up((size_t)T * rows * 4) + up(((size_t)T * rows + 1) * 4) + 256;
+}
+
+calibatt_status calibatt_share_timesteps(const int32_t* row_ptr, const int32_t* col_idx, const int64_t* set_off,
+                                         int T, int H, int nqb, int nkb, int nkb_valid, double tau, double* iou,
+                                         int32_t* cluster_of, int32_t* shared_row_ptr, int64_t* shared_set_off,
+                                         int32_t* shared_col_idx, int64_t nnz_cap, int32_t* n_clusters_out,
+                                         int64_t* nnz_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!row_ptr || !col_idx || !set_off || !iou || !cluster_of || !shared_row_ptr || !shared_set_off ||
+      !n_clusters_out || !nnz_out || !ws)
+    return fail(CALIBATT_ERR_NULL, "every pointer except shared_col_idx must be non-NULL");
+  if (T < 1 || H < 1 || nqb < 1 || nkb < 1) return fail(CALIBATT_ERR_SHAPE, "T, H, nqb and nkb must be >= 1");
+  if (T > 1024) return fail(CALIBATT_ERR_UNSUPPORTED, "T=%d exceeds 1024", T);
+  if (nkb > calibatt::kMaxKeyBlocks) return fail(CALIBATT_ERR_UNSUPPORTED, "nkb=%d exceeds %d", nkb, calibatt::kMaxKeyBlocks);
+  if (nkb_valid < 0 || nkb_valid > nkb) return fail(CALIBATT_ERR_SHAPE, "nkb_valid=%d must be in [0, nkb=%d]", nkb_valid, nkb);
+  if (!(tau == tau)) return fail(CALIBATT_ERR_SHAPE, "tau must not be NaN");
+  if (nnz_cap < 0) return fail(CALIBATT_ERR_SHAPE, "nnz_cap must be >= 0");
+  if (nnz_cap > 0 && !shared_col_idx) return fail(CALIBATT_ERR_NULL, "shared_col_idx must be non-NULL when nnz_cap > 0");
+  const long long rows = (long long)H * nqb;
+  if ((long long)T * rows * nkb >= (1LL << 31)) return fail(CALIBATT_ERR_SHAPE, "T*H*nqb*nkb must be < 2^31");
+  const size_t need = calibatt_share_ws_bytes(T, H, nqb, nkb);
+  if (ws_bytes < need) return fail(CALIBATT_ERR_CAPACITY, "ws_bytes=%zu < %zu required", ws_bytes, need);
+  if (!aligned(ws, 256) || !aligned(row_ptr, 4) || !aligned(col_idx, 4) || !aligned(set_off, 8) || !aligned(iou, 8) ||
+      !aligned(cluster_of, 4) || !aligned(shared_row_ptr, 4) || !aligned(shared_set_off, 8) ||
+      (shared_col_idx && !aligned(shared_col_idx, 4)))
+    return fail(CALIBATT_ERR_ALIGN, "ws must be 256-byte aligned; int64/double arrays 8-, int32 arrays 4-byte aligned");
+
+  calibatt::ShareArgs a;
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.set_off = set_off;
+  a.T = T;
+  a.H = H;
+  a.nqb = nqb;
+  a.nkb = nkb;
+  a.nkb_valid = nkb_valid;
+  a.W = (nkb + 31) / 32;
+  a.tau = tau;
+  a.iou = iou;
+  a.cluster_of = cluster_of;
+  a.shared_row_ptr = shared_row_ptr;
+  a.shared_set_off = shared_set_off;
+  a.shared_col_idx = shared_col_idx;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  const size_t bits = (size_t)T * rows * a.W * 4;
+  a.bits = reinterpret_cast<uint32_t*>(p);
+  p += up(bits);
+  a.shared_bits = reinterpret_cast<uint32_t*>(p);
+  p += up(bits);
+  a.counts = reinterpret_cast<int32_t*>(p);
+  p += up((size_t)T * rows * 4);
+  a.global_ptr = reinterpret_cast<int32_t*>(p);
+  p += up(((size_t)T * rows + 1) * 4);
+  a.n_clusters = reinterpret_cast<int32_t*>(p);
+
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = calibatt::launch_share_cluster(a, st);
+  if (e != hipSuccess) return hip_fail(e, "launching timestep clustering");
+  int32_t C = 0;
+  e = hipMemcpyAsync(&C, a.n_clusters, sizeof(int32_t), hipMemcpyDeviceToHost, st);
+  if (e != hipSuccess) return hip_fail(e, "reading the cluster count");
+  e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "synchronising after timestep clustering");
+  if (C < 1 || C > T) return fail(CALIBATT_ERR_HIP, "cluster count %d out of range", C);
+  *n_clusters_out = C;
+  e = calibatt::launch_share_count(a, C, st);
+  if (e != hipSuccess) return hip_fail(e, "launching shared-mask counts");
+  int32_t total = 0;
+  e = hipMemcpyAsync(&total, a.global_ptr + (size_t)C * rows, sizeof(int32_t), hipMemcpyDeviceToHost, st);
+  if (e != hipSuccess) return hip_fail(e, "reading the shared kept count");
+  e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "synchronising after shared-mask counts");
+  *nnz_out = total;
+  if (total > nnz_cap)
+    return fail(CALIBATT_ERR_CAPACITY, "shared kept blocks %d exceed nnz_cap=%lld", total, (long long)nnz_cap);
+  e = calibatt::launch_share_fill(a, C, st);
+  if (e != hipSuccess) return hip_fail(e, "launching shared-mask fill");
+  return ok();
+}
+
 calibatt_status calibatt_build_schedule(const int32_t* row_ptr, int H, int nqb, int32_t* work_order,
                                         void* stream) {
   if (!row_ptr || !work_order) return fail(CALIBATT_ERR_NULL, "row_ptr and work_order must be non-NULL");

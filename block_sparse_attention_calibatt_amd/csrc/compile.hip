@@ -290,6 +290,11 @@ hipError_t launch_compile_count(const CompileArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+hipError_t launch_row_offsets(const int32_t* counts, int n, int32_t* offsets, hipStream_t st) {
+  hipLaunchKernelGGL(row_offsets_kernel, dim3(1), dim3(kScanThreads), 0, st, counts, n, offsets);
+  return hipGetLastError();
+}
+
 hipError_t launch_compile_fill(const CompileArgs& a, hipStream_t st) {
   const int rows = a.H * a.nqb;
   hipLaunchKernelGGL(fill_columns_kernel, dim3(rows), dim3(kRowThreads), 0, st,

@@ -66,6 +66,35 @@ hipError_t launch_compile_fill(const CompileArgs& a, hipStream_t st);
 hipError_t launch_schedule(const int32_t* row_ptr, int H, int nqb, int32_t* work_order,
                            hipStream_t st);
 
+// Exclusive scan of n counts into offsets[0 .. n] (one workgroup).
+hipError_t launch_row_offsets(const int32_t* counts, int n, int32_t* offsets, hipStream_t st);
+
+struct ShareArgs {
+  const int32_t* row_ptr;   // [T, rows + 1] per-set offsets
+  const int32_t* col_idx;   // concatenated columns
+  const int64_t* set_off;   // [T + 1]
+  int T, H, nqb, nkb, nkb_valid, W;
+  double tau;
+  double* iou;              // [T, T]
+  int32_t* cluster_of;      // [T]
+  int32_t* shared_row_ptr;  // [C, rows + 1]
+  int64_t* shared_set_off;  // [C + 1]
+  int32_t* shared_col_idx;
+  // workspace
+  uint32_t* bits;           // [T, rows, W]
+  uint32_t* shared_bits;    // [T, rows, W] (C <= T runs)
+  int32_t* counts;          // [T * rows]
+  int32_t* global_ptr;      // [T * rows + 1]
+  int32_t* n_clusters;      // [1]
+};
+
+// Bitmasks, pair IoU, runs and the OR of each run (no host sync).
+hipError_t launch_share_cluster(const ShareArgs& a, hipStream_t st);
+// Row counts of the C shared sets and their global offsets.
+hipError_t launch_share_count(const ShareArgs& a, int C, hipStream_t st);
+// Per-set offsets, set starts and the column fill.
+hipError_t launch_share_fill(const ShareArgs& a, int C, hipStream_t st);
+
 constexpr int kMaxKeyBlocks = 1024;   // calibration and compile kernels keep a row in LDS
 constexpr int kMaxHeads = 1024;       // the work-order kernel keeps all head costs in LDS
 // Work partitions: MI355X has 8 XCDs and places workgroup i of a launch on XCD

@@ -223,6 +223,54 @@ calibatt_status calibatt_compile_masks_energy(const float* mass, int P, int H, i
 size_t calibatt_compile_ws_bytes(int P, int H, int nqb, int nkb);
 
 /*
+ * Timestep sharing of a bank of compiled masks (one layer, T timesteps).
+ * Pages: Fig. S11 caption (IoU between the skipped-block masks of two
+ * timesteps, averaged over heads; late steps are alike), Table S3 caption
+ * (timestep sharing clusters masks whose pair-wise IoU is at least tau).
+ * The skipped set of (t, h) is every valid key block (kb < nkb_valid) of the
+ * rows of head h that set t does not keep.  IoU(t1, t2) is the float64 mean
+ * over heads of |S1 & S2| / |S1 | S2| (1 when both are empty), heads summed
+ * in ascending order.  Clusters are greedy runs of consecutive timesteps: t
+ * joins the current run when its IoU with every member is >= tau.  The
+ * shared mask of a run keeps every block any member keeps, so no timestep
+ * computes less than its own mask.
+ *
+ *   row_ptr         [T, H*nqb + 1] int32 (device): set t's row offsets from 0.
+ *   col_idx         int32 (device): every set's columns, concatenated.
+ *   set_off         [T + 1] int64 (device): set t's columns start at
+ *                   col_idx + set_off[t].  The sets must be valid CSR over
+ *                   nkb_valid key blocks (calibatt_validate_csr); columns
+ *                   outside [0, nkb_valid) are ignored.
+ *   T               1 <= T <= 1024 timesteps; nkb <= 1024.
+ *   tau             the IoU threshold (not NaN; <= 0 gives one run, > 1
+ *                   one run per timestep).
+ *   iou             [T, T] float64 output (device).
+ *   cluster_of      [T] int32 output (device): the run of each timestep.
+ *   shared_row_ptr  [T, H*nqb + 1] int32 output (device): the first C rows
+ *                   of offsets are written, one set per run, in the layout of
+ *                   row_ptr.
+ *   shared_set_off  [T + 1] int64 output (device): the first C + 1 written.
+ *   shared_col_idx  [nnz_cap] int32 output (device), concatenated columns.
+ *   n_clusters_out  (host) the run count C.
+ *   nnz_out         (host) columns of all shared sets; set on OK and on
+ *                   CALIBATT_ERR_CAPACITY (then shared_col_idx is not
+ *                   written).  T*H*nqb*nkb_valid always suffices.
+ *   ws              device workspace of calibatt_share_ws_bytes(...) bytes,
+ *                   256-byte aligned.
+ * Synchronises `stream` twice (to read C and the kept count).
+ */
+calibatt_status calibatt_share_timesteps(const int32_t* row_ptr, const int32_t* col_idx,
+                                         const int64_t* set_off, int T, int H, int nqb, int nkb,
+                                         int nkb_valid, double tau, double* iou, int32_t* cluster_of,
+                                         int32_t* shared_row_ptr, int64_t* shared_set_off,
+                                         int32_t* shared_col_idx, int64_t nnz_cap,
+                                         int32_t* n_clusters_out, int64_t* nnz_out, void* ws,
+                                         size_t ws_bytes, void* stream);
+
+/* Workspace bytes calibatt_share_timesteps needs for these sizes (0 on bad sizes). */
+size_t calibatt_share_ws_bytes(int T, int H, int nqb, int nkb);
+
+/*
  * Work order for calibatt_sparse_attn_fwd.  The pages do not describe a
  * scheduler; rows keep very different numbers of blocks (Fig. S9's
  * skip-list row lengths).  Heads (cost = kept blocks) are given, longest

@@ -18,7 +18,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _lib.header_symbols()
-    assert len(names) == 12
+    assert len(names) == 14
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     for n in names:
@@ -143,6 +143,33 @@ def test_compile_and_schedule_reject(lib):
     assert lib.calibatt_build_schedule(P16, 0, 1, P32, None) == 2
     assert lib.calibatt_build_schedule(P16, 1, 4096, P32, None) == 7
     assert lib.calibatt_build_schedule(P16, 2048, 8, P32, None) == 7
+
+
+def test_share_reject(lib):
+    ws = lib.calibatt_share_ws_bytes(50, 40, 256, 256)
+    assert ws > 2 * 50 * 40 * 256 * 8 * 4
+    assert lib.calibatt_share_ws_bytes(0, 1, 1, 1) == 0
+    c, n = ctypes.c_int32(0), ctypes.c_int64(0)
+    W = V(1 << 20)   # 256-byte aligned
+    base = dict(row_ptr=P16, col_idx=P32, set_off=P48, T=50, H=40, nqb=256, nkb=256, nkb_valid=256, tau=0.9,
+                iou=P64, cluster_of=V(80), srp=V(96), soff=V(112), sci=V(128), cap=10, C=ctypes.byref(c),
+                nnz=ctypes.byref(n), ws=W, ws_bytes=ws, stream=None)
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        return lib.calibatt_share_timesteps(*a.values())
+    assert call(row_ptr=None) == 1
+    assert call(iou=None) == 1
+    assert call(sci=None) == 1
+    assert call(T=0) == 2
+    assert call(T=2000) == 7
+    assert call(nkb=2048, nkb_valid=2048) == 7
+    assert call(nkb_valid=300) == 2
+    assert call(tau=float("nan")) == 2
+    assert call(ws_bytes=ws - 1) == 6
+    assert call(ws=V((1 << 20) + 16)) == 4
+    assert call(set_off=V(52)) == 4
 
 
 def test_validate_csr(lib):
