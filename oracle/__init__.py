@@ -21,6 +21,9 @@ What it computes (each function cites the passage it follows):
   masks averaged over heads (Fig. S11 caption), runs of consecutive
   timesteps with pair-wise IoU >= tau (Table S3 caption), one shared mask
   per run.
+* ``intervals``   - 2D skip lists: each row's kept blocks as intervals, the
+  layer width trimmed to a percentile of the row widths and wider rows
+  merged by filling their smallest gaps (Fig. S9, Fig. S10, Table S3).
 * ``schedule``    - the work order: heads spread over 8 partitions longest
   first, rows inside a head longest first.
 
@@ -51,6 +54,13 @@ from .calibration import (
     compile_masks_energy,
 )
 from .schedule import lpt_work_order
+from .intervals import (
+    row_intervals,
+    width_percentile,
+    merge_row,
+    encode_skip_lists,
+    decode_skip_lists,
+)
 from .sharing import (
     kept_from_csr_sets,
     skipped_sets,
@@ -81,4 +91,9 @@ __all__ = [
     "iou_matrix",
     "cluster_timesteps",
     "share_timesteps",
+    "row_intervals",
+    "width_percentile",
+    "merge_row",
+    "encode_skip_lists",
+    "decode_skip_lists",
 ]

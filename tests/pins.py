@@ -512,3 +512,74 @@ def pin_shared_union(share_impl, seed=19):
                 want |= kept[t]
             want[..., 7:] = False
             assert np.array_equal(shared[c], want), "shared mask = union of the members' kept blocks"
+
+
+def pin_intervals_golden(row_intervals_impl, merge_impl, pct_impl):
+    g = _load_golden("skip_lists.json")
+    for row in g["rows"]:
+        assert [list(x) for x in row_intervals_impl(row["cols"])] == row["intervals"], f"intervals of {row['cols']}"
+    for m in g["merges"]:
+        got = [list(x) for x in merge_impl([tuple(x) for x in m["intervals"]], m["width"])]
+        assert got == m["merged"], f"merge {m['intervals']} to {m['width']}: {got}"
+    for p in g["percentiles"]:
+        assert pct_impl(p["widths"], Fraction(p["pct"])) == p["width"], f"percentile {p}"
+
+
+def pin_percentile_numpy(pct_impl, seed=21):
+    """Nearest rank = NumPy's inverted-CDF percentile."""
+    rng = _rng(seed)
+    for trial in range(200):
+        w = rng.integers(0, 30, size=int(rng.integers(1, 60)))
+        pct = int(rng.integers(1, 101))
+        want = int(np.percentile(w, pct, method="inverted_cdf"))
+        assert pct_impl(list(w), Fraction(pct)) == want, f"percentile {pct} of {sorted(w)}"
+
+
+def pin_merge_props(merge_impl, seed=22):
+    """Merged rows keep the original blocks, have min(n, w) intervals, fill only gaps
+    no longer than any gap left open (ties: leftmost filled), and add the fewest blocks
+    of any choice of n - w gaps (enumeration)."""
+    rng = _rng(seed)
+    for trial in range(300):
+        n = int(rng.integers(1, 9))
+        lens = rng.integers(1, 3, size=n)
+        iv, pos = [], 0
+        for i in range(n):
+            a = pos + int(rng.integers(1, 4)) if i else int(rng.integers(0, 3))
+            b = a + int(lens[i])
+            iv.append((a, b))
+            pos = b
+        w = int(rng.integers(1, n + 1))
+        got = merge_impl(iv, w)
+        assert len(got) == min(n, w)
+        orig = {k for a, b in iv for k in range(a, b)}
+        new = {k for a, b in got for k in range(a, b)}
+        assert orig <= new, "merging drops no kept block"
+        gaps = [(iv[i + 1][0] - iv[i][1], i) for i in range(n - 1)]
+        filled = [g for g in gaps if all(k in new for k in range(iv[g[1]][1], iv[g[1] + 1][0]))]
+        open_ = [g for g in gaps if g not in filled]
+        assert len(filled) == n - len(got)
+        for f in filled:
+            for o in open_:
+                assert f[0] < o[0] or (f[0] == o[0] and f[1] < o[1]), "a larger or later gap was filled"
+        best = min(sum(g[0] for g in c) for c in itertools.combinations(gaps, n - min(n, w))) if n > w else 0
+        assert len(new) - len(orig) == best, "not the fewest added blocks"
+
+
+def pin_skip_round_trip(encode_impl, decode_impl, seed=23):
+    """Without merging, decoding the encoded lists gives the sets back exactly; the
+    width is the widest row."""
+    rng = _rng(seed)
+    T, H, nqb, nkb = 3, 2, 4, 23
+    sets = [_rand_csr(rng, H, nqb, nkb, float(rng.random()))[1:] for _ in range(T)]
+    w, counts, pairs = encode_impl(sets, H * nqb, 100)
+    back = decode_impl(counts, pairs, T, H * nqb)
+    for (rp, ci), (rb, cb) in zip(sets, back):
+        assert np.array_equal(rp, rb) and np.array_equal(ci, cb), "round trip"
+    widest = 0
+    for rp, ci in sets:
+        for r in range(H * nqb):
+            c = ci[rp[r]:rp[r + 1]]
+            widest = max(widest, int(np.sum(np.diff(c) != 1) + 1) if len(c) else 0)
+    assert w == widest
+    assert np.all(pairs[np.arange(pairs.shape[1])[None, :] >= counts[:, None]] == -1), "padding"

@@ -271,3 +271,57 @@ def test_sharing_mutants_are_caught():
     assert _trips(_iou_pooled, [pins.pin_iou_brute])
     assert _trips(_cluster_chain, [pins.pin_cluster_props])
     assert _trips(_share_intersection, [pins.pin_shared_union, pins.pin_sharing_golden])
+
+
+def _merge_largest(iv, w):
+    """Mistake: fill the largest gaps."""
+    n = len(iv)
+    if n <= w:
+        return list(iv)
+    gaps = [(-(iv[i + 1][0] - iv[i][1]), i) for i in range(n - 1)]
+    fill = {i for _, i in sorted(gaps)[: n - w]}
+    out = [list(iv[0])]
+    for i in range(1, n):
+        if i - 1 in fill:
+            out[-1][1] = iv[i][1]
+        else:
+            out.append(list(iv[i]))
+    return [tuple(x) for x in out]
+
+
+def _merge_rightmost(iv, w):
+    """Mistake: ties go to the rightmost gap."""
+    n = len(iv)
+    if n <= w:
+        return list(iv)
+    gaps = [(iv[i + 1][0] - iv[i][1], -i) for i in range(n - 1)]
+    fill = {-j for _, j in sorted(gaps)[: n - w]}
+    out = [list(iv[0])]
+    for i in range(1, n):
+        if i - 1 in fill:
+            out[-1][1] = iv[i][1]
+        else:
+            out.append(list(iv[i]))
+    return [tuple(x) for x in out]
+
+
+def _pct_floor(widths, pct):
+    """Mistake: floor instead of ceil for the rank."""
+    w = sorted(int(x) for x in widths)
+    k = max(1, math.floor(float(pct) * len(w) / 100))
+    return w[k - 1]
+
+
+def _intervals_inclusive(cols):
+    """Mistake: closed runs [start, end]."""
+    return [(a, b - 1) for a, b in oracle.row_intervals(cols)]
+
+
+def test_interval_mutants_are_caught():
+    g = lambda r=oracle.row_intervals, m=oracle.merge_row, p=oracle.width_percentile: (r, m, p)
+    assert _trips(_merge_largest, [pins.pin_merge_props])
+    assert _trips(_merge_rightmost, [pins.pin_merge_props])
+    assert _trips(_pct_floor, [pins.pin_percentile_numpy])
+    golden = lambda impls: pins.pin_intervals_golden(*impls)
+    assert _trips((_intervals_inclusive, oracle.merge_row, oracle.width_percentile), [golden])
+    assert _trips((oracle.row_intervals, _merge_rightmost, oracle.width_percentile), [golden])
