@@ -254,6 +254,19 @@ def main():
         extra.setdefault("calib", {})["share_24_sets_tau_0.95"] = {
             "ms_incl_syncs": round(share_s * 1e3, 3), "shared_sets": sb.n_sets,
             "runs": [int(x) for x in sb.cluster_of]}
+        # interval skip lists of the same 24 sets: trimmed, and merged at the 95th percentile
+        sk = {}
+        for pct in (100, 95):
+            tbank.encode_skip_lists(pct, cfg.nkb)
+            torch.cuda.synchronize()
+            t_s = time.perf_counter()
+            lists = tbank.encode_skip_lists(pct, cfg.nkb)
+            enc_s = time.perf_counter() - t_s
+            kept = int(lists.decode().nnz.sum())
+            sk[f"merge_{pct}"] = {"encode_ms_incl_sync": round(enc_s * 1e3, 3), "width": lists.width,
+                                  "widest": lists.widest, "MB": round(lists.size_bytes / 1e6, 2),
+                                  "kept_blocks": kept, "kept_before": int(tbank.nnz.sum())}
+        extra["calib"]["skip_lists_24_sets"] = sk
 
     # the probe runs in its own process, after the timed work
     peak_probe = None if args.no_peak_probe else mfma_rate()

@@ -22,12 +22,15 @@ from .capi import (
     calibatt_build_schedule,
     calibatt_share_ws_bytes,
     calibatt_share_timesteps,
+    calibatt_skip_ws_bytes,
+    calibatt_encode_skip_lists,
+    calibatt_decode_skip_lists,
     calibatt_validate_csr,
     calibatt_status_string,
     calibatt_last_error,
     calibatt_version,
 )
-from .bank import MaskBank, SharedMaskBank
+from .bank import MaskBank, SharedMaskBank, SkipLists
 
 __all__ = [
     "CalibattError",
@@ -45,10 +48,14 @@ __all__ = [
     "calibatt_build_schedule",
     "calibatt_share_ws_bytes",
     "calibatt_share_timesteps",
+    "calibatt_skip_ws_bytes",
+    "calibatt_encode_skip_lists",
+    "calibatt_decode_skip_lists",
     "calibatt_validate_csr",
     "calibatt_status_string",
     "calibatt_last_error",
     "calibatt_version",
     "MaskBank",
     "SharedMaskBank",
+    "SkipLists",
 ]

@@ -49,6 +49,11 @@ SIGNATURES = {
                                         _vp, _vp, _vp, _i64, ctypes.POINTER(_i32), ctypes.POINTER(_i64), _vp, _sz,
                                         _vp]),
     "calibatt_share_ws_bytes": (_sz, [_i32, _i32, _i32, _i32]),
+    "calibatt_encode_skip_lists": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i64, _vp, _vp, _i32,
+                                          ctypes.POINTER(_i32), ctypes.POINTER(_i32), _vp, _sz, _vp]),
+    "calibatt_decode_skip_lists": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i64,
+                                          ctypes.POINTER(_i64), _vp, _sz, _vp]),
+    "calibatt_skip_ws_bytes": (_sz, [_i32, _i32, _i32]),
     "calibatt_build_schedule": (_i32, [_vp, _i32, _i32, _vp, _vp]),
     "calibatt_validate_csr": (_i32, [_vp, _vp, _i32, _i32, _i64]),
     "calibatt_status_string": (ctypes.c_char_p, [_i32]),

@@ -11,7 +11,13 @@ arithmetic: it returns views, nothing is copied or launched.
 import numpy as np
 import torch
 
-from .capi import calibatt_build_schedule, calibatt_share_timesteps, calibatt_validate_csr
+from .capi import (
+    calibatt_build_schedule,
+    calibatt_decode_skip_lists,
+    calibatt_encode_skip_lists,
+    calibatt_share_timesteps,
+    calibatt_validate_csr,
+)
 
 
 class MaskBank:
@@ -58,6 +64,14 @@ class MaskBank:
         shared = MaskBank.from_device(rp, ci, soff.cpu().numpy(), self.H, self.nqb, self.nkb_valid)
         return SharedMaskBank(shared, cluster_of.cpu().numpy(), iou)
 
+    def encode_skip_lists(self, merge_pct=100, nkb=None):
+        """The bank as interval skip lists (calibatt_encode_skip_lists)."""
+        nkb = self.nkb_valid if nkb is None else int(nkb)
+        off = torch.from_numpy(self.offsets).to(self.row_ptr.device)
+        width, widest, counts, pairs = calibatt_encode_skip_lists(self.row_ptr, self.col_idx, off, self.H, self.nqb,
+                                                                  nkb, merge_pct)
+        return SkipLists(width, widest, counts, pairs, len(self), self.H, self.nqb, self.nkb_valid)
+
     def __len__(self):
         return len(self.nnz)
 
@@ -85,3 +99,24 @@ class SharedMaskBank:
 
     def lookup(self, t):
         return self.shared.lookup(int(self.cluster_of[t]))
+
+
+class SkipLists:
+    """A layer's 2D skip lists (Fig. S10 caption): per (timestep, head, query block) entry
+    up to `width` (start, end) pairs of kept key blocks, padded with (-1, -1)."""
+
+    def __init__(self, width, widest, counts, pairs, T, H, nqb, nkb_valid):
+        self.width, self.widest = int(width), int(widest)
+        self.counts, self.pairs = counts, pairs
+        self.T, self.H, self.nqb, self.nkb_valid = int(T), int(H), int(nqb), int(nkb_valid)
+
+    @property
+    def size_bytes(self):
+        """Storage of the trimmed lists: int32 pairs of every entry at the layer width."""
+        return self.T * self.H * self.nqb * self.width * 2 * 4
+
+    def decode(self):
+        """A MaskBank of the kept blocks the lists encode (calibatt_decode_skip_lists)."""
+        rp, off, ci = calibatt_decode_skip_lists(self.counts, self.pairs.reshape(-1), self.width, self.T, self.H,
+                                                 self.nqb)
+        return MaskBank.from_device(rp, ci, off.cpu().numpy(), self.H, self.nqb, self.nkb_valid)

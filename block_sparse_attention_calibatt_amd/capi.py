@@ -258,6 +258,69 @@ def calibatt_share_timesteps(row_ptr, col_idx, set_off, H, nqb, nkb, nkb_valid, 
     return cluster_of, iou, s_rp[:c], s_off[: c + 1], s_ci[: nnz.value]
 
 
+def calibatt_skip_ws_bytes(T, H, nqb):
+    return int(load().calibatt_skip_ws_bytes(int(T), int(H), int(nqb)))
+
+
+def calibatt_encode_skip_lists(row_ptr, col_idx, set_off, H, nqb, nkb, merge_pct=100, ws=None):
+    """Bank (row_ptr [T, H*nqb+1], col_idx, set_off [T+1] int64, device) ->
+    (width, widest, counts [T*H*nqb], pairs [T*H*nqb, width, 2]) int32 device tensors."""
+    from fractions import Fraction
+    _dev_tensor(row_ptr, "row_ptr", torch.int32)
+    _dev_tensor(col_idx, "col_idx", torch.int32)
+    _dev_tensor(set_off, "set_off", torch.int64)
+    _need(row_ptr.dim() == 2 and row_ptr.shape[1] == H * nqb + 1, "row_ptr must be [T, H*nqb+1]")
+    p = Fraction(str(merge_pct)) if isinstance(merge_pct, float) else Fraction(merge_pct)
+    T = row_ptr.shape[0]
+    E = T * H * nqb
+    dev = row_ptr.device
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    cap = int(nkb) // 2 + 1
+    pairs = torch.empty(max(1, E * cap * 2), dtype=torch.int32, device=dev)
+    need = calibatt_skip_ws_bytes(T, H, nqb)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _dev_tensor(ws, "ws", torch.uint8)
+    w, widest = ctypes.c_int32(0), ctypes.c_int32(0)
+    lib = load()
+    check(lib.calibatt_encode_skip_lists(_ptr(row_ptr), _ptr(col_idx), _ptr(set_off), T, int(H), int(nqb), int(nkb),
+                                         p.numerator, p.denominator, _ptr(counts), _ptr(pairs), cap,
+                                         ctypes.byref(w), ctypes.byref(widest), _ptr(ws), ws.numel(), _stream(row_ptr)))
+    return w.value, widest.value, counts, pairs[: E * w.value * 2].view(E, w.value, 2)
+
+
+def calibatt_decode_skip_lists(counts, pairs, width, T, H, nqb, nnz_cap=None, ws=None):
+    """-> (row_ptr [T, H*nqb+1], set_off [T+1] int64, col_idx) device tensors."""
+    _dev_tensor(counts, "counts", torch.int32)
+    _dev_tensor(pairs, "pairs", torch.int32)
+    dev = counts.device
+    rows = H * nqb
+    rp = torch.empty((T, rows + 1), dtype=torch.int32, device=dev)
+    off = torch.empty(T + 1, dtype=torch.int64, device=dev)
+    need = calibatt_skip_ws_bytes(T, H, nqb)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _dev_tensor(ws, "ws", torch.uint8)
+    nnz = ctypes.c_int64(0)
+    lib = load()
+
+    def call(ci, cap):
+        return lib.calibatt_decode_skip_lists(_ptr(counts), _ptr(pairs), int(width), int(T), int(H), int(nqb),
+                                              _ptr(rp), _ptr(off), _ptr(ci), cap, ctypes.byref(nnz), _ptr(ws),
+                                              ws.numel(), _stream(counts))
+    if nnz_cap is None:
+        # size the column array from the library's own count (capacity protocol)
+        probe = torch.empty(1, dtype=torch.int32, device=dev)
+        st = call(probe, 0)
+        if st == 0:
+            return rp, off, probe[:0]
+        _need(st == 6, f"decode count failed: {calibatt_status_string(st)}: {calibatt_last_error()}")
+        nnz_cap = nnz.value
+    ci = torch.empty(max(1, int(nnz_cap)), dtype=torch.int32, device=dev)
+    check(call(ci, int(nnz_cap)))
+    return rp, off, ci[: nnz.value]
+
+
 def calibatt_build_schedule(row_ptr, H, nqb, work_order=None):
     _dev_tensor(row_ptr, "row_ptr", torch.int32)
     _need(row_ptr.numel() == H * nqb + 1, "row_ptr must have H*nqb+1 entries")

@@ -416,6 +416,114 @@ calibatt_status calibatt_share_timesteps(const int32_t* row_ptr, const int32_t* 
   return ok();
 }
 
+size_t calibatt_skip_ws_bytes(int T, int H, int nqb) {
+  if (T < 1 || H < 1 || nqb < 1) return 0;
+  const size_t E = (size_t)T * H * nqb;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  return up(E * 4) + up((E + 1) * 4) + up((size_t)(calibatt::kMaxKeyBlocks / 2 + 1) * 4) + 256;
+}
+
+calibatt_status calibatt_encode_skip_lists(const int32_t* row_ptr, const int32_t* col_idx, const int64_t* set_off,
+                                           int T, int H, int nqb, int nkb, int64_t merge_num, int64_t merge_den,
+                                           int32_t* counts, int32_t* pairs, int width_cap, int32_t* width_out,
+                                           int32_t* widest_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!row_ptr || !col_idx || !set_off || !counts || !width_out || !widest_out || !ws)
+    return fail(CALIBATT_ERR_NULL, "every pointer except pairs must be non-NULL");
+  if (T < 1 || H < 1 || nqb < 1 || nkb < 1) return fail(CALIBATT_ERR_SHAPE, "T, H, nqb and nkb must be >= 1");
+  if (nkb > calibatt::kMaxKeyBlocks) return fail(CALIBATT_ERR_UNSUPPORTED, "nkb=%d exceeds %d", nkb, calibatt::kMaxKeyBlocks);
+  if (merge_den < 1 || merge_num < 1 || merge_num > 100 * merge_den || merge_den > 2147483647LL)
+    return fail(CALIBATT_ERR_SHAPE, "merge percentile %lld/%lld must lie in (0, 100]", (long long)merge_num,
+                (long long)merge_den);
+  if (width_cap < 0) return fail(CALIBATT_ERR_SHAPE, "width_cap must be >= 0");
+  if (width_cap > 0 && !pairs) return fail(CALIBATT_ERR_NULL, "pairs must be non-NULL when width_cap > 0");
+  const long long E = (long long)T * H * nqb;
+  if (E * (long long)(nkb / 2 + 1) * 2 >= (1LL << 31)) return fail(CALIBATT_ERR_SHAPE, "T*H*nqb*(nkb/2+1)*2 must be < 2^31");
+  const size_t need = calibatt_skip_ws_bytes(T, H, nqb);
+  if (ws_bytes < need) return fail(CALIBATT_ERR_CAPACITY, "ws_bytes=%zu < %zu required", ws_bytes, need);
+  if (!aligned(ws, 256) || !aligned(row_ptr, 4) || !aligned(col_idx, 4) || !aligned(set_off, 8) ||
+      !aligned(counts, 4) || (pairs && !aligned(pairs, 4)))
+    return fail(CALIBATT_ERR_ALIGN, "ws must be 256-byte aligned, set_off 8-byte, int32 arrays 4-byte aligned");
+  calibatt::SkipArgs a;
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.set_off = set_off;
+  a.T = T;
+  a.H = H;
+  a.nqb = nqb;
+  a.pct_num = merge_num;
+  a.pct_den = merge_den;
+  a.counts = counts;
+  a.pairs = pairs;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  a.widths = reinterpret_cast<int32_t*>(p);
+  p += up((size_t)E * 4) + up(((size_t)E + 1) * 4);
+  a.hist = reinterpret_cast<int32_t*>(p);
+  p += up((size_t)(calibatt::kMaxKeyBlocks / 2 + 1) * 4);
+  a.width_dev = reinterpret_cast<int32_t*>(p);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = calibatt::launch_skip_widths(a, st);
+  if (e != hipSuccess) return hip_fail(e, "launching skip-list widths");
+  int32_t wd[2] = {0, 0};
+  e = hipMemcpyAsync(wd, a.width_dev, sizeof(wd), hipMemcpyDeviceToHost, st);
+  if (e != hipSuccess) return hip_fail(e, "reading the layer width");
+  e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "synchronising after skip-list widths");
+  *width_out = wd[0];
+  *widest_out = wd[1];
+  if (wd[0] > width_cap)
+    return fail(CALIBATT_ERR_CAPACITY, "layer width %d exceeds width_cap=%d", wd[0], width_cap);
+  e = calibatt::launch_skip_encode(a, st);
+  if (e != hipSuccess) return hip_fail(e, "launching skip-list encode");
+  return ok();
+}
+
+calibatt_status calibatt_decode_skip_lists(const int32_t* counts, const int32_t* pairs, int width, int T, int H,
+                                           int nqb, int32_t* row_ptr, int64_t* set_off, int32_t* col_idx,
+                                           int64_t nnz_cap, int64_t* nnz_out, void* ws, size_t ws_bytes,
+                                           void* stream) {
+  if (!counts || !row_ptr || !set_off || !nnz_out || !ws) return fail(CALIBATT_ERR_NULL, "counts, row_ptr, set_off, nnz_out and ws must be non-NULL");
+  if (width > 0 && !pairs) return fail(CALIBATT_ERR_NULL, "pairs must be non-NULL when width > 0");
+  if (T < 1 || H < 1 || nqb < 1 || width < 0) return fail(CALIBATT_ERR_SHAPE, "T, H, nqb must be >= 1 and width >= 0");
+  if (width > calibatt::kMaxKeyBlocks / 2) return fail(CALIBATT_ERR_UNSUPPORTED, "width=%d exceeds %d", width, calibatt::kMaxKeyBlocks / 2);
+  if (nnz_cap < 0) return fail(CALIBATT_ERR_SHAPE, "nnz_cap must be >= 0");
+  if (nnz_cap > 0 && !col_idx) return fail(CALIBATT_ERR_NULL, "col_idx must be non-NULL when nnz_cap > 0");
+  const long long E = (long long)T * H * nqb;
+  if (E * (long long)calibatt::kMaxKeyBlocks >= (1LL << 31)) return fail(CALIBATT_ERR_SHAPE, "T*H*nqb*1024 must be < 2^31");
+  const size_t need = calibatt_skip_ws_bytes(T, H, nqb);
+  if (ws_bytes < need) return fail(CALIBATT_ERR_CAPACITY, "ws_bytes=%zu < %zu required", ws_bytes, need);
+  if (!aligned(ws, 256) || !aligned(counts, 4) || (pairs && !aligned(pairs, 4)) || !aligned(row_ptr, 4) ||
+      !aligned(set_off, 8) || (col_idx && !aligned(col_idx, 4)))
+    return fail(CALIBATT_ERR_ALIGN, "ws must be 256-byte aligned, set_off 8-byte, int32 arrays 4-byte aligned");
+  calibatt::SkipDecodeArgs a;
+  a.counts = counts;
+  a.pairs = pairs;
+  a.W = width;
+  a.T = T;
+  a.H = H;
+  a.nqb = nqb;
+  a.row_ptr = row_ptr;
+  a.set_off = set_off;
+  a.col_idx = col_idx;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  a.kept = reinterpret_cast<int32_t*>(p);
+  a.global_ptr = reinterpret_cast<int32_t*>(p + up((size_t)E * 4));
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = calibatt::launch_skip_decode_count(a, st);
+  if (e != hipSuccess) return hip_fail(e, "launching skip-list decode (count)");
+  int32_t total = 0;
+  e = hipMemcpyAsync(&total, a.global_ptr + E, sizeof(int32_t), hipMemcpyDeviceToHost, st);
+  if (e != hipSuccess) return hip_fail(e, "reading the decoded count");
+  e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "synchronising after skip-list decode (count)");
+  *nnz_out = total;
+  if (total > nnz_cap) return fail(CALIBATT_ERR_CAPACITY, "decoded blocks %d exceed nnz_cap=%lld", total, (long long)nnz_cap);
+  e = calibatt::launch_skip_decode_fill(a, st);
+  if (e != hipSuccess) return hip_fail(e, "launching skip-list decode (fill)");
+  return ok();
+}
+
 calibatt_status calibatt_build_schedule(const int32_t* row_ptr, int H, int nqb, int32_t* work_order,
                                         void* stream) {
   if (!row_ptr || !work_order) return fail(CALIBATT_ERR_NULL, "row_ptr and work_order must be non-NULL");

@@ -94,6 +94,42 @@ hipError_t launch_share_cluster(const ShareArgs& a, hipStream_t st);
 hipError_t launch_share_count(const ShareArgs& a, int C, hipStream_t st);
 // Per-set offsets, set starts and the column fill.
 hipError_t launch_share_fill(const ShareArgs& a, int C, hipStream_t st);
+// Global offsets over (set, row) -> per-set offsets from 0 and set starts.
+hipError_t launch_local_offsets(const int32_t* global, int C, int rows, int32_t* local, int64_t* set_off,
+                                hipStream_t st);
+
+struct SkipArgs {
+  const int32_t* row_ptr;   // [T, rows + 1] per-set offsets
+  const int32_t* col_idx;
+  const int64_t* set_off;   // [T + 1]
+  int T, H, nqb;
+  long long pct_num, pct_den;   // merge percentile, percent
+  int32_t* counts;          // [E] output
+  int32_t* pairs;           // [E, width, 2] output
+  // workspace
+  int32_t* widths;          // [E]
+  int32_t* hist;            // [kMaxKeyBlocks / 2 + 1]
+  int32_t* width_dev;       // [2]: layer width, widest row
+};
+
+struct SkipDecodeArgs {
+  const int32_t* counts;
+  const int32_t* pairs;
+  int W, T, H, nqb;
+  int32_t* row_ptr;         // [T, rows + 1] output
+  int64_t* set_off;         // [T + 1] output
+  int32_t* col_idx;         // output
+  // workspace
+  int32_t* kept;            // [E]
+  int32_t* global_ptr;      // [E + 1]
+};
+
+// Row widths, their histogram and the layer width (no host sync).
+hipError_t launch_skip_widths(const SkipArgs& a, hipStream_t st);
+// The (merged) runs of every entry, after the caller checked the width fits.
+hipError_t launch_skip_encode(const SkipArgs& a, hipStream_t st);
+hipError_t launch_skip_decode_count(const SkipDecodeArgs& a, hipStream_t st);
+hipError_t launch_skip_decode_fill(const SkipDecodeArgs& a, hipStream_t st);
 
 constexpr int kMaxKeyBlocks = 1024;   // calibration and compile kernels keep a row in LDS
 constexpr int kMaxHeads = 1024;       // the work-order kernel keeps all head costs in LDS

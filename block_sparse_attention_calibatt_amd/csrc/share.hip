@@ -208,6 +208,13 @@ hipError_t launch_share_count(const ShareArgs& a, int C, hipStream_t st) {
   return launch_row_offsets(a.counts, (int)n_rows, a.global_ptr, st);
 }
 
+hipError_t launch_local_offsets(const int32_t* global, int C, int rows, int32_t* local, int64_t* set_off,
+                                hipStream_t st) {
+  hipLaunchKernelGGL(local_offsets_kernel, dim3(blocks_for((long long)C * (rows + 1))), dim3(kShareThreads), 0, st,
+                     global, C, rows, local, set_off);
+  return hipGetLastError();
+}
+
 hipError_t launch_share_fill(const ShareArgs& a, int C, hipStream_t st) {
   const int rows = a.H * a.nqb;
   const long long n_rows = (long long)C * rows;

@@ -271,6 +271,60 @@ calibatt_status calibatt_share_timesteps(const int32_t* row_ptr, const int32_t* 
 size_t calibatt_share_ws_bytes(int T, int H, int nqb, int nkb);
 
 /*
+ * Interval-encoded skip lists of a bank of T compiled sets (one layer).
+ * Pages: Fig. S10 caption (each row stores interval pairs for one (timestep,
+ * head, query block) entry, padded past its data; per-layer trimming to the
+ * widest row; merging outlier rows lowers the width), Fig. S9 caption (row
+ * widths vary widely), Table S3 (merge percentages; merging fills a few
+ * skipped blocks).  A row's intervals are its maximal runs of kept key
+ * blocks, half-open [start, end), ascending.  The layer width is the
+ * nearest-rank merge_num/merge_den-th percentile of the E = T*H*nqb row
+ * widths (the smallest w with at least ceil(p/100 * E) rows no wider; 1 if
+ * that is 0 while some row keeps blocks); p = 100 is plain trimming.  A
+ * wider row fills its smallest gaps between consecutive intervals, ties to
+ * the leftmost, until it has `width` intervals.
+ *
+ *   row_ptr, col_idx, set_off  the bank, as for calibatt_share_timesteps
+ *                     (valid CSR, ascending columns, nkb <= 1024).
+ *   merge_num/den     the percentile p in (0, 100], e.g. 95/1.
+ *   counts            [E] int32 output (device): intervals of entry
+ *                     e = t*H*nqb + r.
+ *   pairs             [E, width, 2] int32 output (device): (start, end) of
+ *                     each interval, (-1, -1) past counts[e]; rows of
+ *                     `width` pairs, so width_cap >= width must hold.
+ *   width_out         (host) the layer width; also set on
+ *                     CALIBATT_ERR_CAPACITY (then pairs is not written).
+ *   widest_out        (host) the widest row before merging.
+ *   ws                calibatt_skip_ws_bytes(T, H, nqb) bytes, 256-byte
+ *                     aligned.
+ * Synchronises `stream` once (to read the width).
+ */
+calibatt_status calibatt_encode_skip_lists(const int32_t* row_ptr, const int32_t* col_idx,
+                                           const int64_t* set_off, int T, int H, int nqb, int nkb,
+                                           int64_t merge_num, int64_t merge_den, int32_t* counts,
+                                           int32_t* pairs, int width_cap, int32_t* width_out,
+                                           int32_t* widest_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Skip lists back to a bank of CSR sets (the kept blocks of every interval,
+ * ascending), so the attention entry points run on the merged masks.
+ *   counts, pairs, width  as written by calibatt_encode_skip_lists.
+ *   row_ptr   [T, H*nqb + 1] int32 output (device), per-set offsets from 0.
+ *   set_off   [T + 1] int64 output (device): set t starts at col_idx + set_off[t].
+ *   col_idx   [nnz_cap] int32 output (device).
+ *   nnz_out   (host) columns of all sets; set on OK and on CALIBATT_ERR_CAPACITY.
+ *   ws        calibatt_skip_ws_bytes(T, H, nqb) bytes, 256-byte aligned.
+ * Synchronises `stream` once (to read the count).
+ */
+calibatt_status calibatt_decode_skip_lists(const int32_t* counts, const int32_t* pairs, int width, int T,
+                                           int H, int nqb, int32_t* row_ptr, int64_t* set_off,
+                                           int32_t* col_idx, int64_t nnz_cap, int64_t* nnz_out, void* ws,
+                                           size_t ws_bytes, void* stream);
+
+/* Workspace bytes the skip-list encode and decode need (0 on bad sizes). */
+size_t calibatt_skip_ws_bytes(int T, int H, int nqb);
+
+/*
  * Work order for calibatt_sparse_attn_fwd.  The pages do not describe a
  * scheduler; rows keep very different numbers of blocks (Fig. S9's
  * skip-list row lengths).  Heads (cost = kept blocks) are given, longest

@@ -18,7 +18,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _lib.header_symbols()
-    assert len(names) == 14
+    assert len(names) == 17
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     for n in names:
@@ -170,6 +170,42 @@ def test_share_reject(lib):
     assert call(ws_bytes=ws - 1) == 6
     assert call(ws=V((1 << 20) + 16)) == 4
     assert call(set_off=V(52)) == 4
+
+
+def test_skip_lists_reject(lib):
+    ws = lib.calibatt_skip_ws_bytes(50, 40, 256)
+    assert ws >= 2 * 50 * 40 * 256 * 4
+    assert lib.calibatt_skip_ws_bytes(0, 1, 1) == 0
+    w, wd, n = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int64(0)
+    W = V(1 << 20)
+    base = dict(row_ptr=P16, col_idx=P32, set_off=P48, T=50, H=40, nqb=256, nkb=256, num=95, den=1, counts=P64,
+                pairs=V(80), cap=129, w=ctypes.byref(w), wd=ctypes.byref(wd), ws=W, ws_bytes=ws, stream=None)
+
+    def enc(**kw):
+        a = dict(base)
+        a.update(kw)
+        return lib.calibatt_encode_skip_lists(*a.values())
+    assert enc(row_ptr=None) == 1
+    assert enc(pairs=None) == 1
+    assert enc(T=0) == 2
+    assert enc(num=0) == 2
+    assert enc(num=101) == 2
+    assert enc(den=0) == 2
+    assert enc(nkb=2048) == 7
+    assert enc(ws_bytes=ws - 1) == 6
+    assert enc(ws=V((1 << 20) + 8)) == 4
+    dbase = dict(counts=P16, pairs=P32, width=8, T=50, H=40, nqb=256, row_ptr=P48, set_off=P64, col_idx=V(96),
+                 cap=10, nnz=ctypes.byref(n), ws=W, ws_bytes=ws, stream=None)
+
+    def dec(**kw):
+        a = dict(dbase)
+        a.update(kw)
+        return lib.calibatt_decode_skip_lists(*a.values())
+    assert dec(counts=None) == 1
+    assert dec(width=-1) == 2
+    assert dec(width=600) == 7
+    assert dec(ws_bytes=ws - 1) == 6
+    assert dec(set_off=V(68)) == 4
 
 
 def test_validate_csr(lib):
