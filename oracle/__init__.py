@@ -24,6 +24,10 @@ What it computes (each function cites the passage it follows):
 * ``intervals``   - 2D skip lists: each row's kept blocks as intervals, the
   layer width trimmed to a percentile of the row widths and wider rows
   merged by filling their smallest gaps (Fig. S9, Fig. S10, Table S3).
+* ``repetition``  - spatial-repetition heads: the mean cosine similarity of
+  vertically adjacent softmax rows (Fig. 4, Fig. 6), heads above tau
+  (Fig. S13), and attention for k anchor rows per frame broadcast to the
+  other rows (Fig. 5(b), Table S4).
 * ``schedule``    - the work order: heads spread over 8 partitions longest
   first, rows inside a head longest first.
 
@@ -61,6 +65,14 @@ from .intervals import (
     encode_skip_lists,
     decode_skip_lists,
 )
+from .repetition import (
+    row_groups,
+    anchor_of_row,
+    anchor_tokens,
+    spatial_similarity,
+    select_repetitive_heads,
+    anchor_attention,
+)
 from .sharing import (
     kept_from_csr_sets,
     skipped_sets,
@@ -96,4 +108,10 @@ __all__ = [
     "merge_row",
     "encode_skip_lists",
     "decode_skip_lists",
+    "row_groups",
+    "anchor_of_row",
+    "anchor_tokens",
+    "spatial_similarity",
+    "select_repetitive_heads",
+    "anchor_attention",
 ]

@@ -15,7 +15,7 @@ sparsities of Table S4 are 1 - k/30) of 52 tokens.
 
 from .bf16 import round_bf16, f32_to_bf16_bits, bf16_bits_to_f32
 from .configs import CONFIGS, Config, get_config
-from .inputs import gen_qkv, gen_qk, positional_term
+from .inputs import gen_qkv, gen_qk, positional_term, repeat_rows
 from .masks import (
     tiny_csr,
     wan_csr,
@@ -36,6 +36,7 @@ __all__ = [
     "gen_qkv",
     "gen_qk",
     "positional_term",
+    "repeat_rows",
     "tiny_csr",
     "wan_csr",
     "mochi_csr",

@@ -85,6 +85,20 @@ def gen_qkv(cfg, seed=None, heads=None, B=None):
     return q, k, v
 
 
+def repeat_rows(x, grid, S, heads, mix, bf16=True):
+    """Spatially repetitive heads: for the listed heads (indices into axis 1),
+    token (f, y, x) becomes (1 - mix) * token (f, 0, x) + mix * itself, so its
+    rows repeat down each frame up to a fraction ``mix`` of fresh draw.  In
+    place; rounded back to bfloat16 when ``bf16``; tokens >= S untouched."""
+    F, Y, X = grid
+    for h in heads:
+        v = x[:, h, :F * Y * X].reshape(x.shape[0], F, Y, X, x.shape[3])
+        v[...] = (1.0 - mix) * v[:, :, :1] + mix * v
+        if bf16:
+            v[...] = round_bf16(v)
+    return x
+
+
 def gen_qk(cfg, seed, heads=None, B=None):
     """Q, K only (calibration prompts need no V)."""
     q, k = _gen(cfg, seed, (0, 1), heads, B)

@@ -583,3 +583,158 @@ def pin_skip_round_trip(encode_impl, decode_impl, seed=23):
             widest = max(widest, int(np.sum(np.diff(c) != 1) + 1) if len(c) else 0)
     assert w == widest
     assert np.all(pairs[np.arange(pairs.shape[1])[None, :] >= counts[:, None]] == -1), "padding"
+
+
+# ---------------------------------------------------------------- spatial repetition
+
+def _eval_closed_form(expr):
+    return eval(expr, {"__builtins__": {}}, {"sqrt": math.sqrt})
+
+
+def _repetition_golden_inputs(case, pad=3):
+    """d = 1, scale 1: key j = log(k_exp[j]); padded tokens get values that
+    would dominate if they leaked into the softmax."""
+    F, R, C = case["grid"]
+    S = F * R * C
+    L = S + pad
+    q = np.full((1, 1, L, 1), 40.0)
+    k = np.full((1, 1, L, 1), 40.0)
+    q[0, 0, :S, 0] = case["q"]
+    k[0, 0, :S, 0] = np.log(np.asarray(case["k_exp"], dtype=np.float64))
+    return q, k, S, (F, R, C)
+
+
+def pin_similarity_golden(sim_impl):
+    """sim_impl(q, k, scale, seq_len, grid) -> [B, H]; hand-worked cosines."""
+    for case in _load_golden("spatial_repetition.json")["similarity"]:
+        q, k, S, grid = _repetition_golden_inputs(case)
+        got = float(np.asarray(sim_impl(q, k, 1.0, S, grid))[0, 0])
+        assert abs(got - _eval_closed_form(case["score"])) < 1e-12, f"golden score on grid {grid}"
+
+
+def _brute_similarity(q, k, scale, S, grid):
+    """Per token softmax and cosine in Python loops."""
+    F, R, C = grid
+    B, H = q.shape[:2]
+    out = np.zeros((B, H))
+    for b in range(B):
+        for h in range(H):
+            def prow(i):
+                s = [scale * sum(q[b, h, i, c] * k[b, h, j, c] for c in range(q.shape[3])) for j in range(S)]
+                m = max(s)
+                e = [math.exp(x - m) for x in s]
+                t = sum(e)
+                return [x / t for x in e]
+            tot, n = 0.0, 0
+            for f in range(F):
+                for y in range(R - 1):
+                    for x in range(C):
+                        a, c = prow((f * R + y) * C + x), prow((f * R + y + 1) * C + x)
+                        dot = sum(u * v for u, v in zip(a, c))
+                        tot += dot / math.sqrt(sum(u * u for u in a) * sum(v * v for v in c))
+                        n += 1
+            out[b, h] = tot / n
+    return out
+
+
+def pin_similarity_special(sim_impl, seed=24):
+    rng = _rng(seed)
+    # brute force on tiny random inputs (ragged padding, two prompts, two heads)
+    for grid, pad in (((2, 3, 2), 5), ((1, 4, 3), 0), ((3, 2, 1), 2)):
+        F, R, C = grid
+        S = F * R * C
+        q, k = (rng.standard_normal((2, 2, S + pad, 3)) for _ in range(2))
+        got = np.asarray(sim_impl(q, k, 0.8, S, grid))
+        assert np.max(np.abs(got - _brute_similarity(q, k, 0.8, S, grid))) < 1e-12, "brute-force cosines"
+        assert np.all(got > 0) and np.all(got <= 1 + 1e-15), "cosine of positive vectors lies in (0, 1]"
+    # Q = 0: every softmax row is uniform, so every cosine is 1
+    F, R, C = 2, 4, 3
+    S = F * R * C
+    k = rng.standard_normal((1, 2, S + 4, 8))
+    got = np.asarray(sim_impl(np.zeros_like(k), k, 1.0, S, (F, R, C)))
+    assert np.max(np.abs(got - 1.0)) < 1e-12, "Q = 0 gives score 1"
+    # queries repeated down the rows of each frame: identical softmax rows
+    q = rng.standard_normal((1, 2, S + 4, 8))
+    for f in range(F):
+        for y in range(1, R):
+            q[:, :, (f * R + y) * C:(f * R + y + 1) * C] = q[:, :, f * R * C:(f * R + 1) * C]
+    got = np.asarray(sim_impl(q, k, 1.3, S, (F, R, C)))
+    assert np.max(np.abs(got - 1.0)) < 1e-12, "rows that repeat give score 1"
+
+
+def pin_row_groups(groups_impl, anchor_of_row_impl):
+    """groups_impl(rows, k) -> [(lo, hi, anchor)]; golden cases, then the
+    properties for every rows <= 40: contiguous cover, near-equal sizes, the
+    lower middle row as anchor."""
+    for case in _load_golden("spatial_repetition.json")["groups"]:
+        got = [tuple(int(v) for v in t) for t in groups_impl(case["rows"], case["k"])]
+        if "groups" in case:
+            assert got == [tuple(t) for t in case["groups"]], f"groups rows={case['rows']} k={case['k']}"
+        else:
+            assert [t[2] for t in got] == case["anchors"], f"anchors rows={case['rows']} k={case['k']}"
+    for R in range(1, 41):
+        for k in range(1, R + 1):
+            got = [tuple(int(v) for v in t) for t in groups_impl(R, k)]
+            assert len(got) == k and got[0][0] == 0 and got[-1][1] == R
+            assert all(got[i][1] == got[i + 1][0] for i in range(k - 1)), "contiguous"
+            assert {hi - lo for lo, hi, _ in got} <= {R // k, -(-R // k)}, "near-equal sizes"
+            for lo, hi, a in got:
+                assert a - lo == (hi - 1 - lo) // 2, "lower middle row"
+            amap = np.asarray(anchor_of_row_impl(R, k))
+            assert [int(amap[y]) for y in range(R)] == [a for lo, hi, a in got for _ in range(lo, hi)]
+
+
+def pin_anchor_sparsity_table(anchor_tokens_impl):
+    """Table S4: the fraction of query rows skipped is 1 - k/30 at the Wan grid
+    (21 frames x 30 rows x 52 columns = 32,760 tokens), printed in percent to
+    one decimal."""
+    for row in _load_golden("pages_tables.json")["anchor_rows"]["rows"]:
+        n = len(np.unique(np.asarray(anchor_tokens_impl((21, 30, 52), row["k"]))))
+        assert abs(100.0 * (1 - n / 32760) - row["sparsity"]) <= 0.05 + 1e-9, f"Table S4 sparsity at k={row['k']}"
+
+
+def pin_anchor_broadcast(anchor_impl, seed=25):
+    """anchor_impl(q, k, v, scale, seq_len, grid, k_anchor, heads) -> [B, len(heads), L, d].
+
+    Query i attends (all but) only to key i (one-hot q and k, a large scale),
+    so an output row is the V row of the token it was computed for: the
+    golden source-token map shows through directly."""
+    g = _load_golden("spatial_repetition.json")["broadcast"]
+    F, R, C = g["grid"]
+    S = F * R * C
+    L = S + 2
+    q = np.zeros((1, 1, L, S))
+    q[0, 0, np.arange(S), np.arange(S)] = 1.0
+    k = q.copy()
+    v = _rng(seed).standard_normal((1, 1, L, 4))
+    O = np.asarray(anchor_impl(q, k, v, 80.0, S, (F, R, C), g["k"], [0]))
+    assert np.max(np.abs(O[0, 0, :S] - v[0, 0, g["source_token"]])) < 1e-12, "golden broadcast map"
+    assert np.all(O[0, 0, S:] == 0.0), "padded rows are zero"
+
+
+def pin_anchor_special(anchor_impl, seed=26):
+    rng = _rng(seed)
+    F, R, C = 2, 5, 3
+    S = F * R * C
+    L = S + 3
+    q, k, v = (rng.standard_normal((2, 3, L, 8)) for _ in range(3))
+    heads = [2, 0]
+    ref = _sdpa(q[:, :, :S], k[:, :, :S], v[:, :, :S], 0.6)
+    # every row its own anchor: ordinary attention (SDPA) for the listed heads
+    O = np.asarray(anchor_impl(q, k, v, 0.6, S, (F, R, C), R, heads))
+    assert np.max(np.abs(O[:, :, :S] - ref[:, heads])) < 1e-12, "k = rows gives dense attention"
+    assert np.all(O[:, :, S:] == 0.0)
+    # queries repeated down the rows of each frame: broadcasting is exact for any k
+    for f in range(F):
+        for y in range(1, R):
+            q[:, :, (f * R + y) * C:(f * R + y + 1) * C] = q[:, :, f * R * C:(f * R + 1) * C]
+    ref = _sdpa(q[:, :, :S], k[:, :, :S], v[:, :, :S], 0.6)
+    for ka in (1, 2, 3):
+        O = np.asarray(anchor_impl(q, k, v, 0.6, S, (F, R, C), ka, heads))
+        assert np.max(np.abs(O[:, :, :S] - ref[:, heads])) < 1e-12, f"repeated rows, k={ka}"
+
+
+def pin_select_golden(select_impl):
+    g = _load_golden("spatial_repetition.json")["selection"]
+    got = [int(x) for x in select_impl(np.array(g["sim"]), g["tau"])]
+    assert got == g["heads_expected"], "heads whose mean score exceeds tau"

@@ -4,6 +4,7 @@ This shows the pins are sharp enough to catch the plausible slips (a dropped
 term, a wrong index, a transposed operand, an off-by-one rule) in the oracle.
 Everything here runs on the CPU."""
 
+import functools
 import math
 
 import numpy as np
@@ -325,3 +326,90 @@ def test_interval_mutants_are_caught():
     golden = lambda impls: pins.pin_intervals_golden(*impls)
     assert _trips((_intervals_inclusive, oracle.merge_row, oracle.width_percentile), [golden])
     assert _trips((oracle.row_intervals, _merge_rightmost, oracle.width_percentile), [golden])
+
+
+# ---------------------------------------------------------------- spatial repetition
+
+def _sim_generic(q, k, scale, seq_len, grid, *, lag=None, normalise=True, skip_last_frame=False):
+    """Adjacent-row cosine with one planted mistake at a time."""
+    q, k = (np.asarray(x, dtype=np.float64) for x in (q, k))
+    B, H = q.shape[:2]
+    F, R, C = grid
+    lag = C if lag is None else lag
+    top = [(f * R + y) * C + x for f in range(F - int(skip_last_frame)) for y in range(R - 1) for x in range(C)]
+    top = np.array(top or [0])
+    out = np.zeros((B, H))
+    for b in range(B):
+        for h in range(H):
+            s = scale * (q[b, h, :seq_len] @ k[b, h, :seq_len].T)
+            P = np.exp(s - s.max(1, keepdims=True))
+            P /= P.sum(1, keepdims=True)
+            a, c = P[top], P[np.minimum(top + lag, seq_len - 1)]
+            num = (a * c).sum(1)
+            out[b, h] = (num / np.sqrt((a * a).sum(1) * (c * c).sum(1)) if normalise else num).mean()
+    return out
+
+
+def _groups_first_row(rows, k):
+    """Mistake: the first row of each group is its anchor."""
+    return [(lo, hi, lo) for lo, hi, _ in oracle.row_groups(rows, k)]
+
+
+def _groups_ceil(rows, k):
+    """Mistake: equal groups of ceil(rows/k) rows, the last one short."""
+    w = -(-rows // k)
+    out = []
+    for g in range(k):
+        lo, hi = min(g * w, rows), min((g + 1) * w, rows)
+        out.append((lo, hi, (lo + max(hi, lo + 1) - 1) // 2))
+    return out
+
+
+def _anchor_of_row_from(groups):
+    def f(rows, k):
+        a = np.zeros(rows, dtype=np.int64)
+        for lo, hi, anc in groups(rows, k):
+            a[lo:hi] = anc
+        return a
+    return f
+
+
+def _anchor_attention_generic(q, k, v, scale, seq_len, grid, k_anchor, heads, *, keys_anchor_only=False,
+                              ignore_frame=False):
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    B, H, L, _ = q.shape
+    F, R, C = grid
+    arow = oracle.anchor_of_row(R, k_anchor)
+    n = np.arange(seq_len)
+    f, y, x = n // (R * C), (n // C) % R, n % C
+    src = ((0 if ignore_frame else f) * R + arow[y]) * C + x
+    anchors = oracle.anchor_tokens(grid, k_anchor)
+    keys = anchors if keys_anchor_only else np.arange(seq_len)
+    O = np.zeros((B, len(heads), L, v.shape[3]))
+    for b in range(B):
+        for i, h in enumerate(heads):
+            s = scale * (q[b, h, anchors] @ k[b, h, keys].T)
+            P = np.exp(s - s.max(1, keepdims=True))
+            P /= P.sum(1, keepdims=True)
+            out = np.zeros((L, v.shape[3]))
+            out[anchors] = P @ v[b, h, keys]
+            O[b, i, :seq_len] = out[src]
+    return O
+
+
+def _select_ge(sim, tau):
+    """Mistake: a score equal to tau also selects."""
+    return np.nonzero(np.asarray(sim, dtype=np.float64).mean(0) >= tau)[0]
+
+
+def test_repetition_mutants_are_caught():
+    sim_pins = [pins.pin_similarity_golden, pins.pin_similarity_special]
+    assert _trips(functools.partial(_sim_generic, lag=1), sim_pins)
+    assert _trips(functools.partial(_sim_generic, normalise=False), sim_pins)
+    assert _trips(functools.partial(_sim_generic, skip_last_frame=True), sim_pins)
+    for groups in (_groups_first_row, _groups_ceil):
+        assert _trips(groups, [lambda g: pins.pin_row_groups(g, _anchor_of_row_from(g))])
+    attn_pins = [pins.pin_anchor_broadcast, pins.pin_anchor_special]
+    assert _trips(functools.partial(_anchor_attention_generic, keys_anchor_only=True), attn_pins)
+    assert _trips(functools.partial(_anchor_attention_generic, ignore_frame=True), attn_pins)
+    assert _trips(_select_ge, [pins.pin_select_golden])
