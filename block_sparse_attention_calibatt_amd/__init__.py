@@ -4,7 +4,8 @@ The compute lives in libcalibatt.so (HIP kernels behind a C ABI, declared in
 include/calibatt.h).  This package is the thin binding: ``capi`` mirrors the
 C entry points one to one, ``MaskBank`` keeps the compiled lists of many
 timesteps on the GPU (``SharedMaskBank``: one mask per run of alike
-timesteps).  Build the library with
+timesteps), and the spatial-repetition entry points score heads and run
+their anchor rows.  Build the library with
 ``python -m block_sparse_attention_calibatt_amd.build``.
 """
 
@@ -25,6 +26,11 @@ from .capi import (
     calibatt_skip_ws_bytes,
     calibatt_encode_skip_lists,
     calibatt_decode_skip_lists,
+    calibatt_similarity_ws_bytes,
+    calibatt_spatial_similarity,
+    calibatt_select_repetitive_heads,
+    calibatt_anchor_ws_bytes,
+    calibatt_anchor_attn_fwd,
     calibatt_validate_csr,
     calibatt_status_string,
     calibatt_last_error,
@@ -51,6 +57,11 @@ __all__ = [
     "calibatt_skip_ws_bytes",
     "calibatt_encode_skip_lists",
     "calibatt_decode_skip_lists",
+    "calibatt_similarity_ws_bytes",
+    "calibatt_spatial_similarity",
+    "calibatt_select_repetitive_heads",
+    "calibatt_anchor_ws_bytes",
+    "calibatt_anchor_attn_fwd",
     "calibatt_validate_csr",
     "calibatt_status_string",
     "calibatt_last_error",

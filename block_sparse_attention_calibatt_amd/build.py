@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libcalibatt.so")
 PROBE_SRC = os.path.join(CSRC, "probes", "mfma_rate.hip")
 PROBE = os.path.join(PKG, "mfma_rate")
-SOURCES = ["api.hip", "attn_fwd.hip", "mass.hip", "compile.hip", "share.hip", "intervals.hip"]
+SOURCES = ["api.hip", "attn_fwd.hip", "mass.hip", "compile.hip", "share.hip", "intervals.hip", "repeat.hip"]
 ARCH = os.environ.get("CALIBATT_ARCH", "gfx950")
 
 FLAGS = [

@@ -321,6 +321,74 @@ def calibatt_decode_skip_lists(counts, pairs, width, T, H, nqb, nnz_cap=None, ws
     return rp, off, ci[: nnz.value]
 
 
+def calibatt_similarity_ws_bytes(B, H, L):
+    return int(load().calibatt_similarity_ws_bytes(int(B), int(H), int(L)))
+
+
+def calibatt_spatial_similarity(Q, K, scale, grid, seq_len=None, sim=None, ws=None):
+    """Score per (b, h): mean cosine of the softmax rows of vertically adjacent
+    tokens on the (frames, rows, cols) grid.  Returns sim [B, H] float64."""
+    for n, t in (("Q", Q), ("K", K)):
+        _dev_tensor(t, n, torch.bfloat16)
+    _need(Q.dim() == 4 and K.shape == Q.shape and K.device == Q.device, "Q, K must be [B, H, L, d] alike")
+    B, H, L, d = Q.shape
+    seq_len = L if seq_len is None else int(seq_len)
+    F, R, C = (int(x) for x in grid)
+    if sim is None:
+        sim = torch.empty((B, H), dtype=torch.float64, device=Q.device)
+    _dev_tensor(sim, "sim", torch.float64)
+    _need(sim.numel() == B * H, "sim must have B*H entries")
+    need = calibatt_similarity_ws_bytes(B, H, L)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=Q.device)
+    _dev_tensor(ws, "ws", torch.uint8)
+    lib = load()
+    check(lib.calibatt_spatial_similarity(_ptr(Q), _ptr(K), B, H, L, seq_len, d, BF16, float(scale), F, R, C,
+                                          _ptr(sim), _ptr(ws), ws.numel(), _stream(Q)))
+    return sim
+
+
+def calibatt_select_repetitive_heads(sim, tau):
+    """sim [P, H] float64 (device) -> ascending list of heads whose mean over P exceeds tau."""
+    _dev_tensor(sim, "sim", torch.float64)
+    _need(sim.dim() == 2, "sim must be [P, H]")
+    P, H = sim.shape
+    heads = np.zeros(H, dtype=np.int32)
+    n = ctypes.c_int(0)
+    lib = load()
+    check(lib.calibatt_select_repetitive_heads(_ptr(sim), P, H, float(tau), heads.ctypes.data_as(ctypes.c_void_p),
+                                               ctypes.byref(n), _stream(sim)))
+    return [int(h) for h in heads[:n.value]]
+
+
+def calibatt_anchor_ws_bytes(B, H, frames, grid_cols, k_anchor, d):
+    return int(load().calibatt_anchor_ws_bytes(int(B), int(H), int(frames), int(grid_cols), int(k_anchor), int(d)))
+
+
+def calibatt_anchor_attn_fwd(Q, K, V, O, heads, grid, k_anchor, scale, seq_len=None, queue_ws=None,
+                             v_transposed=False, vt_ws=None, ws=None):
+    """Anchor-row attention for the listed heads; other heads of O are left as they are."""
+    B, H, L, d = _qkv(Q, K, V, O, v_transposed)
+    _need(Q.dtype == torch.bfloat16, "anchor attention takes bfloat16 tensors")
+    seq_len = L if seq_len is None else int(seq_len)
+    F, R, C = (int(x) for x in grid)
+    hl = np.ascontiguousarray(np.asarray(list(heads), dtype=np.int32))
+    if queue_ws is None:
+        queue_ws = new_queue(Q.device)
+    _queue(queue_ws)
+    layout, vt_ws = _vt_args(Q, v_transposed, vt_ws)
+    need = calibatt_anchor_ws_bytes(B, H, F, C, k_anchor, d)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=Q.device)
+    _dev_tensor(ws, "ws", torch.uint8)
+    lib = load()
+    check(lib.calibatt_anchor_attn_fwd(
+        _ptr(Q), _ptr(K), _ptr(V), _ptr(O), hl.ctypes.data_as(ctypes.c_void_p), int(hl.size), F, R, C,
+        int(k_anchor), float(scale), B, H, L, seq_len, d, BF16, _ptr(queue_ws), layout, _ptr(vt_ws),
+        _ptr(ws), ws.numel(), _stream(Q)))
+    return O
+
+
 def calibatt_build_schedule(row_ptr, H, nqb, work_order=None):
     _dev_tensor(row_ptr, "row_ptr", torch.int32)
     _need(row_ptr.numel() == H * nqb + 1, "row_ptr must have H*nqb+1 entries")

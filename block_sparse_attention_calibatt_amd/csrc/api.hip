@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/calibatt.h"
 #include "launch.h"
@@ -533,6 +534,158 @@ calibatt_status calibatt_build_schedule(const int32_t* row_ptr, int H, int nqb, 
   if (!aligned(row_ptr, 4) || !aligned(work_order, 4)) return fail(CALIBATT_ERR_ALIGN, "row_ptr and work_order must be 4-byte aligned");
   hipError_t e = calibatt::launch_schedule(row_ptr, H, nqb, work_order, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "launching work-order build");
+  return ok();
+}
+
+size_t calibatt_similarity_ws_bytes(int B, int H, int L) {
+  if (B < 1 || H < 1 || L < 128 || L % 128 != 0) return 0;
+  const size_t bh = (size_t)B * H;
+  return (bh * L * sizeof(float) + 255) / 256 * 256 + bh * (L / 128) * sizeof(double);
+}
+
+static calibatt_status check_grid(int frames, int grid_rows, int grid_cols, int seq_len) {
+  if (frames < 1 || grid_rows < 1 || grid_cols < 1)
+    return fail(CALIBATT_ERR_SHAPE, "frames=%d, grid_rows=%d and grid_cols=%d must be >= 1", frames, grid_rows, grid_cols);
+  if ((long long)frames * grid_rows * grid_cols != seq_len)
+    return fail(CALIBATT_ERR_SHAPE, "frames*grid_rows*grid_cols=%lld must equal seq_len=%d",
+                (long long)frames * grid_rows * grid_cols, seq_len);
+  return CALIBATT_OK;
+}
+
+calibatt_status calibatt_spatial_similarity(const void* Q, const void* K, int B, int H, int L, int seq_len,
+                                            int d, calibatt_dtype dt, float scale, int frames, int grid_rows,
+                                            int grid_cols, double* sim, void* ws, size_t ws_bytes, void* stream) {
+  if (!Q || !K || !sim || !ws) return fail(CALIBATT_ERR_NULL, "Q, K, sim and ws must be non-NULL");
+  if (!aligned(Q, 16) || !aligned(K, 16)) return fail(CALIBATT_ERR_ALIGN, "Q and K must be 16-byte aligned");
+  if (!aligned(sim, 8) || !aligned(ws, 256)) return fail(CALIBATT_ERR_ALIGN, "sim must be 8-byte and ws 256-byte aligned");
+  calibatt_status s = check_qkv_shape(B, H, L, seq_len, d, dt, 128);
+  if (s != CALIBATT_OK) return s;
+  if (dt != CALIBATT_BF16) return fail(CALIBATT_ERR_UNSUPPORTED, "spatial similarity supports bf16 inputs only");
+  s = check_grid(frames, grid_rows, grid_cols, seq_len);
+  if (s != CALIBATT_OK) return s;
+  if (grid_rows < 2) return fail(CALIBATT_ERR_SHAPE, "grid_rows=%d: the score needs at least two rows", grid_rows);
+  const size_t need = calibatt_similarity_ws_bytes(B, H, L);
+  if (ws_bytes < need) return fail(CALIBATT_ERR_CAPACITY, "ws_bytes=%zu, need %zu", ws_bytes, need);
+  calibatt::SimArgs a;
+  a.Q = Q;
+  a.K = K;
+  a.lse = static_cast<float*>(ws);
+  a.part = reinterpret_cast<double*>(static_cast<char*>(ws) + ((size_t)B * H * L * sizeof(float) + 255) / 256 * 256);
+  a.sim = sim;
+  a.B = B;
+  a.H = H;
+  a.L = L;
+  a.seq_len = seq_len;
+  a.d = d;
+  a.frames = frames;
+  a.rows = grid_rows;
+  a.cols = grid_cols;
+  a.scale = scale;
+  hipError_t e = calibatt::launch_spatial_similarity(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "launching spatial similarity");
+  return ok();
+}
+
+calibatt_status calibatt_select_repetitive_heads(const double* sim, int P, int H, double tau, int32_t* heads,
+                                                 int32_t* n_heads, void* stream) {
+  if (!sim || !heads || !n_heads) return fail(CALIBATT_ERR_NULL, "sim, heads and n_heads must be non-NULL");
+  if (P < 1 || H < 1) return fail(CALIBATT_ERR_SHAPE, "P=%d and H=%d must be >= 1", P, H);
+  if (!aligned(sim, 8)) return fail(CALIBATT_ERR_ALIGN, "sim must be 8-byte aligned");
+  std::vector<double> host((size_t)P * H);
+  hipError_t e = hipMemcpyAsync(host.data(), sim, host.size() * sizeof(double), hipMemcpyDeviceToHost,
+                                (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "reading the similarity scores");
+  int n = 0;
+  for (int h = 0; h < H; ++h) {
+    double acc = 0.0;
+    for (int p = 0; p < P; ++p) acc += host[(size_t)p * H + h];
+    if (acc / P > tau) heads[n++] = h;
+  }
+  *n_heads = n;
+  return ok();
+}
+
+static long long anchor_queries(int frames, int grid_cols, int k_anchor) {
+  return (long long)frames * k_anchor * grid_cols;
+}
+
+size_t calibatt_anchor_ws_bytes(int B, int H, int frames, int grid_cols, int k_anchor, int d) {
+  if (B < 1 || H < 1 || frames < 1 || grid_cols < 1 || k_anchor < 1 || (d != 64 && d != 128)) return 0;
+  const long long Lq = (anchor_queries(frames, grid_cols, k_anchor) + 127) / 128 * 128;
+  const size_t qa = ((size_t)B * H * Lq * d * 2 + 255) / 256 * 256;
+  return 2 * qa + ((size_t)H * (Lq / 128) + calibatt::kParts + 1) * sizeof(int32_t);
+}
+
+calibatt_status calibatt_anchor_attn_fwd(const void* Q, const void* K, const void* V, void* O,
+                                         const int32_t* heads, int n_heads, int frames, int grid_rows,
+                                         int grid_cols, int k_anchor, float scale, int B, int H, int L,
+                                         int seq_len, int d, calibatt_dtype dt, int32_t* queue_ws,
+                                         calibatt_vlayout v_layout, void* vt_ws, void* ws, size_t ws_bytes,
+                                         void* stream) {
+  calibatt_status s = check_ptrs4(Q, K, V, O);
+  if (s != CALIBATT_OK) return s;
+  s = check_qkv_shape(B, H, L, seq_len, d, dt, 128);
+  if (s != CALIBATT_OK) return s;
+  if (dt != CALIBATT_BF16) return fail(CALIBATT_ERR_UNSUPPORTED, "anchor attention supports bf16 inputs only");
+  s = check_v_layout(v_layout, Q, K, V, O, vt_ws, B, H, L, d, dt);
+  if (s != CALIBATT_OK) return s;
+  s = check_grid(frames, grid_rows, grid_cols, seq_len);
+  if (s != CALIBATT_OK) return s;
+  if (k_anchor < 1 || k_anchor > grid_rows)
+    return fail(CALIBATT_ERR_SHAPE, "k_anchor=%d must be in [1, grid_rows=%d]", k_anchor, grid_rows);
+  if (n_heads < 0 || n_heads > H) return fail(CALIBATT_ERR_SHAPE, "n_heads=%d must be in [0, H=%d]", n_heads, H);
+  if (n_heads > calibatt::kMaxListHeads)
+    return fail(CALIBATT_ERR_UNSUPPORTED, "n_heads=%d exceeds %d", n_heads, calibatt::kMaxListHeads);
+  if (n_heads > 0 && !heads) return fail(CALIBATT_ERR_NULL, "heads must be non-NULL when n_heads > 0");
+  if (!queue_ws || !ws) return fail(CALIBATT_ERR_NULL, "queue_ws and ws must be non-NULL");
+  if (!aligned(queue_ws, 16) || !aligned(ws, 256)) return fail(CALIBATT_ERR_ALIGN, "queue_ws must be 16-byte and ws 256-byte aligned");
+  calibatt::AnchorArgs a;
+  a.heads.n = n_heads;
+  for (int i = 0; i < n_heads; ++i) {
+    if (heads[i] < 0 || heads[i] >= H) return fail(CALIBATT_ERR_SHAPE, "heads[%d]=%d outside [0, H=%d)", i, heads[i], H);
+    for (int j = 0; j < i; ++j)
+      if (heads[j] == heads[i]) return fail(CALIBATT_ERR_SHAPE, "head %d is listed twice", heads[i]);
+    a.heads.h[i] = heads[i];
+  }
+  const long long La = anchor_queries(frames, grid_cols, k_anchor);
+  const long long Lq = (La + 127) / 128 * 128;
+  if ((long long)B * H * Lq * d >= (1LL << 31)) return fail(CALIBATT_ERR_SHAPE, "B*H*Lq*d must be < 2^31");
+  const size_t need = calibatt_anchor_ws_bytes(B, H, frames, grid_cols, k_anchor, d);
+  if (ws_bytes < need) return fail(CALIBATT_ERR_CAPACITY, "ws_bytes=%zu, need %zu", ws_bytes, need);
+  if (n_heads == 0) return ok();
+  int ncu = 256;
+  hipError_t e = cu_count(&ncu);
+  if (e != hipSuccess) return hip_fail(e, "querying the compute-unit count");
+  const void* Vt = V;
+  if (v_layout == CALIBATT_V_BHLD) {
+    s = enqueue_transpose(V, vt_ws, B, H, L, seq_len, d, dt, stream);
+    if (s != CALIBATT_OK) return s;
+    Vt = vt_ws;
+  }
+  const size_t qa = ((size_t)B * H * Lq * d * 2 + 255) / 256 * 256;
+  a.Q = Q;
+  a.K = K;
+  a.Vt = Vt;
+  a.O = O;
+  a.Qa = ws;
+  a.Oa = static_cast<char*>(ws) + qa;
+  a.order = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + 2 * qa);
+  a.queue = queue_ws;
+  a.B = B;
+  a.H = H;
+  a.L = L;
+  a.seq_len = seq_len;
+  a.d = d;
+  a.rows = grid_rows;
+  a.cols = grid_cols;
+  a.k = k_anchor;
+  a.La = (int)La;
+  a.Lq = (int)Lq;
+  a.scale = scale;
+  a.num_cu = ncu;
+  e = calibatt::launch_anchor_fwd(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "launching anchor-row attention");
   return ok();
 }
 

@@ -436,12 +436,17 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(
 // A DMA issued in phase t has landed by the end of phase t+1, so K(x) is
 // issued two phases before S(x) reads it and V^T(x) two phases before
 // P*V(x).  K and V^T rotate through three LDS stages each.
-template <int D, bool DENSE>
+//
+// SPLITQ: Q and O have their own length Lq (a multiple of 128) and only
+// their first q_valid rows are real (the anchor queries of the
+// spatial-repetition heads); rows are h*(Lq/128) + qb, and keys still run
+// over K and V^T of length L with seq_len valid.
+template <int D, bool DENSE, bool SPLITQ = false>
 __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ Vt,
     bf16* __restrict__ O, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     const int32_t* __restrict__ work_order, int32_t* __restrict__ queue, int items, int H, int L,
-    int seq_len, int nkb_valid, float c2) {
+    int seq_len, int nkb_valid, float c2, int Lq, int q_valid) {
   constexpr int BLK = 128;
   using G = Geo<D, BLK>;   // one wave group: NW = 4 waves of 32 queries
   constexpr int DS = G::DS, DT = G::DT, KS = G::KS, CH = G::CH;
@@ -456,7 +461,7 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
   u32x4* const kst[3] = {ks0, ks1, ks2};
   u32x4* const vst[3] = {vs0, vs1, vs2};
 
-  const int nqb = L / BLK;
+  const int nqb = (SPLITQ ? Lq : L) / BLK;
   const int rows = H * nqb;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -506,6 +511,7 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
   for_each_row(src, queue, &s_item, [&](int b, int r) {
     const int h = r / nqb, qb = r - h * nqb;
     const size_t base = ((size_t)b * H + h) * (size_t)L * D;
+    const size_t qbase = SPLITQ ? ((size_t)b * H + h) * (size_t)Lq * D : base;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + base, slab_bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vt + base, slab_bytes);
     const int q = qb * BLK + 32 * w + c;   // this lane's query
@@ -553,7 +559,7 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
     bf16x8 qreg[DS];
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
-      const bf16x8 qv = *reinterpret_cast<const bf16x8*>(Q + base + (size_t)q * D + 16 * s + 8 * g);
+      const bf16x8 qv = *reinterpret_cast<const bf16x8*>(Q + qbase + (size_t)q * D + 16 * s + 8 * g);
 #pragma unroll
       for (int e = 0; e < 8; ++e) qreg[s][e] = (bf16)((float)qv[e] * c2);
     }
@@ -803,9 +809,9 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
       if (m == kNegInf) m = 0.f;
       const float aa = fast_exp2(mca - m), ab = fast_exp2(mcb - m);
       const float l_tot = pair_sum(l_run * aa + lb * ab);
-      const float inv = (q < seq_len && l_tot > 0.f) ? 1.f / l_tot : 0.f;
+      const float inv = (q < (SPLITQ ? q_valid : seq_len) && l_tot > 0.f) ? 1.f / l_tot : 0.f;
       const float fa = aa * inv, fb = ab * inv;
-      bf16* Ob = O + base + (size_t)q * D;
+      bf16* Ob = O + qbase + (size_t)q * D;
 #pragma unroll
       for (int u = 0; u < 2 * DT; ++u) {
         const f32x4 lo = reinterpret_cast<const f32x4*>(chunk(u))[0];
@@ -968,24 +974,31 @@ static hipError_t occupancy(Kern k, int threads, int* blocks_per_cu) {
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, k, threads, 0);
 }
 
-template <int D, bool DENSE>
+template <int D, bool DENSE, bool SPLITQ = false>
 static hipError_t launch_pp(const AttnArgs& a, hipStream_t st) {
-  const int items = a.B * a.H * (a.L / 128);
+  const int Lq = SPLITQ ? a.Lq : a.L;
+  const int items = a.B * a.H * (Lq / 128);
   const float c2 = a.scale * kLog2e;
   if (items == 0) return hipSuccess;
   int grid = items;
   if (a.queue) {
     hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(kQueueInts), 0, st, a.queue, kQueueInts, 0);
     int per_cu = 1;
-    hipError_t e = occupancy(attn_fwd_pp_kernel<D, DENSE>, 512, &per_cu);
+    hipError_t e = occupancy(attn_fwd_pp_kernel<D, DENSE, SPLITQ>, 512, &per_cu);
     if (e != hipSuccess) return e;
     const long long cap = (long long)a.num_cu * (per_cu > 0 ? per_cu : 1);
     grid = (int)(cap < items ? cap : items);
   }
-  hipLaunchKernelGGL((attn_fwd_pp_kernel<D, DENSE>), dim3(grid), dim3(512), 0, st, (const bf16*)a.Q,
+  hipLaunchKernelGGL((attn_fwd_pp_kernel<D, DENSE, SPLITQ>), dim3(grid), dim3(512), 0, st, (const bf16*)a.Q,
                      (const bf16*)a.K, (const bf16*)a.Vt, (bf16*)a.O, a.row_ptr, a.col_idx, a.work_order, a.queue,
-                     items, a.H, a.L, a.seq_len, a.nkb_valid, c2);
+                     items, a.H, a.L, a.seq_len, a.nkb_valid, c2, Lq, SPLITQ ? a.q_valid : a.seq_len);
   return hipGetLastError();
+}
+
+hipError_t launch_anchor_attention(const AttnArgs& a, hipStream_t st) {
+  if (a.dtype_f32 || a.block != 128 || !a.work_order || !a.queue) return hipErrorInvalidValue;
+  if (a.d == 128) return launch_pp<128, true, true>(a, st);
+  return launch_pp<64, true, true>(a, st);
 }
 
 template <int D, int BLK, bool DENSE>

@@ -21,9 +21,14 @@ struct AttnArgs {
   float scale;
   bool dtype_f32;
   int num_cu;
+  // anchor-row launches only: Q and O are [B, H, Lq, d] with q_valid real rows
+  int Lq = 0, q_valid = 0;
 };
 
 hipError_t launch_attention(const AttnArgs& a, bool dense, hipStream_t st);
+// Dense attention of the anchor queries (bf16, block 128; needs a work_order
+// that lists the rows to run, and a queue).
+hipError_t launch_anchor_attention(const AttnArgs& a, hipStream_t st);
 
 struct TransposeArgs {
   const void* V;   // [B, H, L, d]
@@ -44,6 +49,48 @@ struct MassArgs {
 };
 
 hipError_t launch_block_mass(const MassArgs& a, hipStream_t st);
+// Pass 1 of the pooling alone: lse per query over the valid keys (block 128 tiles).
+hipError_t launch_row_lse(const MassArgs& a, hipStream_t st);
+
+// Heads handed to a kernel by value (kernel arguments), so that no device
+// list has to be written first.
+constexpr int kMaxListHeads = 256;
+struct HeadList {
+  int n;
+  int32_t h[kMaxListHeads];
+};
+
+struct SimArgs {
+  const void* Q;
+  const void* K;
+  float* lse;      // [B, H, L]
+  double* part;    // [B, H, L/128]
+  double* sim;     // [B, H]
+  int B, H, L, seq_len, d;
+  int frames, rows, cols;
+  float scale;
+};
+
+hipError_t launch_spatial_similarity(const SimArgs& a, hipStream_t st);
+
+struct AnchorArgs {
+  const void* Q;
+  const void* K;
+  const void* Vt;  // [B, H, d, L]
+  void* O;
+  void* Qa;        // [B, H, Lq, d]
+  void* Oa;        // [B, H, Lq, d]
+  int32_t* order;  // [H*(Lq/128) + kParts + 1]
+  int32_t* queue;
+  HeadList heads;
+  int B, H, L, seq_len, d;
+  int rows, cols, k;   // grid rows and columns, anchors per frame
+  int La, Lq;          // anchor queries, padded to a multiple of 128
+  float scale;
+  int num_cu;
+};
+
+hipError_t launch_anchor_fwd(const AnchorArgs& a, hipStream_t st);
 
 struct CompileArgs {
   const float* mass;

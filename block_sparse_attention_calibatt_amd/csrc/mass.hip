@@ -155,6 +155,18 @@ static hipError_t launch_mass_typed(const MassArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+hipError_t launch_row_lse(const MassArgs& a, hipStream_t st) {
+  const int items = a.B * a.H * (a.L / 128);
+  const float c2 = a.scale * kLog2e;
+  if (a.d == 128)
+    hipLaunchKernelGGL((row_lse_kernel<128, 128>), dim3(items), dim3(256), 0, st, (const bf16*)a.Q,
+                       (const bf16*)a.K, a.lse, a.H, a.L, a.seq_len, a.nkb_valid, c2);
+  else
+    hipLaunchKernelGGL((row_lse_kernel<64, 128>), dim3(items), dim3(256), 0, st, (const bf16*)a.Q,
+                       (const bf16*)a.K, a.lse, a.H, a.L, a.seq_len, a.nkb_valid, c2);
+  return hipGetLastError();
+}
+
 hipError_t launch_block_mass(const MassArgs& a, hipStream_t st) {
   if (a.d == 128 && a.block == 128) return launch_mass_typed<128, 128>(a, st);
   if (a.d == 128 && a.block == 64) return launch_mass_typed<128, 64>(a, st);

@@ -1,0 +1,279 @@
+// Spatial-repetition heads on gfx950: the similarity score that selects
+// them, and the anchor-row forward that runs them.
+//
+// Pages: Fig. 4 caption (in some heads a query frame's attention pattern
+// repeats from one spatial row to the next), Fig. 5(b) caption (such heads
+// compute attention for a few anchor rows per frame and hand the outputs to
+// the neighbouring rows), Fig. 6 and Fig. S13 captions (one similarity score
+// per map, heads above tau), Table S4 (anchors attend to all keys; 1 - k/30
+// of the query rows are skipped).
+//
+// Token layout: token n < seq_len sits at frame f, spatial row y, column x of
+// a (frames, rows, cols) grid with n = (f*rows + y)*cols + x.  The rows of a
+// frame form k contiguous groups [floor(g*rows/k), floor((g+1)*rows/k)),
+// anchored at their lower middle row.
+//
+// Similarity (spatial_sim_kernel): for each token with a row below it in the
+// same frame, the cosine of the two tokens' softmax rows,
+//     sum_j p_ij p_i'j / sqrt(sum_j p_ij^2 * sum_j p_i'j^2),  i' = i + cols,
+// with p = exp(s - lse) from the row log-sum-exp pass of the pooling code.
+// Both score tiles come from the matrix cores with the same lane layout, so
+// the products are lane-local.  Each workgroup adds its 128 cosines in a
+// fixed order in float64; a second kernel adds the workgroup partials in
+// order, so the score is bitwise reproducible.
+//
+// Anchor forward: gather the anchor queries of the listed heads into a
+// [B, H, Lq, d] buffer (Lq = anchor count rounded up to 128, the rest
+// zero), run the persistent dense kernel over them in its split-query mode
+// (keys: the full K and V^T), and write every token's output from its
+// anchor's row.
+#include "tiles.h"
+#include "launch.h"
+
+namespace calibatt {
+
+namespace {
+
+__device__ __forceinline__ int anchor_token(int m, int R, int C, int k) {
+  const int per_frame = k * C;
+  const int f = m / per_frame, rem = m - f * per_frame;
+  const int g = rem / C, x = rem - g * C;
+  const int lo = (g * R) / k, hi = ((g + 1) * R) / k;
+  return (f * R + (lo + hi - 1) / 2) * C + x;
+}
+
+// Index of the anchor query whose output token n takes (n < seq_len).
+__device__ __forceinline__ int source_anchor(int n, int R, int C, int k) {
+  const int RC = R * C;
+  const int f = n / RC, rem = n - f * RC;
+  const int y = rem / C, x = rem - y * C;
+  const int g = ((y + 1) * k - 1) / R;   // the group g with lo_g <= y < lo_{g+1}
+  return (f * k + g) * C + x;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void anchor_gather_kernel(const T* __restrict__ Q, T* __restrict__ Qa,
+                                                            HeadList hl, int B, int H, int L, int Lq, int La,
+                                                            int R, int C, int k) {
+  constexpr int U = D * (int)sizeof(T) / 16;   // 16-byte units per row
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long total = (long long)B * hl.n * Lq * U;
+  if (t >= total) return;
+  const int u = (int)(t % U);
+  const long long row = t / U;
+  const int m = (int)(row % Lq);
+  const long long rest = row / Lq;
+  const int slot = (int)(rest % hl.n), b = (int)(rest / hl.n);
+  const size_t bh = (size_t)b * H + hl.h[slot];
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (m < La) {
+    const int tok = anchor_token(m, R, C, k);
+    v = reinterpret_cast<const u32x4*>(Q + (bh * L + tok) * D)[u];
+  }
+  reinterpret_cast<u32x4*>(Qa + (bh * Lq + m) * D)[u] = v;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void anchor_broadcast_kernel(const T* __restrict__ Oa, T* __restrict__ O,
+                                                               HeadList hl, int B, int H, int L, int Lq,
+                                                               int seq_len, int R, int C, int k) {
+  constexpr int U = D * (int)sizeof(T) / 16;
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long total = (long long)B * hl.n * L * U;
+  if (t >= total) return;
+  const int u = (int)(t % U);
+  const long long row = t / U;
+  const int n = (int)(row % L);
+  const long long rest = row / L;
+  const int slot = (int)(rest % hl.n), b = (int)(rest / hl.n);
+  const size_t bh = (size_t)b * H + hl.h[slot];
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (n < seq_len) v = reinterpret_cast<const u32x4*>(Oa + (bh * Lq + source_anchor(n, R, C, k)) * D)[u];
+  reinterpret_cast<u32x4*>(O + (bh * L + n) * D)[u] = v;
+}
+
+// Work order for the anchor rows: listed head i goes to partition i % 8, its
+// rows in order; the partition offsets follow the H*nqb row slots.
+__global__ __launch_bounds__(256) void anchor_order_kernel(HeadList hl, int H, int nqb, int32_t* __restrict__ order) {
+  const int rows = H * nqb;
+  auto part_heads = [&](int p) { return p < hl.n ? (hl.n - p + kParts - 1) / kParts : 0; };
+  for (int i = threadIdx.x; i < hl.n * nqb; i += 256) {
+    const int slot = i / nqb, qb = i - slot * nqb;
+    const int p = slot % kParts, j = slot / kParts;
+    int off = 0;
+    for (int q = 0; q < p; ++q) off += part_heads(q) * nqb;
+    order[off + j * nqb + qb] = hl.h[slot] * nqb + qb;
+  }
+  if (threadIdx.x == 0) {
+    int off = 0;
+    for (int p = 0; p <= kParts; ++p) {
+      order[rows + p] = off;
+      if (p < kParts) off += part_heads(p) * nqb;
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void spatial_sim_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                                                          const float* __restrict__ lse,
+                                                          double* __restrict__ part, int L, int seq_len,
+                                                          int nkb_valid, int C, int RC, float c2) {
+  constexpr int BLK = 128, NT = 256, DS = D / 16, CH = D / 8;
+  __shared__ u32x4 ldsK[BLK * D / 8];
+  __shared__ double wsum[4];
+  const int nqb = L / BLK;
+  const int item = blockIdx.x;
+  const int bh = item / nqb, qt = item - bh * nqb;
+  const size_t base = (size_t)bh * L * D;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 5, c = lane & 31;
+  const int q = qt * BLK + 32 * w + c;
+  // a token counts when the row below it lies in the same frame
+  const bool prim = q < seq_len && (q % RC) < RC - C;
+  const int q2 = prim ? q + C : q;
+  const float l1 = prim ? lse[(size_t)bh * L + q] * kLog2e : 0.f;
+  const float l2 = prim ? lse[(size_t)bh * L + q2] * kLog2e : 0.f;
+
+  bf16x8 qa[DS], qb2[DS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) {
+    qa[s] = *reinterpret_cast<const bf16x8*>(Q + base + (size_t)q * D + 16 * s + 8 * g);
+    qb2[s] = *reinterpret_cast<const bf16x8*>(Q + base + (size_t)q2 * D + 16 * s + 8 * g);
+  }
+  const int prow = qk_row_perm(c);
+  float dot = 0.f, n1 = 0.f, n2 = 0.f;
+  for (int kb = 0; kb < nkb_valid; ++kb) {
+    __syncthreads();
+    load_k_tile<D, BLK, NT>(K + base + (size_t)kb * BLK * D, ldsK);
+    __syncthreads();
+    const int k0 = kb * BLK;
+#pragma unroll
+    for (int mt = 0; mt < BLK / 32; ++mt) {
+      f32x16 s1 = {}, s2 = {};
+      const int row = 32 * mt + prow;
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, ldsK[chunk_index<CH>(row, 2 * s + g)]);
+        s1 = mfma_bf16(a, qa[s], s1);
+        s2 = mfma_bf16(a, qb2[s], s2);
+      }
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const bool kv = k0 + 32 * mt + slice_key(rr, g) < seq_len;
+        const float p1 = kv ? fast_exp2(fmaf(s1[rr], c2, -l1)) : 0.f;
+        const float p2 = kv ? fast_exp2(fmaf(s2[rr], c2, -l2)) : 0.f;
+        dot = fmaf(p1, p2, dot);
+        n1 = fmaf(p1, p1, n1);
+        n2 = fmaf(p2, p2, n2);
+      }
+    }
+  }
+  dot = pair_sum(dot);
+  n1 = pair_sum(n1);
+  n2 = pair_sum(n2);
+  double cs = (prim && g == 0) ? (double)(dot / sqrtf(n1 * n2)) : 0.0;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) cs += __shfl_xor(cs, off);
+  if (lane == 0) wsum[w] = cs;
+  __syncthreads();
+  if (threadIdx.x == 0) part[item] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+}
+
+__global__ __launch_bounds__(64) void spatial_sim_reduce_kernel(const double* __restrict__ part, int BH, int nqb,
+                                                                double inv_pairs, double* __restrict__ sim) {
+  const int bh = blockIdx.x * 64 + threadIdx.x;
+  if (bh >= BH) return;
+  double s = 0.0;
+  for (int i = 0; i < nqb; ++i) s += part[(size_t)bh * nqb + i];
+  sim[bh] = s * inv_pairs;
+}
+
+}  // namespace
+
+hipError_t launch_spatial_similarity(const SimArgs& a, hipStream_t st) {
+  MassArgs m;
+  m.Q = a.Q;
+  m.K = a.K;
+  m.lse = a.lse;
+  m.mass = nullptr;
+  m.B = a.B;
+  m.H = a.H;
+  m.L = a.L;
+  m.seq_len = a.seq_len;
+  m.d = a.d;
+  m.block = 128;
+  m.nkb_valid = (a.seq_len + 127) / 128;
+  m.scale = a.scale;
+  hipError_t e = launch_row_lse(m, st);
+  if (e != hipSuccess) return e;
+  const int nqb = a.L / 128;
+  const int items = a.B * a.H * nqb;
+  const float c2 = a.scale * kLog2e;
+  if (a.d == 128)
+    hipLaunchKernelGGL((spatial_sim_kernel<128>), dim3(items), dim3(256), 0, st, (const bf16*)a.Q,
+                       (const bf16*)a.K, a.lse, a.part, a.L, a.seq_len, m.nkb_valid, a.cols, a.rows * a.cols, c2);
+  else
+    hipLaunchKernelGGL((spatial_sim_kernel<64>), dim3(items), dim3(256), 0, st, (const bf16*)a.Q,
+                       (const bf16*)a.K, a.lse, a.part, a.L, a.seq_len, m.nkb_valid, a.cols, a.rows * a.cols, c2);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const double pairs = (double)a.frames * (a.rows - 1) * a.cols;
+  hipLaunchKernelGGL(spatial_sim_reduce_kernel, dim3((a.B * a.H + 63) / 64), dim3(64), 0, st,
+                     (const double*)a.part, a.B * a.H, nqb, 1.0 / pairs, a.sim);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t anchor_copy(const AnchorArgs& a, bool gather, hipStream_t st) {
+  constexpr int U = D * (int)sizeof(T) / 16;
+  const long long rows = (long long)a.B * a.heads.n * (gather ? a.Lq : a.L);
+  const long long threads = rows * U;
+  const unsigned grid = (unsigned)((threads + 255) / 256);
+  if (gather)
+    hipLaunchKernelGGL((anchor_gather_kernel<T, D>), dim3(grid), dim3(256), 0, st, (const T*)a.Q, (T*)a.Qa, a.heads,
+                       a.B, a.H, a.L, a.Lq, a.La, a.rows, a.cols, a.k);
+  else
+    hipLaunchKernelGGL((anchor_broadcast_kernel<T, D>), dim3(grid), dim3(256), 0, st, (const T*)a.Oa, (T*)a.O,
+                       a.heads, a.B, a.H, a.L, a.Lq, a.seq_len, a.rows, a.cols, a.k);
+  return hipGetLastError();
+}
+
+static hipError_t anchor_copy_any(const AnchorArgs& a, bool gather, hipStream_t st) {
+  return a.d == 128 ? anchor_copy<bf16, 128>(a, gather, st) : anchor_copy<bf16, 64>(a, gather, st);
+}
+
+hipError_t launch_anchor_fwd(const AnchorArgs& a, hipStream_t st) {
+  if (a.heads.n == 0) return hipSuccess;
+  hipError_t e = anchor_copy_any(a, true, st);
+  if (e != hipSuccess) return e;
+  const int nqb = a.Lq / 128;
+  hipLaunchKernelGGL(anchor_order_kernel, dim3(1), dim3(256), 0, st, a.heads, a.H, nqb, a.order);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  AttnArgs t;
+  t.Q = a.Qa;
+  t.K = a.K;
+  t.Vt = a.Vt;
+  t.O = a.Oa;
+  t.row_ptr = nullptr;
+  t.col_idx = nullptr;
+  t.work_order = a.order;
+  t.queue = a.queue;
+  t.B = a.B;
+  t.H = a.H;
+  t.L = a.L;
+  t.seq_len = a.seq_len;
+  t.d = a.d;
+  t.block = 128;
+  t.nkb_valid = (a.seq_len + 127) / 128;
+  t.scale = a.scale;
+  t.dtype_f32 = false;
+  t.num_cu = a.num_cu;
+  t.Lq = a.Lq;
+  t.q_valid = a.La;
+  e = launch_anchor_attention(t, st);
+  if (e != hipSuccess) return e;
+  return anchor_copy_any(a, false, st);
+}
+
+}  // namespace calibatt

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define CALIBATT_VERSION 210 /* major * 100 + minor */
+#define CALIBATT_VERSION 220 /* major * 100 + minor */
 
 typedef enum {
   CALIBATT_OK = 0,
@@ -323,6 +323,79 @@ calibatt_status calibatt_decode_skip_lists(const int32_t* counts, const int32_t*
 
 /* Workspace bytes the skip-list encode and decode need (0 on bad sizes). */
 size_t calibatt_skip_ws_bytes(int T, int H, int nqb);
+
+/*
+ * Spatial-repetition score per attention map (calibration).  Pages: Fig. 4
+ * caption (a query frame's attention repeats from one spatial row to the
+ * next), Fig. 6 caption (one spatial-similarity score per map), Fig. S13
+ * caption (heads above tau = 0.87).  The pages give no formula; this is the
+ * mean, over every token i = (f, y, x) with y < grid_rows - 1 and its
+ * neighbour one spatial row down, i' = i + grid_cols, of the cosine of their
+ * softmax rows over the valid keys:
+ *     sim[b,h] = mean_i  sum_j p_ij p_i'j / sqrt(sum_j p_ij^2 sum_j p_i'j^2)
+ * Tokens are n = (f*grid_rows + y)*grid_cols + x on a (frames, grid_rows,
+ * grid_cols) grid that covers exactly seq_len tokens.
+ *   Q, K     [B, H, L, d] bf16 (device); L a multiple of 128, d in {64, 128}.
+ *   sim      [B, H] float64 output (device).
+ *   ws       calibatt_similarity_ws_bytes(B, H, L) bytes (device), 256-byte
+ *            aligned: per-query log-sum-exp and per-tile partial sums.
+ * Softmax rows are formed in float32 from the bf16 matrix-core scores; each
+ * workgroup adds its cosines in a fixed order in float64 and the partials
+ * are added in tile order, so the result is bitwise reproducible.
+ * grid_rows < 2 or a grid that does not cover seq_len: CALIBATT_ERR_SHAPE.
+ */
+calibatt_status calibatt_spatial_similarity(const void* Q, const void* K, int B, int H, int L, int seq_len,
+                                            int d, calibatt_dtype dt, float scale, int frames, int grid_rows,
+                                            int grid_cols, double* sim, void* ws, size_t ws_bytes, void* stream);
+size_t calibatt_similarity_ws_bytes(int B, int H, int L);
+
+/*
+ * Heads flagged as spatially repetitive (Fig. 5(a) caption: a dictionary of
+ * such heads; Fig. S13 caption: score above tau).  The score of head h is the
+ * mean over the P calibration prompts, added in prompt order in float64; h is
+ * selected when that mean is strictly greater than tau.
+ *   sim      [P, H] float64 (device), e.g. P calls of
+ *            calibatt_spatial_similarity with B = 1.
+ *   heads    [H] int32 output (host): the selected heads, ascending.
+ *   n_heads  int32 output (host): how many.
+ * Synchronizes `stream` (the scores are read back to the host).
+ */
+calibatt_status calibatt_select_repetitive_heads(const double* sim, int P, int H, double tau, int32_t* heads,
+                                                 int32_t* n_heads, void* stream);
+
+/*
+ * Anchor-row attention for spatially repetitive heads (inference).  Pages:
+ * Fig. 5(b) caption (attention only for anchor rows of each frame, outputs
+ * handed to the neighbouring rows), Table S4 (anchors attend to all keys;
+ * 1 - k/30 of the query rows skipped at 30 rows per frame).  The rows of a
+ * frame form k_anchor contiguous groups [floor(g*R/k), floor((g+1)*R/k))
+ * (R = grid_rows), each anchored at its lower middle row
+ * floor((lo + hi - 1)/2).  For each listed head h and token n = (f, y, x) <
+ * seq_len, with a = the anchor row of y's group:
+ *     O[b,h,n,:] = attention of query (f, a, x) over all valid keys
+ * and O[b,h,n,:] = 0 for n >= seq_len.  Heads not listed are not written.
+ *   Q, K, V, O  as in calibatt_dense_attn_fwd; bf16 only, block 128.
+ *   heads       [n_heads] int32 (host): distinct heads in [0, H); at most 256.
+ *   frames, grid_rows, grid_cols  the token grid (frames*grid_rows*grid_cols
+ *               = seq_len); 1 <= k_anchor <= grid_rows.
+ *   queue_ws    int32 workspace of >= 128 entries (device), required.
+ *   v_layout, vt_ws  as in calibatt_sparse_attn_fwd (a [B, H, L, d] V is
+ *               transposed for all H heads).
+ *   ws          calibatt_anchor_ws_bytes(B, H, frames, grid_cols, k_anchor,
+ *               d) bytes (device), 256-byte aligned: the gathered anchor
+ *               queries and their outputs as [B, H, Lq, d] (Lq = frames *
+ *               k_anchor * grid_cols rounded up to 128), and the row order.
+ * The anchor queries run through the persistent dense kernel in a
+ * split-query mode (bf16 matrix cores with float32 accumulation, float32
+ * softmax, probabilities and O rounded to bf16).
+ */
+calibatt_status calibatt_anchor_attn_fwd(const void* Q, const void* K, const void* V, void* O,
+                                         const int32_t* heads, int n_heads, int frames, int grid_rows,
+                                         int grid_cols, int k_anchor, float scale, int B, int H, int L,
+                                         int seq_len, int d, calibatt_dtype dt, int32_t* queue_ws,
+                                         calibatt_vlayout v_layout, void* vt_ws, void* ws, size_t ws_bytes,
+                                         void* stream);
+size_t calibatt_anchor_ws_bytes(int B, int H, int frames, int grid_cols, int k_anchor, int d);
 
 /*
  * Work order for calibatt_sparse_attn_fwd.  The pages do not describe a

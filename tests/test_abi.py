@@ -18,7 +18,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _lib.header_symbols()
-    assert len(names) == 17
+    assert len(names) == 22
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     for n in names:
@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert cal.calibatt_version() == 210
+    assert cal.calibatt_version() == 220
     for code, name in _lib.STATUS.items():
         assert cal.calibatt_status_string(code) != "unknown status"
     assert cal.calibatt_status_string(99) == "unknown status"
@@ -225,3 +225,58 @@ def test_validate_csr(lib):
         with pytest.raises(cal.CalibattError) as e:
             cal.calibatt_validate_csr(rp, ci, 3, 8)
         assert e.value.status == 5 or e.value.status == 1
+
+
+def test_repetition_entry_points_reject(lib):
+    ws = lib.calibatt_similarity_ws_bytes(1, 40, 32768)
+    assert ws == 40 * 32768 * 4 + 40 * 256 * 8
+    assert lib.calibatt_similarity_ws_bytes(1, 1, 100) == 0
+
+    def sim(**kw):
+        a = dict(Q=P16, K=P32, B=1, H=40, L=32768, S=32760, d=128, dt=0, scale=0.1, F=21, R=30, C=52,
+                 sim=V(1 << 20), ws=V(1 << 30), ws_bytes=ws, stream=None)
+        a.update(kw)
+        return lib.calibatt_spatial_similarity(*a.values())
+    assert sim(Q=None) == 1
+    assert sim(sim=V(4)) == 4
+    assert sim(ws=V((1 << 30) + 16)) == 4
+    assert sim(dt=1) == 7
+    assert sim(F=20) == 2                    # grid does not cover seq_len
+    assert sim(R=1, C=52 * 30) == 2          # one row per frame: no pairs
+    assert sim(ws_bytes=ws - 1) == 6
+    assert sim(L=32760) == 2
+
+    n = ctypes.c_int32(0)
+    heads = np.zeros(4, dtype=np.int32)
+    hp = heads.ctypes.data_as(ctypes.c_void_p)
+    assert lib.calibatt_select_repetitive_heads(None, 2, 4, 0.87, hp, ctypes.byref(n), None) == 1
+    assert lib.calibatt_select_repetitive_heads(P16, 0, 4, 0.87, hp, ctypes.byref(n), None) == 2
+    assert lib.calibatt_select_repetitive_heads(V(12), 2, 4, 0.87, hp, ctypes.byref(n), None) == 4
+
+    aws = lib.calibatt_anchor_ws_bytes(1, 40, 21, 52, 5, 128)
+    lq = (21 * 5 * 52 + 127) // 128 * 128
+    assert aws == 2 * 40 * lq * 128 * 2 + (40 * lq // 128 + 9) * 4
+    assert lib.calibatt_anchor_ws_bytes(1, 40, 21, 52, 0, 128) == 0
+    hl = np.array([3, 7], dtype=np.int32)
+
+    def anchor(heads_arr=hl, **kw):
+        a = dict(Q=P16, K=P32, V=P48, O=P64, heads=heads_arr.ctypes.data_as(ctypes.c_void_p), n=len(heads_arr),
+                 F=21, R=30, C=52, k=5, scale=0.1, B=1, H=40, L=32768, S=32760, d=128, dt=0, queue=V(1 << 20),
+                 layout=1, vt=None, ws=V(1 << 30), ws_bytes=aws, stream=None)
+        a.update(kw)
+        return lib.calibatt_anchor_attn_fwd(*a.values())
+    assert anchor(Q=None) == 1
+    assert anchor(queue=None) == 1
+    assert anchor(ws=V((1 << 30) + 64)) == 4
+    assert anchor(dt=1) == 7
+    assert anchor(k=0) == 2
+    assert anchor(k=31) == 2
+    assert anchor(C=51) == 2
+    assert anchor(n=41) == 2
+    assert anchor(np.array([3, 40], dtype=np.int32)) == 2
+    assert anchor(np.array([-1], dtype=np.int32)) == 2
+    assert anchor(np.array([5, 5], dtype=np.int32)) == 2
+    assert anchor(ws_bytes=aws - 1) == 6
+    assert anchor(heads=None) == 1
+    assert anchor(layout=0) == 1
+    assert cal.calibatt_last_error() != ""

@@ -1,0 +1,210 @@
+"""GPU parity: spatial-repetition score, head selection and anchor-row
+attention vs the float64 oracle.
+
+Tolerances: the score is a mean of cosines in [0, 1] formed from float32
+softmax rows of bf16 matrix-core scores; |sim_gpu - sim_oracle| <= 1e-4.
+Head selection is bit-exact given the same float64 scores.  Anchor outputs:
+max |O_gpu - O_oracle| <= 2e-2 (bf16, as for the attention forward); the
+broadcast itself is a copy, so every token equals its anchor's output bit
+for bit."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import block_sparse_attention_calibatt_amd as cal
+from tests.gpu_util import say, to_dev, small_cfg, inputs, err
+
+pytestmark = pytest.mark.gpu
+SIM_TOL = 1e-4
+TOL = 2e-2
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _grid_cfg(grid, d, H, seed, pad_to=128):
+    F, R, C = grid
+    S = F * R * C
+    L = -(-S // pad_to) * pad_to
+    return small_cfg(B=1, H=H, L=L, S=S, d=d, block=128, seed=seed, grid=grid)
+
+
+def _sim_gpu(q, k, cfg):
+    Q, K = to_dev(q, torch.bfloat16), to_dev(k, torch.bfloat16)
+    sim = cal.calibatt_spatial_similarity(Q, K, cfg.scale, cfg.grid, cfg.S)
+    torch.cuda.synchronize()
+    return sim.cpu().numpy()
+
+
+@pytest.mark.parametrize("grid,d,H,repeat", [
+    ((3, 4, 20), 64, 3, ()),
+    ((2, 5, 13), 128, 2, (1,)),
+    ((2, 30, 52), 128, 3, (1,)),
+])
+def test_similarity_small(gpu, grid, d, H, repeat):
+    cfg = _grid_cfg(grid, d, H, seed=40 + d)
+    say(f"case: spatial similarity grid={grid} d={d} H={H} L={cfg.L} repeated heads={repeat}")
+    q, k, _ = inputs(cfg)
+    synth.repeat_rows(q, grid, cfg.S, repeat, 0.0)
+    if H > 2:
+        synth.repeat_rows(q, grid, cfg.S, [2], 0.5)
+    got = _sim_gpu(q, k, cfg)
+    ref = oracle.spatial_similarity(q, k, cfg.scale, cfg.S, grid)
+    e = float(np.max(np.abs(got - ref)))
+    say(f"  sims gpu {np.round(got, 5).tolist()} oracle {np.round(ref, 5).tolist()} max err {e:.2e}")
+    assert e <= SIM_TOL
+    for h in repeat:
+        assert abs(got[0, h] - 1.0) <= 1e-5, "repeated rows score 1"
+    # bitwise reproducible
+    assert np.array_equal(_sim_gpu(q, k, cfg), got)
+
+
+def test_similarity_wan_full_size(gpu):
+    """Wan shape, all 40 heads: repeated heads score 1, a partly repeated one
+    scores above every untouched head."""
+    cfg = synth.get_config("wan")
+    say("case: spatial similarity, Wan full size")
+    q, k, _ = inputs(cfg)
+    synth.repeat_rows(q, cfg.grid, cfg.S, [3, 17], 0.0)
+    synth.repeat_rows(q, cfg.grid, cfg.S, [29], 0.3)
+    got = _sim_gpu(q, k, cfg)
+    say(f"  sims {np.round(got[0], 4).tolist()}")
+    assert np.all(np.isfinite(got)) and np.all(got > 0) and np.all(got <= 1 + 1e-6)
+    assert abs(got[0, 3] - 1.0) <= 1e-5 and abs(got[0, 17] - 1.0) <= 1e-5
+    others = [h for h in range(cfg.H) if h not in (3, 17, 29)]
+    assert got[0, 29] > max(got[0, h] for h in others)
+
+
+def test_select_golden(gpu):
+    g = json.load(open(os.path.join(GOLDEN, "spatial_repetition.json")))["selection"]
+    sim = torch.tensor(g["sim"], dtype=torch.float64, device="cuda:0")
+    assert cal.calibatt_select_repetitive_heads(sim, g["tau"]) == g["heads_expected"]
+
+
+def test_select_matches_oracle(gpu):
+    grid = (2, 5, 13)
+    cfg = _grid_cfg(grid, 128, 6, seed=60)
+    sims = []
+    for p in range(3):
+        q, k, _ = inputs(cfg, seed=600 + p)
+        synth.repeat_rows(q, grid, cfg.S, [1, 4], 0.1 * (p + 1))
+        sims.append(_sim_gpu(q, k, cfg)[0])
+    sims = np.array(sims)
+    dev = torch.from_numpy(sims).to("cuda:0")
+    means = np.zeros(cfg.H)
+    for p in range(3):
+        means = means + sims[p]
+    means = means / 3
+    say(f"case: head selection, prompt means {np.round(means, 4).tolist()}")
+    for tau in [0.0, float(np.median(means)), float(means[1]), float(means.max()), 0.87, 1.0]:
+        got = cal.calibatt_select_repetitive_heads(dev, tau)
+        want = [int(h) for h in oracle.select_repetitive_heads(sims, tau)]
+        assert got == want, f"tau={tau}"
+    assert 1 not in cal.calibatt_select_repetitive_heads(dev, float(means[1])), "equal to tau is not above it"
+
+
+def _anchor_gpu(q, k, v, cfg, heads, k_anchor, v_transposed=False, sentinel=7.0):
+    Q, K, V = (to_dev(x, torch.bfloat16) for x in (q, k, v))
+    if v_transposed:
+        V = cal.calibatt_transpose_v(V, seq_len=cfg.S)
+    O = torch.full_like(Q, sentinel)
+    cal.calibatt_anchor_attn_fwd(Q, K, V, O, heads, cfg.grid, k_anchor, cfg.scale, cfg.S,
+                                 v_transposed=v_transposed)
+    torch.cuda.synchronize()
+    return O
+
+
+def _source_tokens(cfg, k_anchor):
+    F, R, C = cfg.grid
+    arow = oracle.anchor_of_row(R, k_anchor)
+    n = np.arange(cfg.S)
+    return (n // (R * C) * R + arow[(n // C) % R]) * C + n % C
+
+
+def _check_untouched(O, cfg, heads, sentinel=7.0):
+    other = [h for h in range(cfg.H) if h not in heads]
+    if other:
+        assert torch.all(O[:, other].float() == sentinel), "unlisted heads must not be written"
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("k_anchor", [1, 2, 5])
+def test_anchor_small(gpu, d, k_anchor):
+    grid = (3, 5, 20)
+    cfg = _grid_cfg(grid, d, 4, seed=70 + d)
+    heads = [3, 1]
+    say(f"case: anchor attention grid={grid} d={d} k={k_anchor} heads={heads} L={cfg.L}")
+    q, k, v = inputs(cfg)
+    ref = oracle.anchor_attention(q, k, v, cfg.scale, cfg.S, grid, k_anchor, heads)
+    for vt in (False, True):
+        O = _anchor_gpu(q, k, v, cfg, heads, k_anchor, v_transposed=vt)
+        e = err(O[:, heads], ref)
+        say(f"  v_transposed={vt} max err {e:.3e}")
+        assert e <= TOL
+        _check_untouched(O, cfg, heads)
+        assert torch.count_nonzero(O[:, heads, cfg.S:].float()).item() == 0
+        src = torch.from_numpy(_source_tokens(cfg, k_anchor)).to("cuda:0")
+        assert torch.equal(O[:, heads, :cfg.S], O[:, heads][:, :, src]), "broadcast is a copy"
+
+
+def test_anchor_every_row_matches_dense(gpu):
+    """k = rows: every row is its own anchor, so the result is dense attention."""
+    grid = (2, 6, 30)
+    cfg = _grid_cfg(grid, 128, 3, seed=80)
+    say(f"case: anchor attention with k = rows, grid={grid}")
+    q, k, v = inputs(cfg)
+    O = _anchor_gpu(q, k, v, cfg, [0, 1, 2], grid[1])
+    ref = oracle.dense_attention(q, k, v, cfg.scale, cfg.S)
+    e = err(O, ref)
+    Od = torch.empty_like(O)
+    Q, K, V = (to_dev(x, torch.bfloat16) for x in (q, k, v))
+    cal.calibatt_dense_attn_fwd(Q, K, V, Od, 128, cfg.scale, cfg.S, cal.new_queue("cuda:0"))
+    torch.cuda.synchronize()
+    say(f"  max err vs oracle {e:.3e}, vs dense kernel {float((O.float() - Od.float()).abs().max()):.3e}")
+    assert e <= TOL
+    assert float((O.float() - Od.float()).abs().max()) <= TOL
+
+
+def test_anchor_no_heads(gpu):
+    grid = (2, 5, 13)
+    cfg = _grid_cfg(grid, 128, 2, seed=81)
+    q, k, v = inputs(cfg)
+    O = _anchor_gpu(q, k, v, cfg, [], 2)
+    assert torch.all(O.float() == 7.0)
+
+
+def test_anchor_wan_full_size(gpu):
+    """Wan shape, 4 listed heads, k = 5 (Table S4's 83.3% row sparsity): every
+    output of those heads against the oracle; heads 13 and 27 have queries
+    that repeat down the rows, where the anchors reproduce dense attention."""
+    cfg = synth.get_config("wan")
+    heads, k_anchor = [0, 13, 27, 39], 5
+    say(f"case: anchor attention, Wan full size, heads {heads}, k={k_anchor}")
+    q, k, v = inputs(cfg)
+    synth.repeat_rows(q, cfg.grid, cfg.S, [13, 27], 0.0)
+    O = _anchor_gpu(q, k, v, cfg, heads, k_anchor)
+    _check_untouched(O, cfg, heads)
+    src = torch.from_numpy(_source_tokens(cfg, k_anchor)).to("cuda:0")
+    assert torch.equal(O[:, heads, :cfg.S], O[:, heads][:, :, src]), "broadcast is a copy"
+    assert torch.count_nonzero(O[:, heads, cfg.S:].float()).item() == 0
+    worst = 0.0
+    for i, h in enumerate(heads):
+        ref = oracle.anchor_attention(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], cfg.scale, cfg.S, cfg.grid,
+                                      k_anchor, [0])
+        e = err(O[:, h:h + 1], ref)
+        worst = max(worst, e)
+        if h in (13, 27):
+            rp = (np.arange(cfg.nqb + 1) * cfg.nkb_valid).astype(np.int32)
+            ci = np.tile(np.arange(cfg.nkb_valid), cfg.nqb).astype(np.int32)
+            items = [(0, 0, 0), (0, 0, 100), (0, 0, 255)]
+            dense_rows = oracle.sparse_attention_rows(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], rp, ci,
+                                                      cfg.block, cfg.scale, cfg.S, items)
+            for (_, _, qb), rr in zip(items, dense_rows):
+                g = O[0, h, qb * 128:(qb + 1) * 128].float().cpu().numpy()
+                assert float(np.max(np.abs(g - rr))) <= TOL, "repeated rows: anchors give dense attention"
+    say(f"  max err over {len(heads)} heads {worst:.3e}")
+    assert worst <= TOL
