@@ -129,6 +129,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-calib", action="store_true")
+    ap.add_argument("--no-anchor", action="store_true")
     ap.add_argument("--no-peak-probe", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB")
     args = ap.parse_args()
@@ -209,6 +210,39 @@ def main():
         extra["dense_tflops"] = round(dense_flops / (dense_ms * 1e-3) / 1e12, 2)
         extra["speedup_vs_dense"] = round(speedup(dense_ms, ms), 3)
 
+    if not args.no_anchor and cfg.grid is not None:
+        # anchor rows (spatial-repetition heads) for every head, V^T given as in
+        # the step: the workload of the pages' anchor-row table
+        F, R, C = cfg.grid
+        heads = list(range(cfg.H))
+        nkv = cfg.nkb_valid
+        rows_out = {}
+        for ka in (15, 10, 5, 4, 3):
+            aws = torch.empty(cal.calibatt_anchor_ws_bytes(cfg.B, cfg.H, F, C, ka, cfg.d), dtype=torch.uint8,
+                              device=dev)
+            for _ in range(2):
+                cal.calibatt_anchor_attn_fwd(Q, K, VT, O, heads, cfg.grid, ka, cfg.scale, cfg.S, qws,
+                                             v_transposed=True, ws=aws)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            na = 5
+            e0.record(stream)
+            for _ in range(na):
+                cal.calibatt_anchor_attn_fwd(Q, K, VT, O, heads, cfg.grid, ka, cfg.scale, cfg.S, qws,
+                                             v_transposed=True, ws=aws)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            a_ms = e0.elapsed_time(e1) / na
+            lq = -(-(F * ka * C) // 128) * 128
+            a_flops = tile_flops(128, cfg.d) * cfg.B * cfg.H * (lq // 128) * nkv
+            rows_out[f"k{ka}"] = {
+                "ms": round(a_ms, 4),
+                "row_sparsity": round(1 - ka / R, 4),
+                "speedup_vs_dense": round(speedup(extra["dense_ms"], a_ms), 2) if "dense_ms" in extra else None,
+                "anchor_tile_tflops": round(a_flops / (a_ms * 1e-3) / 1e12, 1),
+            }
+            del aws
+        extra["anchor_rows_all_heads"] = rows_out
+
     if not args.no_calib:
         # offline calibration steps on one prompt at this shape, then compile of 8 prompts' masses
         lse = torch.empty(cfg.B * cfg.H * cfg.L, dtype=torch.float32, device=dev)
@@ -268,6 +302,26 @@ def main():
                                   "kept_blocks": kept, "kept_before": int(tbank.nnz.sum())}
         extra["calib"]["skip_lists_24_sets"] = sk
 
+    if not args.no_calib and cfg.grid is not None:
+        # spatial-similarity score of every head of one prompt
+        sws = torch.empty(cal.calibatt_similarity_ws_bytes(cfg.B, cfg.H, cfg.L), dtype=torch.uint8, device=dev)
+        sim = cal.calibatt_spatial_similarity(Q, K, cfg.scale, cfg.grid, cfg.S, ws=sws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(3):
+            cal.calibatt_spatial_similarity(Q, K, cfg.scale, cfg.grid, cfg.S, sim=sim, ws=sws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        sim_ms = e0.elapsed_time(e1) / 3
+        # three score products per tile: the log-sum-exp pass and the two rows of each pair
+        sim_flops = 3 * tile_flops(128, cfg.d) / 2 * cfg.B * cfg.H * cfg.nqb * cfg.nkb_valid
+        extra.setdefault("calib", {})["spatial_similarity"] = {
+            "ms_per_prompt": round(sim_ms, 3),
+            "qk_tflops": round(sim_flops / (sim_ms * 1e-3) / 1e12, 1),
+            "max_score": round(float(sim.max()), 4),
+            "mean_score": round(float(sim.mean()), 4),
+        }
+
     # the probe runs in its own process, after the timed work
     peak_probe = None if args.no_peak_probe else mfma_rate()
 
@@ -305,7 +359,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic_from_profile(flops),
-            "kernel": "attn_fwd_pp_kernel<128,false>",
+            "kernel": "attn_fwd_pp_kernel<128,false,false>",
             "avg_launch_ms": round(float(np.mean(launch_ms)), 4),
             "measured_mfma_rate": peak_probe,
             "frac_of_random_operand_rate": (round(achieved / peak_probe["random_operands_tflops"], 4)
