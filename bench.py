@@ -56,14 +56,15 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(launch_flops):
-    """HBM bytes per launch from the committed counter summary, if it matches the current kernel."""
+def traffic_from_profile(workload):
+    """HBM bytes per launch from the committed counter summary, if it covers this
+    workload and matches the current kernel source."""
     try:
         with open(COUNTERS) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
-    if c.get("kernel_source_hash") != kernel_source_hash():
+    if c.get("kernel_source_hash") != kernel_source_hash() or not c.get("workload", "").startswith(workload + ":"):
         return None
     return c.get("hbm_bytes_per_launch")
 
@@ -124,12 +125,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="wan", choices=["wan", "mochi", "imbalance"])
+    ap.add_argument("--config", default="wan", choices=["wan", "mochi", "imbalance", "calib"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-calib", action="store_true")
     ap.add_argument("--no-anchor", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-peak-probe", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB")
     args = ap.parse_args()
@@ -150,8 +152,41 @@ def main():
     cfg = synth.get_config(args.config)
     dev = torch.device("cuda:0")
     t_gen = time.perf_counter()
-    q, k, v = synth.gen_qkv(cfg)
-    sets = [synth.csr_for_config(cfg, t) for t in range(cfg.n_sets)]
+    calib_pipeline = None
+    if cfg.name == "calib":
+        # the mask comes from calibration on the GPU: pooled mass of each
+        # prompt, top ceil(keep_frac * nkb) blocks per row, agreement of
+        # ceil(rho * P) prompts, CSR; inference then runs on another input
+        P = len(cfg.prompt_seeds)
+        keep = -(-cfg.nkb * cfg.keep_frac.numerator // cfg.keep_frac.denominator)
+        agree = -(-P * cfg.rho.numerator // cfg.rho.denominator)
+        lse = torch.empty(cfg.B * cfg.H * cfg.L, dtype=torch.float32, device=dev)
+        masses = torch.empty((P, cfg.H, cfg.nqb, cfg.nkb), dtype=torch.float32, device=dev)
+        pool_ms = 0.0
+        for p, seed in enumerate(cfg.prompt_seeds):
+            qp, kp = synth.gen_qk(cfg, seed)
+            Qp, Kp = (torch.from_numpy(x).to(dev).to(torch.bfloat16).contiguous() for x in (qp, kp))
+            del qp, kp
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record()
+            cal.calibatt_block_mass(Qp, Kp, cfg.block, cfg.scale, lse, masses[p], cfg.S)
+            c1.record()
+            torch.cuda.synchronize()
+            pool_ms += c0.elapsed_time(c1)
+            del Qp, Kp
+        t_c = time.perf_counter()
+        crp, cci = cal.calibatt_compile_masks(masses, keep, agree, cfg.nkb_valid)
+        compile_ms = (time.perf_counter() - t_c) * 1e3
+        sets = [(crp.cpu().numpy(), cci.cpu().numpy())]
+        calib_pipeline = {"prompts": P, "keep_per_row": int(keep), "min_agree": int(agree),
+                          "block_mass_ms_all_prompts": round(pool_ms, 2),
+                          "compile_ms_incl_sync": round(compile_ms, 3),
+                          "kept_blocks": int(cci.numel())}
+        del masses, lse
+        q, k, v = synth.gen_qkv(cfg, cfg.infer_seed)
+    else:
+        q, k, v = synth.gen_qkv(cfg)
+        sets = [synth.csr_for_config(cfg, t) for t in range(cfg.n_sets)]
     Q, K, V = (torch.from_numpy(x).to(dev).to(torch.bfloat16).contiguous() for x in (q, k, v))
     O = torch.empty_like(Q)
     bank = cal.MaskBank(sets, cfg.H, cfg.nqb, cfg.nkb_valid, dev)
@@ -194,6 +229,54 @@ def main():
     density = float(np.mean(bank.nnz)) / (cfg.rows * cfg.nkb_valid)
 
     extra = {}
+    if calib_pipeline is not None:
+        extra["calibration_pipeline"] = calib_pipeline
+    # one cold launch: L2 and MALL flushed by a 512 MB scratch write first
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    scratch.fill_(1)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    rp0, ci0, wo0, _ = bank.lookup(0)
+    c0.record(stream)
+    cal.calibatt_sparse_attn_fwd(Q, K, VT, O, rp0, ci0, cfg.block, cfg.scale, cfg.S, wo0, qws, v_transposed=True)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    del scratch
+    extra["launch_ms_stats"] = {
+        "median": round(float(np.median(launch_ms)), 4),
+        "min": round(float(np.min(launch_ms)), 4),
+        "cold_after_512MB_write": round(c0.elapsed_time(c1), 4),
+    }
+
+    if not args.no_sweep and cfg.name == "wan":
+        # time vs kept density: the structured Wan masks (band + frame + position
+        # + random fill) at several targets, and uniform random masks below
+        # the structured floor
+        sweep = []
+        rng = np.random.default_rng(7)
+        cases = [("random", 0.05), ("random", 0.10), ("random", 0.20), ("structured", 0.30),
+                 ("structured", 0.50), ("structured", 0.70), ("structured", 0.90)]
+        for kind, target in cases:
+            m = (synth.random_csr(rng, cfg.H, cfg.nqb, cfg.nkb_valid, target) if kind == "random"
+                 else synth.wan_csr(cfg, 0, target=target))
+            sb = cal.MaskBank([m], cfg.H, cfg.nqb, cfg.nkb_valid, dev, validate=False)
+            srp, sci, swo, _ = sb.lookup(0)
+            for _ in range(2):
+                cal.calibatt_sparse_attn_fwd(Q, K, VT, O, srp, sci, cfg.block, cfg.scale, cfg.S, swo, qws,
+                                             v_transposed=True)
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            for _ in range(5):
+                cal.calibatt_sparse_attn_fwd(Q, K, VT, O, srp, sci, cfg.block, cfg.scale, cfg.S, swo, qws,
+                                             v_transposed=True)
+            s1.record(stream)
+            torch.cuda.synchronize()
+            t_ms = s0.elapsed_time(s1) / 5
+            nnz = int(sb.nnz[0])
+            sweep.append({"mask": kind, "density": round(nnz / (cfg.rows * cfg.nkb_valid), 4), "ms": round(t_ms, 4),
+                          "tflops": round(tile_flops(cfg.block, cfg.d) * cfg.B * nnz / (t_ms * 1e-3) / 1e12, 1)})
+            del sb
+        extra["time_vs_density"] = sweep
+
     if not args.no_dense:
         for _ in range(2):
             cal.calibatt_dense_attn_fwd(Q, K, V, O, cfg.block, cfg.scale, cfg.S, qws, vt_ws=VT)
@@ -358,7 +441,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic_from_profile(flops),
+            "traffic": traffic_from_profile(cfg.name),
             "kernel": "attn_fwd_pp_kernel<128,false,false>",
             "avg_launch_ms": round(float(np.mean(launch_ms)), 4),
             "measured_mfma_rate": peak_probe,
