@@ -125,7 +125,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="wan", choices=["wan", "mochi", "imbalance", "calib"])
+    ap.add_argument("--config", default="wan", choices=["wan", "wan720", "mochi", "imbalance", "calib"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")

@@ -1,4 +1,4 @@
-"""The five synthetic workloads.
+"""The synthetic workloads.
 
 * ``tiny``      - 1 head, d=64, 512 tokens (2 frames x 256), 64-token blocks,
                   float32, i.i.d. N(0,1) inputs; mask = the 8 diagonal blocks
@@ -6,6 +6,10 @@
 * ``wan``       - one Wan 2.1 14B attention call: B=1, 40 heads, d=128,
                   32,760 valid tokens (21 frames x 30 rows x 52 columns) padded
                   to 32,768, bfloat16, 128-token blocks; structured ~30% masks.
+* ``wan720``    - the Wan call at 720p: 75,600 valid tokens (21 frames x 45
+                  rows x 80 columns) padded to 75,648 (591 blocks), structured
+                  masks at 37.5% kept (the 62.5% sparsity of the pages' 720p
+                  rows, Table S3).
 * ``mochi``     - B=1, 24 heads, d=128, 16,384 tokens (16 x 32 x 32 grid),
                   bfloat16, 128-token blocks; band + random rows of exactly 26
                   kept blocks (20.3%).
@@ -68,6 +72,10 @@ CONFIGS = {
                   data_seed=10, mask_seed=11, grid=(21, 30, 52)),
     "mochi": Config("mochi", B=1, H=24, L=16384, S=16384, d=128, block=128, dtype="bf16",
                     data_seed=20, mask_seed=21, grid=(16, 32, 32)),
+    # 720p: 21 latent frames of 45 x 80 tokens (75,600, padded to 591 blocks),
+    # structured masks at the pages' 720p sparsity (62.5% skipped, Table S3)
+    "wan720": Config("wan720", B=1, H=40, L=75648, S=75600, d=128, block=128, dtype="bf16",
+                     data_seed=50, mask_seed=51, grid=(21, 45, 80)),
     "imbalance": Config("imbalance", B=1, H=40, L=32768, S=32760, d=128, block=128,
                         dtype="bf16", data_seed=30, mask_seed=1000, grid=(21, 30, 52),
                         n_sets=50),

@@ -208,6 +208,8 @@ def csr_for_config(cfg, set_index=0):
         return tiny_csr(cfg, set_index)
     if cfg.name == "wan":
         return wan_csr(cfg, set_index)
+    if cfg.name == "wan720":
+        return wan_csr(cfg, set_index, target=0.375)
     if cfg.name == "mochi":
         return mochi_csr(cfg, set_index)
     if cfg.name == "imbalance":

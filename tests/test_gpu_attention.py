@@ -240,6 +240,13 @@ def test_wan_full_size_sampled(gpu):
     _full_size_check(cfg, rp, ci, 11, 24)
 
 
+def test_wan720_full_size_sampled(gpu):
+    cfg = synth.get_config("wan720")
+    say("case: Wan 720p full size (591 blocks per head), sampled rows")
+    rp, ci = synth.csr_for_config(cfg)
+    _full_size_check(cfg, rp, ci, 51, 12)
+
+
 def test_mochi_full_size_sampled(gpu):
     cfg = synth.get_config("mochi")
     say("case: Mochi full size, sampled rows")
