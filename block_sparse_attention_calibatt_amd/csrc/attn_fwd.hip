@@ -456,7 +456,8 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
   constexpr int OBJ = G::KUNITS * 16;   // bytes of one stage
   __shared__ u32x4 ks0[G::KUNITS], ks1[G::KUNITS], ks2[G::KUNITS];
   __shared__ u32x4 vs0[G::VUNITS], vs1[G::VUNITS], vs2[G::VUNITS];
-  __shared__ int s_item;
+  __shared__ int s_next[8];   // the next row: b, r (-1: none), first list entry, blocks, kb0, kb1, kb2
+  __shared__ int s_fstate[2];   // the fetching wave's queue state: partition, partitions tried
   __shared__ float s_ml[G::NW * 64 * 2];   // group B's reference and row sum, per lane
   u32x4* const kst[3] = {ks0, ks1, ks2};
   u32x4* const vst[3] = {vs0, vs1, vs2};
@@ -508,7 +509,71 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
   __syncthreads();
 
   const RowSource src{work_order, rows, nqb, H, items / rows};
-  for_each_row(src, queue, &s_item, [&](int b, int r) {
+  // Rows come from the same per-XCD queues as in for_each_row, but wave 4
+  // fetches the next row while group A merges the current one: the queue
+  // pop, its work-order entry, the row's list bounds and first three key
+  // blocks (a chain of dependent loads) land in LDS before the row starts.
+  // The queue state lives in LDS too, so that no register is held through
+  // the phase loop for it.
+  if (threadIdx.x == 0) {
+    s_fstate[0] = blockIdx.x % kParts;
+    s_fstate[1] = 0;
+  }
+  __syncthreads();
+  auto fetch_next = [&]() __attribute__((always_inline)) {
+    int p_f = __builtin_amdgcn_readfirstlane(s_fstate[0]);
+    int tries_f = __builtin_amdgcn_readfirstlane(s_fstate[1]);
+    int b_ = 0, r_ = -1;
+    if (!queue) {   // one workgroup per row: row blockIdx.x of the order, once
+      if (tries_f == 0) {
+        tries_f = kParts;
+        const int item = blockIdx.x;
+        b_ = item / src.rows;
+        const int j = item - b_ * src.rows;
+        r_ = src.order ? src.order[j] : j;
+      }
+    }
+    while (queue && tries_f < kParts) {
+      int k = 0;
+      if (lane == 0) k = atomicAdd(queue + p_f * kQueueStride, 1);
+      k = __builtin_amdgcn_readfirstlane(k);
+      const int len = src.part_len(p_f);
+      if (k >= src.B * len) {
+        p_f = (p_f + 1) % kParts;
+        ++tries_f;
+        continue;
+      }
+      b_ = k / len;
+      r_ = src.part_row(p_f, k - b_ * len);
+      break;
+    }
+    int beg_ = 0, nblk_ = 0, k0_ = 0, k1_ = 0, k2_ = 0;
+    if (r_ >= 0) {
+      beg_ = DENSE ? 0 : row_ptr[r_];
+      nblk_ = (DENSE ? nkb_valid : row_ptr[r_ + 1]) - beg_;
+      if (nblk_ > 0) {
+        auto bl = [&](int i) __attribute__((always_inline)) -> int {
+          i = i < nblk_ ? i : nblk_ - 1;
+          return DENSE ? i : col_idx[beg_ + i];
+        };
+        k0_ = bl(0);
+        k1_ = bl(1);
+        k2_ = bl(2);
+      }
+    }
+    if (lane == 0) {
+      s_fstate[0] = p_f;
+      s_fstate[1] = tries_f;
+      s_next[0] = b_;
+      s_next[1] = r_;
+      s_next[2] = beg_;
+      s_next[3] = nblk_;
+      s_next[4] = k0_;
+      s_next[5] = k1_;
+      s_next[6] = k2_;
+    }
+  };
+  auto body = [&](int b, int r, int beg, int nblk, int pk0, int pk1, int pk2) {
     const int h = r / nqb, qb = r - h * nqb;
     const size_t base = ((size_t)b * H + h) * (size_t)L * D;
     const size_t qbase = SPLITQ ? ((size_t)b * H + h) * (size_t)Lq * D : base;
@@ -516,14 +581,7 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vt + base, slab_bytes);
     const int q = qb * BLK + 32 * w + c;   // this lane's query
 
-    const int beg = DENSE ? 0 : row_ptr[r];
-    const int nblk = (DENSE ? nkb_valid : row_ptr[r + 1]) - beg;
     const int n = nblk * 2;   // sub-tiles
-    auto blk = [&](int i) __attribute__((always_inline)) -> int {
-      i = i < nblk ? i : nblk - 1;
-      i = i < 0 ? 0 : i;
-      return DENSE ? i : col_idx[beg + i];
-    };
     // key blocks around phase t (block b = t/2): kbm = b-1, kb0 = b, kb1 =
     // b+1; kb2 (b+2) is loaded a block ahead
     int kbm = 0, kb0 = 0, kb1 = 0, kb2 = 0;
@@ -539,9 +597,9 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
     };
     int cbase = 0, ck_cur = 0, ck_nxt = 0;
     if (n > 0) {
-      kb0 = blk(0);
-      kb1 = blk(1);
-      kb2 = blk(2);
+      kb0 = pk0;
+      kb1 = pk1;
+      kb2 = pk2;
       if (!DENSE) {
         ck_cur = idx_chunk(0);
         ck_nxt = idx_chunk(1);
@@ -828,10 +886,29 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
           *reinterpret_cast<bf16x4*>(Ob + 32 * t + 8 * rq + 4 * g) = o;
         }
       }
+    } else if (wv == 4) {
+      // group B is idle while A merges: fetch the next row
+      fetch_next();
     }
     // the stages are free again for the next row's DMA
     lds_barrier();
-  });
+  };
+  if (wv == 4) fetch_next();
+  __syncthreads();
+  for (;;) {
+    const int nb = __builtin_amdgcn_readfirstlane(s_next[0]);
+    const int nr = __builtin_amdgcn_readfirstlane(s_next[1]);
+    const int nbeg = __builtin_amdgcn_readfirstlane(s_next[2]);
+    const int nn = __builtin_amdgcn_readfirstlane(s_next[3]);
+    const int n0 = __builtin_amdgcn_readfirstlane(s_next[4]);
+    const int n1 = __builtin_amdgcn_readfirstlane(s_next[5]);
+    const int n2 = __builtin_amdgcn_readfirstlane(s_next[6]);
+    // every wave has read the entry before wave 4 may write the next one
+    // (it does so only in the row's merge, many barriers later)
+    __syncthreads();
+    if (nr < 0) break;
+    body(nb, nr, nbeg, nn, n0, n1, n2);
+  }
 }
 
 // float32 path: 32-key slices, fp32 matrix cores (32x32x2), P kept in float32.
