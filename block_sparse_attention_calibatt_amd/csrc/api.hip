@@ -613,8 +613,8 @@ static long long anchor_queries(int frames, int grid_cols, int k_anchor) {
 size_t calibatt_anchor_ws_bytes(int B, int H, int frames, int grid_cols, int k_anchor, int d) {
   if (B < 1 || H < 1 || frames < 1 || grid_cols < 1 || k_anchor < 1 || (d != 64 && d != 128)) return 0;
   const long long Lq = (anchor_queries(frames, grid_cols, k_anchor) + 127) / 128 * 128;
-  const size_t qa = ((size_t)B * H * Lq * d * 2 + 255) / 256 * 256;
-  return 2 * qa + ((size_t)H * (Lq / 128) + calibatt::kParts + 1) * sizeof(int32_t);
+  const size_t oa = ((size_t)B * H * Lq * d * 2 + 255) / 256 * 256;
+  return oa + ((size_t)H * (Lq / 128) + calibatt::kParts + 1) * sizeof(int32_t);
 }
 
 calibatt_status calibatt_anchor_attn_fwd(const void* Q, const void* K, const void* V, void* O,
@@ -663,14 +663,13 @@ calibatt_status calibatt_anchor_attn_fwd(const void* Q, const void* K, const voi
     if (s != CALIBATT_OK) return s;
     Vt = vt_ws;
   }
-  const size_t qa = ((size_t)B * H * Lq * d * 2 + 255) / 256 * 256;
+  const size_t oa = ((size_t)B * H * Lq * d * 2 + 255) / 256 * 256;
   a.Q = Q;
   a.K = K;
   a.Vt = Vt;
   a.O = O;
-  a.Qa = ws;
-  a.Oa = static_cast<char*>(ws) + qa;
-  a.order = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + 2 * qa);
+  a.Oa = ws;
+  a.order = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + oa);
   a.queue = queue_ws;
   a.B = B;
   a.H = H;

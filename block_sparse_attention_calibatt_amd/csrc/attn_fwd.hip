@@ -437,16 +437,16 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(
 // issued two phases before S(x) reads it and V^T(x) two phases before
 // P*V(x).  K and V^T rotate through three LDS stages each.
 //
-// SPLITQ: Q and O have their own length Lq (a multiple of 128) and only
-// their first q_valid rows are real (the anchor queries of the
-// spatial-repetition heads); rows are h*(Lq/128) + qb, and keys still run
-// over K and V^T of length L with seq_len valid.
+// SPLITQ: the rows are the anchor queries of the spatial-repetition heads:
+// query m < q_valid of head h is token anchor_token(m) of Q (read in place),
+// O is [B, H, Lq, d] with Lq a multiple of 128, rows h*(Lq/128) + qb; keys
+// still run over K and V^T of length L with seq_len valid.
 template <int D, bool DENSE, bool SPLITQ = false>
 __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ Vt,
     bf16* __restrict__ O, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     const int32_t* __restrict__ work_order, int32_t* __restrict__ queue, int items, int H, int L,
-    int seq_len, int nkb_valid, float c2, int Lq, int q_valid) {
+    int seq_len, int nkb_valid, float c2, int Lq, int q_valid, int grid_rows, int grid_cols, int k_anchor) {
   constexpr int BLK = 128;
   using G = Geo<D, BLK>;   // one wave group: NW = 4 waves of 32 queries
   constexpr int DS = G::DS, DT = G::DT, KS = G::KS, CH = G::CH;
@@ -614,10 +614,13 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
     // rounded to bf16, so that the products give scores in log2 units and,
     // with the accumulators started at -ref, exp2 needs no vector arithmetic
     // before it
+    // the token this lane's query reads (anchor rows: through the anchor
+    // map; padding rows past q_valid read token 0 and are never written)
+    const int qsrc = SPLITQ ? (q < q_valid ? anchor_token(q, grid_rows, grid_cols, k_anchor) : 0) : q;
     bf16x8 qreg[DS];
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
-      const bf16x8 qv = *reinterpret_cast<const bf16x8*>(Q + qbase + (size_t)q * D + 16 * s + 8 * g);
+      const bf16x8 qv = *reinterpret_cast<const bf16x8*>(Q + base + (size_t)qsrc * D + 16 * s + 8 * g);
 #pragma unroll
       for (int e = 0; e < 8; ++e) qreg[s][e] = (bf16)((float)qv[e] * c2);
     }
@@ -1068,7 +1071,8 @@ static hipError_t launch_pp(const AttnArgs& a, hipStream_t st) {
   }
   hipLaunchKernelGGL((attn_fwd_pp_kernel<D, DENSE, SPLITQ>), dim3(grid), dim3(512), 0, st, (const bf16*)a.Q,
                      (const bf16*)a.K, (const bf16*)a.Vt, (bf16*)a.O, a.row_ptr, a.col_idx, a.work_order, a.queue,
-                     items, a.H, a.L, a.seq_len, a.nkb_valid, c2, Lq, SPLITQ ? a.q_valid : a.seq_len);
+                     items, a.H, a.L, a.seq_len, a.nkb_valid, c2, Lq, SPLITQ ? a.q_valid : a.seq_len,
+                     a.grid_rows, a.grid_cols, a.k_anchor);
   return hipGetLastError();
 }
 

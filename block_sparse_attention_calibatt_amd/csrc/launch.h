@@ -21,8 +21,11 @@ struct AttnArgs {
   float scale;
   bool dtype_f32;
   int num_cu;
-  // anchor-row launches only: Q and O are [B, H, Lq, d] with q_valid real rows
-  int Lq = 0, q_valid = 0;
+  // anchor-row launches only: rows index the q_valid anchor queries (padded
+  // to Lq, a multiple of 128) of a (frames, grid_rows, grid_cols) token grid
+  // with k_anchor anchors per frame; Q is read through the anchor map, O is
+  // [B, H, Lq, d]
+  int Lq = 0, q_valid = 0, grid_rows = 0, grid_cols = 0, k_anchor = 0;
 };
 
 hipError_t launch_attention(const AttnArgs& a, bool dense, hipStream_t st);
@@ -78,7 +81,6 @@ struct AnchorArgs {
   const void* K;
   const void* Vt;  // [B, H, d, L]
   void* O;
-  void* Qa;        // [B, H, Lq, d]
   void* Oa;        // [B, H, Lq, d]
   int32_t* order;  // [H*(Lq/128) + kParts + 1]
   int32_t* queue;

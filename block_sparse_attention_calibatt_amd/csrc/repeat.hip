@@ -22,25 +22,17 @@
 // fixed order in float64; a second kernel adds the workgroup partials in
 // order, so the score is bitwise reproducible.
 //
-// Anchor forward: gather the anchor queries of the listed heads into a
-// [B, H, Lq, d] buffer (Lq = anchor count rounded up to 128, the rest
-// zero), run the persistent dense kernel over them in its split-query mode
-// (keys: the full K and V^T), and write every token's output from its
-// anchor's row.
+// Anchor forward: the persistent dense kernel runs over the anchor queries
+// of the listed heads in its split-query mode (each query read in place
+// through the anchor map; keys: the full K and V^T) into a [B, H, Lq, d]
+// buffer (Lq = anchor count rounded up to 128), and every token's output
+// row is then copied from its anchor's.
 #include "tiles.h"
 #include "launch.h"
 
 namespace calibatt {
 
 namespace {
-
-__device__ __forceinline__ int anchor_token(int m, int R, int C, int k) {
-  const int per_frame = k * C;
-  const int f = m / per_frame, rem = m - f * per_frame;
-  const int g = rem / C, x = rem - g * C;
-  const int lo = (g * R) / k, hi = ((g + 1) * R) / k;
-  return (f * R + (lo + hi - 1) / 2) * C + x;
-}
 
 // Index of the anchor query whose output token n takes (n < seq_len).
 __device__ __forceinline__ int source_anchor(int n, int R, int C, int k) {
@@ -51,45 +43,31 @@ __device__ __forceinline__ int source_anchor(int n, int R, int C, int k) {
   return (f * k + g) * C + x;
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void anchor_gather_kernel(const T* __restrict__ Q, T* __restrict__ Qa,
-                                                            HeadList hl, int B, int H, int L, int Lq, int La,
-                                                            int R, int C, int k) {
-  constexpr int U = D * (int)sizeof(T) / 16;   // 16-byte units per row
-  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long total = (long long)B * hl.n * Lq * U;
-  if (t >= total) return;
-  const int u = (int)(t % U);
-  const long long row = t / U;
-  const int m = (int)(row % Lq);
-  const long long rest = row / Lq;
-  const int slot = (int)(rest % hl.n), b = (int)(rest / hl.n);
-  const size_t bh = (size_t)b * H + hl.h[slot];
-  u32x4 v = {0u, 0u, 0u, 0u};
-  if (m < La) {
-    const int tok = anchor_token(m, R, C, k);
-    v = reinterpret_cast<const u32x4*>(Q + (bh * L + tok) * D)[u];
-  }
-  reinterpret_cast<u32x4*>(Qa + (bh * Lq + m) * D)[u] = v;
-}
-
+// One thread copies a 64-byte run of one output row (four 16-byte units).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void anchor_broadcast_kernel(const T* __restrict__ Oa, T* __restrict__ O,
                                                                HeadList hl, int B, int H, int L, int Lq,
                                                                int seq_len, int R, int C, int k) {
-  constexpr int U = D * (int)sizeof(T) / 16;
+  constexpr int U = D * (int)sizeof(T) / 16;   // 16-byte units per row
+  constexpr int RUNS = U / 4;                  // 64-byte runs per row
   const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long total = (long long)B * hl.n * L * U;
+  const long long total = (long long)B * hl.n * L * RUNS;
   if (t >= total) return;
-  const int u = (int)(t % U);
-  const long long row = t / U;
+  const int run = (int)(t % RUNS);
+  const long long row = t / RUNS;
   const int n = (int)(row % L);
   const long long rest = row / L;
   const int slot = (int)(rest % hl.n), b = (int)(rest / hl.n);
   const size_t bh = (size_t)b * H + hl.h[slot];
-  u32x4 v = {0u, 0u, 0u, 0u};
-  if (n < seq_len) v = reinterpret_cast<const u32x4*>(Oa + (bh * Lq + source_anchor(n, R, C, k)) * D)[u];
-  reinterpret_cast<u32x4*>(O + (bh * L + n) * D)[u] = v;
+  u32x4 v[4] = {};
+  if (n < seq_len) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(Oa + (bh * Lq + source_anchor(n, R, C, k)) * D) + 4 * run;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = src[i];
+  }
+  u32x4* dst = reinterpret_cast<u32x4*>(O + (bh * L + n) * D) + 4 * run;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dst[i] = v[i];
 }
 
 // Work order for the anchor rows: listed head i goes to partition i % 8, its
@@ -223,35 +201,24 @@ hipError_t launch_spatial_similarity(const SimArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <typename T, int D>
-static hipError_t anchor_copy(const AnchorArgs& a, bool gather, hipStream_t st) {
-  constexpr int U = D * (int)sizeof(T) / 16;
-  const long long rows = (long long)a.B * a.heads.n * (gather ? a.Lq : a.L);
-  const long long threads = rows * U;
+template <int D>
+static hipError_t anchor_broadcast(const AnchorArgs& a, hipStream_t st) {
+  constexpr int RUNS = D * 2 / 64;
+  const long long threads = (long long)a.B * a.heads.n * a.L * RUNS;
   const unsigned grid = (unsigned)((threads + 255) / 256);
-  if (gather)
-    hipLaunchKernelGGL((anchor_gather_kernel<T, D>), dim3(grid), dim3(256), 0, st, (const T*)a.Q, (T*)a.Qa, a.heads,
-                       a.B, a.H, a.L, a.Lq, a.La, a.rows, a.cols, a.k);
-  else
-    hipLaunchKernelGGL((anchor_broadcast_kernel<T, D>), dim3(grid), dim3(256), 0, st, (const T*)a.Oa, (T*)a.O,
-                       a.heads, a.B, a.H, a.L, a.Lq, a.seq_len, a.rows, a.cols, a.k);
+  hipLaunchKernelGGL((anchor_broadcast_kernel<bf16, D>), dim3(grid), dim3(256), 0, st, (const bf16*)a.Oa, (bf16*)a.O,
+                     a.heads, a.B, a.H, a.L, a.Lq, a.seq_len, a.rows, a.cols, a.k);
   return hipGetLastError();
-}
-
-static hipError_t anchor_copy_any(const AnchorArgs& a, bool gather, hipStream_t st) {
-  return a.d == 128 ? anchor_copy<bf16, 128>(a, gather, st) : anchor_copy<bf16, 64>(a, gather, st);
 }
 
 hipError_t launch_anchor_fwd(const AnchorArgs& a, hipStream_t st) {
   if (a.heads.n == 0) return hipSuccess;
-  hipError_t e = anchor_copy_any(a, true, st);
-  if (e != hipSuccess) return e;
   const int nqb = a.Lq / 128;
   hipLaunchKernelGGL(anchor_order_kernel, dim3(1), dim3(256), 0, st, a.heads, a.H, nqb, a.order);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   AttnArgs t;
-  t.Q = a.Qa;
+  t.Q = a.Q;
   t.K = a.K;
   t.Vt = a.Vt;
   t.O = a.Oa;
@@ -271,9 +238,12 @@ hipError_t launch_anchor_fwd(const AnchorArgs& a, hipStream_t st) {
   t.num_cu = a.num_cu;
   t.Lq = a.Lq;
   t.q_valid = a.La;
+  t.grid_rows = a.rows;
+  t.grid_cols = a.cols;
+  t.k_anchor = a.k;
   e = launch_anchor_attention(t, st);
   if (e != hipSuccess) return e;
-  return anchor_copy_any(a, false, st);
+  return a.d == 128 ? anchor_broadcast<128>(a, st) : anchor_broadcast<64>(a, st);
 }
 
 }  // namespace calibatt

@@ -117,4 +117,16 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Spatial-repetition anchor rows: anchor query m (frame-major, then group,
+// then column) of a (frames, R rows, C columns) token grid with k groups of
+// rows [floor(g R / k), floor((g+1) R / k)), each anchored at its lower
+// middle row, is token (f R + a) C + x.
+__device__ __forceinline__ int anchor_token(int m, int R, int C, int k) {
+  const int per_frame = k * C;
+  const int f = m / per_frame, rem = m - f * per_frame;
+  const int g = rem / C, x = rem - g * C;
+  const int lo = (g * R) / k, hi = ((g + 1) * R) / k;
+  return (f * R + (lo + hi - 1) / 2) * C + x;
+}
+
 }  // namespace calibatt

@@ -382,12 +382,13 @@ calibatt_status calibatt_select_repetitive_heads(const double* sim, int P, int H
  *   v_layout, vt_ws  as in calibatt_sparse_attn_fwd (a [B, H, L, d] V is
  *               transposed for all H heads).
  *   ws          calibatt_anchor_ws_bytes(B, H, frames, grid_cols, k_anchor,
- *               d) bytes (device), 256-byte aligned: the gathered anchor
- *               queries and their outputs as [B, H, Lq, d] (Lq = frames *
- *               k_anchor * grid_cols rounded up to 128), and the row order.
+ *               d) bytes (device), 256-byte aligned: the anchor outputs as
+ *               [B, H, Lq, d] (Lq = frames * k_anchor * grid_cols rounded up
+ *               to 128) and the row order.
  * The anchor queries run through the persistent dense kernel in a
- * split-query mode (bf16 matrix cores with float32 accumulation, float32
- * softmax, probabilities and O rounded to bf16).
+ * split-query mode that reads each anchor query of Q in place (bf16 matrix
+ * cores with float32 accumulation, float32 softmax, probabilities and O
+ * rounded to bf16); a copy kernel then writes every token's row.
  */
 calibatt_status calibatt_anchor_attn_fwd(const void* Q, const void* K, const void* V, void* O,
                                          const int32_t* heads, int n_heads, int frames, int grid_rows,

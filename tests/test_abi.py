@@ -255,7 +255,7 @@ def test_repetition_entry_points_reject(lib):
 
     aws = lib.calibatt_anchor_ws_bytes(1, 40, 21, 52, 5, 128)
     lq = (21 * 5 * 52 + 127) // 128 * 128
-    assert aws == 2 * 40 * lq * 128 * 2 + (40 * lq // 128 + 9) * 4
+    assert aws == 40 * lq * 128 * 2 + (40 * lq // 128 + 9) * 4
     assert lib.calibatt_anchor_ws_bytes(1, 40, 21, 52, 0, 128) == 0
     hl = np.array([3, 7], dtype=np.int32)
 
