@@ -26,11 +26,11 @@ TOL = 2e-2
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
-def _grid_cfg(grid, d, H, seed, pad_to=128):
+def _grid_cfg(grid, d, H, seed, pad_to=128, B=1):
     F, R, C = grid
     S = F * R * C
     L = -(-S // pad_to) * pad_to
-    return small_cfg(B=1, H=H, L=L, S=S, d=d, block=128, seed=seed, grid=grid)
+    return small_cfg(B=B, H=H, L=L, S=S, d=d, block=128, seed=seed, grid=grid)
 
 
 def _sim_gpu(q, k, cfg):
@@ -149,6 +149,24 @@ def test_anchor_small(gpu, d, k_anchor):
         assert torch.count_nonzero(O[:, heads, cfg.S:].float()).item() == 0
         src = torch.from_numpy(_source_tokens(cfg, k_anchor)).to("cuda:0")
         assert torch.equal(O[:, heads, :cfg.S], O[:, heads][:, :, src]), "broadcast is a copy"
+
+
+def test_batch_of_two(gpu):
+    """B = 2: each batch entry has its own scores and outputs."""
+    grid = (2, 4, 24)
+    cfg = _grid_cfg(grid, 128, 3, seed=90, B=2)
+    say(f"case: spatial similarity and anchor rows with B=2, grid={grid}")
+    q, k, v = inputs(cfg)
+    synth.repeat_rows(q, grid, cfg.S, [1], 0.2)
+    got = _sim_gpu(q, k, cfg)
+    ref = oracle.spatial_similarity(q, k, cfg.scale, cfg.S, grid)
+    assert got.shape == (2, 3) and float(np.max(np.abs(got - ref))) <= SIM_TOL
+    heads = [2, 0]
+    O = _anchor_gpu(q, k, v, cfg, heads, 2)
+    e = err(O[:, heads], oracle.anchor_attention(q, k, v, cfg.scale, cfg.S, grid, 2, heads))
+    say(f"  similarity max err {float(np.max(np.abs(got - ref))):.2e}, anchor max err {e:.3e}")
+    assert e <= TOL
+    _check_untouched(O, cfg, heads)
 
 
 def test_anchor_every_row_matches_dense(gpu):
