@@ -40,10 +40,14 @@ __global__ __launch_bounds__(BLK * 2) void row_lse_kernel(const bf16* __restrict
     qreg[s] = *reinterpret_cast<const bf16x8*>(Q + base + (size_t)q * D + 16 * s + 8 * g);
 
   float m_run = kNegInf, l_run = 0.f;
+  // tile kb + 1 is loaded into registers while tile kb is in use
+  KTileRegs<D, BLK, NT> kt;
+  if (nkb_valid > 0) fetch_k_tile<D, BLK, NT>(K + base, kt);
   for (int kb = 0; kb < nkb_valid; ++kb) {
     __syncthreads();
-    load_k_tile<D, BLK, NT>(K + base + (size_t)kb * BLK * D, ldsK);
+    store_k_tile<D, BLK, NT>(kt, ldsK);
     __syncthreads();
+    if (kb + 1 < nkb_valid) fetch_k_tile<D, BLK, NT>(K + base + (size_t)(kb + 1) * BLK * D, kt);
     f32x16 sacc[KT];
     qk_tile<D, BLK>(ldsK, qreg, sacc, g, c);
     const int k0 = kb * BLK;
@@ -108,10 +112,14 @@ __global__ __launch_bounds__(BLK * 2) void block_pool_kernel(const bf16* __restr
   for (int s = 0; s < DS; ++s)
     qreg[s] = *reinterpret_cast<const bf16x8*>(Q + base + (size_t)q * D + 16 * s + 8 * g);
 
+  // tile kb + 1 is loaded into registers while tile kb is in use
+  KTileRegs<D, BLK, NT> kt;
+  if (nkb_valid > 0) fetch_k_tile<D, BLK, NT>(K + base, kt);
   for (int kb = 0; kb < nkb_valid; ++kb) {
     __syncthreads();
-    load_k_tile<D, BLK, NT>(K + base + (size_t)kb * BLK * D, ldsK);
+    store_k_tile<D, BLK, NT>(kt, ldsK);
     __syncthreads();
+    if (kb + 1 < nkb_valid) fetch_k_tile<D, BLK, NT>(K + base + (size_t)(kb + 1) * BLK * D, kt);
     f32x16 sacc[KT];
     qk_tile<D, BLK>(ldsK, qreg, sacc, g, c);
     const int k0 = kb * BLK;
