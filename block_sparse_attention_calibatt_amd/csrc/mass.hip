@@ -17,6 +17,10 @@
 
 namespace calibatt {
 
+// Pass 1 keeps its reference until a tile's per-lane sum passes this bound
+// (or is not finite); the row sum stays far inside float32's range.
+constexpr float kLseCap = 1048576.f;
+
 template <int D, int BLK>
 __global__ __launch_bounds__(BLK * 2) void row_lse_kernel(const bf16* __restrict__ Q,
                                                           const bf16* __restrict__ K,
@@ -39,7 +43,9 @@ __global__ __launch_bounds__(BLK * 2) void row_lse_kernel(const bf16* __restrict
   for (int s = 0; s < DS; ++s)
     qreg[s] = *reinterpret_cast<const bf16x8*>(Q + base + (size_t)q * D + 16 * s + 8 * g);
 
-  float m_run = kNegInf, l_run = 0.f;
+  // m_run: the reference (raw score units), valid once `fresh` is false
+  float m_run = 0.f, l_run = 0.f;
+  bool fresh = true;
   // tile kb + 1 is loaded into registers while tile kb is in use
   KTileRegs<D, BLK, NT> kt;
   if (nkb_valid > 0) fetch_k_tile<D, BLK, NT>(K + base, kt);
@@ -58,23 +64,33 @@ __global__ __launch_bounds__(BLK * 2) void row_lse_kernel(const bf16* __restrict
         for (int rr = 0; rr < 16; ++rr)
           if (k0 + 32 * mt + slice_key(rr, g) >= seq_len) sacc[mt][rr] = kNegInf;
     }
-    float mx = kNegInf;
+    // lazy reference (scaled units): set from the first tile's maximum and
+    // moved to the running maximum only when a tile's sum passes kLseCap or
+    // is not finite, so most tiles need no maximum
+    auto tile_sum = [&](float mc) __attribute__((always_inline)) {
+      float ps = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < KT; ++mt)
+      for (int mt = 0; mt < KT; ++mt)
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, sacc[mt][rr]);
-    mx = pair_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = fast_exp2((m_run - m_use) * c2);
-    const float mc = m_use * c2;
-    m_run = m_new;
-    float psum = 0.f;
+        for (int rr = 0; rr < 16; ++rr) ps += fast_exp2(fmaf(sacc[mt][rr], c2, -mc));
+      return ps;
+    };
+    float psum = fresh ? 0.f : tile_sum(m_run * c2);
+    if (__any(fresh || !(psum <= kLseCap))) {
+      float mx = kNegInf;
 #pragma unroll
-    for (int mt = 0; mt < KT; ++mt)
+      for (int mt = 0; mt < KT; ++mt)
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) psum += fast_exp2(fmaf(sacc[mt][rr], c2, -mc));
-    l_run = l_run * alpha + psum;
+        for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, sacc[mt][rr]);
+      mx = pair_max(mx);
+      const float m_new = fresh ? mx : fmaxf(m_run, mx);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      l_run *= fresh ? 0.f : fast_exp2((m_run - m_use) * c2);
+      m_run = m_use;
+      fresh = m_new == kNegInf;
+      psum = tile_sum(m_run * c2);
+    }
+    l_run += psum;
   }
   const float l_tot = pair_sum(l_run);
   if (g == 0) {
@@ -125,13 +141,20 @@ __global__ __launch_bounds__(BLK * 2) void block_pool_kernel(const bf16* __restr
     const int k0 = kb * BLK;
     float psum = 0.f;
     if (qvalid) {
+      if (k0 + BLK > seq_len) {   // the tile holding the padded keys
 #pragma unroll
-      for (int mt = 0; mt < KT; ++mt)
+        for (int mt = 0; mt < KT; ++mt)
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const bool kvalid = k0 + 32 * mt + slice_key(rr, g) < seq_len;
-          psum += kvalid ? fast_exp2(fmaf(sacc[mt][rr], c2, -lse2)) : 0.f;
-        }
+          for (int rr = 0; rr < 16; ++rr) {
+            const bool kvalid = k0 + 32 * mt + slice_key(rr, g) < seq_len;
+            psum += kvalid ? fast_exp2(fmaf(sacc[mt][rr], c2, -lse2)) : 0.f;
+          }
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < KT; ++mt)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) psum += fast_exp2(fmaf(sacc[mt][rr], c2, -lse2));
+      }
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) psum += __shfl_xor(psum, off);

@@ -139,14 +139,25 @@ __global__ __launch_bounds__(256) void spatial_sim_kernel(const bf16* __restrict
         s1 = mfma_bf16(a, qa[s], s1);
         s2 = mfma_bf16(a, qb2[s], s2);
       }
+      if (k0 + BLK > seq_len) {   // the tile holding the padded keys
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const bool kv = k0 + 32 * mt + slice_key(rr, g) < seq_len;
-        const float p1 = kv ? fast_exp2(fmaf(s1[rr], c2, -l1)) : 0.f;
-        const float p2 = kv ? fast_exp2(fmaf(s2[rr], c2, -l2)) : 0.f;
-        dot = fmaf(p1, p2, dot);
-        n1 = fmaf(p1, p1, n1);
-        n2 = fmaf(p2, p2, n2);
+        for (int rr = 0; rr < 16; ++rr) {
+          const bool kv = k0 + 32 * mt + slice_key(rr, g) < seq_len;
+          const float p1 = kv ? fast_exp2(fmaf(s1[rr], c2, -l1)) : 0.f;
+          const float p2 = kv ? fast_exp2(fmaf(s2[rr], c2, -l2)) : 0.f;
+          dot = fmaf(p1, p2, dot);
+          n1 = fmaf(p1, p1, n1);
+          n2 = fmaf(p2, p2, n2);
+        }
+      } else {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const float p1 = fast_exp2(fmaf(s1[rr], c2, -l1));
+          const float p2 = fast_exp2(fmaf(s2[rr], c2, -l2));
+          dot = fmaf(p1, p2, dot);
+          n1 = fmaf(p1, p1, n1);
+          n2 = fmaf(p2, p2, n2);
+        }
       }
     }
   }
