@@ -37,11 +37,12 @@ def hipcc():
     return "hipcc"
 
 
-# The attention kernels keep their matrix-core accumulators in ordinary
-# vector registers (mixing in accumulation registers splits the register
-# file in half at two waves per SIMD and spills), which needs the
+# The attention and calibration kernels keep their matrix-core accumulators
+# in ordinary vector registers (mixing in accumulation registers splits the
+# register file in half at two waves per SIMD and spills, and every score
+# the vector units read would first be copied out), which needs the
 # vector-register form of the matrix instructions.
-PER_FILE_FLAGS = {"attn_fwd.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
+PER_FILE_FLAGS = {f: ["-mllvm", "--amdgpu-mfma-vgpr-form"] for f in ("attn_fwd.hip", "mass.hip", "repeat.hip")}
 
 
 def build(verbose=False, extra=()):
