@@ -46,14 +46,10 @@ __global__ __launch_bounds__(BLK * 2) void row_lse_kernel(const bf16* __restrict
   // m_run: the reference (raw score units), valid once `fresh` is false
   float m_run = 0.f, l_run = 0.f;
   bool fresh = true;
-  // tile kb + 1 is loaded into registers while tile kb is in use
-  KTileRegs<D, BLK, NT> kt;
-  if (nkb_valid > 0) fetch_k_tile<D, BLK, NT>(K + base, kt);
   for (int kb = 0; kb < nkb_valid; ++kb) {
     __syncthreads();
-    store_k_tile<D, BLK, NT>(kt, ldsK);
+    load_k_tile<D, BLK, NT>(K + base + (size_t)kb * BLK * D, ldsK);
     __syncthreads();
-    if (kb + 1 < nkb_valid) fetch_k_tile<D, BLK, NT>(K + base + (size_t)(kb + 1) * BLK * D, kt);
     f32x16 sacc[KT];
     qk_tile<D, BLK>(ldsK, qreg, sacc, g, c);
     const int k0 = kb * BLK;
@@ -128,14 +124,10 @@ __global__ __launch_bounds__(BLK * 2) void block_pool_kernel(const bf16* __restr
   for (int s = 0; s < DS; ++s)
     qreg[s] = *reinterpret_cast<const bf16x8*>(Q + base + (size_t)q * D + 16 * s + 8 * g);
 
-  // tile kb + 1 is loaded into registers while tile kb is in use
-  KTileRegs<D, BLK, NT> kt;
-  if (nkb_valid > 0) fetch_k_tile<D, BLK, NT>(K + base, kt);
   for (int kb = 0; kb < nkb_valid; ++kb) {
     __syncthreads();
-    store_k_tile<D, BLK, NT>(kt, ldsK);
+    load_k_tile<D, BLK, NT>(K + base + (size_t)kb * BLK * D, ldsK);
     __syncthreads();
-    if (kb + 1 < nkb_valid) fetch_k_tile<D, BLK, NT>(K + base + (size_t)(kb + 1) * BLK * D, kt);
     f32x16 sacc[KT];
     qk_tile<D, BLK>(ldsK, qreg, sacc, g, c);
     const int k0 = kb * BLK;

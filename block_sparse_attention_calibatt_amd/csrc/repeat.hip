@@ -120,14 +120,10 @@ __global__ __launch_bounds__(256) void spatial_sim_kernel(const bf16* __restrict
   }
   const int prow = qk_row_perm(c);
   float dot = 0.f, n1 = 0.f, n2 = 0.f;
-  // tile kb + 1 is loaded into registers while tile kb is in use
-  KTileRegs<D, BLK, NT> kt;
-  if (nkb_valid > 0) fetch_k_tile<D, BLK, NT>(K + base, kt);
   for (int kb = 0; kb < nkb_valid; ++kb) {
     __syncthreads();
-    store_k_tile<D, BLK, NT>(kt, ldsK);
+    load_k_tile<D, BLK, NT>(K + base + (size_t)kb * BLK * D, ldsK);
     __syncthreads();
-    if (kb + 1 < nkb_valid) fetch_k_tile<D, BLK, NT>(K + base + (size_t)(kb + 1) * BLK * D, kt);
     const int k0 = kb * BLK;
 #pragma unroll
     for (int mt = 0; mt < BLK / 32; ++mt) {

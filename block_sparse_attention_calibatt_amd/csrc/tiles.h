@@ -87,35 +87,6 @@ __device__ __forceinline__ void load_k_tile(const bf16* __restrict__ src, u32x4*
   }
 }
 
-// The same load split in two, so that the next tile can be in flight from
-// HBM while the current one is in use: fetch_k_tile issues the loads into
-// registers, store_k_tile writes them to LDS.
-template <int D, int BLK, int NT>
-struct KTileRegs {
-  static constexpr int PER = BLK * (D / 8) / NT;
-  u32x4 r[PER];
-};
-
-template <int D, int BLK, int NT>
-__device__ __forceinline__ void fetch_k_tile(const bf16* __restrict__ src, KTileRegs<D, BLK, NT>& t) {
-  constexpr int CH = D / 8;
-#pragma unroll
-  for (int i = 0; i < KTileRegs<D, BLK, NT>::PER; ++i) {
-    const int idx = threadIdx.x + i * NT;
-    t.r[i] = *reinterpret_cast<const u32x4*>(src + (idx / CH) * D + (idx % CH) * 8);
-  }
-}
-
-template <int D, int BLK, int NT>
-__device__ __forceinline__ void store_k_tile(const KTileRegs<D, BLK, NT>& t, u32x4* __restrict__ lds) {
-  constexpr int CH = D / 8;
-#pragma unroll
-  for (int i = 0; i < KTileRegs<D, BLK, NT>::PER; ++i) {
-    const int idx = threadIdx.x + i * NT;
-    lds[chunk_index<CH>(idx / CH, idx % CH)] = t.r[i];
-  }
-}
-
 // S^T for one wave: BLK keys x 32 queries, as BLK/32 accumulators of 32x32.
 template <int D, int BLK>
 __device__ __forceinline__ void qk_tile(const u32x4* __restrict__ ldsK, const bf16x8* qreg,
