@@ -163,13 +163,15 @@ def main():
         lse = torch.empty(cfg.B * cfg.H * cfg.L, dtype=torch.float32, device=dev)
         masses = torch.empty((P, cfg.H, cfg.nqb, cfg.nkb), dtype=torch.float32, device=dev)
         pool_ms = 0.0
+        mws = torch.empty(cal.calibatt_block_mass_ws_bytes(cfg.B, cfg.H, cfg.L, cfg.block), dtype=torch.uint8,
+                          device=dev)
         for p, seed in enumerate(cfg.prompt_seeds):
             qp, kp = synth.gen_qk(cfg, seed)
             Qp, Kp = (torch.from_numpy(x).to(dev).to(torch.bfloat16).contiguous() for x in (qp, kp))
             del qp, kp
             c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             c0.record()
-            cal.calibatt_block_mass(Qp, Kp, cfg.block, cfg.scale, lse, masses[p], cfg.S)
+            cal.calibatt_block_mass_single_pass(Qp, Kp, cfg.block, cfg.scale, lse, masses[p], cfg.S, ws=mws)
             c1.record()
             torch.cuda.synchronize()
             pool_ms += c0.elapsed_time(c1)
@@ -182,7 +184,7 @@ def main():
                           "block_mass_ms_all_prompts": round(pool_ms, 2),
                           "compile_ms_incl_sync": round(compile_ms, 3),
                           "kept_blocks": int(cci.numel())}
-        del masses, lse
+        del masses, lse, mws
         q, k, v = synth.gen_qkv(cfg, cfg.infer_seed)
     else:
         q, k, v = synth.gen_qkv(cfg)
@@ -337,6 +339,20 @@ def main():
             cal.calibatt_block_mass(Q, K, cfg.block, cfg.scale, lse, mass[p], cfg.S)
         e[1].record(stream)
         torch.cuda.synchronize()
+        # the single-pass pooling of the same 8 prompts
+        mws = torch.empty(cal.calibatt_block_mass_ws_bytes(cfg.B, cfg.H, cfg.L, cfg.block), dtype=torch.uint8,
+                          device=dev)
+        mass1 = torch.empty_like(mass)
+        cal.calibatt_block_mass_single_pass(Q, K, cfg.block, cfg.scale, lse, mass1[0], cfg.S, ws=mws)
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        for p in range(8):
+            cal.calibatt_block_mass_single_pass(Q, K, cfg.block, cfg.scale, lse, mass1[p], cfg.S, ws=mws)
+        s1.record(stream)
+        torch.cuda.synchronize()
+        single_ms = s0.elapsed_time(s1) / 8
+        single_diff = float(((mass1 - mass).abs() / mass.abs().clamp_min(1e-30)).max())
+        del mass1, mws
         t_c = time.perf_counter()
         rp, ci = cal.calibatt_compile_masks(mass, cfg.nkb // 4, 4, cfg.nkb_valid)
         compile_s = time.perf_counter() - t_c
@@ -352,6 +368,8 @@ def main():
         extra["calib"] = {
             "block_mass_ms_per_prompt": round(pool_ms, 3),
             "block_mass_qk_tflops": round(2 * 2.0 * cfg.B * cfg.H * cfg.S * cfg.S * cfg.d / (pool_ms * 1e-3) / 1e12, 2),
+            "block_mass_single_pass_ms_per_prompt": round(single_ms, 3),
+            "block_mass_single_pass_max_rel_diff": single_diff,
             "compile_ms_8_prompts_incl_sync": round(compile_s * 1e3, 3),
             "schedule_ms": round(e[2].elapsed_time(e[3]), 4),
             "compiled_density": round(ci.numel() / (cfg.rows * cfg.nkb_valid), 4),

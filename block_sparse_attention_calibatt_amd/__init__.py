@@ -17,6 +17,8 @@ from .capi import (
     calibatt_sparse_attn_fwd,
     calibatt_dense_attn_fwd,
     calibatt_block_mass,
+    calibatt_block_mass_single_pass,
+    calibatt_block_mass_ws_bytes,
     calibatt_compile_ws_bytes,
     calibatt_compile_masks,
     calibatt_compile_masks_energy,
@@ -48,6 +50,8 @@ __all__ = [
     "calibatt_sparse_attn_fwd",
     "calibatt_dense_attn_fwd",
     "calibatt_block_mass",
+    "calibatt_block_mass_single_pass",
+    "calibatt_block_mass_ws_bytes",
     "calibatt_compile_ws_bytes",
     "calibatt_compile_masks",
     "calibatt_compile_masks_energy",

@@ -40,6 +40,9 @@ SIGNATURES = {
     "calibatt_transpose_v": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "calibatt_block_mass": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp,
                                    _vp]),
+    "calibatt_block_mass_single_pass": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
+                                               _vp, _vp, _sz, _vp]),
+    "calibatt_block_mass_ws_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "calibatt_compile_masks": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i64,
                                       ctypes.POINTER(_i64), _vp, _sz, _vp]),
     "calibatt_compile_masks_energy": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _i64, _i64, _i32, _vp, _vp,

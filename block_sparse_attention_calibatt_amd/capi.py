@@ -155,6 +155,36 @@ def calibatt_block_mass(Q, K, block, scale, lse_ws, mass, seq_len=None):
     return mass
 
 
+def calibatt_block_mass_ws_bytes(B, H, L, block):
+    return int(load().calibatt_block_mass_ws_bytes(int(B), int(H), int(L), int(block)))
+
+
+def calibatt_block_mass_single_pass(Q, K, block, scale, lse_ws, mass, seq_len=None, ws=None):
+    """The pooled mass in one pass over the scores (per-(key block, query) log2
+    partials in `ws`, a uint8 device tensor of calibatt_block_mass_ws_bytes bytes)."""
+    for n, t in (("Q", Q), ("K", K)):
+        _dev_tensor(t, n)
+    _need(Q.dim() == 4 and K.shape == Q.shape and K.dtype == Q.dtype, "Q, K must be [B, H, L, d] alike")
+    _need(Q.dtype in _DT, f"unsupported dtype {Q.dtype}")
+    B, H, L, d = Q.shape
+    seq_len = L if seq_len is None else int(seq_len)
+    _need(block > 0 and L % block == 0, "L must be a multiple of block")
+    nb = L // block
+    _dev_tensor(lse_ws, "lse_ws", torch.float32)
+    _dev_tensor(mass, "mass", torch.float32)
+    _need(lse_ws.numel() == B * H * L, "lse_ws must have B*H*L entries")
+    _need(mass.numel() == B * H * nb * nb, "mass must have B*H*nqb*nkb entries")
+    need = calibatt_block_mass_ws_bytes(B, H, L, block)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=Q.device)
+    _dev_tensor(ws, "ws", torch.uint8)
+    lib = load()
+    check(lib.calibatt_block_mass_single_pass(_ptr(Q), _ptr(K), B, H, L, seq_len, d, _DT[Q.dtype], int(block),
+                                              float(scale), _ptr(lse_ws), _ptr(mass), _ptr(ws), ws.numel(),
+                                              _stream(Q)))
+    return mass
+
+
 def calibatt_compile_ws_bytes(P, H, nqb, nkb):
     return int(load().calibatt_compile_ws_bytes(int(P), int(H), int(nqb), int(nkb)))
 

@@ -250,6 +250,43 @@ calibatt_status calibatt_block_mass(const void* Q, const void* K, int B, int H, 
   return ok();
 }
 
+size_t calibatt_block_mass_ws_bytes(int B, int H, int L, int block) {
+  if (B < 1 || H < 1 || (block != 64 && block != 128) || L < block || L % block != 0) return 0;
+  return (size_t)B * H * (L / block) * L * sizeof(float);
+}
+
+calibatt_status calibatt_block_mass_single_pass(const void* Q, const void* K, int B, int H, int L, int seq_len,
+                                                int d, calibatt_dtype dt, int block, float scale, float* lse_ws,
+                                                float* mass, void* ws, size_t ws_bytes, void* stream) {
+  if (!Q || !K || !lse_ws || !mass || !ws) return fail(CALIBATT_ERR_NULL, "Q, K, lse_ws, mass and ws must be non-NULL");
+  if (!aligned(Q, 16) || !aligned(K, 16)) return fail(CALIBATT_ERR_ALIGN, "Q and K must be 16-byte aligned");
+  if (!aligned(lse_ws, 4) || !aligned(mass, 4) || !aligned(ws, 256))
+    return fail(CALIBATT_ERR_ALIGN, "lse_ws and mass must be 4-byte aligned, ws 256-byte aligned");
+  calibatt_status s = check_qkv_shape(B, H, L, seq_len, d, dt, block);
+  if (s != CALIBATT_OK) return s;
+  if (dt != CALIBATT_BF16) return fail(CALIBATT_ERR_UNSUPPORTED, "block_mass supports bf16 inputs only");
+  if (L / block > calibatt::kMaxKeyBlocks)
+    return fail(CALIBATT_ERR_UNSUPPORTED, "L/block=%d exceeds %d key blocks", L / block, calibatt::kMaxKeyBlocks);
+  const size_t need = calibatt_block_mass_ws_bytes(B, H, L, block);
+  if (ws_bytes < need) return fail(CALIBATT_ERR_CAPACITY, "ws_bytes=%zu, need %zu", ws_bytes, need);
+  calibatt::MassArgs a;
+  a.Q = Q;
+  a.K = K;
+  a.lse = lse_ws;
+  a.mass = mass;
+  a.B = B;
+  a.H = H;
+  a.L = L;
+  a.seq_len = seq_len;
+  a.d = d;
+  a.block = block;
+  a.nkb_valid = (seq_len + block - 1) / block;
+  a.scale = scale;
+  hipError_t e = calibatt::launch_block_mass_single(a, static_cast<float*>(ws), (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "launching single-pass block mass");
+  return ok();
+}
+
 size_t calibatt_compile_ws_bytes(int P, int H, int nqb, int nkb) {
   if (P < 1 || H < 1 || nqb < 1 || nkb < 1) return 0;
   const size_t rows = (size_t)H * nqb;

@@ -52,6 +52,8 @@ struct MassArgs {
 };
 
 hipError_t launch_block_mass(const MassArgs& a, hipStream_t st);
+// The single-pass pooling: lpart is a [B, H, L/block, L] float32 workspace.
+hipError_t launch_block_mass_single(const MassArgs& a, float* lpart, hipStream_t st);
 // Pass 1 of the pooling alone: lse per query over the valid keys (block 128 tiles).
 hipError_t launch_row_lse(const MassArgs& a, hipStream_t st);
 

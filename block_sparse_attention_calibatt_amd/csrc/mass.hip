@@ -12,6 +12,14 @@
 // butterfly, keep one partial per wave per key block in LDS, and add the
 // partials of the block's waves in wave order at the end.  The reduction
 // order is fixed, so the mass is bitwise reproducible.
+//
+// Single pass (row_lse_kernel<.., true> + mass_from_partials_kernel): pass 1
+// also stores, per (key block, query), the block's log2 partial
+// lp = log2 sum_{j in kb} exp2(c s_ij), i.e. the reference plus the log of
+// the tile's sum against it, so a later move of the lazy reference does not
+// touch it.  The mass is then sum_{i in qb} exp2(lp_i,kb - lse2_i): one score
+// product and one exp per (query, key) instead of two, for a [B, H, nkb, L]
+// float32 workspace.
 #include "tiles.h"
 #include "launch.h"
 
@@ -21,11 +29,12 @@ namespace calibatt {
 // (or is not finite); the row sum stays far inside float32's range.
 constexpr float kLseCap = 1048576.f;
 
-template <int D, int BLK>
+template <int D, int BLK, bool PARTIALS = false>
 __global__ __launch_bounds__(BLK * 2) void row_lse_kernel(const bf16* __restrict__ Q,
                                                           const bf16* __restrict__ K,
                                                           float* __restrict__ lse, int H, int L,
-                                                          int seq_len, int nkb_valid, float c2) {
+                                                          int seq_len, int nkb_valid, float c2,
+                                                          float* __restrict__ lpart = nullptr) {
   constexpr int NT = BLK * 2;
   constexpr int KT = BLK / 32;
   constexpr int DS = D / 16;
@@ -87,6 +96,11 @@ __global__ __launch_bounds__(BLK * 2) void row_lse_kernel(const bf16* __restrict
       psum = tile_sum(m_run * c2);
     }
     l_run += psum;
+    if constexpr (PARTIALS) {
+      // the block's log2 partial for this query: [bh][kb][q], coalesced over q
+      const float tot = pair_sum(psum);
+      if (g == 0) lpart[((size_t)bh * nqb + kb) * L + q] = fresh ? kNegInf : m_run * c2 + __log2f(tot);
+    }
   }
   const float l_tot = pair_sum(l_run);
   if (g == 0) {
@@ -162,6 +176,65 @@ __global__ __launch_bounds__(BLK * 2) void block_pool_kernel(const bf16* __restr
     }
     out[kb] = s;
   }
+}
+
+// mass[bh, qb, kb] = sum over the block's valid queries of exp2(lp - lse2),
+// for every key block: threads 0..BLK-1 take the queries of one key block,
+// the rest those of the next; sums by a fixed butterfly, then in wave order.
+template <int BLK>
+__global__ __launch_bounds__(256) void mass_from_partials_kernel(const float* __restrict__ lpart,
+                                                                 const float* __restrict__ lse,
+                                                                 float* __restrict__ mass, int L, int seq_len,
+                                                                 int nkb_valid) {
+  constexpr int PER = 256 / BLK;   // key blocks per step
+  constexpr int WPB = BLK / 64;    // waves per key block
+  __shared__ float part[4];
+  const int nqb = L / BLK;
+  const int nkb = nqb;
+  const int item = blockIdx.x;
+  const int bh = item / nqb, qb = item - bh * nqb;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int sub = threadIdx.x / BLK, t = threadIdx.x % BLK;
+  const int q = qb * BLK + t;
+  const bool qvalid = q < seq_len;
+  const float lse2 = qvalid ? lse[(size_t)bh * L + q] * kLog2e : 0.f;
+  float* out = mass + ((size_t)bh * nqb + qb) * nkb;
+  for (int kb0 = 0; kb0 < nkb; kb0 += PER) {
+    const int kb = kb0 + sub;
+    float v = 0.f;
+    if (qvalid && kb < nkb_valid) v = fast_exp2(lpart[((size_t)bh * nqb + kb) * L + q] - lse2);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    __syncthreads();
+    if (lane == 0) part[w] = v;
+    __syncthreads();
+    if (t == 0 && kb < nkb) {
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < WPB; ++i) s += part[sub * WPB + i];
+      out[kb] = s;
+    }
+  }
+}
+
+template <int D, int BLK>
+static hipError_t launch_mass_single_typed(const MassArgs& a, float* lpart, hipStream_t st) {
+  const int items = a.B * a.H * (a.L / BLK);
+  const float c2 = a.scale * kLog2e;
+  hipLaunchKernelGGL((row_lse_kernel<D, BLK, true>), dim3(items), dim3(BLK * 2), 0, st, (const bf16*)a.Q,
+                     (const bf16*)a.K, a.lse, a.H, a.L, a.seq_len, a.nkb_valid, c2, lpart);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((mass_from_partials_kernel<BLK>), dim3(items), dim3(256), 0, st, (const float*)lpart,
+                     (const float*)a.lse, a.mass, a.L, a.seq_len, a.nkb_valid);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_mass_single(const MassArgs& a, float* lpart, hipStream_t st) {
+  if (a.d == 128 && a.block == 128) return launch_mass_single_typed<128, 128>(a, lpart, st);
+  if (a.d == 128 && a.block == 64) return launch_mass_single_typed<128, 64>(a, lpart, st);
+  if (a.d == 64 && a.block == 128) return launch_mass_single_typed<64, 128>(a, lpart, st);
+  return launch_mass_single_typed<64, 64>(a, lpart, st);
 }
 
 template <int D, int BLK>

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define CALIBATT_VERSION 220 /* major * 100 + minor */
+#define CALIBATT_VERSION 230 /* major * 100 + minor */
 
 typedef enum {
   CALIBATT_OK = 0,
@@ -164,6 +164,25 @@ calibatt_status calibatt_transpose_v(const void* V, void* Vt, int B, int H, int 
 calibatt_status calibatt_block_mass(const void* Q, const void* K, int B, int H, int L, int seq_len,
                                     int d, calibatt_dtype dt, int block, float scale,
                                     float* lse_ws, float* mass, void* stream);
+
+/*
+ * The same pooling in one pass over the scores.  While the log-sum-exp is
+ * accumulated, every (key block, query) pair's partial
+ *     lp[b,h,kb,i] = log2 sum_{j in kb, j < seq_len} exp2(scale * log2(e) * q_i . k_j)
+ * is stored in `ws`; then mass[b,h,qb,kb] = sum_{i in qb, i < seq_len}
+ * exp2(lp[b,h,kb,i] - lse_i * log2(e)).  One matrix-core score product and
+ * one exp per (query, key) instead of two.  Arguments as calibatt_block_mass,
+ * plus:
+ *   ws, ws_bytes  calibatt_block_mass_ws_bytes(B, H, L, block) bytes (device),
+ *                 256-byte aligned: the partials as float32 [B, H, L/block, L]
+ *                 (1.34 GB at B = 1, H = 40, L = 32,768, block 128).
+ * The result equals calibatt_block_mass's up to float32 rounding (a few
+ * units in the sixth significant digit); it is bitwise reproducible.
+ */
+calibatt_status calibatt_block_mass_single_pass(const void* Q, const void* K, int B, int H, int L, int seq_len,
+                                                int d, calibatt_dtype dt, int block, float scale, float* lse_ws,
+                                                float* mass, void* ws, size_t ws_bytes, void* stream);
+size_t calibatt_block_mass_ws_bytes(int B, int H, int L, int block);
 
 /*
  * Mask compile: per-prompt top-K key blocks -> cross-prompt agreement -> CSR.

@@ -18,7 +18,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _lib.header_symbols()
-    assert len(names) == 22
+    assert len(names) == 24
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     for n in names:
@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert cal.calibatt_version() == 220
+    assert cal.calibatt_version() == 230
     for code, name in _lib.STATUS.items():
         assert cal.calibatt_status_string(code) != "unknown status"
     assert cal.calibatt_status_string(99) == "unknown status"
@@ -280,3 +280,21 @@ def test_repetition_entry_points_reject(lib):
     assert anchor(heads=None) == 1
     assert anchor(layout=0) == 1
     assert cal.calibatt_last_error() != ""
+
+
+def test_single_pass_mass_rejects(lib):
+    ws = lib.calibatt_block_mass_ws_bytes(1, 40, 32768, 128)
+    assert ws == 40 * 256 * 32768 * 4
+    assert lib.calibatt_block_mass_ws_bytes(1, 1, 100, 128) == 0
+
+    def call(**kw):
+        a = dict(Q=P16, K=P32, B=1, H=40, L=32768, S=32760, d=128, dt=0, block=128, scale=0.1, lse=P48, mass=P64,
+                 ws=V(1 << 30), ws_bytes=ws, stream=None)
+        a.update(kw)
+        return lib.calibatt_block_mass_single_pass(*a.values())
+    assert call(ws=None) == 1
+    assert call(ws=V((1 << 30) + 64)) == 4
+    assert call(ws_bytes=ws - 1) == 6
+    assert call(dt=1) == 7
+    assert call(S=32769) == 2
+    assert call(block=32) == 7

@@ -33,16 +33,23 @@ def mass_tol(m):
     return 1e-3 * np.abs(m) + 1e-6
 
 
-def gpu_mass(q, k, cfg):
+def gpu_mass(q, k, cfg, method="two_pass"):
     Q, K = (to_dev(x, torch.bfloat16) for x in (q, k))
     B, H = q.shape[:2]
     lse = torch.empty(B * H * cfg.L, dtype=torch.float32, device="cuda:0")
     mass = torch.full((B, H, cfg.nqb, cfg.nkb), float("nan"), dtype=torch.float32, device="cuda:0")
-    cal.calibatt_block_mass(Q, K, cfg.block, cfg.scale, lse, mass, cfg.S)
+    if method == "two_pass":
+        cal.calibatt_block_mass(Q, K, cfg.block, cfg.scale, lse, mass, cfg.S)
+    else:
+        cal.calibatt_block_mass_single_pass(Q, K, cfg.block, cfg.scale, lse, mass, cfg.S)
     torch.cuda.synchronize()
     return mass, lse
 
 
+METHODS = ["two_pass", "single_pass"]
+
+
+@pytest.mark.parametrize("method", METHODS)
 @pytest.mark.parametrize("shape", [
     (1, 2, 1024, 1000, 128, 128),
     (2, 1, 768, 768, 128, 128),
@@ -50,13 +57,13 @@ def gpu_mass(q, k, cfg):
     (1, 1, 1024, 1000, 128, 64),
     (1, 1, 1024, 1000, 64, 128),
 ], ids=lambda s: "x".join(map(str, s)))
-def test_block_mass_small(gpu, shape):
+def test_block_mass_small(gpu, shape, method):
     B, H, L, S, d, block = shape
     cfg = Config("m", B=B, H=H, L=L, S=S, d=d, block=block, dtype="bf16", data_seed=40, mask_seed=0,
                  grid=(4, 8, 16))
-    say("case: block mass", shape)
+    say("case: block mass", method, shape)
     q, k, _ = synth.gen_qkv(cfg)
-    mass, lse = gpu_mass(q, k, cfg)
+    mass, lse = gpu_mass(q, k, cfg, method)
     ref = oracle.block_mass(q, k, block, cfg.scale, S)
     got = mass.cpu().numpy().astype(np.float64)
     excess = np.abs(got - ref) - mass_tol(ref)
@@ -68,11 +75,12 @@ def test_block_mass_small(gpu, shape):
     assert np.all(np.isfinite(lse_h[:, :, :S]))
 
 
-def test_block_mass_wan_sampled(gpu):
+@pytest.mark.parametrize("method", METHODS)
+def test_block_mass_wan_sampled(gpu, method):
     cfg = synth.get_config("calib")
-    say("case: block mass at Wan size, sampled query blocks (prompt seed 100)")
+    say("case: block mass at Wan size, sampled query blocks (prompt seed 100)", method)
     q, k = synth.gen_qk(cfg, cfg.prompt_seeds[0])
-    mass, _ = gpu_mass(q, k, cfg)
+    mass, _ = gpu_mass(q, k, cfg, method)
     rng = np.random.default_rng(3)
     items = [(0, 0), (cfg.H - 1, cfg.nqb - 1)] + [(int(rng.integers(cfg.H)), int(rng.integers(cfg.nqb))) for _ in range(6)]
     worst = -1.0
@@ -84,6 +92,20 @@ def test_block_mass_wan_sampled(gpu):
         assert abs(got.sum() - nvalid) < 1e-3 * nvalid
     say(f"  {len(items)} rows, worst excess over tolerance {worst:.2e}")
     assert worst <= 0
+
+
+def test_block_mass_methods_agree_wan(gpu):
+    """Every tile at the Wan shape: the single pass against the two passes
+    (both are float32 sums of the same bf16 products)."""
+    cfg = synth.get_config("calib")
+    q, k = synth.gen_qk(cfg, cfg.prompt_seeds[1])
+    a, la = gpu_mass(q, k, cfg, "two_pass")
+    b, lb = gpu_mass(q, k, cfg, "single_pass")
+    assert torch.equal(la, lb), "the same log-sum-exp pass"
+    d = (a - b).abs()
+    rel = float((d / a.abs().clamp_min(1e-30)).max())
+    say(f"case: block mass methods at Wan size: max abs diff {float(d.max()):.2e}, max rel {rel:.2e}")
+    assert bool((d <= 1e-5 * a.abs() + 1e-9).all())
 
 
 def _masses(rng, P, H, nqb, nkb, kind):
@@ -227,7 +249,7 @@ def certain_keep(ms, K, nv):
     return out
 
 
-def _pipeline(cfg, prompt_seeds, infer_seed, check_rows, tag):
+def _pipeline(cfg, prompt_seeds, infer_seed, check_rows, tag, single_pass=False):
     P = len(prompt_seeds)
     K = math.ceil(cfg.keep_frac * cfg.nkb_valid)
     t = oracle.min_agree_count(cfg.rho, P)
@@ -239,7 +261,10 @@ def _pipeline(cfg, prompt_seeds, infer_seed, check_rows, tag):
     for p, seed in enumerate(prompt_seeds):
         q, k = synth.gen_qk(cfg, seed)
         Q, Kt = (to_dev(x, torch.bfloat16) for x in (q, k))
-        cal.calibatt_block_mass(Q, Kt, cfg.block, cfg.scale, lse, mass[p], cfg.S)
+        if single_pass:
+            cal.calibatt_block_mass_single_pass(Q, Kt, cfg.block, cfg.scale, lse, mass[p], cfg.S)
+        else:
+            cal.calibatt_block_mass(Q, Kt, cfg.block, cfg.scale, lse, mass[p], cfg.S)
         for h, qb in check_rows:
             ref_mass[(p, h, qb)] = oracle.block_mass_rows(q[0, h], k[0, h], cfg.block, cfg.scale, cfg.S, qb)
         del Q, Kt, q, k
@@ -303,7 +328,7 @@ def test_pipeline_small(gpu):
 
 def test_pipeline_wan_sampled(gpu):
     cfg = synth.get_config("calib")
-    say("case: calibrate 8 Wan prompts -> compile -> infer on the 9th, sampled rows")
+    say("case: calibrate 8 Wan prompts (single-pass pooling) -> compile -> infer on the 9th, sampled rows")
     rng = np.random.default_rng(8)
     rows = [(0, 0), (39, 255)] + [(int(rng.integers(cfg.H)), int(rng.integers(cfg.nqb))) for _ in range(4)]
-    _pipeline(cfg, cfg.prompt_seeds, cfg.infer_seed, rows, "wan")
+    _pipeline(cfg, cfg.prompt_seeds, cfg.infer_seed, rows, "wan", single_pass=True)
