@@ -209,6 +209,23 @@ def test_lone_valid_key(gpu):
     assert torch.count_nonzero(O[0, 0, 449:].float()).item() == 0
 
 
+def test_single_valid_token(gpu):
+    """seq_len = 1 in one 128-token block: every valid row attends to key 0 only,
+    so its output is V[0] exactly (after bf16 rounding of O); padded rows are zero."""
+    cfg = small_cfg(H=2, L=128, S=1, d=128, block=128)
+    say("case: seq_len 1")
+    q, k, v = inputs(cfg)
+    rp = np.arange(cfg.rows + 1).astype(np.int32)
+    ci = np.zeros(cfg.rows, np.int32)
+    for persistent in (False, True):
+        O = run_sparse(q, k, v, rp, ci, cfg, persistent=persistent)
+        Od = run_dense(q, k, v, cfg, persistent=persistent)
+        for out in (O, Od):
+            want = torch.from_numpy(v[0, :, 0]).to(torch.bfloat16)
+            assert torch.equal(out[0, :, 0].cpu(), want)
+            assert torch.count_nonzero(out[0, :, 1:].float()).item() == 0
+
+
 def _sample_items(cfg, rng, n):
     items = [(0, 0, 0), (0, cfg.H - 1, cfg.nqb - 1)]
     while len(items) < n:

@@ -44,6 +44,7 @@ def _sim_gpu(q, k, cfg):
     ((3, 4, 20), 64, 3, ()),
     ((2, 5, 13), 128, 2, (1,)),
     ((2, 30, 52), 128, 3, (1,)),
+    ((3, 2, 40), 128, 2, ()),      # two rows per frame: one pair per column
 ])
 def test_similarity_small(gpu, grid, d, H, repeat):
     cfg = _grid_cfg(grid, d, H, seed=40 + d)
