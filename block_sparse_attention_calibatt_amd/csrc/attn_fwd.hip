@@ -187,9 +187,10 @@ __device__ __forceinline__ void tile_dma(int i, __amdgpu_buffer_rsrc_t rk, __amd
 // loads have returned when a DMA needs them.  Past the row's last sub-tile
 // the DMA loads that sub-tile again into the free stage, so every step has
 // the same shape.  Two waves per SIMD (two workgroups per CU) let one wave's
-// softmax run beside the other's products.
+// softmax run beside the other's products; at d = 128 with 64-token blocks
+// the registers allow only one.
 template <int D, int BLK, bool DENSE>
-__global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(
+__global__ __launch_bounds__(BLK * 2, (D == 128 && BLK == 64) ? 1 : 2) void attn_fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ Vt,
     bf16* __restrict__ O, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     const int32_t* __restrict__ work_order, int32_t* __restrict__ queue, int items, int H, int L,
@@ -499,9 +500,6 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
   auto vread = [&](const u32x4* t, int dt, int ks) __attribute__((always_inline)) {
     return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(t) + dt * 32 * 8 * 16 + voffs[ks]);
   };
-
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 one2 = {(bf16)1.f, (bf16)1.f};
 
   // the V^T stages start as zeros, so that a product with zero
   // probabilities never meets a non-finite LDS value
