@@ -58,7 +58,7 @@ SIGNATURES = {
                                           ctypes.POINTER(_i64), _vp, _sz, _vp]),
     "calibatt_skip_ws_bytes": (_sz, [_i32, _i32, _i32]),
     "calibatt_spatial_similarity": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _i32,
-                                           _vp, _vp, _sz, _vp]),
+                                           _vp, _vp, _vp, _sz, _vp]),
     "calibatt_similarity_ws_bytes": (_sz, [_i32, _i32, _i32]),
     "calibatt_select_repetitive_heads": (_i32, [_vp, _i32, _i32, ctypes.c_double, _vp, ctypes.POINTER(_i32), _vp]),
     "calibatt_anchor_attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32,

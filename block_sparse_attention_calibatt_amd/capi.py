@@ -355,9 +355,11 @@ def calibatt_similarity_ws_bytes(B, H, L):
     return int(load().calibatt_similarity_ws_bytes(int(B), int(H), int(L)))
 
 
-def calibatt_spatial_similarity(Q, K, scale, grid, seq_len=None, sim=None, ws=None):
+def calibatt_spatial_similarity(Q, K, scale, grid, seq_len=None, sim=None, ws=None, lse=None):
     """Score per (b, h): mean cosine of the softmax rows of vertically adjacent
-    tokens on the (frames, rows, cols) grid.  Returns sim [B, H] float64."""
+    tokens on the (frames, rows, cols) grid.  Returns sim [B, H] float64.
+    `lse`: the [B*H*L] float32 log-sum-exp a block-mass call left for the same
+    Q, K, scale and seq_len (skips recomputing it), or None."""
     for n, t in (("Q", Q), ("K", K)):
         _dev_tensor(t, n, torch.bfloat16)
     _need(Q.dim() == 4 and K.shape == Q.shape and K.device == Q.device, "Q, K must be [B, H, L, d] alike")
@@ -372,9 +374,12 @@ def calibatt_spatial_similarity(Q, K, scale, grid, seq_len=None, sim=None, ws=No
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=Q.device)
     _dev_tensor(ws, "ws", torch.uint8)
+    if lse is not None:
+        _dev_tensor(lse, "lse", torch.float32)
+        _need(lse.numel() == B * H * L, "lse must have B*H*L entries")
     lib = load()
     check(lib.calibatt_spatial_similarity(_ptr(Q), _ptr(K), B, H, L, seq_len, d, BF16, float(scale), F, R, C,
-                                          _ptr(sim), _ptr(ws), ws.numel(), _stream(Q)))
+                                          _ptr(lse), _ptr(sim), _ptr(ws), ws.numel(), _stream(Q)))
     return sim
 
 

@@ -591,10 +591,12 @@ static calibatt_status check_grid(int frames, int grid_rows, int grid_cols, int 
 
 calibatt_status calibatt_spatial_similarity(const void* Q, const void* K, int B, int H, int L, int seq_len,
                                             int d, calibatt_dtype dt, float scale, int frames, int grid_rows,
-                                            int grid_cols, double* sim, void* ws, size_t ws_bytes, void* stream) {
+                                            int grid_cols, const float* lse_in, double* sim, void* ws,
+                                            size_t ws_bytes, void* stream) {
   if (!Q || !K || !sim || !ws) return fail(CALIBATT_ERR_NULL, "Q, K, sim and ws must be non-NULL");
   if (!aligned(Q, 16) || !aligned(K, 16)) return fail(CALIBATT_ERR_ALIGN, "Q and K must be 16-byte aligned");
   if (!aligned(sim, 8) || !aligned(ws, 256)) return fail(CALIBATT_ERR_ALIGN, "sim must be 8-byte and ws 256-byte aligned");
+  if (lse_in && !aligned(lse_in, 4)) return fail(CALIBATT_ERR_ALIGN, "lse_in must be 4-byte aligned");
   calibatt_status s = check_qkv_shape(B, H, L, seq_len, d, dt, 128);
   if (s != CALIBATT_OK) return s;
   if (dt != CALIBATT_BF16) return fail(CALIBATT_ERR_UNSUPPORTED, "spatial similarity supports bf16 inputs only");
@@ -606,6 +608,7 @@ calibatt_status calibatt_spatial_similarity(const void* Q, const void* K, int B,
   calibatt::SimArgs a;
   a.Q = Q;
   a.K = K;
+  a.lse_in = lse_in;
   a.lse = static_cast<float*>(ws);
   a.part = reinterpret_cast<double*>(static_cast<char*>(ws) + ((size_t)B * H * L * sizeof(float) + 255) / 256 * 256);
   a.sim = sim;

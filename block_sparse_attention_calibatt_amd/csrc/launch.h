@@ -68,7 +68,8 @@ struct HeadList {
 struct SimArgs {
   const void* Q;
   const void* K;
-  float* lse;      // [B, H, L]
+  const float* lse_in;   // [B, H, L] log-sum-exp given by the caller, or null
+  float* lse;      // [B, H, L] (computed here when lse_in is null)
   double* part;    // [B, H, L/128]
   double* sim;     // [B, H]
   int B, H, L, seq_len, d;

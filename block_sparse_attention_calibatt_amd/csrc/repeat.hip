@@ -193,17 +193,22 @@ hipError_t launch_spatial_similarity(const SimArgs& a, hipStream_t st) {
   m.block = 128;
   m.nkb_valid = (a.seq_len + 127) / 128;
   m.scale = a.scale;
-  hipError_t e = launch_row_lse(m, st);
-  if (e != hipSuccess) return e;
+  const float* lse = a.lse_in;
+  if (!lse) {
+    hipError_t e0 = launch_row_lse(m, st);
+    if (e0 != hipSuccess) return e0;
+    lse = a.lse;
+  }
+  hipError_t e;
   const int nqb = a.L / 128;
   const int items = a.B * a.H * nqb;
   const float c2 = a.scale * kLog2e;
   if (a.d == 128)
     hipLaunchKernelGGL((spatial_sim_kernel<128>), dim3(items), dim3(256), 0, st, (const bf16*)a.Q,
-                       (const bf16*)a.K, a.lse, a.part, a.L, a.seq_len, m.nkb_valid, a.cols, a.rows * a.cols, c2);
+                       (const bf16*)a.K, lse, a.part, a.L, a.seq_len, m.nkb_valid, a.cols, a.rows * a.cols, c2);
   else
     hipLaunchKernelGGL((spatial_sim_kernel<64>), dim3(items), dim3(256), 0, st, (const bf16*)a.Q,
-                       (const bf16*)a.K, a.lse, a.part, a.L, a.seq_len, m.nkb_valid, a.cols, a.rows * a.cols, c2);
+                       (const bf16*)a.K, lse, a.part, a.L, a.seq_len, m.nkb_valid, a.cols, a.rows * a.cols, c2);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const double pairs = (double)a.frames * (a.rows - 1) * a.cols;

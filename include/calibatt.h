@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define CALIBATT_VERSION 230 /* major * 100 + minor */
+#define CALIBATT_VERSION 240 /* major * 100 + minor */
 
 typedef enum {
   CALIBATT_OK = 0,
@@ -355,6 +355,10 @@ size_t calibatt_skip_ws_bytes(int T, int H, int nqb);
  * Tokens are n = (f*grid_rows + y)*grid_cols + x on a (frames, grid_rows,
  * grid_cols) grid that covers exactly seq_len tokens.
  *   Q, K     [B, H, L, d] bf16 (device); L a multiple of 128, d in {64, 128}.
+ *   lse_in   [B, H, L] float32 (device) or NULL: the per-query log-sum-exp
+ *            over the same Q, K, scale and seq_len, as calibatt_block_mass
+ *            and calibatt_block_mass_single_pass leave in their lse_ws (the
+ *            pooling of the same prompt); NULL computes it here.
  *   sim      [B, H] float64 output (device).
  *   ws       calibatt_similarity_ws_bytes(B, H, L) bytes (device), 256-byte
  *            aligned: per-query log-sum-exp and per-tile partial sums.
@@ -365,7 +369,8 @@ size_t calibatt_skip_ws_bytes(int T, int H, int nqb);
  */
 calibatt_status calibatt_spatial_similarity(const void* Q, const void* K, int B, int H, int L, int seq_len,
                                             int d, calibatt_dtype dt, float scale, int frames, int grid_rows,
-                                            int grid_cols, double* sim, void* ws, size_t ws_bytes, void* stream);
+                                            int grid_cols, const float* lse_in, double* sim, void* ws,
+                                            size_t ws_bytes, void* stream);
 size_t calibatt_similarity_ws_bytes(int B, int H, int L);
 
 /*

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert cal.calibatt_version() == 230
+    assert cal.calibatt_version() == 240
     for code, name in _lib.STATUS.items():
         assert cal.calibatt_status_string(code) != "unknown status"
     assert cal.calibatt_status_string(99) == "unknown status"
@@ -234,7 +234,7 @@ def test_repetition_entry_points_reject(lib):
 
     def sim(**kw):
         a = dict(Q=P16, K=P32, B=1, H=40, L=32768, S=32760, d=128, dt=0, scale=0.1, F=21, R=30, C=52,
-                 sim=V(1 << 20), ws=V(1 << 30), ws_bytes=ws, stream=None)
+                 lse=None, sim=V(1 << 20), ws=V(1 << 30), ws_bytes=ws, stream=None)
         a.update(kw)
         return lib.calibatt_spatial_similarity(*a.values())
     assert sim(Q=None) == 1
@@ -245,6 +245,7 @@ def test_repetition_entry_points_reject(lib):
     assert sim(R=1, C=52 * 30) == 2          # one row per frame: no pairs
     assert sim(ws_bytes=ws - 1) == 6
     assert sim(L=32760) == 2
+    assert sim(lse=V((1 << 21) + 2)) == 4
 
     n = ctypes.c_int32(0)
     heads = np.zeros(4, dtype=np.int32)

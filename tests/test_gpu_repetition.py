@@ -80,6 +80,23 @@ def test_similarity_wan_full_size(gpu):
     assert got[0, 29] > max(got[0, h] for h in others)
 
 
+def test_similarity_with_pooling_lse(gpu):
+    """The log-sum-exp the single-pass pooling leaves for the same prompt gives
+    the same scores, bit for bit, as the similarity's own pass."""
+    grid = (2, 30, 52)
+    cfg = _grid_cfg(grid, 128, 3, seed=95)
+    q, k, _ = inputs(cfg)
+    Q, K = to_dev(q, torch.bfloat16), to_dev(k, torch.bfloat16)
+    lse = torch.empty(cfg.H * cfg.L, dtype=torch.float32, device="cuda:0")
+    mass = torch.empty((cfg.H, cfg.nqb, cfg.nkb), dtype=torch.float32, device="cuda:0")
+    cal.calibatt_block_mass_single_pass(Q, K, 128, cfg.scale, lse, mass, cfg.S)
+    a = cal.calibatt_spatial_similarity(Q, K, cfg.scale, grid, cfg.S)
+    b = cal.calibatt_spatial_similarity(Q, K, cfg.scale, grid, cfg.S, lse=lse)
+    torch.cuda.synchronize()
+    say(f"case: similarity with the pooling's lse: {a.cpu().numpy().tolist()}")
+    assert torch.equal(a, b)
+
+
 def test_select_golden(gpu):
     g = json.load(open(os.path.join(GOLDEN, "spatial_repetition.json")))["selection"]
     sim = torch.tensor(g["sim"], dtype=torch.float64, device="cuda:0")
