@@ -43,21 +43,19 @@ __device__ __forceinline__ int source_anchor(int n, int R, int C, int k) {
   return (f * k + g) * C + x;
 }
 
-// One thread copies a 64-byte run of one output row (four 16-byte units).
+// One thread copies a 64-byte run of one output row (four 16-byte units);
+// grid.y enumerates the (batch entry, listed head) pairs, so the index
+// arithmetic stays in 32 bits.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void anchor_broadcast_kernel(const T* __restrict__ Oa, T* __restrict__ O,
-                                                               HeadList hl, int B, int H, int L, int Lq,
-                                                               int seq_len, int R, int C, int k) {
+                                                               HeadList hl, int H, int L, int Lq, int seq_len,
+                                                               int R, int C, int k) {
   constexpr int U = D * (int)sizeof(T) / 16;   // 16-byte units per row
   constexpr int RUNS = U / 4;                  // 64-byte runs per row
-  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long total = (long long)B * hl.n * L * RUNS;
-  if (t >= total) return;
-  const int run = (int)(t % RUNS);
-  const long long row = t / RUNS;
-  const int n = (int)(row % L);
-  const long long rest = row / L;
-  const int slot = (int)(rest % hl.n), b = (int)(rest / hl.n);
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= L * RUNS) return;
+  const int n = t / RUNS, run = t % RUNS;
+  const int slot = blockIdx.y % hl.n, b = blockIdx.y / hl.n;
   const size_t bh = (size_t)b * H + hl.h[slot];
   u32x4 v[4] = {};
   if (n < seq_len) {
@@ -220,10 +218,9 @@ hipError_t launch_spatial_similarity(const SimArgs& a, hipStream_t st) {
 template <int D>
 static hipError_t anchor_broadcast(const AnchorArgs& a, hipStream_t st) {
   constexpr int RUNS = D * 2 / 64;
-  const long long threads = (long long)a.B * a.heads.n * a.L * RUNS;
-  const unsigned grid = (unsigned)((threads + 255) / 256);
-  hipLaunchKernelGGL((anchor_broadcast_kernel<bf16, D>), dim3(grid), dim3(256), 0, st, (const bf16*)a.Oa, (bf16*)a.O,
-                     a.heads, a.B, a.H, a.L, a.Lq, a.seq_len, a.rows, a.cols, a.k);
+  const dim3 grid((unsigned)((a.L * RUNS + 255) / 256), (unsigned)(a.B * a.heads.n));
+  hipLaunchKernelGGL((anchor_broadcast_kernel<bf16, D>), grid, dim3(256), 0, st, (const bf16*)a.Oa, (bf16*)a.O,
+                     a.heads, a.H, a.L, a.Lq, a.seq_len, a.rows, a.cols, a.k);
   return hipGetLastError();
 }
 
