@@ -113,9 +113,10 @@ def test_all_kept_sparse_is_dense_bitwise(gpu):
     assert torch.equal(a, b) and torch.equal(a, c)
 
 
-def test_schedule_invariance_bitwise(gpu):
-    cfg = small_cfg(H=4, L=2048, S=2040)
-    say("case: work order / persistence invariance")
+@pytest.mark.parametrize("B", [1, 2])
+def test_schedule_invariance_bitwise(gpu, B):
+    cfg = small_cfg(B=B, H=4, L=2048, S=2040)
+    say(f"case: work order / persistence invariance, B={B}")
     q, k, v = inputs(cfg)
     rng = np.random.default_rng(9)
     rp, ci = synth.random_csr(rng, cfg.H, cfg.nqb, cfg.nkb_valid, 0.3, empty_rows=2, full_rows=2)
