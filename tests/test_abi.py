@@ -6,6 +6,7 @@ import subprocess
 
 import numpy as np
 import pytest
+from hypothesis import given, settings, strategies as st
 
 import block_sparse_attention_calibatt_amd as cal
 from block_sparse_attention_calibatt_amd import _lib
@@ -226,6 +227,41 @@ def test_validate_csr(lib):
             cal.calibatt_validate_csr(rp, ci, 3, 8)
         assert e.value.status == 5 or e.value.status == 1
 
+
+
+@settings(max_examples=200, deadline=None, derandomize=True, database=None)
+@given(st.integers(1, 6), st.integers(1, 10), st.data())
+def test_validate_csr_property(lib, rows, nkb, data):
+    """Random kept-block lists: a well-formed list is accepted, and each single
+    defect (a column out of range, a repeated or descending column, a row_ptr
+    that starts off zero or decreases) is rejected on the host."""
+    lists = [sorted(data.draw(st.sets(st.integers(0, nkb - 1), max_size=nkb))) for _ in range(rows)]
+    rp = np.concatenate([[0], np.cumsum([len(c) for c in lists])]).astype(np.int32)
+    ci = np.array([c for row in lists for c in row], dtype=np.int32)
+    cal.calibatt_validate_csr(rp, ci, rows, nkb)
+    bad = []
+    if len(ci):
+        i = data.draw(st.integers(0, len(ci) - 1))
+        for val in (nkb, -1, nkb + 1000):
+            c2 = ci.copy()
+            c2[i] = val
+            bad.append((rp, c2))
+        r = int(np.searchsorted(rp, i, side="right")) - 1        # the row holding entry i
+        if i > rp[r]:
+            c2 = ci.copy()
+            c2[i] = c2[i - 1]                                     # repeated column
+            bad.append((rp, c2))
+        rp2 = rp.copy()
+        rp2[0] = 1
+        bad.append((rp2, ci))
+    if rows >= 2 and rp[1] > 0:
+        rp2 = rp.copy()
+        rp2[1] = rp[2] + 1                                        # row 1 would end before it starts
+        bad.append((rp2, ci))
+    for brp, bci in bad:
+        with pytest.raises(cal.CalibattError) as e:
+            cal.calibatt_validate_csr(brp, bci, rows, nkb)
+        assert e.value.status == 5
 
 def test_repetition_entry_points_reject(lib):
     ws = lib.calibatt_similarity_ws_bytes(1, 40, 32768)
