@@ -393,11 +393,15 @@ def main():
         e[3].record(stream)
         torch.cuda.synchronize()
         pool_ms = e[0].elapsed_time(e[1]) / 8
+        # the single pass makes one score product per (query, key): 2*B*H*S^2*d FLOP per prompt
+        single_tf = 2.0 * cfg.B * cfg.H * cfg.S * cfg.S * cfg.d / (single_ms * 1e-3) / 1e12
         extra["calib"] = {
             "block_mass_ms_per_prompt": round(pool_ms, 3),
             "block_mass_qk_tflops": round(2 * 2.0 * cfg.B * cfg.H * cfg.S * cfg.S * cfg.d / (pool_ms * 1e-3) / 1e12, 2),
             "block_mass_single_pass_ms_per_prompt": round(single_ms, 3),
             "block_mass_single_pass_max_rel_diff": single_diff,
+            "block_mass_single_pass_roofline": {"bound": "mfma", "achieved": round(single_tf, 1), "peak": PEAK_BF16_TFLOPS,
+                                                "unit": "TFLOP/s", "frac": round(single_tf / PEAK_BF16_TFLOPS, 4)},
             "compile_ms_8_prompts_incl_sync": round(compile_s * 1e3, 3),
             "schedule_ms": round(e[2].elapsed_time(e[3]), 4),
             "compiled_density": round(ci.numel() / (cfg.rows * cfg.nkb_valid), 4),
