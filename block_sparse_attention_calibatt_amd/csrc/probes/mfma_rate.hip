@@ -8,7 +8,12 @@
 // random N(0,1) bf16 operands (the data the attention kernel multiplies).
 // Under sustained random-operand products the GPU lowers its clock to stay
 // within its power limit, so the second rate, not the vendor figure, is what
-// a matrix-core-bound kernel can reach.  Prints one JSON line.
+// a matrix-core-bound kernel can reach.
+//
+// Also the vector pipe's issue interval for the three instructions the
+// calibration pooling spends per score (exp2, fma, add): two waves per SIMD,
+// 32 independent values per lane, cycles per wave-wide instruction per SIMD
+// from s_memtime.  Prints one JSON line.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -61,6 +66,38 @@ __global__ __launch_bounds__(kThreads) void mfma_rate_kernel(const bf16x8* __res
     clk[blockIdx.x * 2] = t1 - t0;
     clk[blockIdx.x * 2 + 1] = r1 - r0;
   }
+}
+
+// OP 0: v_exp_f32, 1: v_fma_f32, 2: v_add_f32; 32 per lane per iteration.
+template <int OP>
+__global__ __launch_bounds__(kThreads) void valu_rate_kernel(float* __restrict__ out,
+                                                             unsigned long long* __restrict__ clk, int iters) {
+  const int lane = threadIdx.x & 63;
+  float x[32];
+#pragma unroll
+  for (int e = 0; e < 32; ++e) x[e] = -(lane * 0.001f + e * 0.01f);
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+    // the inputs are opaque to the compiler, so nothing leaves the loop
+#pragma unroll
+    for (int e = 0; e < 32; e += 8)
+      asm volatile("" : "+v"(x[e]), "+v"(x[e + 1]), "+v"(x[e + 2]), "+v"(x[e + 3]), "+v"(x[e + 4]),
+                   "+v"(x[e + 5]), "+v"(x[e + 6]), "+v"(x[e + 7]));
+    float y[32];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      if (OP == 0) y[e] = __builtin_amdgcn_exp2f(x[e]);
+      else if (OP == 1) y[e] = fmaf(x[e], 1.0001f, -0.5f);
+      else y[e] = x[e] + x[(e + 1) & 31];
+    }
+#pragma unroll
+    for (int e = 0; e < 32; e += 8)
+      asm volatile("" ::"v"(y[e]), "v"(y[e + 1]), "v"(y[e + 2]), "v"(y[e + 3]), "v"(y[e + 4]), "v"(y[e + 5]),
+                   "v"(y[e + 6]), "v"(y[e + 7]));
+  }
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  out[(size_t)blockIdx.x * kThreads + threadIdx.x] = x[0] + x[31];
+  if (threadIdx.x == 0 && blockIdx.x < 8) clk[blockIdx.x * 2] = t1 - t0;
 }
 
 int main(int argc, char** argv) {
@@ -117,9 +154,26 @@ int main(int argc, char** argv) {
     tf[mode] = flops / (ms * 1e-3) / 1e12;
     ghz[mode] = g;
   }
+  // vector pipe: cycles per wave-wide instruction per SIMD (two waves issue 32 each per iteration)
+  double vcyc[3];
+  const int viters = 4000;
+  for (int op = 0; op < 3; ++op) {
+    auto kern = op == 0 ? valu_rate_kernel<0> : (op == 1 ? valu_rate_kernel<1> : valu_rate_kernel<2>);
+    for (int rep = 0; rep < 2; ++rep) {
+      hipLaunchKernelGGL(kern, dim3(ncu), dim3(kThreads), 0, 0, out, clk, viters);
+      CHECK(hipGetLastError());
+      CHECK(hipDeviceSynchronize());
+    }
+    unsigned long long c[16];
+    CHECK(hipMemcpy(c, clk, sizeof(c), hipMemcpyDeviceToHost));
+    double s = 0.0;
+    for (int i = 0; i < 8; ++i) s += (double)c[2 * i] / 8.0;
+    vcyc[op] = s / viters / 64.0;
+  }
   printf("{\"zero_operands_tflops\": %.1f, \"zero_operands_clock_ghz\": %.3f, "
-         "\"random_operands_tflops\": %.1f, \"random_operands_clock_ghz\": %.3f, \"cus\": %d}\n",
-         tf[0], ghz[0], tf[1], ghz[1], ncu);
+         "\"random_operands_tflops\": %.1f, \"random_operands_clock_ghz\": %.3f, \"cus\": %d, "
+         "\"valu_cycles_per_wave_instruction\": {\"exp2\": %.2f, \"fma\": %.2f, \"add\": %.2f}}\n",
+         tf[0], ghz[0], tf[1], ghz[1], ncu, vcyc[0], vcyc[1], vcyc[2]);
   CHECK(hipFree(in));
   CHECK(hipFree(out));
   CHECK(hipFree(clk));
