@@ -31,12 +31,6 @@
 
 namespace calibatt {
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
 // s_waitcnt immediate (gfx9 encoding) for vmcnt(N) with expcnt and lgkmcnt
 // left unconstrained.  Written with the builtin rather than inline asm so that
 // the compiler's own wait insertion knows which DMA has landed.

@@ -35,7 +35,6 @@ __global__ __launch_bounds__(BLK * 2) void row_lse_kernel(const bf16* __restrict
                                                           float* __restrict__ lse, int H, int L,
                                                           int seq_len, int nkb_valid, float c2,
                                                           float* __restrict__ lpart = nullptr) {
-  constexpr int NT = BLK * 2;
   constexpr int KT = BLK / 32;
   constexpr int DS = D / 16;
   __shared__ u32x4 ldsK[BLK * D / 8];
@@ -46,6 +45,8 @@ __global__ __launch_bounds__(BLK * 2) void row_lse_kernel(const bf16* __restrict
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 5, c = lane & 31;
   const int q = qb * BLK + 32 * w + c;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + base, (uint32_t)L * D * 2);
 
   bf16x8 qreg[DS];
 #pragma unroll
@@ -57,7 +58,8 @@ __global__ __launch_bounds__(BLK * 2) void row_lse_kernel(const bf16* __restrict
   bool fresh = true;
   for (int kb = 0; kb < nkb_valid; ++kb) {
     __syncthreads();
-    load_k_tile<D, BLK, NT>(K + base + (size_t)kb * BLK * D, ldsK);
+    dma_k_tile<D, BLK>(rk, kb * BLK, ldsK, wu, lane);
+    wait_vm_all();
     __syncthreads();
     f32x16 sacc[KT];
     qk_tile<D, BLK>(ldsK, qreg, sacc, g, c);
@@ -130,6 +132,8 @@ __global__ __launch_bounds__(BLK * 2) void block_pool_kernel(const bf16* __restr
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 5, c = lane & 31;
   const int q = qb * BLK + 32 * w + c;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + base, (uint32_t)L * D * 2);
   const bool qvalid = q < seq_len;
   const float lse2 = qvalid ? lse[(size_t)bh * L + q] * kLog2e : 0.f;
 
@@ -140,7 +144,8 @@ __global__ __launch_bounds__(BLK * 2) void block_pool_kernel(const bf16* __restr
 
   for (int kb = 0; kb < nkb_valid; ++kb) {
     __syncthreads();
-    load_k_tile<D, BLK, NT>(K + base + (size_t)kb * BLK * D, ldsK);
+    dma_k_tile<D, BLK>(rk, kb * BLK, ldsK, wu, lane);
+    wait_vm_all();
     __syncthreads();
     f32x16 sacc[KT];
     qk_tile<D, BLK>(ldsK, qreg, sacc, g, c);

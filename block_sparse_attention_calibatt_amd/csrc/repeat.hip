@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void spatial_sim_kernel(const bf16* __restrict
                                                           const float* __restrict__ lse,
                                                           double* __restrict__ part, int L, int seq_len,
                                                           int nkb_valid, int C, int RC, float c2) {
-  constexpr int BLK = 128, NT = 256, DS = D / 16, CH = D / 8;
+  constexpr int BLK = 128, DS = D / 16, CH = D / 8;
   __shared__ u32x4 ldsK[BLK * D / 8];
   __shared__ double wsum[4];
   const int nqb = L / BLK;
@@ -104,6 +104,8 @@ __global__ __launch_bounds__(256) void spatial_sim_kernel(const bf16* __restrict
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 5, c = lane & 31;
   const int q = qt * BLK + 32 * w + c;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + base, (uint32_t)L * D * 2);
   // a token counts when the row below it lies in the same frame
   const bool prim = q < seq_len && (q % RC) < RC - C;
   const int q2 = prim ? q + C : q;
@@ -120,7 +122,8 @@ __global__ __launch_bounds__(256) void spatial_sim_kernel(const bf16* __restrict
   float dot = 0.f, n1 = 0.f, n2 = 0.f;
   for (int kb = 0; kb < nkb_valid; ++kb) {
     __syncthreads();
-    load_k_tile<D, BLK, NT>(K + base + (size_t)kb * BLK * D, ldsK);
+    dma_k_tile<D, BLK>(rk, kb * BLK, ldsK, wu, lane);
+    wait_vm_all();
     __syncthreads();
     const int k0 = kb * BLK;
 #pragma unroll

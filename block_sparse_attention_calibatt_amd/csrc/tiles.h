@@ -68,24 +68,38 @@ __device__ __forceinline__ int qk_row_perm(int c) {
 // Key (within a 32-key slice) held in accumulator register r by lane half g.
 __device__ __forceinline__ int slice_key(int r, int g) { return 16 * (r >> 3) + 8 * g + (r & 7); }
 
-// K tile [BLK keys][D] bf16, row-major in HBM -> swizzled LDS.  NT threads.
-template <int D, int BLK, int NT>
-__device__ __forceinline__ void load_k_tile(const bf16* __restrict__ src, u32x4* __restrict__ lds) {
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer resource over `bytes` bytes at base: loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// K tile [BLK keys][D] bf16 (row-major in the slab behind rk, keys k0 ..
+// k0+BLK-1) -> swizzled LDS (the chunk_index layout), by LDS DMA with no
+// register staging.  Instruction m writes LDS units 64m .. 64m+63, i.e. key
+// rows m*(64/CH) ..; wave w of the BLK/32 waves issues m = w, w + BLK/32, ...
+// The caller waits (s_waitcnt vmcnt) and then synchronises the workgroup
+// before reading the tile.
+template <int D, int BLK>
+__device__ __forceinline__ void dma_k_tile(__amdgpu_buffer_rsrc_t rk, int k0, u32x4* lds, int w, int lane) {
   constexpr int CH = D / 8;
-  constexpr int PER = BLK * CH / NT;
-  static_assert(PER * NT == BLK * CH, "tile must split evenly over the threads");
-  u32x4 r[PER];
+  constexpr int NW = BLK / 32;
+  constexpr int NI = BLK * CH / 64;
+  static_assert(NI % NW == 0, "tile must split evenly over the waves");
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int idx = threadIdx.x + i * NT;
-    r[i] = *reinterpret_cast<const u32x4*>(src + (idx / CH) * D + (idx % CH) * 8);
-  }
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int idx = threadIdx.x + i * NT;
-    lds[chunk_index<CH>(idx / CH, idx % CH)] = r[i];
+  for (int i = 0; i < NI / NW; ++i) {
+    const int m = w + NW * i;
+    const int row = m * (64 / CH) + lane / CH;
+    const int voff = (lane / CH) * D * 2 + (((lane % CH) ^ swz<CH>(row)) * 16);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(lds + 64 * m), 16, voff, k0 * D * 2 + m * 1024, 0, 0);
   }
 }
+
+// s_waitcnt vmcnt(0) with expcnt and lgkmcnt left unconstrained (gfx9
+// encoding), written with the builtin so that the compiler's own wait
+// insertion knows the DMA has landed.
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); }
 
 // S^T for one wave: BLK keys x 32 queries, as BLK/32 accumulators of 32x32.
 template <int D, int BLK>
