@@ -73,6 +73,9 @@ def test_block_mass_small(gpu, shape, method):
     lse_h = lse.cpu().numpy().reshape(B, H, L)
     assert np.all(np.isneginf(lse_h[:, :, S:])), "padded rows hold -inf"
     assert np.all(np.isfinite(lse_h[:, :, :S]))
+    # fixed reduction order: a second run gives the same bits
+    mass2, lse2 = gpu_mass(q, k, cfg, method)
+    assert torch.equal(mass2, mass) and torch.equal(lse2, lse), "repeat run"
 
 
 @pytest.mark.parametrize("method", METHODS)
