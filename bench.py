@@ -1,11 +1,12 @@
 """Benchmark: block-sparse attention forward at the Wan 2.1 14B attention shape.
 
 One step = one inference call of the hot path on the GPU: look up the mask
-set of the timestep in the resident bank, lay V out as V^T in a preallocated
-workspace (the attention kernel reads V transposed) and run the block-sparse
-forward (persistent launch, longest-row-first order).  Inputs are resident
-in HBM before the timed region starts.  The roofline figures are for the
-attention kernel alone, timed with events on the launch stream around it.  The metric is effective kept-block
+set of the timestep in the resident bank and run the block-sparse forward on
+Q, K, V as they lie ([B, H, L, d]; persistent launch, longest-row-first
+order).  Inputs are resident in HBM before the timed region starts.  The
+roofline figures are for the attention kernel, timed with events on the
+launch stream around the call (which also enqueues a 4-microsecond
+queue-reset kernel).  The metric is effective kept-block
 throughput: 4 * block^2 * d FLOP per kept (query block, key block) tile,
 counting full tiles, divided by the step time.  Also reported: the dense
 forward on the same inputs (speedup = t_dense / t_sparse, the ratio the pages
@@ -221,35 +222,28 @@ def main():
     O = torch.empty_like(Q)
     bank = cal.MaskBank(sets, cfg.H, cfg.nqb, cfg.nkb_valid, dev)
     qws = cal.new_queue(dev)
-    VT = cal.new_vt(Q)
     torch.cuda.synchronize()
     gen_s = time.perf_counter() - t_gen
 
     stream = torch.cuda.current_stream(dev)
 
-    def step(i, mid=None):
+    def step(i):
         rp, ci, wo, _ = bank.lookup(i % len(bank))
-        cal.calibatt_transpose_v(V, VT, cfg.S)
-        if mid is not None:
-            mid.record(stream)
-        cal.calibatt_sparse_attn_fwd(Q, K, VT, O, rp, ci, cfg.block, cfg.scale, cfg.S, wo, qws,
-                                     v_transposed=True)
+        cal.calibatt_sparse_attn_fwd(Q, K, V, O, rp, ci, cfg.block, cfg.scale, cfg.S, wo, qws)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    mid = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev[0].record(stream)
     for i in range(args.steps):
-        step(i, mid[i])
+        step(i)
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = [mid[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
-    transpose_ms = [ev[i].elapsed_time(mid[i]) for i in range(args.steps)]
+    launch_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
     ms = ev[0].elapsed_time(ev[-1]) / args.steps
     nnz_steps = [int(bank.nnz[i % len(bank)]) for i in range(args.steps)]
     flops = tile_flops(cfg.block, cfg.d) * cfg.B * float(np.mean(nnz_steps))
@@ -267,7 +261,7 @@ def main():
     c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     rp0, ci0, wo0, _ = bank.lookup(0)
     c0.record(stream)
-    cal.calibatt_sparse_attn_fwd(Q, K, VT, O, rp0, ci0, cfg.block, cfg.scale, cfg.S, wo0, qws, v_transposed=True)
+    cal.calibatt_sparse_attn_fwd(Q, K, V, O, rp0, ci0, cfg.block, cfg.scale, cfg.S, wo0, qws)
     c1.record(stream)
     torch.cuda.synchronize()
     del scratch
@@ -291,13 +285,11 @@ def main():
             sb = cal.MaskBank([m], cfg.H, cfg.nqb, cfg.nkb_valid, dev, validate=False)
             srp, sci, swo, _ = sb.lookup(0)
             for _ in range(2):
-                cal.calibatt_sparse_attn_fwd(Q, K, VT, O, srp, sci, cfg.block, cfg.scale, cfg.S, swo, qws,
-                                             v_transposed=True)
+                cal.calibatt_sparse_attn_fwd(Q, K, V, O, srp, sci, cfg.block, cfg.scale, cfg.S, swo, qws)
             s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             s0.record(stream)
             for _ in range(5):
-                cal.calibatt_sparse_attn_fwd(Q, K, VT, O, srp, sci, cfg.block, cfg.scale, cfg.S, swo, qws,
-                                             v_transposed=True)
+                cal.calibatt_sparse_attn_fwd(Q, K, V, O, srp, sci, cfg.block, cfg.scale, cfg.S, swo, qws)
             s1.record(stream)
             torch.cuda.synchronize()
             t_ms = s0.elapsed_time(s1) / 5
@@ -309,12 +301,12 @@ def main():
 
     if not args.no_dense:
         for _ in range(2):
-            cal.calibatt_dense_attn_fwd(Q, K, V, O, cfg.block, cfg.scale, cfg.S, qws, vt_ws=VT)
+            cal.calibatt_dense_attn_fwd(Q, K, V, O, cfg.block, cfg.scale, cfg.S, qws)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         nd = 5
         e0.record(stream)
         for _ in range(nd):
-            cal.calibatt_dense_attn_fwd(Q, K, V, O, cfg.block, cfg.scale, cfg.S, qws, vt_ws=VT)
+            cal.calibatt_dense_attn_fwd(Q, K, V, O, cfg.block, cfg.scale, cfg.S, qws)
         e1.record(stream)
         torch.cuda.synchronize()
         dense_ms = e0.elapsed_time(e1) / nd
@@ -324,8 +316,8 @@ def main():
         extra["speedup_vs_dense"] = round(speedup(dense_ms, ms), 3)
 
     if not args.no_anchor and cfg.grid is not None:
-        # anchor rows (spatial-repetition heads) for every head, V^T given as in
-        # the step: the workload of the pages' anchor-row table
+        # anchor rows (spatial-repetition heads) for every head: the workload
+        # of the pages' anchor-row table
         F, R, C = cfg.grid
         heads = list(range(cfg.H))
         nkv = cfg.nkb_valid
@@ -334,14 +326,12 @@ def main():
             aws = torch.empty(cal.calibatt_anchor_ws_bytes(cfg.B, cfg.H, F, C, ka, cfg.d), dtype=torch.uint8,
                               device=dev)
             for _ in range(2):
-                cal.calibatt_anchor_attn_fwd(Q, K, VT, O, heads, cfg.grid, ka, cfg.scale, cfg.S, qws,
-                                             v_transposed=True, ws=aws)
+                cal.calibatt_anchor_attn_fwd(Q, K, V, O, heads, cfg.grid, ka, cfg.scale, cfg.S, qws, ws=aws)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             na = 5
             e0.record(stream)
             for _ in range(na):
-                cal.calibatt_anchor_attn_fwd(Q, K, VT, O, heads, cfg.grid, ka, cfg.scale, cfg.S, qws,
-                                             v_transposed=True, ws=aws)
+                cal.calibatt_anchor_attn_fwd(Q, K, V, O, heads, cfg.grid, ka, cfg.scale, cfg.S, qws, ws=aws)
             e1.record(stream)
             torch.cuda.synchronize()
             a_ms = e0.elapsed_time(e1) / na
@@ -510,10 +500,6 @@ def main():
             "measured_mfma_rate": peak_probe,
             "frac_of_random_operand_rate": (round(achieved / peak_probe["random_operands_tflops"], 4)
                                             if peak_probe else None),
-        },
-        "transpose_v": {
-            "avg_ms": round(float(np.mean(transpose_ms)), 4),
-            "GB/s": round(2 * V.numel() * 2 / (float(np.mean(transpose_ms)) * 1e-3) / 1e9, 1),
         },
         "cpu_baseline": cpu,
         "cpu_oracle_other_calls": cpu_more,

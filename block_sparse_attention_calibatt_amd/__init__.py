@@ -12,7 +12,6 @@ their anchor rows.  Build the library with
 from ._lib import CalibattError, LIB_PATH, load
 from .capi import (
     new_queue,
-    new_vt,
     calibatt_transpose_v,
     calibatt_sparse_attn_fwd,
     calibatt_dense_attn_fwd,
@@ -45,7 +44,6 @@ __all__ = [
     "LIB_PATH",
     "load",
     "new_queue",
-    "new_vt",
     "calibatt_transpose_v",
     "calibatt_sparse_attn_fwd",
     "calibatt_dense_attn_fwd",

@@ -34,9 +34,9 @@ _sz = ctypes.c_size_t
 
 SIGNATURES = {
     "calibatt_sparse_attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _f32, _i32, _i32, _i32,
-                                        _i32, _i32, _i32, _vp, _vp, _i64, _i32, _vp, _vp]),
+                                        _i32, _i32, _i32, _vp, _vp, _i64, _i32, _vp]),
     "calibatt_dense_attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _i32, _f32, _i32, _i32, _i32, _i32, _i32,
-                                       _i32, _vp, _i32, _vp, _vp]),
+                                       _i32, _vp, _i32, _vp]),
     "calibatt_transpose_v": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "calibatt_block_mass": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp,
                                    _vp]),
@@ -62,7 +62,7 @@ SIGNATURES = {
     "calibatt_similarity_ws_bytes": (_sz, [_i32, _i32, _i32]),
     "calibatt_select_repetitive_heads": (_i32, [_vp, _i32, _i32, ctypes.c_double, _vp, ctypes.POINTER(_i32), _vp]),
     "calibatt_anchor_attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32,
-                                        _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _sz, _vp]),
+                                        _i32, _i32, _i32, _i32, _vp, _i32, _vp, _sz, _vp]),
     "calibatt_anchor_ws_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "calibatt_build_schedule": (_i32, [_vp, _i32, _i32, _vp, _vp]),
     "calibatt_validate_csr": (_i32, [_vp, _vp, _i32, _i32, _i64]),

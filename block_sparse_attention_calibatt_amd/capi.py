@@ -68,26 +68,9 @@ def _qkv(Q, K, V, O, v_transposed=False):
     return Q.shape
 
 
-def new_vt(Q):
-    """A V^T workspace [B, H, d, L] for the attention entry points (V given as [B, H, L, d])."""
-    B, H, L, d = Q.shape
-    return torch.empty((B, H, d, L), dtype=Q.dtype, device=Q.device)
-
-
-def _vt_args(Q, v_transposed, vt_ws):
-    """(layout code, workspace) for the C call; allocates the workspace if none is given."""
-    if v_transposed:
-        return V_BHDL, None
-    if vt_ws is None:
-        vt_ws = new_vt(Q)
-    _dev_tensor(vt_ws, "vt_ws", Q.dtype)
-    _need(vt_ws.numel() == Q.numel() and vt_ws.device == Q.device, "vt_ws must hold B*H*d*L elements on Q's device")
-    return V_BHLD, vt_ws
-
-
 def calibatt_sparse_attn_fwd(Q, K, V, O, row_ptr, col_idx, block, scale, seq_len=None,
-                             work_order=None, queue_ws=None, v_transposed=False, vt_ws=None):
-    """V is [B, H, L, d], or V^T [B, H, d, L] with v_transposed=True; vt_ws receives V^T."""
+                             work_order=None, queue_ws=None, v_transposed=False):
+    """V is [B, H, L, d], or V^T [B, H, d, L] with v_transposed=True."""
     B, H, L, d = _qkv(Q, K, V, O, v_transposed)
     seq_len = L if seq_len is None else int(seq_len)
     _dev_tensor(row_ptr, "row_ptr", torch.int32)
@@ -99,25 +82,22 @@ def calibatt_sparse_attn_fwd(Q, K, V, O, row_ptr, col_idx, block, scale, seq_len
         _dev_tensor(work_order, "work_order", torch.int32)
         _need(work_order.numel() == rows + PARTS + 1, f"work_order must have H*nqb+9 = {rows + PARTS + 1} entries")
     _queue(queue_ws)
-    layout, vt_ws = _vt_args(Q, v_transposed, vt_ws)
     lib = load()
     check(lib.calibatt_sparse_attn_fwd(
         _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(row_ptr), _ptr(col_idx), int(block), float(scale),
         B, H, L, seq_len, d, _DT[Q.dtype], _ptr(work_order), _ptr(queue_ws), col_idx.numel(),
-        layout, _ptr(vt_ws), _stream(Q)))
+        V_BHDL if v_transposed else V_BHLD, _stream(Q)))
     return O
 
 
-def calibatt_dense_attn_fwd(Q, K, V, O, block, scale, seq_len=None, queue_ws=None, v_transposed=False,
-                            vt_ws=None):
+def calibatt_dense_attn_fwd(Q, K, V, O, block, scale, seq_len=None, queue_ws=None, v_transposed=False):
     B, H, L, d = _qkv(Q, K, V, O, v_transposed)
     seq_len = L if seq_len is None else int(seq_len)
     _queue(queue_ws)
-    layout, vt_ws = _vt_args(Q, v_transposed, vt_ws)
     lib = load()
     check(lib.calibatt_dense_attn_fwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), int(block), float(scale),
-                                      B, H, L, seq_len, d, _DT[Q.dtype], _ptr(queue_ws), layout,
-                                      _ptr(vt_ws), _stream(Q)))
+                                      B, H, L, seq_len, d, _DT[Q.dtype], _ptr(queue_ws),
+                                      V_BHDL if v_transposed else V_BHLD, _stream(Q)))
     return O
 
 
@@ -401,7 +381,7 @@ def calibatt_anchor_ws_bytes(B, H, frames, grid_cols, k_anchor, d):
 
 
 def calibatt_anchor_attn_fwd(Q, K, V, O, heads, grid, k_anchor, scale, seq_len=None, queue_ws=None,
-                             v_transposed=False, vt_ws=None, ws=None):
+                             v_transposed=False, ws=None):
     """Anchor-row attention for the listed heads; other heads of O are left as they are."""
     B, H, L, d = _qkv(Q, K, V, O, v_transposed)
     _need(Q.dtype == torch.bfloat16, "anchor attention takes bfloat16 tensors")
@@ -411,7 +391,6 @@ def calibatt_anchor_attn_fwd(Q, K, V, O, heads, grid, k_anchor, scale, seq_len=N
     if queue_ws is None:
         queue_ws = new_queue(Q.device)
     _queue(queue_ws)
-    layout, vt_ws = _vt_args(Q, v_transposed, vt_ws)
     need = calibatt_anchor_ws_bytes(B, H, F, C, k_anchor, d)
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=Q.device)
@@ -419,8 +398,8 @@ def calibatt_anchor_attn_fwd(Q, K, V, O, heads, grid, k_anchor, scale, seq_len=N
     lib = load()
     check(lib.calibatt_anchor_attn_fwd(
         _ptr(Q), _ptr(K), _ptr(V), _ptr(O), hl.ctypes.data_as(ctypes.c_void_p), int(hl.size), F, R, C,
-        int(k_anchor), float(scale), B, H, L, seq_len, d, BF16, _ptr(queue_ws), layout, _ptr(vt_ws),
-        _ptr(ws), ws.numel(), _stream(Q)))
+        int(k_anchor), float(scale), B, H, L, seq_len, d, BF16, _ptr(queue_ws),
+        V_BHDL if v_transposed else V_BHLD, _ptr(ws), ws.numel(), _stream(Q)))
     return O
 
 
@@ -463,7 +442,6 @@ def calibatt_version():
 __all__ = [
     "CalibattError",
     "new_queue",
-    "new_vt",
     "calibatt_transpose_v",
     "calibatt_sparse_attn_fwd",
     "calibatt_dense_attn_fwd",

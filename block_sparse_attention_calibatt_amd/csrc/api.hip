@@ -4,6 +4,7 @@
 // machine without a GPU.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -82,8 +83,6 @@ calibatt_status check_ptrs4(const void* Q, const void* K, const void* V, const v
   return CALIBATT_OK;
 }
 
-// V layout: with CALIBATT_V_BHLD the kernels need V^T, which is written into
-// vt_ws first; with CALIBATT_V_BHDL V already is V^T.
 // Two [B, H, L, d] tensors of `bytes` bytes each share memory.
 bool overlap(const void* p, const void* q, uintptr_t bytes) {
   const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
@@ -94,16 +93,29 @@ uintptr_t tensor_bytes(int B, int H, int L, int d, calibatt_dtype dt) {
   return (uintptr_t)B * H * L * d * (dt == CALIBATT_F32 ? 4 : 2);
 }
 
-calibatt_status check_v_layout(calibatt_vlayout v_layout, const void* Q, const void* K, const void* V,
-                               const void* O, const void* vt_ws, int B, int H, int L, int d,
-                               calibatt_dtype dt) {
-  if (v_layout == CALIBATT_V_BHDL) return CALIBATT_OK;
-  if (v_layout != CALIBATT_V_BHLD) return fail(CALIBATT_ERR_SHAPE, "unknown v_layout code %d", (int)v_layout);
-  if (!vt_ws) return fail(CALIBATT_ERR_NULL, "vt_ws must be non-NULL when V is [B, H, L, d]");
-  if (!aligned(vt_ws, 16)) return fail(CALIBATT_ERR_ALIGN, "vt_ws must be 16-byte aligned");
+// The kernels read V in either layout (natural, or V^T with
+// CALIBATT_V_BHDL); no copy of it is made.
+calibatt_status check_v_layout(calibatt_vlayout v_layout) {
+  if (v_layout != CALIBATT_V_BHLD && v_layout != CALIBATT_V_BHDL)
+    return fail(CALIBATT_ERR_SHAPE, "unknown v_layout code %d", (int)v_layout);
+  return CALIBATT_OK;
+}
+
+// The softmax scale multiplies every score; a non-positive or non-finite one
+// has no meaning for the method and would give non-finite outputs.
+calibatt_status check_scale(float scale) {
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(CALIBATT_ERR_SHAPE, "scale=%g must be finite and > 0", (double)scale);
+  return CALIBATT_OK;
+}
+
+// O is written while other workgroups still read Q, K and V, so it may not
+// share memory with them.
+calibatt_status check_out_alias(const void* Q, const void* K, const void* V, const void* O, int B, int H, int L,
+                                int d, calibatt_dtype dt) {
   const uintptr_t bytes = tensor_bytes(B, H, L, d, dt);
-  if (overlap(vt_ws, Q, bytes) || overlap(vt_ws, K, bytes) || overlap(vt_ws, V, bytes) || overlap(vt_ws, O, bytes))
-    return fail(CALIBATT_ERR_SHAPE, "vt_ws must not overlap Q, K, V or O");
+  if (overlap(O, Q, bytes) || overlap(O, K, bytes) || overlap(O, V, bytes))
+    return fail(CALIBATT_ERR_SHAPE, "O must not overlap Q, K or V");
   return CALIBATT_OK;
 }
 
@@ -127,22 +139,16 @@ calibatt_status run_attention(const void* Q, const void* K, const void* V, void*
                               const int32_t* row_ptr, const int32_t* col_idx, int block, float scale,
                               int B, int H, int L, int seq_len, int d, calibatt_dtype dt,
                               const int32_t* work_order, int32_t* queue_ws, calibatt_vlayout v_layout,
-                              void* vt_ws, bool dense, void* stream) {
+                              bool dense, void* stream) {
   int ncu = 256;
   if (queue_ws) {
     hipError_t e = cu_count(&ncu);
     if (e != hipSuccess) return hip_fail(e, "querying the compute-unit count");
   }
-  const void* Vt = V;
-  if (v_layout == CALIBATT_V_BHLD) {
-    calibatt_status s = enqueue_transpose(V, vt_ws, B, H, L, seq_len, d, dt, stream);
-    if (s != CALIBATT_OK) return s;
-    Vt = vt_ws;
-  }
   calibatt::AttnArgs a;
   a.Q = Q;
   a.K = K;
-  a.Vt = Vt;
+  a.V = V;
   a.O = O;
   a.row_ptr = row_ptr;
   a.col_idx = col_idx;
@@ -157,10 +163,39 @@ calibatt_status run_attention(const void* Q, const void* K, const void* V, void*
   a.nkb_valid = (seq_len + block - 1) / block;
   a.scale = scale;
   a.dtype_f32 = dt == CALIBATT_F32;
+  a.v_transposed = v_layout == CALIBATT_V_BHDL;
   a.num_cu = ncu;
   hipError_t e = calibatt::launch_attention(a, dense, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, dense ? "launching dense attention" : "launching sparse attention");
   return ok();
+}
+
+// Checks shared by the sparse entry points: tensors, shape, V layout, scale,
+// O aliasing and the kept-block list's pointers and size.
+calibatt_status check_sparse_args(const void* Q, const void* K, const void* V, void* O, const int32_t* row_ptr,
+                                  const int32_t* col_idx, int block, float scale, int B, int H, int L, int seq_len,
+                                  int d, calibatt_dtype dt, const int32_t* work_order, int64_t nnz,
+                                  calibatt_vlayout v_layout) {
+  calibatt_status s = check_ptrs4(Q, K, V, O);
+  if (s != CALIBATT_OK) return s;
+  s = check_qkv_shape(B, H, L, seq_len, d, dt, block);
+  if (s != CALIBATT_OK) return s;
+  s = check_v_layout(v_layout);
+  if (s != CALIBATT_OK) return s;
+  s = check_scale(scale);
+  if (s != CALIBATT_OK) return s;
+  s = check_out_alias(Q, K, V, O, B, H, L, d, dt);
+  if (s != CALIBATT_OK) return s;
+  if (!row_ptr) return fail(CALIBATT_ERR_NULL, "row_ptr must be non-NULL");
+  if (nnz < 0) return fail(CALIBATT_ERR_CSR, "nnz=%lld must be >= 0", (long long)nnz);
+  const long long rows = (long long)H * (L / block);
+  const long long nkb_valid = (seq_len + block - 1) / block;
+  if (nnz > rows * nkb_valid)
+    return fail(CALIBATT_ERR_CSR, "nnz=%lld exceeds rows*nkb_valid=%lld", (long long)nnz, rows * nkb_valid);
+  if (nnz > 0 && !col_idx) return fail(CALIBATT_ERR_NULL, "col_idx must be non-NULL when nnz > 0");
+  if (!aligned(row_ptr, 4) || (col_idx && !aligned(col_idx, 4)) || (work_order && !aligned(work_order, 4)))
+    return fail(CALIBATT_ERR_ALIGN, "row_ptr, col_idx and work_order must be 4-byte aligned");
+  return CALIBATT_OK;
 }
 
 }  // namespace
@@ -172,40 +207,32 @@ calibatt_status calibatt_sparse_attn_fwd(const void* Q, const void* K, const voi
                                          float scale, int B, int H, int L, int seq_len, int d,
                                          calibatt_dtype dt, const int32_t* work_order,
                                          int32_t* queue_ws, int64_t nnz, calibatt_vlayout v_layout,
-                                         void* vt_ws, void* stream) {
-  calibatt_status s = check_ptrs4(Q, K, V, O);
+                                         void* stream) {
+  calibatt_status s = check_sparse_args(Q, K, V, O, row_ptr, col_idx, block, scale, B, H, L, seq_len, d, dt,
+                                        work_order, nnz, v_layout);
   if (s != CALIBATT_OK) return s;
-  s = check_qkv_shape(B, H, L, seq_len, d, dt, block);
-  if (s != CALIBATT_OK) return s;
-  s = check_v_layout(v_layout, Q, K, V, O, vt_ws, B, H, L, d, dt);
-  if (s != CALIBATT_OK) return s;
-  if (!row_ptr) return fail(CALIBATT_ERR_NULL, "row_ptr must be non-NULL");
-  if (nnz < 0) return fail(CALIBATT_ERR_CSR, "nnz=%lld must be >= 0", (long long)nnz);
-  const long long rows = (long long)H * (L / block);
-  const long long nkb_valid = (seq_len + block - 1) / block;
-  if (nnz > rows * nkb_valid)
-    return fail(CALIBATT_ERR_CSR, "nnz=%lld exceeds rows*nkb_valid=%lld", (long long)nnz, rows * nkb_valid);
-  if (nnz > 0 && !col_idx) return fail(CALIBATT_ERR_NULL, "col_idx must be non-NULL when nnz > 0");
-  if (!aligned(row_ptr, 4) || (col_idx && !aligned(col_idx, 4)) || (work_order && !aligned(work_order, 4)))
-    return fail(CALIBATT_ERR_ALIGN, "row_ptr, col_idx and work_order must be 4-byte aligned");
   if (queue_ws && !aligned(queue_ws, 16)) return fail(CALIBATT_ERR_ALIGN, "queue_ws must be 16-byte aligned");
   return run_attention(Q, K, V, O, row_ptr, col_idx, block, scale, B, H, L, seq_len, d, dt, work_order,
-                       queue_ws, v_layout, vt_ws, false, stream);
+                       queue_ws, v_layout, false, stream);
 }
 
 calibatt_status calibatt_dense_attn_fwd(const void* Q, const void* K, const void* V, void* O,
                                         int block, float scale, int B, int H, int L, int seq_len,
                                         int d, calibatt_dtype dt, int32_t* queue_ws,
-                                        calibatt_vlayout v_layout, void* vt_ws, void* stream) {
+                                        calibatt_vlayout v_layout, void* stream) {
   calibatt_status s = check_ptrs4(Q, K, V, O);
   if (s != CALIBATT_OK) return s;
   s = check_qkv_shape(B, H, L, seq_len, d, dt, block);
   if (s != CALIBATT_OK) return s;
-  s = check_v_layout(v_layout, Q, K, V, O, vt_ws, B, H, L, d, dt);
+  s = check_v_layout(v_layout);
+  if (s != CALIBATT_OK) return s;
+  s = check_scale(scale);
+  if (s != CALIBATT_OK) return s;
+  s = check_out_alias(Q, K, V, O, B, H, L, d, dt);
   if (s != CALIBATT_OK) return s;
   if (queue_ws && !aligned(queue_ws, 16)) return fail(CALIBATT_ERR_ALIGN, "queue_ws must be 16-byte aligned");
   return run_attention(Q, K, V, O, nullptr, nullptr, block, scale, B, H, L, seq_len, d, dt, nullptr,
-                       queue_ws, v_layout, vt_ws, true, stream);
+                       queue_ws, v_layout, true, stream);
 }
 
 calibatt_status calibatt_transpose_v(const void* V, void* Vt, int B, int H, int L, int seq_len, int d,
@@ -228,6 +255,8 @@ calibatt_status calibatt_block_mass(const void* Q, const void* K, int B, int H, 
   if (!aligned(Q, 16) || !aligned(K, 16)) return fail(CALIBATT_ERR_ALIGN, "Q and K must be 16-byte aligned");
   if (!aligned(lse_ws, 4) || !aligned(mass, 4)) return fail(CALIBATT_ERR_ALIGN, "lse_ws and mass must be 4-byte aligned");
   calibatt_status s = check_qkv_shape(B, H, L, seq_len, d, dt, block);
+  if (s != CALIBATT_OK) return s;
+  s = check_scale(scale);
   if (s != CALIBATT_OK) return s;
   if (dt != CALIBATT_BF16) return fail(CALIBATT_ERR_UNSUPPORTED, "block_mass supports bf16 inputs only");
   if (L / block > calibatt::kMaxKeyBlocks)
@@ -263,6 +292,8 @@ calibatt_status calibatt_block_mass_single_pass(const void* Q, const void* K, in
   if (!aligned(lse_ws, 4) || !aligned(mass, 4) || !aligned(ws, 256))
     return fail(CALIBATT_ERR_ALIGN, "lse_ws and mass must be 4-byte aligned, ws 256-byte aligned");
   calibatt_status s = check_qkv_shape(B, H, L, seq_len, d, dt, block);
+  if (s != CALIBATT_OK) return s;
+  s = check_scale(scale);
   if (s != CALIBATT_OK) return s;
   if (dt != CALIBATT_BF16) return fail(CALIBATT_ERR_UNSUPPORTED, "block_mass supports bf16 inputs only");
   if (L / block > calibatt::kMaxKeyBlocks)
@@ -600,6 +631,8 @@ calibatt_status calibatt_spatial_similarity(const void* Q, const void* K, int B,
   calibatt_status s = check_qkv_shape(B, H, L, seq_len, d, dt, 128);
   if (s != CALIBATT_OK) return s;
   if (dt != CALIBATT_BF16) return fail(CALIBATT_ERR_UNSUPPORTED, "spatial similarity supports bf16 inputs only");
+  s = check_scale(scale);
+  if (s != CALIBATT_OK) return s;
   s = check_grid(frames, grid_rows, grid_cols, seq_len);
   if (s != CALIBATT_OK) return s;
   if (grid_rows < 2) return fail(CALIBATT_ERR_SHAPE, "grid_rows=%d: the score needs at least two rows", grid_rows);
@@ -661,14 +694,17 @@ calibatt_status calibatt_anchor_attn_fwd(const void* Q, const void* K, const voi
                                          const int32_t* heads, int n_heads, int frames, int grid_rows,
                                          int grid_cols, int k_anchor, float scale, int B, int H, int L,
                                          int seq_len, int d, calibatt_dtype dt, int32_t* queue_ws,
-                                         calibatt_vlayout v_layout, void* vt_ws, void* ws, size_t ws_bytes,
-                                         void* stream) {
+                                         calibatt_vlayout v_layout, void* ws, size_t ws_bytes, void* stream) {
   calibatt_status s = check_ptrs4(Q, K, V, O);
   if (s != CALIBATT_OK) return s;
   s = check_qkv_shape(B, H, L, seq_len, d, dt, 128);
   if (s != CALIBATT_OK) return s;
   if (dt != CALIBATT_BF16) return fail(CALIBATT_ERR_UNSUPPORTED, "anchor attention supports bf16 inputs only");
-  s = check_v_layout(v_layout, Q, K, V, O, vt_ws, B, H, L, d, dt);
+  s = check_v_layout(v_layout);
+  if (s != CALIBATT_OK) return s;
+  s = check_scale(scale);
+  if (s != CALIBATT_OK) return s;
+  s = check_out_alias(Q, K, V, O, B, H, L, d, dt);
   if (s != CALIBATT_OK) return s;
   s = check_grid(frames, grid_rows, grid_cols, seq_len);
   if (s != CALIBATT_OK) return s;
@@ -697,16 +733,11 @@ calibatt_status calibatt_anchor_attn_fwd(const void* Q, const void* K, const voi
   int ncu = 256;
   hipError_t e = cu_count(&ncu);
   if (e != hipSuccess) return hip_fail(e, "querying the compute-unit count");
-  const void* Vt = V;
-  if (v_layout == CALIBATT_V_BHLD) {
-    s = enqueue_transpose(V, vt_ws, B, H, L, seq_len, d, dt, stream);
-    if (s != CALIBATT_OK) return s;
-    Vt = vt_ws;
-  }
   const size_t oa = ((size_t)B * H * Lq * d * 2 + 255) / 256 * 256;
   a.Q = Q;
   a.K = K;
-  a.Vt = Vt;
+  a.V = V;
+  a.v_transposed = v_layout == CALIBATT_V_BHDL;
   a.O = O;
   a.Oa = ws;
   a.order = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + oa);

@@ -112,8 +112,9 @@ struct Cst {
 
 // Geometry of the 32-queries-per-wave bf16 kernel: BLK/32 waves, each owning
 // 32 queries, keys in sub-tiles of 64 (a kept block of 128 is two), two LDS
-// stages that each hold a K sub-tile (64 rows of D/8 16-byte units) and a
-// V^T sub-tile (D rows of 8 units), both filled by DMA.
+// stages that each hold a K sub-tile (64 rows of D/8 16-byte units) and a V
+// sub-tile (64 rows of D/8 units in natural layout, or D rows of 8 units of
+// V^T), both filled by DMA.
 template <int D, int BLK>
 struct Geo {
   static constexpr int NW = BLK / 32;
@@ -145,28 +146,30 @@ __device__ __forceinline__ void k_dma_one(int i, __amdgpu_buffer_rsrc_t rk, int 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kt + 64 * m), 16, voff, k0 * D * 2 + m * 1024, 0, 0);
 }
 
-// V^T DMA instruction i (0 .. VPER-1) of wave w for the V^T sub-tile at key
-// k0 (D rows of 128 contiguous bytes of V^T; instruction m covers rows
-// 8m .. 8m+7) into its swizzled LDS tile.
-template <int D, int BLK>
+// V DMA instruction i (0 .. VPER-1) of wave w for the V sub-tile at key k0
+// into its swizzled LDS tile: natural layout, instruction m covering key rows
+// m*(64/CH) ..; or (VT) D rows of 128 contiguous bytes of V^T, instruction m
+// covering rows 8m .. 8m+7.
+template <int D, int BLK, bool VT>
 __device__ __forceinline__ void v_dma_one(int i, __amdgpu_buffer_rsrc_t rv, int k0, int L, u32x4* vt, int w,
                                           const int* vpat) {
   using G = Geo<D, BLK>;
   const int m = w + G::NW * i;
   const int voff = vpat[i % G::PAT];
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vt + 64 * m), 16, voff, k0 * 2 + m * 16 * L, 0, 0);
+  const int soff = VT ? k0 * 2 + m * 16 * L : k0 * D * 2 + m * 1024;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vt + 64 * m), 16, voff, soff, 0, 0);
 }
 
 // DMA instruction i (0 .. KPER+VPER-1) of this wave for the sub-tile at key
-// k0, into a stage that holds the K tile followed by the V^T tile.
-template <int D, int BLK>
+// k0, into a stage that holds the K tile followed by the V tile.
+template <int D, int BLK, bool VT>
 __device__ __forceinline__ void tile_dma(int i, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int k0,
                                          int L, u32x4* stage, int w, const int* kpat, const int* vpat) {
   using G = Geo<D, BLK>;
   if (i < G::KPER)
     k_dma_one<D, BLK>(i, rk, k0, stage, w, kpat);
   else
-    v_dma_one<D, BLK>(i - G::KPER, rv, k0, L, stage + G::KUNITS, w, vpat);
+    v_dma_one<D, BLK, VT>(i - G::KPER, rv, k0, L, stage + G::KUNITS, w, vpat);
 }
 
 // bf16 kernel, 32 queries per wave.  Sub-tile j of a row is computed from
@@ -176,16 +179,18 @@ __device__ __forceinline__ void tile_dma(int i, __amdgpu_buffer_rsrc_t rk, __amd
 //   between the products (issued in one burst right after the barrier they
 //   queue behind the other waves' and stall the wave); tail keys masked;
 //   P = exp2(S c2 - mc) rounded to bf16 and its row sums; the lazy rescale;
-//   O^T += V^T P^T on the matrix cores; wait for the DMA, barrier.
+//   O^T += V^T P^T on the matrix cores (the V^T operand by transposed LDS
+//   reads of the natural-layout tile, or with VT plain reads of a V^T
+//   tile); wait for the DMA, barrier.
 // The key-block indices of a row are read two blocks ahead, so their scalar
 // loads have returned when a DMA needs them.  Past the row's last sub-tile
 // the DMA loads that sub-tile again into the free stage, so every step has
 // the same shape.  Two waves per SIMD (two workgroups per CU) let one wave's
 // softmax run beside the other's products; at d = 128 with 64-token blocks
 // the registers allow only one.
-template <int D, int BLK, bool DENSE>
+template <int D, int BLK, bool DENSE, bool VT>
 __global__ __launch_bounds__(BLK * 2, (D == 128 && BLK == 64) ? 1 : 2) void attn_fwd_bf16_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ Vt,
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     const int32_t* __restrict__ work_order, int32_t* __restrict__ queue, int items, int H, int L,
     int seq_len, int nkb_valid, float c2) {
@@ -203,39 +208,62 @@ __global__ __launch_bounds__(BLK * 2, (D == 128 && BLK == 64) ? 1 : 2) void attn
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5, c = lane & 31;
   const int prow = qk_row_perm(c);
-  const uint32_t slab_bytes = (uint32_t)L * D * 2;
+  constexpr int RB = D * 2;
+  // K and V rows past seq_len read as zero (buffer range check)
+  const uint32_t k_bytes = (uint32_t)seq_len * RB;
+  const uint32_t v_bytes = VT ? (uint32_t)L * RB : (uint32_t)seq_len * RB;
 
   int kpat[G::PAT], vpat[G::PAT];
 #pragma unroll
   for (int i = 0; i < G::PAT; ++i) {
     const int m = w + G::NW * i;
     const int krow = m * (64 / CH) + lane / CH;
-    kpat[i] = (lane / CH) * D * 2 + (((lane % CH) ^ swz<CH>(krow)) * 16);
-    const int vrow = m * 8 + lane / 8;
-    vpat[i] = (lane / 8) * L * 2 + (((lane % 8) ^ swz<8>(vrow)) * 16);
+    kpat[i] = (lane / CH) * RB + (((lane % CH) ^ swz<CH>(krow)) * 16);
+    if (VT) {
+      const int vrow = m * 8 + lane / 8;
+      vpat[i] = (lane / 8) * L * 2 + (((lane % 8) ^ swz<8>(vrow)) * 16);
+    } else {
+      const int vrow = m * (64 / CH) + lane / CH;
+      vpat[i] = (lane / CH) * RB + (((lane % CH) ^ vswz<D>(vrow)) * 16);
+    }
   }
-  // operand reads: K row 32*mt + prow, unit 2s+g; V^T row 32*t + c, unit
-  // 2ks+g.  The swizzles see row bits 0..4 only, so the unit is the lane's
-  // constant XOR the k-step.
-  // The byte offsets of the DS + KS operand reads are kept in registers for
-  // the whole kernel, so that a read costs no address arithmetic: the stage
-  // and the 32-row tile are added as the instruction's immediate offset.
+  // operand reads: K row 32*mt + prow, unit 2s+g.  V (natural layout): lane
+  // 16G + 4jj + mm reads 8 bytes of key row 16ks + 8g + 4h + jj at d = 32t +
+  // 16(G%2) + 4mm and the transposed read hands lane (g, c) its 4 keys at d =
+  // 32t + c; V^T: row 32*t + c, unit 2ks+g.  The swizzles see row bits 0..4
+  // only, so the unit is the lane's constant XOR the k-step.
+  // The byte offsets of the operand reads are kept in registers for the
+  // whole kernel, so that a read costs no address arithmetic: the stage and
+  // the 32-row tile are added as the instruction's immediate offset.
+  constexpr int NV = VT ? KS : DT;
   const int kx = g ^ swz<CH>(prow);
-  const int vx = g ^ swz<8>(c);
-  int koffs[DS], voffs[KS];
+  int koffs[DS], voffs[NV];
 #pragma unroll
   for (int s = 0; s < DS; ++s) koffs[s] = (prow * CH + ((2 * s) ^ kx)) * 16;
+  if (VT) {
+    const int vx = g ^ swz<8>(c);
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) voffs[ks] = (G::KUNITS + c * 8 + ((2 * ks) ^ vx)) * 16;
+    for (int ks = 0; ks < NV; ++ks) voffs[ks] = (G::KUNITS + c * 8 + ((2 * ks) ^ vx)) * 16;
+  } else {
+    const int jj = (lane >> 2) & 3, mm = lane & 3;
+#pragma unroll
+    for (int t = 0; t < NV; ++t)
+      voffs[t] = G::KUNITS * 16 + (8 * g + jj) * RB +
+                 (((4 * t + 2 * (c >> 4) + (mm >> 1)) ^ vswz<D>(jj)) * 16) + (mm & 1) * 8;
+  }
 #pragma unroll
   for (int s = 0; s < DS; ++s) asm volatile("" : "+v"(koffs[s]));
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(voffs[ks]));
+  for (int i = 0; i < NV; ++i) asm volatile("" : "+v"(voffs[i]));
   auto kread = [&](const u32x4* t, int mt, int s) __attribute__((always_inline)) {
     return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(t) + mt * 32 * CH * 16 + koffs[s]);
   };
-  auto vread = [&](const u32x4* t, int dt, int ks) __attribute__((always_inline)) {
-    return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(t) + dt * 32 * 8 * 16 + voffs[ks]);
+  auto vread = [&](const u32x4* t, int dt, int ks) __attribute__((always_inline)) -> u32x4 {
+    if (VT) return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(t) + dt * 32 * 8 * 16 + voffs[ks]);
+    const char* p = reinterpret_cast<const char*>(t) + voffs[dt] + 16 * ks * RB;
+    const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(p));
+    const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(p + 4 * RB));
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
   };
 
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -245,8 +273,8 @@ __global__ __launch_bounds__(BLK * 2, (D == 128 && BLK == 64) ? 1 : 2) void attn
   for_each_row(src, queue, &s_item, [&](int b, int r) {
     const int h = r / nqb, qb = r - h * nqb;
     const size_t base = ((size_t)b * H + h) * (size_t)L * D;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + base, slab_bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vt + base, slab_bytes);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + base, k_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + base, v_bytes);
     const int q = qb * BLK + 32 * w + c;   // this lane's query
 
     const int beg = DENSE ? 0 : row_ptr[r];
@@ -264,13 +292,15 @@ __global__ __launch_bounds__(BLK * 2, (D == 128 && BLK == 64) ? 1 : 2) void attn
       kb1 = blk(1);
       kb2 = blk(2);
 #pragma unroll
-      for (int i = 0; i < G::KPER + G::VPER; ++i) tile_dma<D, BLK>(i, rk, rv, kb0 * BLK, L, st0, w, kpat, vpat);
+      for (int i = 0; i < G::KPER + G::VPER; ++i) tile_dma<D, BLK, VT>(i, rk, rv, kb0 * BLK, L, st0, w, kpat, vpat);
     }
 
+    // a padded query is taken as zero (its output is zeroed; a non-finite
+    // value would also move the wave's shared rescale decisions)
     bf16x8 qreg[DS];
 #pragma unroll
     for (int s = 0; s < DS; ++s)
-      qreg[s] = *reinterpret_cast<const bf16x8*>(Q + base + (size_t)q * D + 16 * s + 8 * g);
+      qreg[s] = q < seq_len ? *reinterpret_cast<const bf16x8*>(Q + base + (size_t)q * D + 16 * s + 8 * g) : bf16x8{};
 
     f32x16 oacc[DT];
 #pragma unroll
@@ -310,7 +340,7 @@ __global__ __launch_bounds__(BLK * 2, (D == 128 && BLK == 64) ? 1 : 2) void attn
           sacc[1] = mfma_bf16(__builtin_bit_cast(bf16x8, ra[s % 3][1]), qreg[s], s == 0 ? f32x16{} : sacc[1]);
 #pragma unroll
           for (int i = s * NDMA / DS; i < (s + 1) * NDMA / DS; ++i)
-            tile_dma<D, BLK>(i, rk, rv, kd, L, nxt, w, kpat, vpat);
+            tile_dma<D, BLK, VT>(i, rk, rv, kd, L, nxt, w, kpat, vpat);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -392,8 +422,11 @@ __global__ __launch_bounds__(BLK * 2, (D == 128 && BLK == 64) ? 1 : 2) void attn
       shift();
     }
 
+    // padded query rows (and rows that saw no key) are written as zero,
+    // whatever their accumulators hold
     const float l_tot = pair_sum(l_run);
-    const float inv = (q < seq_len && l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    const bool valid = q < seq_len && l_tot > 0.f;
+    const float inv = valid ? 1.f / l_tot : 0.f;
     bf16* Ob = O + base + (size_t)q * D;
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
@@ -403,515 +436,710 @@ __global__ __launch_bounds__(BLK * 2, (D == 128 && BLK == 64) ? 1 : 2) void attn
         typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
         bf16x4 o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = (bf16)(oacc[t][4 * rq + e] * inv);
+        for (int e = 0; e < 4; ++e) o[e] = valid ? (bf16)(oacc[t][4 * rq + e] * inv) : (bf16)0.f;
         *reinterpret_cast<bf16x4*>(Ob + d0) = o;
       }
     }
   });
 }
 
-// bf16 kernel for 128-token blocks in ping-pong form.  One workgroup of 8
-// waves per CU serves one row: wave group A (waves 0-3) takes the even
-// 64-key sub-tiles of the row and group B (waves 4-7) the odd ones, each
-// wave the same 32 queries as its partner w ^ 4, which shares its SIMD.
-// Each group keeps its own reference, row sums and O; at the end of the row
-// B hands its state to A through LDS and A writes the combined result (a
-// fixed split, so the result does not depend on scheduling).
+// Geometry of the 128-token-block kernel: keys in 64-key sub-tiles; a K
+// stage holds one sub-tile as 64 rows of D/8 16-byte units, a V stage the
+// same sub-tile of V (64 rows, natural layout) or of V^T (D rows of 8 units).
+// Each wave group owns four stages: K0, K1, V0, V1.  The stages are four LDS
+// objects, each holding both groups' stage of that name, so that the DMA
+// into one stage and the operand reads of another are accesses to different
+// objects, which the compiler can tell apart (it would otherwise wait for
+// every DMA in flight before each read).
+template <int D>
+struct PPGeo {
+  static constexpr int CH = D / 8;
+  static constexpr int DS = D / 16;
+  static constexpr int DT = D / 32;
+  static constexpr int KS = 4;
+  static constexpr int UNITS = 64 * CH;
+  static constexpr int STAGE = UNITS * 16;
+  static constexpr int NDMA = UNITS / 64 / 4;   // DMA instructions per wave per stage (4 waves)
+  static constexpr int RB = D * 2;              // bytes of one K or V row
+};
+
+// bf16 kernel for 128-token blocks.  One workgroup of 8 waves per CU, in two
+// groups of 4 (A: waves 0-3, B: waves 4-7; wave w and w+4 share a SIMD).  Each
+// group serves rows on its own: its 4 waves own 32 queries each of the row's
+// 128 and walk the row's 64-key sub-tiles in list order, so one group reduces
+// a whole row and the result does not depend on scheduling.
 //
-// Time is cut into barrier-separated phases t = 0 .. n+1 (n sub-tiles).  In
-// phase t the group of parity t does only matrix-core work and the other
-// only vector work, so the two waves of a SIMD always hold complementary
-// work:
-//   matrix phase  S(t) = K(t) Q^T, with this wave's share of the DMA of
-//                 K(t+2) and V^T(t) spread between the products; then
-//                 O^T += V^T(t-2) P(t-2)^T
-//   vector phase  P(t-1) = exp2(S(t-1) c2 - mc) rounded to bf16, its row
-//                 sums and the lazy rescale; then wait for this wave's DMA
-//                 of the phase before
-// A DMA issued in phase t has landed by the end of phase t+1, so K(x) is
-// issued two phases before S(x) reads it and V^T(x) two phases before
-// P*V(x).  K and V^T rotate through three LDS stages each.
+// Time is cut into barrier-separated phases, and the groups alternate: in a
+// phase one group does only matrix-core work and the other only vector work,
+// so the two waves of a SIMD always hold complementary work.  A group's
+// sub-tiles form one stream across its rows; cycle x of the stream is
+//   matrix phase  S(x) = K(x) Q^T (Q in registers, pre-scaled), with this
+//                 wave's share of the DMA of K(x+1) and V(x) spread between
+//                 the products; then O^T += V^T(x-1) P(x-1)^T
+//   vector phase  P(x) = exp2(S(x) - ref) rounded to bf16, its row sums and
+//                 the lazy rescale; then wait for this wave's DMA
+// so a DMA issued in a matrix phase has landed by the end of the next phase.
+// At a row boundary the stream does not stop: the matrix phase that computes
+// the last scores of a row loads the next row's Q after them and its first K
+// tile, the next matrix phase computes the new row's first scores beside the
+// old row's last P*V, and the vector phase after it writes the old row's O.
+//
+// V is read in its natural layout by default: a V tile goes to LDS by DMA as
+// it lies (padded keys read as zero through the buffer's range check), and
+// the transposed-read LDS instruction forms the P*V operand, whose
+// contracted index (keys) must be contiguous in each lane.  With VT the
+// kernel reads V^T [B, H, d, L] tiles instead, with plain 16-byte reads.
+//
+// Rows come from per-XCD partitions of the work order through atomic
+// counters.  Wave 0 of a group fetches the group's next row one dependent
+// load per vector phase (counter, work-order entry, list bounds, first key
+// blocks) while the current row runs, and finishes the chain at once if the
+// row is about to end; the result sits in LDS for the group.
 //
 // SPLITQ: the rows are the anchor queries of the spatial-repetition heads:
 // query m < q_valid of head h is token anchor_token(m) of Q (read in place),
 // O is [B, H, Lq, d] with Lq a multiple of 128, rows h*(Lq/128) + qb; keys
-// still run over K and V^T of length L with seq_len valid.
-template <int D, bool DENSE, bool SPLITQ = false>
+// still run over K and V of length L with seq_len valid.
+template <int D, bool DENSE, bool SPLITQ, bool VT>
 __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ Vt,
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     const int32_t* __restrict__ work_order, int32_t* __restrict__ queue, int items, int H, int L,
     int seq_len, int nkb_valid, float c2, int Lq, int q_valid, int grid_rows, int grid_cols, int k_anchor) {
   constexpr int BLK = 128;
-  using G = Geo<D, BLK>;   // one wave group: NW = 4 waves of 32 queries
-  constexpr int DS = G::DS, DT = G::DT, KS = G::KS, CH = G::CH;
-  constexpr int NDMA = G::KPER + G::VPER;
-  static_assert(G::KUNITS == G::VUNITS, "K and V^T stages have one size");
-  static_assert(DT * 2 * 8192 <= 4 * G::KUNITS * 16, "group B's O fits in K0, K1, K2 and V0");
-  constexpr int OBJ = G::KUNITS * 16;   // bytes of one stage
-  __shared__ u32x4 ks0[G::KUNITS], ks1[G::KUNITS], ks2[G::KUNITS];
-  __shared__ u32x4 vs0[G::VUNITS], vs1[G::VUNITS], vs2[G::VUNITS];
-  __shared__ int s_next[8];   // the next row: b, r (-1: none), first list entry, blocks, kb0, kb1, kb2
-  __shared__ int s_fstate[2];   // the fetching wave's queue state: partition, partitions tried
-  __shared__ float s_ml[G::NW * 64 * 2];   // group B's reference and row sum, per lane
-  u32x4* const kst[3] = {ks0, ks1, ks2};
-  u32x4* const vst[3] = {vs0, vs1, vs2};
+  using G = PPGeo<D>;
+  constexpr int CH = G::CH, DS = G::DS, DT = G::DT, KS = G::KS, NDMA = G::NDMA;
+  constexpr int STAGE = G::STAGE, RB = G::RB;
+  __shared__ u32x4 lk0[2 * G::UNITS], lk1[2 * G::UNITS], lv0[2 * G::UNITS], lv1[2 * G::UNITS];
+  __shared__ int s_desc[2][8];        // per group: next row b, r (-1: none), list start, blocks, kb0, kb1
+  __shared__ int s_poff[kParts + 1];  // partition offsets of the work order
+  __shared__ int s_fin[2];            // phase in which each group finished
+  __shared__ int s_fst[2][8];         // per group: the fetch state between calls
+  __shared__ int s_prev[2][2];        // per group: batch and row of the row whose O is due
+  // Arguments only the rare paths use (row fetch, row switch, O store) are
+  // read from LDS there, so that the compiler does not keep them, or values
+  // derived from them, in scalar registers through the phase loop.
+  __shared__ uint32_t s_arg[20];
 
   const int nqb = (SPLITQ ? Lq : L) / BLK;
   const int rows = H * nqb;
+  const int qlim = SPLITQ ? q_valid : seq_len;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int grp = wv >> 2;   // 0: even sub-tiles, 1: odd
-  const int w = wv & 3;      // query slice of the block
+  const int grp = wv >> 2;   // wave group
+  const int w = wv & 3;      // 32-query slice of the row
   const int g = lane >> 5, c = lane & 31;
   const int prow = qk_row_perm(c);
-  const uint32_t slab_bytes = (uint32_t)L * D * 2;
+  // K and V rows past seq_len read as zero (buffer range check)
+  const uint32_t k_bytes = (uint32_t)seq_len * RB;
+  const uint32_t v_bytes = VT ? (uint32_t)L * RB : (uint32_t)seq_len * RB;
+  char* const kst[2] = {reinterpret_cast<char*>(lk0), reinterpret_cast<char*>(lk1)};
+  char* const vst[2] = {reinterpret_cast<char*>(lv0), reinterpret_cast<char*>(lv1)};
+  const int gbase = grp * STAGE;   // the group's half of each stage object
 
-  int kpat[G::PAT], vpat[G::PAT];
-#pragma unroll
-  for (int i = 0; i < G::PAT; ++i) {
-    const int m = w + G::NW * i;
-    const int krow = m * (64 / CH) + lane / CH;
-    kpat[i] = (lane / CH) * D * 2 + (((lane % CH) ^ swz<CH>(krow)) * 16);
-    const int vrow = m * 8 + lane / 8;
-    vpat[i] = (lane / 8) * L * 2 + (((lane % 8) ^ swz<8>(vrow)) * 16);
+  // DMA lane patterns: instruction m of a stage writes LDS units 64m ..
+  // 64m+63; this wave issues m = w, w+4, ...  The K swizzle sees row bits
+  // 0..4 (m mod 4 = w), the natural-V swizzle only the lane.
+  int kpat, vpat;
+  {
+    const int krow = w * (64 / CH) + lane / CH;
+    kpat = (lane / CH) * RB + (((lane % CH) ^ swz<CH>(krow)) * 16);
+    if (VT) {
+      const int vrow = w * 8 + lane / 8;
+      vpat = (lane / 8) * L * 2 + (((lane % 8) ^ swz<8>(vrow)) * 16);
+    } else {
+      const int vrow = w * (64 / CH) + lane / CH;
+      vpat = (lane / CH) * RB + (((lane % CH) ^ vswz<D>(vrow)) * 16);
+    }
   }
-  // operand read offsets, kept in registers (see the 4-wave kernel)
-  const int kx = g ^ swz<CH>(prow);
-  const int vx = g ^ swz<8>(c);
-  int koffs[DS], voffs[KS];
+  // operand read offsets, kept in registers: the stage and tile are added as
+  // the instruction's immediate offset.  K: row 32*mt + prow, unit 2s+g.
+  // V (natural): lane 16G + 4jj + mm reads 8 bytes of row 16ks + 8g + 4h +
+  // jj at d = 32t + 16(G%2) + 4mm; the transposed read hands lane (g, c) the
+  // 4 keys of its half at d = 32t + c.  V^T: row 32t + c, unit 2ks + g.
+  constexpr int NV = VT ? KS : DT;
+  int koffs[DS], voffs[NV];
+  {
+    const int kx = g ^ swz<CH>(prow);
 #pragma unroll
-  for (int s = 0; s < DS; ++s) koffs[s] = (prow * CH + ((2 * s) ^ kx)) * 16;
+    for (int s = 0; s < DS; ++s) koffs[s] = gbase + (prow * CH + ((2 * s) ^ kx)) * 16;
+    if (VT) {
+      const int vx = g ^ swz<8>(c);
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) voffs[ks] = (c * 8 + ((2 * ks) ^ vx)) * 16;
+      for (int ks = 0; ks < NV; ++ks) voffs[ks] = gbase + (c * 8 + ((2 * ks) ^ vx)) * 16;
+    } else {
+      const int jj = (lane >> 2) & 3, mm = lane & 3;
+#pragma unroll
+      for (int t = 0; t < NV; ++t)
+        voffs[t] = gbase + (8 * g + jj) * RB +
+                   (((4 * t + 2 * (c >> 4) + (mm >> 1)) ^ vswz<D>(jj)) * 16) + (mm & 1) * 8;
+    }
+  }
 #pragma unroll
   for (int s = 0; s < DS; ++s) asm volatile("" : "+v"(koffs[s]));
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(voffs[ks]));
-  auto kread = [&](const u32x4* t, int mt, int s) __attribute__((always_inline)) {
-    return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(t) + mt * 32 * CH * 16 + koffs[s]);
+  for (int i = 0; i < NV; ++i) asm volatile("" : "+v"(voffs[i]));
+  auto kread = [&](int st, int mt, int s) __attribute__((always_inline)) -> u32x4 {
+    return *reinterpret_cast<const u32x4*>(kst[st] + koffs[s] + mt * 32 * CH * 16);
   };
-  auto vread = [&](const u32x4* t, int dt, int ks) __attribute__((always_inline)) {
-    return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(t) + dt * 32 * 8 * 16 + voffs[ks]);
+  // A operand of P*V product (t, ks) from V stage st
+  auto vop = [&](int st, int t, int ks) __attribute__((always_inline)) -> u32x4 {
+    if (VT) return *reinterpret_cast<const u32x4*>(vst[st] + voffs[ks] + t * 32 * 8 * 16);
+    const char* p = vst[st] + voffs[t] + 16 * ks * RB;
+    const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(p));
+    const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(p + 4 * RB));
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
   };
 
-  // the V^T stages start as zeros, so that a product with zero
-  // probabilities never meets a non-finite LDS value
-  for (int u = threadIdx.x; u < G::VUNITS; u += 512) vs0[u] = vs1[u] = vs2[u] = u32x4{0u, 0u, 0u, 0u};
-  __syncthreads();
-
-  const RowSource src{work_order, rows, nqb, H, items / rows};
-  // Rows come from the same per-XCD queues as in for_each_row, but wave 4
-  // fetches the next row while group A merges the current one: the queue
-  // pop, its work-order entry, the row's list bounds and first three key
-  // blocks (a chain of dependent loads) land in LDS before the row starts.
-  // The queue state lives in LDS too, so that no register is held through
-  // the phase loop for it.
+  // every stage starts as zeros: the first P*V of a group multiplies zero
+  // probabilities with a V stage no tile has been loaded into yet
+  for (int u = threadIdx.x; u < 2 * G::UNITS; u += 512) lk0[u] = lk1[u] = lv0[u] = lv1[u] = u32x4{0u, 0u, 0u, 0u};
+  if (threadIdx.x <= kParts) s_poff[threadIdx.x] = work_order ? work_order[rows + threadIdx.x] : 0;
   if (threadIdx.x == 0) {
-    s_fstate[0] = blockIdx.x % kParts;
-    s_fstate[1] = 0;
+    const void* const ptrs[8] = {Q, K, V, O, row_ptr, col_idx, work_order, queue};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      s_arg[2 * i] = (uint32_t)(uintptr_t)ptrs[i];
+      s_arg[2 * i + 1] = (uint32_t)((uintptr_t)ptrs[i] >> 32);
+    }
+    s_arg[16] = (uint32_t)H;
+    s_arg[17] = (uint32_t)items;
+    s_arg[18] = __float_as_uint(c2);
+  }
+  if (threadIdx.x < 2) {
+    s_fin[threadIdx.x] = 0x7fffffff;
+    s_fst[threadIdx.x][0] = blockIdx.x % kParts;   // partition to serve first
+    s_fst[threadIdx.x][1] = 0;                     // partitions tried
   }
   __syncthreads();
-  auto fetch_next = [&]() __attribute__((always_inline)) {
-    int p_f = __builtin_amdgcn_readfirstlane(s_fstate[0]);
-    int tries_f = __builtin_amdgcn_readfirstlane(s_fstate[1]);
-    int b_ = 0, r_ = -1;
-    if (!queue) {   // one workgroup per row: row blockIdx.x of the order, once
-      if (tries_f == 0) {
-        tries_f = kParts;
-        const int item = blockIdx.x;
-        b_ = item / src.rows;
-        const int j = item - b_ * src.rows;
-        r_ = src.order ? src.order[j] : j;
-      }
+
+  // (readfirstlane returns a signed int: each half goes through uint32_t so
+  // that a low word with bit 31 set is not sign-extended into the high word)
+  auto ap = [&](int i) __attribute__((always_inline)) -> uintptr_t {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane(s_arg[2 * i]);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane(s_arg[2 * i + 1]);
+    return (uintptr_t)lo | ((uintptr_t)hi << 32);
+  };
+  auto nheads = [&]() __attribute__((always_inline)) -> int { return __builtin_amdgcn_readfirstlane(s_arg[16]); };
+  auto part_len = [&](int p) __attribute__((always_inline)) -> int {
+    if (ap(6)) return s_poff[p + 1] - s_poff[p];
+    return ((nheads() - p + kParts - 1) / kParts) * nqb;
+  };
+  auto o_row = [&](int b, int r) __attribute__((always_inline)) -> size_t {
+    const int h = r / nqb, qb = r - h * nqb;
+    return (((size_t)b * nheads() + h) * (size_t)nqb + qb) * (size_t)BLK * D;
+  };
+
+  // ---- row fetch (wave 0 of each group) ----
+  // f_step: 0 done (the group's descriptor holds the next row or none),
+  // 1 counter pop due, 2 pop in flight, 3 work-order entry in flight, 4 list
+  // bounds in flight, 5 first key blocks in flight.  The rest of the fetch
+  // state (partition, partitions tried, batch, row, list start, blocks) lives
+  // in LDS between calls, so that no scalar register holds it through the
+  // phase loop.
+  int f_step = 1;
+  int f_val = 0;   // result of the load in flight
+  auto write_desc = [&](int b, int r, int beg, int n, int k0, int k1) __attribute__((always_inline)) {
+    if (lane == 0) {
+      s_desc[grp][0] = b;
+      s_desc[grp][1] = r;
+      s_desc[grp][2] = beg;
+      s_desc[grp][3] = n;
+      s_desc[grp][4] = k0;
+      s_desc[grp][5] = k1;
     }
-    while (queue && tries_f < kParts) {
-      int k = 0;
-      if (lane == 0) k = atomicAdd(queue + p_f * kQueueStride, 1);
-      k = __builtin_amdgcn_readfirstlane(k);
-      const int len = src.part_len(p_f);
-      if (k >= src.B * len) {
-        p_f = (p_f + 1) % kParts;
-        ++tries_f;
-        continue;
+  };
+  // an empty row is written as zeros by the fetching wave
+  auto zero_row = [&](int b, int r) __attribute__((always_inline)) {
+    g_u32x4* const dst = (g_u32x4*)((g_bf16*)ap(3) + o_row(b, r));
+    for (int i = lane; i < BLK * D / 8; i += 64) dst[i] = u32x4{0u, 0u, 0u, 0u};
+  };
+  // take the result of the link in flight and issue the next; with finish,
+  // run the chain to its end
+  auto fetch = [&](bool finish) __attribute__((always_inline)) {
+    const g_i32* const rp_ = (const g_i32*)ap(4);
+    const g_i32* const ci_ = (const g_i32*)ap(5);
+    const g_i32* const wo_ = (const g_i32*)ap(6);
+    g_i32* const qu_ = (g_i32*)ap(7);
+    const int items_ = __builtin_amdgcn_readfirstlane(s_arg[17]);
+    const int rows_ = nheads() * nqb;
+    int f_p = __builtin_amdgcn_readfirstlane(s_fst[grp][0]);
+    int f_tries = __builtin_amdgcn_readfirstlane(s_fst[grp][1]);
+    int f_b = __builtin_amdgcn_readfirstlane(s_fst[grp][2]);
+    int f_r = __builtin_amdgcn_readfirstlane(s_fst[grp][3]);
+    int f_beg = __builtin_amdgcn_readfirstlane(s_fst[grp][4]);
+    int f_n = __builtin_amdgcn_readfirstlane(s_fst[grp][5]);
+    auto issue_bounds = [&]() __attribute__((always_inline)) {
+      if (DENSE) {
+        write_desc(f_b, f_r, 0, nkb_valid, 0, nkb_valid > 1 ? 1 : 0);
+        f_step = 0;
+      } else {
+        if (lane < 2) f_val = rp_[f_r + lane];
+        f_step = 4;
       }
-      b_ = k / len;
-      r_ = src.part_row(p_f, k - b_ * len);
-      break;
-    }
-    int beg_ = 0, nblk_ = 0, k0_ = 0, k1_ = 0, k2_ = 0;
-    if (r_ >= 0) {
-      beg_ = DENSE ? 0 : row_ptr[r_];
-      nblk_ = (DENSE ? nkb_valid : row_ptr[r_ + 1]) - beg_;
-      if (nblk_ > 0) {
-        auto bl = [&](int i) __attribute__((always_inline)) -> int {
-          i = i < nblk_ ? i : nblk_ - 1;
-          return DENSE ? i : col_idx[beg_ + i];
-        };
-        k0_ = bl(0);
-        k1_ = bl(1);
-        k2_ = bl(2);
+    };
+    auto issue_pop = [&]() __attribute__((always_inline)) {
+      if (!qu_) {   // no queue: workgroup i serves rows 2i and 2i+1 of the order, one per group
+        const int item = 2 * blockIdx.x + grp;
+        if (f_tries == 0 && item < items_) {
+          f_tries = 1;
+          f_b = item / rows_;
+          const int jr = item - f_b * rows_;
+          if (wo_) {
+            if (lane == 0) f_val = wo_[jr];
+            f_step = 3;
+          } else {
+            f_r = jr;
+            issue_bounds();
+          }
+        } else {
+          write_desc(0, -1, 0, 0, 0, 0);
+          f_step = 0;
+        }
+        return;
       }
+      if (lane == 0) f_val = __hip_atomic_fetch_add(qu_ + f_p * kQueueStride, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      f_step = 2;
+    };
+    for (;;) {
+      if (f_step == 1) {
+        issue_pop();
+      } else if (f_step == 2) {
+        const int k = __builtin_amdgcn_readfirstlane(f_val);
+        const int len = part_len(f_p);
+        if (k >= (items_ / rows_) * len) {
+          f_p = (f_p + 1) % kParts;
+          if (++f_tries >= kParts) {
+            write_desc(0, -1, 0, 0, 0, 0);
+            f_step = 0;
+          } else {
+            issue_pop();
+          }
+        } else {
+          f_b = k / len;
+          const int jr = k - f_b * len;
+          if (wo_) {
+            if (lane == 0) f_val = wo_[s_poff[f_p] + jr];
+            f_step = 3;
+          } else {
+            f_r = (f_p + kParts * (jr / nqb)) * nqb + jr % nqb;
+            issue_bounds();
+          }
+        }
+      } else if (f_step == 3) {
+        f_r = __builtin_amdgcn_readfirstlane(f_val);
+        issue_bounds();
+      } else if (f_step == 4) {
+        f_beg = __builtin_amdgcn_readlane(f_val, 0);
+        f_n = __builtin_amdgcn_readlane(f_val, 1) - f_beg;
+        if (f_n <= 0) {
+          zero_row(f_b, f_r);
+          f_step = 1;
+        } else {
+          if (lane < 2) f_val = ci_[f_beg + (lane < f_n ? lane : f_n - 1)];
+          f_step = 5;
+        }
+      } else if (f_step == 5) {
+        write_desc(f_b, f_r, f_beg, f_n, __builtin_amdgcn_readlane(f_val, 0), __builtin_amdgcn_readlane(f_val, 1));
+        f_step = 0;
+      }
+      if (f_step == 0 || !finish) break;
+      if (f_step != 1) wait_vm();
     }
     if (lane == 0) {
-      s_fstate[0] = p_f;
-      s_fstate[1] = tries_f;
-      s_next[0] = b_;
-      s_next[1] = r_;
-      s_next[2] = beg_;
-      s_next[3] = nblk_;
-      s_next[4] = k0_;
-      s_next[5] = k1_;
-      s_next[6] = k2_;
+      s_fst[grp][0] = f_p;
+      s_fst[grp][1] = f_tries;
+      s_fst[grp][2] = f_b;
+      s_fst[grp][3] = f_r;
+      s_fst[grp][4] = f_beg;
+      s_fst[grp][5] = f_n;
     }
   };
-  auto body = [&](int b, int r, int beg, int nblk, int pk0, int pk1, int pk2) {
+
+  // ---- the group's row state ----
+  // (flags are ints: wave-uniform values the compiler keeps in scalar
+  // registers, not per-lane masks)
+  bool cur = false;    // a row is being computed (S side)
+  int cb = 0, cr = 0, cbeg = 0, cnb = 0, cn = 0, j = 0;   // batch, row, list start, blocks, sub-tiles, sub-tile
+  int kb0 = 0, kb1 = 0;         // key blocks of the current and the next block
+  int cbase = 0, ck_cur = 0, ck_nxt = 0;   // readlane window over the row's list
+  __amdgpu_buffer_rsrc_t rk = make_rsrc(K, 0), rv = make_rsrc(V, 0);
+  bool pend = false;   // the previous row's O is due (after its last P*V); its row in s_prev
+  float l_fin = 0.f;
+  bool nxt = false;    // at a row's end: a next row is in the group's descriptor
+
+  auto chunk_load = [&](int beg, int nblk, int cix) __attribute__((always_inline)) -> int {
+    int i = 64 * cix + lane;
+    i = i < nblk ? i : nblk - 1;
+    return ((const g_i32*)ap(5))[beg + i];
+  };
+  // key block i of the current row (i grows by one per call, clamped to the row)
+  auto blk_at = [&](int i) __attribute__((always_inline)) -> int {
+    i = i < cnb ? i : cnb - 1;
+    if (DENSE) return i;
+    const bool adv = (i >> 6) != cbase;
+    if (adv) {
+      ++cbase;
+      ck_cur = ck_nxt;
+    }
+    const int v = __builtin_amdgcn_readlane(ck_cur, i & 63);
+    if (adv) ck_nxt = chunk_load(cbeg, cnb, cbase + 1);
+    return v;
+  };
+  auto set_row = [&](int b, int r, int beg, int nblk, int k0, int k1) __attribute__((always_inline)) {
+    cb = b;
+    cr = r;
+    cbeg = beg;
+    cnb = nblk;
+    cn = 2 * nblk;
+    j = 0;
+    kb0 = k0;
+    kb1 = k1;
+    cbase = 0;
+    const int h = r / nqb;
+    const size_t base = ((size_t)b * nheads() + h) * (size_t)L * D;
+    rk = make_rsrc((const bf16*)ap(1) + base, k_bytes);
+    rv = make_rsrc((const bf16*)ap(2) + base, v_bytes);
+  };
+  // this lane's Q row of row (b, r): 8 consecutive d per k-step, raw bf16.
+  // A padded query (q >= seq_len) is taken as zero, so that whatever the
+  // padding holds its lane computes exactly what zero padding gives (its
+  // output is zeroed anyway, but a non-finite value would also move the
+  // wave's shared rescale decisions).
+  auto q_load = [&](int b, int r, bf16x8* qr) __attribute__((always_inline)) {
     const int h = r / nqb, qb = r - h * nqb;
-    const size_t base = ((size_t)b * H + h) * (size_t)L * D;
-    const size_t qbase = SPLITQ ? ((size_t)b * H + h) * (size_t)Lq * D : base;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + base, slab_bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vt + base, slab_bytes);
-    const int q = qb * BLK + 32 * w + c;   // this lane's query
-
-    const int n = nblk * 2;   // sub-tiles
-    // key blocks around phase t (block b = t/2): kbm = b-1, kb0 = b, kb1 =
-    // b+1; kb2 (b+2) is loaded a block ahead
-    int kbm = 0, kb0 = 0, kb1 = 0, kb2 = 0;
-    // Inside the phase loop the indices come from two vector registers that
-    // hold 64 consecutive entries of the row's list each (lane l: entry
-    // 64*chunk + l), read with readlane: a scalar memory load there would
-    // make the next LDS wait also wait for it.  The next chunk is loaded 64
-    // blocks before it is read.
-    auto idx_chunk = [&](int cix) __attribute__((always_inline)) -> int {
-      int j = 64 * cix + lane;
-      j = j < nblk ? j : nblk - 1;
-      return DENSE ? j : col_idx[beg + j];
-    };
-    int cbase = 0, ck_cur = 0, ck_nxt = 0;
-    if (n > 0) {
-      kb0 = pk0;
-      kb1 = pk1;
-      kb2 = pk2;
-      if (!DENSE) {
-        ck_cur = idx_chunk(0);
-        ck_nxt = idx_chunk(1);
-      }
-      // K(0) by group A, K(1) by group B
-#pragma unroll
-      for (int i = 0; i < G::KPER; ++i)
-        k_dma_one<D, BLK>(i, rk, kb0 * BLK + grp * G::BN, grp == 0 ? ks0 : ks1, w, kpat);
-    }
-
-    // Q is scaled by c2 (the softmax scale in log2 units) on loading and
-    // rounded to bf16, so that the products give scores in log2 units and,
-    // with the accumulators started at -ref, exp2 needs no vector arithmetic
-    // before it
-    // the token this lane's query reads (anchor rows: through the anchor
-    // map; padding rows past q_valid read token 0 and are never written)
+    const int q = qb * BLK + 32 * w + c;
     const int qsrc = SPLITQ ? (q < q_valid ? anchor_token(q, grid_rows, grid_cols, k_anchor) : 0) : q;
-    bf16x8 qreg[DS];
+    const g_bf16* src = (const g_bf16*)ap(0) + ((size_t)b * nheads() + h) * (size_t)L * D + (size_t)qsrc * D + 8 * g;
+    const bool live = SPLITQ || q < seq_len;
 #pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      const bf16x8 qv = *reinterpret_cast<const bf16x8*>(Q + base + (size_t)qsrc * D + 16 * s + 8 * g);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qreg[s][e] = (bf16)((float)qv[e] * c2);
-    }
+    for (int s = 0; s < DS; ++s) qr[s] = live ? *(const g_bf16x8*)(src + 16 * s) : bf16x8{};
+  };
 
-    f32x16 oacc[DT];
+  // the row's Q: raw bf16 from the load until it is scaled in place
+  bf16x8 qreg[DS];
+  f32x16 oacc[DT];
 #pragma unroll
-    for (int t = 0; t < DT; ++t) oacc[t] = f32x16{};
-    // this group's reference (log2 units) and row sum; fresh until the
-    // reference has been set from the maximum of a sub-tile with valid keys
-    float ref = 0.f, l_run = 0.f;
-    bool fresh = true;
-    f32x16 cneg = {};   // -ref in every accumulator register
-    f32x16 sacc[2];
-    bf16x8 pb[KS];
+  for (int t = 0; t < DT; ++t) oacc[t] = f32x16{};
+  // Q is scaled by c2 (the softmax scale in log2 units) on loading and
+  // rounded to bf16, so that the products give scores in log2 units and,
+  // with the accumulators started at -ref, exp2 needs no vector arithmetic
+  // before it
+  auto q_scale = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) pb[ks] = bf16x8{};   // P*V of phases 0 and 1 adds nothing
-    bool rescale = false;   // O *= alpha is due before the next P*V
-    float alpha = 1.f;
+    for (int s = 0; s < DS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qreg[s][e] = (bf16)((float)qreg[s][e] * __uint_as_float(s_arg[18]));
+  };
+  // the group's reference (log2 units) and row sum; fresh until the
+  // reference has been set from the maximum of a sub-tile with valid keys
+  float ref = 0.f, l_run = 0.f;
+  bool fresh = true;
+  f32x16 cneg = {};   // -ref in every accumulator register
+  f32x16 sacc[2];
+  bf16x8 pb[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) pb[ks] = bf16x8{};
+  bool rescale = false;   // O *= alpha is due before the next P*V
+  float alpha = 1.f;
+
+  // ---- prologue: each group's first row, its K(0) tile and Q ----
+  if (w == 0) fetch(true);
+  __syncthreads();
+  {
+    const int r0 = __builtin_amdgcn_readfirstlane(s_desc[grp][1]);
+    if (r0 >= 0) {
+      set_row(__builtin_amdgcn_readfirstlane(s_desc[grp][0]), r0, __builtin_amdgcn_readfirstlane(s_desc[grp][2]),
+              __builtin_amdgcn_readfirstlane(s_desc[grp][3]), __builtin_amdgcn_readfirstlane(s_desc[grp][4]),
+              __builtin_amdgcn_readfirstlane(s_desc[grp][5]));
+      if (!DENSE) {
+        ck_cur = chunk_load(cbeg, cnb, 0);
+        ck_nxt = chunk_load(cbeg, cnb, 1);
+      }
+#pragma unroll
+      for (int i = 0; i < NDMA; ++i) {
+        const int m = w + 4 * i;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kst[0] + gbase + m * 1024), 16, kpat,
+                                                 kb0 * BLK * RB + m * 1024, 0, 0);
+      }
+      q_load(cb, cr, qreg);
+      cur = true;
+      f_step = 1;
+    } else {
+      f_step = 0;
+      if (w == 0 && lane == 0) s_fin[grp] = -1;
+    }
     wait_vm();
-    lds_barrier();
+    if (cur) q_scale();
+  }
+  __syncthreads();
+  if (s_fin[0] < 0 && s_fin[1] < 0) return;
+  int done = !cur;   // the group has finished (read through readfirstlane: uniform)
 
-    // after a phase of odd t the next phase is in the next block
-    auto shift = [&](int t) __attribute__((always_inline)) {
-      kbm = kb0;
-      kb0 = kb1;
-      kb1 = kb2;
-      int j = (t + 1) / 2 + 2;
-      j = j < nblk ? j : nblk - 1;
-      if (DENSE) {
-        kb2 = j;
+  // matrix phase of stream cycle x (TM = x % 2 fixes the stages)
+  auto mphase = [&](auto tmc) __attribute__((always_inline)) {
+    constexpr int TM = decltype(tmc)::value;
+    if (__builtin_expect(!cur && !pend, 0)) {
+      lds_barrier();
+      return;
+    }
+    // O moves to the reference P(x-1) was computed against
+    if (__builtin_expect(rescale, 0)) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
+      rescale = false;
+    }
+    // K(x+1): the second half of this block, the next block, or at the end
+    // of a row the next row's first block; V(x): this sub-tile
+    int kd = TM == 0 ? kb0 * BLK + 64 : kb1 * BLK;
+    __amdgpu_buffer_rsrc_t rkd = rk;
+    const bool last = TM == 1 && cur && j == cn - 1;
+    int nb = 0, nr = 0;
+    if (__builtin_expect(last, 0)) {
+      nr = __builtin_amdgcn_readfirstlane(s_desc[grp][1]);
+      nxt = nr >= 0;
+      if (nxt) {
+        nb = __builtin_amdgcn_readfirstlane(s_desc[grp][0]);
+        rkd = make_rsrc((const bf16*)ap(1) + ((size_t)nb * nheads() + nr / nqb) * (size_t)L * D, k_bytes);
+        kd = __builtin_amdgcn_readfirstlane(s_desc[grp][4]) * BLK;
+        // the current row's list is not read past this point
+        if (!DENSE) {
+          const int nbeg = __builtin_amdgcn_readfirstlane(s_desc[grp][2]);
+          const int nn = __builtin_amdgcn_readfirstlane(s_desc[grp][3]);
+          ck_cur = chunk_load(nbeg, nn, 0);
+          ck_nxt = chunk_load(nbeg, nn, 1);
+        }
+      }
+    }
+    const int vd = kb0 * BLK + TM * 64;
+    // this wave's first DMA destination in its group's half of a stage,
+    // re-formed in every phase so that the destinations (one per stage and
+    // instruction) are not all kept in scalar registers through the loop
+    int wq, wdst;
+    asm volatile("s_mov_b32 %0, %1" : "=s"(wq) : "s"(w));
+    asm volatile("s_mov_b32 %0, %1" : "=s"(wdst) : "s"(gbase));
+    wdst += wq * 1024;
+    auto dma_share = [&](int s) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = s * 2 * NDMA / DS; i < (s + 1) * 2 * NDMA / DS; ++i) {
+        const int m = wq + 4 * (i % NDMA);
+        if (i < NDMA) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rkd, (lds_void*)(kst[TM ^ 1] + wdst + 4096 * i), 16,
+                                                   kpat, kd * RB + m * 1024, 0, 0);
+        } else {
+          const int soff = VT ? vd * 2 + m * 16 * L : vd * RB + m * 1024;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vst[TM] + wdst + 4096 * (i - NDMA)), 16,
+                                                   vpat, soff, 0, 0);
+        }
+      }
+    };
+    __builtin_amdgcn_s_setprio(2);
+    // S(x) and P*V(x-1) run as one sequence of slots, each one pair of
+    // products and the operand reads of the slot PF ahead
+    constexpr int NSL = DS + DT * KS / 2;
+    constexpr int PF = 2;
+    auto rd = [&](int sl, int h) __attribute__((always_inline)) -> u32x4 {
+      if (sl < DS) return kread(TM, h, sl);
+      const int i = 2 * (sl - DS) + h;
+      return vop(TM ^ 1, i % DT, i / DT);
+    };
+    u32x4 ra[PF + 1][2];
+#pragma unroll
+    for (int sl = 0; sl < PF; ++sl) {
+      ra[sl][0] = rd(sl, 0);
+      ra[sl][1] = rd(sl, 1);
+    }
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl) {
+      if (sl + PF < NSL) {
+        ra[(sl + PF) % (PF + 1)][0] = rd(sl + PF, 0);
+        ra[(sl + PF) % (PF + 1)][1] = rd(sl + PF, 1);
+      }
+      const bf16x8 a0 = __builtin_bit_cast(bf16x8, ra[sl % (PF + 1)][0]);
+      const bf16x8 a1 = __builtin_bit_cast(bf16x8, ra[sl % (PF + 1)][1]);
+      if (sl < DS) {
+        sacc[0] = mfma_bf16(a0, qreg[sl], sl == 0 ? cneg : sacc[0]);
+        sacc[1] = mfma_bf16(a1, qreg[sl], sl == 0 ? cneg : sacc[1]);
+        dma_share(sl);
+        // past the row's last scores its Q is dead: load the next row's
+        if (TM == 1 && sl == DS - 1 && __builtin_expect(last && nxt, 0)) q_load(nb, nr, qreg);
       } else {
-        const bool adv = (j >> 6) != cbase;   // j moves on by at most one per call
-        if (adv) {
-          ++cbase;
-          ck_cur = ck_nxt;
-        }
-        kb2 = __builtin_amdgcn_readlane(ck_cur, j & 63);
-        if (adv) ck_nxt = idx_chunk(cbase + 1);
+        const int i0 = 2 * (sl - DS), i1 = i0 + 1;
+        oacc[i0 % DT] = mfma_bf16(a0, pb[i0 / DT], oacc[i0 % DT]);
+        oacc[i1 % DT] = mfma_bf16(a1, pb[i1 / DT], oacc[i1 % DT]);
       }
-    };
-    // matrix phase t, with TM = t % 6 fixing the stages.  S(t) and
-    // P*V(t-2) run as one sequence of slots, each one pair of products and
-    // the operand reads of the slot PF ahead, so the P*V operands are in
-    // flight while the last scores are computed.  Every phase up to n+1 has
-    // this one shape: in phases 0 and 1 P is zero, so P*V adds nothing (the
-    // V^T stages always hold finite values: zeroed at the start, later only
-    // V^T tiles); in phases n and n+1 the scores come from a stale K stage
-    // and are never used; the DMA keys are clamped to the row.
-    auto mphase = [&](int t, auto tmc) __attribute__((always_inline)) {
-      constexpr int TM = decltype(tmc)::value;
-      constexpr int KST = TM % 3, KDST = (TM + 2) % 3, VST = (TM + 1) % 3, VDST = TM % 3;
-      // the wave index, re-read in every phase so that the DMA destinations
-      // (one per stage and instruction) are formed where they are used
-      // instead of all being kept in scalar registers
-      int wq;
-      asm volatile("s_mov_b32 %0, %1" : "=s"(wq) : "s"(w));
-      const int kd = kb1 * BLK + (TM & 1) * G::BN;   // K(t+2), clamped by blk()
-      const int vd = kb0 * BLK + (TM & 1) * G::BN;   // V^T(t)
-      const u32x4* const kc = kst[KST];
-      const u32x4* const vc = vst[VST];
-      auto dma_share = [&](int s) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = s * NDMA / DS; i < (s + 1) * NDMA / DS; ++i) {
-          if (i < G::KPER)
-            k_dma_one<D, BLK>(i, rk, kd, kst[KDST], wq, kpat);
-          else
-            v_dma_one<D, BLK>(i - G::KPER, rv, vd, L, vst[VDST], wq, vpat);
-        }
-      };
-      // O moves to the reference P(t-2) was computed against
-      auto apply_rescale = [&]() __attribute__((always_inline)) {
-        if (rescale) {
-#pragma unroll
-          for (int tt = 0; tt < DT; ++tt) oacc[tt] *= alpha;
-          rescale = false;
-        }
-      };
-      if (t < n + 2) {
-        apply_rescale();
-        constexpr int NSL = DS + DT * KS / 2;   // slots: DS of scores, then P*V
-        constexpr int PF = 2;                   // operand reads run PF slots ahead
-        // operand h of slot sl: K row tile h at k-step sl, or the V^T tile of
-        // P*V product 2 (sl - DS) + h (ks = i / DT, dt = i % DT)
-        auto rd = [&](int sl, int h) __attribute__((always_inline)) -> u32x4 {
-          if (sl < DS) return kread(kc, h, sl);
-          const int i = 2 * (sl - DS) + h;
-          return vread(vc, i % DT, i / DT);
-        };
-        u32x4 ra[PF + 1][2];
-#pragma unroll
-        for (int sl = 0; sl < PF; ++sl) {
-          ra[sl][0] = rd(sl, 0);
-          ra[sl][1] = rd(sl, 1);
-        }
-#pragma unroll
-        for (int sl = 0; sl < NSL; ++sl) {
-          if (sl + PF < NSL) {
-            ra[(sl + PF) % (PF + 1)][0] = rd(sl + PF, 0);
-            ra[(sl + PF) % (PF + 1)][1] = rd(sl + PF, 1);
-          }
-          const bf16x8 a0 = __builtin_bit_cast(bf16x8, ra[sl % (PF + 1)][0]);
-          const bf16x8 a1 = __builtin_bit_cast(bf16x8, ra[sl % (PF + 1)][1]);
-          if (sl < DS) {
-            sacc[0] = mfma_bf16(a0, qreg[sl], sl == 0 ? cneg : sacc[0]);
-            sacc[1] = mfma_bf16(a1, qreg[sl], sl == 0 ? cneg : sacc[1]);
-            dma_share(sl);
-          } else {
-            const int i0 = 2 * (sl - DS), i1 = i0 + 1;
-            oacc[i0 % DT] = mfma_bf16(a0, pb[i0 / DT], oacc[i0 % DT]);
-            oacc[i1 % DT] = mfma_bf16(a1, pb[i1 / DT], oacc[i1 % DT]);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      lds_barrier();
-      if (TM & 1) shift(t);
-    };
-    // vector phase t: P(t-1); then this wave's DMA of the phase before, which
-    // the next phase reads, must have landed
-    auto vphase = [&](int t, auto tmc) __attribute__((always_inline)) {
-      constexpr int TM = decltype(tmc)::value;
-      {
-        const int x = t - 1;
-        if (x >= 0 && x < n) {
-          const int k0 = (TM & 1) ? kb0 * BLK : kbm * BLK + G::BN;
-          if (k0 + G::BN > seq_len) {
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-              for (int rr = 0; rr < 16; ++rr)
-                if (k0 + 32 * mt + slice_key(rr, g) >= seq_len) sacc[mt][rr] = kNegInf;
-          }
-          // P rounded to bf16 for the products; its row sums in fp32 from
-          // the unrounded values, in four chains (plain adds run beside the
-          // other wave's matrix products far better than dot2 does)
-          float ls[2];
-          auto probs = [&]() __attribute__((always_inline)) {
-            float ch[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-              bf16x8 v;
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const float pe = fast_exp2(sacc[ks >> 1][8 * (ks & 1) + e]);
-                v[e] = (bf16)pe;
-                ch[e & 3] += pe;
-              }
-              pb[ks] = v;
-            }
-            ls[0] = ch[0] + ch[1];
-            ls[1] = ch[2] + ch[3];
-          };
-          probs();
-          // the reference moves to the row maximum on the first sub-tile
-          // with valid keys, and later only when a lane's sum passes kSumCap
-          const bool redo = (fresh && k0 < seq_len) || __any(!(ls[0] + ls[1] <= kSumCap));
-          if (redo) {
-            float mx = kNegInf;
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-              for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, sacc[mt][rr]);
-            mx = pair_max(mx);   // relative to ref; finite (a valid key is in range)
-            const float delta = fresh ? mx : fmaxf(mx, 0.f);
-            if (!fresh) {
-              alpha = fast_exp2(-delta);
-              l_run *= alpha;
-              rescale = true;
-            }
-            fresh = false;
-            ref += delta;
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-              for (int rr = 0; rr < 16; ++rr) {
-                sacc[mt][rr] -= delta;
-                cneg[rr] = -ref;
-              }
-          }
-          if (redo) probs();
-          l_run += ls[0] + ls[1];
-        }
-        wait_vm();
-      }
-      lds_barrier();
-      if (TM & 1) shift(t);
-    };
-
-    // each wave alternates matrix and vector phases, six to a loop turn with
-    // no phase skipped (a phase past the row's work only meets the barrier),
-    // so on every path a matrix phase follows the vector phase that waited
-    // for its DMA.  Both groups meet T + 1 barriers: group A runs phases
-    // 0 .. T-1 and one empty one, group B an empty vector phase 0 and then
-    // phases 1 .. T.
-    const int T = ((n + 2 + 5) / 6) * 6;
-    auto run = [&](auto gc) __attribute__((always_inline)) {
-      constexpr int GR = decltype(gc)::value;
-      if (GR == 1) vphase(0, Cst<0>{});
-      for (int t = GR; t < T + GR; t += 6) {
-        mphase(t, Cst<GR % 6>{});
-        vphase(t + 1, Cst<(GR + 1) % 6>{});
-        mphase(t + 2, Cst<(GR + 2) % 6>{});
-        vphase(t + 3, Cst<(GR + 3) % 6>{});
-        mphase(t + 4, Cst<(GR + 4) % 6>{});
-        vphase(t + 5, Cst<(GR + 5) % 6>{});
-      }
-      if (GR == 0) lds_barrier();
-    };
-    if (n > 0) {
-      if (grp == 0)
-        run(Cst<0>{});
-      else
-        run(Cst<1>{});
+      __builtin_amdgcn_sched_barrier(0);
     }
-
-    // group B hands O, ref and l to group A: O in 8-float chunks u = 0 ..
-    // 2*DT-1 of every lane, chunk u in stage object (u * 8 KiB) / OBJ of
-    // K0, K1, K2, V0 (never V1 or V2: the P*V of the next row's phases 0
-    // and 1 reads those with zero probabilities, so they may only hold V^T
-    // tiles or zeros), ref and l in s_ml
-    char* const objs[4] = {(char*)ks0, (char*)ks1, (char*)ks2, (char*)vs0};
-    auto chunk = [&](int u) __attribute__((always_inline)) -> float* {
-      return reinterpret_cast<float*>(objs[(u * 8192) / OBJ] + (u * 8192) % OBJ) + (w * 64 + lane) * 8;
-    };
-    float* const ml = s_ml + (w * 64 + lane) * 2;
-    if (grp == 1) {
-#pragma unroll
-      for (int u = 0; u < 2 * DT; ++u) {
-        f32x4 lo, hi;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          lo[e] = oacc[u >> 1][8 * (u & 1) + e];
-          hi[e] = oacc[u >> 1][8 * (u & 1) + 4 + e];
-        }
-        reinterpret_cast<f32x4*>(chunk(u))[0] = lo;
-        reinterpret_cast<f32x4*>(chunk(u))[1] = hi;
-      }
-      ml[0] = fresh ? kNegInf : ref;
-      ml[1] = l_run;
-    }
+    __builtin_amdgcn_s_setprio(0);
     lds_barrier();
-    if (grp == 0) {
-      // a group that saw no valid key (fresh) holds nothing and is left out
-      const float mca = fresh ? kNegInf : ref;
-      const float mcb = ml[0], lb = ml[1];
-      float m = fmaxf(mca, mcb);
-      if (m == kNegInf) m = 0.f;
-      const float aa = fast_exp2(mca - m), ab = fast_exp2(mcb - m);
-      const float l_tot = pair_sum(l_run * aa + lb * ab);
-      const float inv = (q < (SPLITQ ? q_valid : seq_len) && l_tot > 0.f) ? 1.f / l_tot : 0.f;
-      const float fa = aa * inv, fb = ab * inv;
-      bf16* Ob = O + qbase + (size_t)q * D;
+  };
+
+  // vector phase of stream cycle x; gp is the global phase index
+  auto vphase = [&](auto tmc, int gp) __attribute__((always_inline)) {
+    constexpr int TM = decltype(tmc)::value;
+    if (__builtin_expect(!cur && !pend, 0)) {
+      lds_barrier();
+      return;
+    }
+    if (__builtin_expect(pend, 0)) {
+      // the previous row's last P*V ran in the matrix phase just ended: O =
+      // acc / l; padded query rows (and rows that saw no key) are zero
+      const int pb = __builtin_amdgcn_readfirstlane(s_prev[grp][0]);
+      const int pr = __builtin_amdgcn_readfirstlane(s_prev[grp][1]);
+      const float l_tot = pair_sum(l_fin);
+      const int q = (pr % nqb) * BLK + 32 * w + c;
+      const bool valid = q < qlim && l_tot > 0.f;
+      const float inv = valid ? 1.f / l_tot : 0.f;
+      g_bf16* const Ob = (g_bf16*)ap(3) + o_row(pb, pr) + (size_t)(32 * w + c) * D;
 #pragma unroll
-      for (int u = 0; u < 2 * DT; ++u) {
-        const f32x4 lo = reinterpret_cast<const f32x4*>(chunk(u))[0];
-        const f32x4 hi = reinterpret_cast<const f32x4*>(chunk(u))[1];
-        const int t = u >> 1;
+      for (int t = 0; t < DT; ++t) {
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int rq = 2 * (u & 1) + half;   // register quad: rows 4*rq .. 4*rq+3 of the tile
-          const f32x4 ob = half ? hi : lo;
-          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        for (int rq = 0; rq < 4; ++rq) {
           bf16x4 o;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = (bf16)(oacc[t][4 * rq + e] * fa + ob[e] * fb);
-          *reinterpret_cast<bf16x4*>(Ob + 32 * t + 8 * rq + 4 * g) = o;
+          for (int e = 0; e < 4; ++e) o[e] = valid ? (bf16)(oacc[t][4 * rq + e] * inv) : (bf16)0.f;
+          *(g_bf16x4*)(Ob + 32 * t + 8 * rq + 4 * g) = o;
+        }
+        oacc[t] = f32x16{};
+      }
+      pend = false;
+      if (!cur) {
+        done = 1;
+        s_fin[grp] = gp;   // every lane of the group writes the same value
+      }
+    }
+    if (__builtin_expect(cur, 1)) {
+      const int k0 = kb0 * BLK + TM * 64;
+      if (__builtin_expect(k0 + 64 > seq_len, 0)) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr)
+            if (k0 + 32 * mt + slice_key(rr, g) >= seq_len) sacc[mt][rr] = kNegInf;
+      }
+      // P rounded to bf16 for the products; its row sums in fp32 from the
+      // unrounded values, in four chains (plain adds run beside the other
+      // wave's matrix products far better than dot2 does)
+      float ls[2] = {0.f, 0.f};
+      auto probs = [&]() __attribute__((always_inline)) {
+        float ch[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          bf16x8 v;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float pe = fast_exp2(sacc[ks >> 1][8 * (ks & 1) + e]);
+            v[e] = (bf16)pe;
+            ch[e & 3] += pe;
+          }
+          pb[ks] = v;
+        }
+        ls[0] = ch[0] + ch[1];
+        ls[1] = ch[2] + ch[3];
+      };
+      // the reference moves to the row maximum on the first sub-tile with
+      // valid keys, and later only when a lane's sum passes kSumCap
+      bool redo = fresh && k0 < seq_len;
+      if (__builtin_expect(!redo, 1)) {
+        probs();
+        redo = __any(!(ls[0] + ls[1] <= kSumCap));
+      }
+      if (__builtin_expect(redo, 0)) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, sacc[mt][rr]);
+        mx = pair_max(mx);   // relative to ref; finite (a valid key is in range)
+        const float delta = fresh ? mx : fmaxf(mx, 0.f);
+        if (!fresh) {
+          alpha = fast_exp2(-delta);
+          l_run *= alpha;
+          rescale = true;
+        }
+        fresh = false;
+        ref += delta;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) {
+            sacc[mt][rr] -= delta;
+            cneg[rr] = -ref;
+          }
+        probs();
+      }
+      l_run += ls[0] + ls[1];
+
+      if (__builtin_expect(w == 0 && f_step != 0, 0)) fetch(j >= cn - 2);
+
+      if (TM == 1 && __builtin_expect(j == cn - 1, 0)) {
+        // the row's last sub-tile: its O is written after the next P*V.
+        // Every wave of the group writes the same row to s_prev; it is read
+        // in the next phase, after the barrier.
+        l_fin = l_run;
+        s_prev[grp][0] = cb;
+        s_prev[grp][1] = cr;
+        pend = true;
+        if (nxt) {
+          set_row(__builtin_amdgcn_readfirstlane(s_desc[grp][0]), __builtin_amdgcn_readfirstlane(s_desc[grp][1]),
+                  __builtin_amdgcn_readfirstlane(s_desc[grp][2]), __builtin_amdgcn_readfirstlane(s_desc[grp][3]),
+                  __builtin_amdgcn_readfirstlane(s_desc[grp][4]), __builtin_amdgcn_readfirstlane(s_desc[grp][5]));
+          ref = 0.f;
+          l_run = 0.f;
+          fresh = true;
+          cneg = f32x16{};
+          wait_vm();
+          q_scale();
+          f_step = 1;
+        } else {
+          cur = false;
+        }
+      } else {
+        ++j;
+        if (TM == 1) {
+          kb0 = kb1;
+          kb1 = blk_at(j / 2 + 1);
         }
       }
-    } else if (wv == 4) {
-      // group B is idle while A merges: fetch the next row
-      fetch_next();
     }
-    // the stages are free again for the next row's DMA
+    wait_vm();
     lds_barrier();
   };
-  if (wv == 4) fetch_next();
-  __syncthreads();
+
+  // a finished group meets barriers until the other one has finished too;
+  // both decide from values written before the same barrier
+  int gp = 0;
+  auto stop = [&](int p) __attribute__((always_inline)) -> bool {
+    return __builtin_expect(__builtin_amdgcn_readfirstlane(done), 0) &&
+           __builtin_amdgcn_readfirstlane(s_fin[grp ^ 1]) <= p;
+  };
+  if (grp == 1) {
+    lds_barrier();
+    if (stop(gp)) return;
+    ++gp;
+  }
   for (;;) {
-    const int nb = __builtin_amdgcn_readfirstlane(s_next[0]);
-    const int nr = __builtin_amdgcn_readfirstlane(s_next[1]);
-    const int nbeg = __builtin_amdgcn_readfirstlane(s_next[2]);
-    const int nn = __builtin_amdgcn_readfirstlane(s_next[3]);
-    const int n0 = __builtin_amdgcn_readfirstlane(s_next[4]);
-    const int n1 = __builtin_amdgcn_readfirstlane(s_next[5]);
-    const int n2 = __builtin_amdgcn_readfirstlane(s_next[6]);
-    // every wave has read the entry before wave 4 may write the next one
-    // (it does so only in the row's merge, many barriers later)
-    __syncthreads();
-    if (nr < 0) break;
-    body(nb, nr, nbeg, nn, n0, n1, n2);
+    mphase(Cst<0>{});
+    if (stop(gp)) break;
+    ++gp;
+    vphase(Cst<0>{}, gp);
+    if (stop(gp)) break;
+    ++gp;
+    mphase(Cst<1>{});
+    if (stop(gp)) break;
+    ++gp;
+    vphase(Cst<1>{}, gp);
+    if (stop(gp)) break;
+    ++gp;
   }
 }
 
 // float32 path: 32-key slices, fp32 matrix cores (32x32x2), P kept in float32.
 // Lane (g, c) holds, for slice accumulator register r, key 2r + g (rows of
 // the K slice are fed in that order), which is the B layout of P^T.
-template <int D, int BLK, bool DENSE>
+template <int D, int BLK, bool DENSE, bool VT>
 __global__ __launch_bounds__(BLK * 2) void attn_fwd_f32_kernel(
-    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ Vt,
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     const int32_t* __restrict__ work_order, int32_t* __restrict__ queue, int items, int H, int L,
     int seq_len, int nkb_valid, float c2) {
@@ -935,9 +1163,9 @@ __global__ __launch_bounds__(BLK * 2) void attn_fwd_f32_kernel(
     const size_t base = ((size_t)b * H + h) * (size_t)L * D;
     const int q = qb * BLK + 32 * w + c;
 
-    float qreg[D / 2];
+    float qreg[D / 2];   // a padded query is taken as zero
 #pragma unroll
-    for (int s = 0; s < D / 2; ++s) qreg[s] = Q[base + (size_t)q * D + 2 * s + g];
+    for (int s = 0; s < D / 2; ++s) qreg[s] = q < seq_len ? Q[base + (size_t)q * D + 2 * s + g] : 0.f;
 
     f32x16 oacc[DT];
 #pragma unroll
@@ -954,8 +1182,13 @@ __global__ __launch_bounds__(BLK * 2) void attn_fwd_f32_kernel(
         for (int i = threadIdx.x; i < 32 * D; i += NT) {
           const int kr = i / D, dd = i % D;
           ldsK[kr * KP + dd] = K[base + (size_t)(k0 + kr) * D + dd];
-          const int vk = i % 32, vd = i / 32;   // V^T row vd, 32 consecutive keys
-          ldsV[vk * KP + vd] = Vt[base + (size_t)vd * L + k0 + vk];
+          if (VT) {
+            const int vk = i % 32, vd = i / 32;   // V^T row vd, 32 consecutive keys
+            ldsV[vk * KP + vd] = V[base + (size_t)vd * L + k0 + vk];
+          } else {
+            // padded keys meet zero probabilities: their V rows are taken as 0
+            ldsV[kr * KP + dd] = k0 + kr < seq_len ? V[base + (size_t)(k0 + kr) * D + dd] : 0.f;
+          }
         }
         __syncthreads();
         f32x16 sacc = {};
@@ -995,12 +1228,14 @@ __global__ __launch_bounds__(BLK * 2) void attn_fwd_f32_kernel(
       }
     }
     const float l_tot = pair_sum(l_run);
-    const float inv = (q < seq_len && l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    const bool valid = q < seq_len && l_tot > 0.f;
+    const float inv = valid ? 1.f / l_tot : 0.f;
     float* Ob = O + base + (size_t)q * D;
 #pragma unroll
     for (int t = 0; t < DT; ++t)
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) Ob[32 * t + 8 * (rr >> 2) + 4 * g + (rr & 3)] = oacc[t][rr] * inv;
+      for (int rr = 0; rr < 16; ++rr)
+        Ob[32 * t + 8 * (rr >> 2) + 4 * g + (rr & 3)] = valid ? oacc[t][rr] * inv : 0.f;
   });
 }
 
@@ -1046,23 +1281,24 @@ static hipError_t occupancy(Kern k, int threads, int* blocks_per_cu) {
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, k, threads, 0);
 }
 
-template <int D, bool DENSE, bool SPLITQ = false>
+template <int D, bool DENSE, bool SPLITQ, bool VT>
 static hipError_t launch_pp(const AttnArgs& a, hipStream_t st) {
   const int Lq = SPLITQ ? a.Lq : a.L;
   const int items = a.B * a.H * (Lq / 128);
   const float c2 = a.scale * kLog2e;
   if (items == 0) return hipSuccess;
-  int grid = items;
+  // two rows in flight per workgroup (one per wave group)
+  int grid = (items + 1) / 2;
   if (a.queue) {
     hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(kQueueInts), 0, st, a.queue, kQueueInts, 0);
     int per_cu = 1;
-    hipError_t e = occupancy(attn_fwd_pp_kernel<D, DENSE, SPLITQ>, 512, &per_cu);
+    hipError_t e = occupancy(attn_fwd_pp_kernel<D, DENSE, SPLITQ, VT>, 512, &per_cu);
     if (e != hipSuccess) return e;
     const long long cap = (long long)a.num_cu * (per_cu > 0 ? per_cu : 1);
-    grid = (int)(cap < items ? cap : items);
+    grid = (int)(cap < grid ? cap : grid);
   }
-  hipLaunchKernelGGL((attn_fwd_pp_kernel<D, DENSE, SPLITQ>), dim3(grid), dim3(512), 0, st, (const bf16*)a.Q,
-                     (const bf16*)a.K, (const bf16*)a.Vt, (bf16*)a.O, a.row_ptr, a.col_idx, a.work_order, a.queue,
+  hipLaunchKernelGGL((attn_fwd_pp_kernel<D, DENSE, SPLITQ, VT>), dim3(grid), dim3(512), 0, st, (const bf16*)a.Q,
+                     (const bf16*)a.K, (const bf16*)a.V, (bf16*)a.O, a.row_ptr, a.col_idx, a.work_order, a.queue,
                      items, a.H, a.L, a.seq_len, a.nkb_valid, c2, Lq, SPLITQ ? a.q_valid : a.seq_len,
                      a.grid_rows, a.grid_cols, a.k_anchor);
   return hipGetLastError();
@@ -1070,13 +1306,14 @@ static hipError_t launch_pp(const AttnArgs& a, hipStream_t st) {
 
 hipError_t launch_anchor_attention(const AttnArgs& a, hipStream_t st) {
   if (a.dtype_f32 || a.block != 128 || !a.work_order || !a.queue) return hipErrorInvalidValue;
-  if (a.d == 128) return launch_pp<128, true, true>(a, st);
-  return launch_pp<64, true, true>(a, st);
+  if (a.d == 128)
+    return a.v_transposed ? launch_pp<128, true, true, true>(a, st) : launch_pp<128, true, true, false>(a, st);
+  return a.v_transposed ? launch_pp<64, true, true, true>(a, st) : launch_pp<64, true, true, false>(a, st);
 }
 
-template <int D, int BLK, bool DENSE>
+template <int D, int BLK, bool DENSE, bool VT>
 static hipError_t launch_typed(const AttnArgs& a, hipStream_t st) {
-  if (BLK == 128 && !a.dtype_f32) return launch_pp<D, DENSE>(a, st);
+  if (BLK == 128 && !a.dtype_f32) return launch_pp<D, DENSE, false, VT>(a, st);
   const int threads = BLK * 2;
   const int items = a.B * a.H * (a.L / BLK);
   const float c2 = a.scale * kLog2e;
@@ -1086,35 +1323,36 @@ static hipError_t launch_typed(const AttnArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(kQueueInts), 0, st, a.queue, kQueueInts, 0);
     int per_cu = 1;
     hipError_t e = a.dtype_f32
-        ? occupancy(attn_fwd_f32_kernel<D, BLK, DENSE>, threads, &per_cu)
-        : occupancy(attn_fwd_bf16_kernel<D, BLK, DENSE>, threads, &per_cu);
+        ? occupancy(attn_fwd_f32_kernel<D, BLK, DENSE, VT>, threads, &per_cu)
+        : occupancy(attn_fwd_bf16_kernel<D, BLK, DENSE, VT>, threads, &per_cu);
     if (e != hipSuccess) return e;
     const long long cap = (long long)a.num_cu * (per_cu > 0 ? per_cu : 1);
     grid = (int)(cap < items ? cap : items);
   }
   if (a.dtype_f32) {
-    hipLaunchKernelGGL((attn_fwd_f32_kernel<D, BLK, DENSE>), dim3(grid), dim3(threads), 0, st,
-                       (const float*)a.Q, (const float*)a.K, (const float*)a.Vt, (float*)a.O,
+    hipLaunchKernelGGL((attn_fwd_f32_kernel<D, BLK, DENSE, VT>), dim3(grid), dim3(threads), 0, st,
+                       (const float*)a.Q, (const float*)a.K, (const float*)a.V, (float*)a.O,
                        a.row_ptr, a.col_idx, a.work_order, a.queue, items, a.H, a.L, a.seq_len,
                        a.nkb_valid, c2);
   } else {
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, BLK, DENSE>), dim3(grid), dim3(threads), 0, st,
-                       (const bf16*)a.Q, (const bf16*)a.K, (const bf16*)a.Vt, (bf16*)a.O, a.row_ptr,
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, BLK, DENSE, VT>), dim3(grid), dim3(threads), 0, st,
+                       (const bf16*)a.Q, (const bf16*)a.K, (const bf16*)a.V, (bf16*)a.O, a.row_ptr,
                        a.col_idx, a.work_order, a.queue, items, a.H, a.L, a.seq_len, a.nkb_valid, c2);
   }
   return hipGetLastError();
 }
 
-template <bool DENSE>
+template <bool DENSE, bool VT>
 static hipError_t dispatch(const AttnArgs& a, hipStream_t st) {
-  if (a.d == 128 && a.block == 128) return launch_typed<128, 128, DENSE>(a, st);
-  if (a.d == 128 && a.block == 64) return launch_typed<128, 64, DENSE>(a, st);
-  if (a.d == 64 && a.block == 128) return launch_typed<64, 128, DENSE>(a, st);
-  return launch_typed<64, 64, DENSE>(a, st);
+  if (a.d == 128 && a.block == 128) return launch_typed<128, 128, DENSE, VT>(a, st);
+  if (a.d == 128 && a.block == 64) return launch_typed<128, 64, DENSE, VT>(a, st);
+  if (a.d == 64 && a.block == 128) return launch_typed<64, 128, DENSE, VT>(a, st);
+  return launch_typed<64, 64, DENSE, VT>(a, st);
 }
 
 hipError_t launch_attention(const AttnArgs& a, bool dense, hipStream_t st) {
-  return dense ? dispatch<true>(a, st) : dispatch<false>(a, st);
+  if (a.v_transposed) return dense ? dispatch<true, true>(a, st) : dispatch<false, true>(a, st);
+  return dense ? dispatch<true, false>(a, st) : dispatch<false, false>(a, st);
 }
 
 template <typename T>

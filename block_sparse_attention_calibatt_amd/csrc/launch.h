@@ -11,7 +11,7 @@ namespace calibatt {
 struct AttnArgs {
   const void* Q;
   const void* K;
-  const void* Vt;              // V^T [B, H, d, L]
+  const void* V;               // V [B, H, L, d], or V^T [B, H, d, L] with v_transposed
   void* O;
   const int32_t* row_ptr;      // unused by the dense kernel
   const int32_t* col_idx;      // unused by the dense kernel
@@ -20,6 +20,7 @@ struct AttnArgs {
   int B, H, L, seq_len, d, block, nkb_valid;
   float scale;
   bool dtype_f32;
+  bool v_transposed = false;
   int num_cu;
   // anchor-row launches only: rows index the q_valid anchor queries (padded
   // to Lq, a multiple of 128) of a (frames, grid_rows, grid_cols) token grid
@@ -82,7 +83,8 @@ hipError_t launch_spatial_similarity(const SimArgs& a, hipStream_t st);
 struct AnchorArgs {
   const void* Q;
   const void* K;
-  const void* Vt;  // [B, H, d, L]
+  const void* V;   // [B, H, L, d], or V^T [B, H, d, L] with v_transposed
+  bool v_transposed;
   void* O;
   void* Oa;        // [B, H, Lq, d]
   int32_t* order;  // [H*(Lq/128) + kParts + 1]

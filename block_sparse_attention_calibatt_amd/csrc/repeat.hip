@@ -24,7 +24,7 @@
 //
 // Anchor forward: the persistent dense kernel runs over the anchor queries
 // of the listed heads in its split-query mode (each query read in place
-// through the anchor map; keys: the full K and V^T) into a [B, H, Lq, d]
+// through the anchor map; keys: the full K and V) into a [B, H, Lq, d]
 // buffer (Lq = anchor count rounded up to 128), and every token's output
 // row is then copied from its anchor's.
 #include "tiles.h"
@@ -236,7 +236,8 @@ hipError_t launch_anchor_fwd(const AnchorArgs& a, hipStream_t st) {
   AttnArgs t;
   t.Q = a.Q;
   t.K = a.K;
-  t.Vt = a.Vt;
+  t.V = a.V;
+  t.v_transposed = a.v_transposed;
   t.O = a.Oa;
   t.row_ptr = nullptr;
   t.col_idx = nullptr;

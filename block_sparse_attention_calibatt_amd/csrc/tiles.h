@@ -55,6 +55,32 @@ __device__ __forceinline__ int swz(int row) {
   }
 }
 
+// Unit swizzle of a V stage in natural layout (64 key rows of D/8 units).
+// The transposed operand reads of 16 lanes cover 4 consecutive rows at 2
+// units, those of 32 lanes 4 rows at 4 units; XOR-ing bits 2..3 of the unit
+// with row bits 0..1 (D = 128, rows of 256 bytes) or row bit 1 (D = 64, rows
+// of 128 bytes) puts them in distinct bank groups.  Rows that share row bits
+// 0..1 share it, so a read advances by a constant between such rows.
+template <int D>
+__device__ __forceinline__ int vswz(int row) {
+  if constexpr (D == 128) {
+    return 4 * (row & 3);
+  } else {
+    return 4 * ((row >> 1) & 1);
+  }
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Transposed LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane
+// 4j + m reads 4 consecutive 16-bit elements at its own address, and lane i
+// receives element i % 4 of the reads of lanes i / 4, 4 + i / 4, 8 + i / 4,
+// 12 + i / 4: the group reads a 4 x 16 block (lanes 4j .. 4j+3 one row of 16)
+// and lane i gets column i of it.
+__device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+}
+
 template <int CH>
 __device__ __forceinline__ int chunk_index(int row, int chunk) {
   return row * CH + (chunk ^ swz<CH>(row));
@@ -69,6 +95,17 @@ __device__ __forceinline__ int qk_row_perm(int c) {
 __device__ __forceinline__ int slice_key(int r, int g) { return 16 * (r >> 3) + 8 * g + (r & 7); }
 
 typedef __attribute__((address_space(3))) void lds_void;
+
+// Global-memory (address space 1) views, for pointers rebuilt from integers:
+// accesses through them are global, not flat, instructions, so that they are
+// not counted with the LDS accesses (a flat access counts toward both
+// counters, and would make every later LDS wait also wait for it).
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) int32_t g_i32;
+typedef __attribute__((address_space(1))) __bf16 g_bf16;
+typedef __attribute__((address_space(1))) bf16x8 g_bf16x8;
+typedef __attribute__((address_space(1))) bf16x4 g_bf16x4;
+typedef __attribute__((address_space(1))) u32x4 g_u32x4;
 
 // Buffer resource over `bytes` bytes at base: loads past the end return 0.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {

@@ -16,8 +16,8 @@
  *   the padded token count and must be a multiple of `block`; tokens
  *   t >= seq_len are padding: they are never keys, and their output rows are
  *   written as zero.  The attention entry points also accept V transposed,
- *   as V^T [B, H, d, L] (CALIBATT_V_BHDL): the kernels read V^T, and given V
- *   they first write V^T into a caller workspace.
+ *   as V^T [B, H, d, L] (CALIBATT_V_BHDL); they read either layout as it
+ *   lies and need no copy of it.
  * - One block is `block` tokens; query blocks and key blocks have the same
  *   size.  nqb = nkb = L / block; nkb_valid = ceil(seq_len / block).
  * - A mask set is CSR over rows r = h * nqb + qb (h-major): the kept key
@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define CALIBATT_VERSION 240 /* major * 100 + minor */
+#define CALIBATT_VERSION 300 /* major * 100 + minor */
 
 typedef enum {
   CALIBATT_OK = 0,
@@ -67,8 +67,8 @@ typedef enum { CALIBATT_BF16 = 0, CALIBATT_F32 = 1 } calibatt_dtype;
 
 /* Layout of the V argument of the attention entry points. */
 typedef enum {
-  CALIBATT_V_BHLD = 0, /* V [B, H, L, d]; the call transposes it into vt_ws first */
-  CALIBATT_V_BHDL = 1  /* V^T [B, H, d, L] (V[b,h,j,:] is column j); vt_ws unused */
+  CALIBATT_V_BHLD = 0, /* V [B, H, L, d], like Q and K */
+  CALIBATT_V_BHDL = 1  /* V^T [B, H, d, L] (V[b,h,j,:] is column j) */
 } calibatt_vlayout;
 
 /*
@@ -79,37 +79,38 @@ typedef enum {
  * query block qb (row r = h*nqb + qb), with J_i the valid tokens of the kept
  * key blocks of row r:
  *     O[b,h,i,:] = sum_{j in J_i} softmax_j(scale * Q[b,h,i,:] . K[b,h,j,:]) V[b,h,j,:]
- * A row with no kept block, and every padded query row, is written as zero.
+ * A row with no kept block, and every padded query row, is written as zero
+ * (whatever the padded rows of Q, K and V hold).
  *
  *   Q, K        [B, H, L, d] inputs of dtype `dt` (device).
  *   V           input of dtype `dt` (device) in the layout `v_layout` names.
  *               With CALIBATT_V_BHDL its entries for keys >= seq_len must be
- *               finite (they are multiplied by zero probabilities).
+ *               finite (they are multiplied by zero probabilities); with
+ *               CALIBATT_V_BHLD padded rows may hold anything.
  *   O           [B, H, L, d] output of dtype `dt` (device); fully written.
+ *               It must not overlap Q, K or V (CALIBATT_ERR_SHAPE).
  *   row_ptr     [H*nqb + 1] int32 CSR row offsets (device).
  *   col_idx     [row_ptr[H*nqb]] int32 kept key blocks (device).
  *   block       tokens per block (64 or 128).
- *   scale       softmax scale applied to q.k (usually 1/sqrt(d)).
+ *   scale       softmax scale applied to q.k (usually 1/sqrt(d)); finite
+ *               and > 0, else CALIBATT_ERR_SHAPE.
  *   work_order  optional [H*nqb + 9] int32 from calibatt_build_schedule: a
  *               permutation of the rows split into 8 partition lists,
  *               followed by the 9 list offsets (0, ..., H*nqb).  NULL =
  *               partition p holds heads p, p+8, ... in natural order.  The
  *               result does not depend on it (each row is reduced by one
- *               workgroup in col_idx order).
+ *               group of waves in col_idx order).
  *   queue_ws    optional int32 workspace of >= 128 entries (device), 16-byte
  *               aligned.  Non-NULL selects the persistent launch: one grid
  *               that fills the GPU; workgroup i serves partition i % 8 (the
  *               XCD it runs on) from an atomic counter in queue_ws, then the
  *               other partitions.  The call resets the counters on `stream`
- *               itself.  NULL = one workgroup per row.  Calls that share a
- *               queue_ws must not overlap in time.
+ *               itself.  NULL = one workgroup per row (block 128 bf16: per
+ *               two rows).  Calls that share a queue_ws must not overlap in
+ *               time.
  *   nnz         number of entries of col_idx (= row_ptr[H*nqb]); used only
  *               for the host-side size check.
  *   v_layout    CALIBATT_V_BHLD or CALIBATT_V_BHDL (see V).
- *   vt_ws       with CALIBATT_V_BHLD: workspace of B*H*d*L elements of `dt`
- *               (device), 16-byte aligned, not overlapping Q, K, V or O; on
- *               return (once the stream reaches it) it holds V^T, as written
- *               by calibatt_transpose_v.  Ignored with CALIBATT_V_BHDL.
  * The bf16 path computes q.k and p.v on bf16 matrix cores with float32
  * accumulation and a float32 softmax; probabilities are rounded to bf16
  * before the p.v product; O is rounded to bf16.  The f32 path is float32
@@ -120,8 +121,7 @@ calibatt_status calibatt_sparse_attn_fwd(const void* Q, const void* K, const voi
                                          int block, float scale, int B, int H, int L,
                                          int seq_len, int d, calibatt_dtype dt,
                                          const int32_t* work_order, int32_t* queue_ws,
-                                         int64_t nnz, calibatt_vlayout v_layout, void* vt_ws,
-                                         void* stream);
+                                         int64_t nnz, calibatt_vlayout v_layout, void* stream);
 
 /*
  * Dense attention forward: the same computation with every valid key block
@@ -132,13 +132,13 @@ calibatt_status calibatt_sparse_attn_fwd(const void* Q, const void* K, const voi
 calibatt_status calibatt_dense_attn_fwd(const void* Q, const void* K, const void* V, void* O,
                                         int block, float scale, int B, int H, int L, int seq_len,
                                         int d, calibatt_dtype dt, int32_t* queue_ws,
-                                        calibatt_vlayout v_layout, void* vt_ws, void* stream);
+                                        calibatt_vlayout v_layout, void* stream);
 
 /*
  * V [B, H, L, d] -> V^T [B, H, d, L]: Vt[b,h,c,j] = V[b,h,j,c] for j <
- * seq_len and 0 for the padded keys j >= seq_len.  A layout change only (the
- * attention kernels contract P*V over keys and read V^T tiles as they lie);
- * the attention entry points call it themselves for CALIBATT_V_BHLD.
+ * seq_len and 0 for the padded keys j >= seq_len.  A layout change only: for
+ * callers that keep V transposed (CALIBATT_V_BHDL); the attention entry
+ * points read either layout themselves.
  *   V, Vt   inputs/outputs of dtype `dt` (device), 16-byte aligned, not
  *           overlapping.  L must be a multiple of 64; d in {64, 128}.
  */
@@ -155,6 +155,8 @@ calibatt_status calibatt_transpose_v(const void* V, void* Vt, int B, int H, int 
  * so each valid query contributes 1 to its row of blocks.
  *
  *   Q, K     [B, H, L, d] inputs of dtype `dt` (device).
+ *   scale    softmax scale, finite and > 0 (else CALIBATT_ERR_SHAPE; the
+ *            same holds for every entry point that takes a scale).
  *   lse_ws   [B, H, L] float32 workspace (device); on return it holds
  *            log(sum_{j < seq_len} exp(scale * q_i . k_j)) per query (natural
  *            log; padded rows hold -inf).
@@ -398,13 +400,13 @@ calibatt_status calibatt_select_repetitive_heads(const double* sim, int P, int H
  * seq_len, with a = the anchor row of y's group:
  *     O[b,h,n,:] = attention of query (f, a, x) over all valid keys
  * and O[b,h,n,:] = 0 for n >= seq_len.  Heads not listed are not written.
- *   Q, K, V, O  as in calibatt_dense_attn_fwd; bf16 only, block 128.
+ *   Q, K, V, O  as in calibatt_dense_attn_fwd; bf16 only, block 128; scale
+ *               finite and > 0; O must not overlap Q, K or V.
  *   heads       [n_heads] int32 (host): distinct heads in [0, H); at most 256.
  *   frames, grid_rows, grid_cols  the token grid (frames*grid_rows*grid_cols
  *               = seq_len); 1 <= k_anchor <= grid_rows.
  *   queue_ws    int32 workspace of >= 128 entries (device), required.
- *   v_layout, vt_ws  as in calibatt_sparse_attn_fwd (a [B, H, L, d] V is
- *               transposed for all H heads).
+ *   v_layout    as in calibatt_sparse_attn_fwd.
  *   ws          calibatt_anchor_ws_bytes(B, H, frames, grid_cols, k_anchor,
  *               d) bytes (device), 256-byte aligned: the anchor outputs as
  *               [B, H, Lq, d] (Lq = frames * k_anchor * grid_cols rounded up
@@ -418,8 +420,7 @@ calibatt_status calibatt_anchor_attn_fwd(const void* Q, const void* K, const voi
                                          const int32_t* heads, int n_heads, int frames, int grid_rows,
                                          int grid_cols, int k_anchor, float scale, int B, int H, int L,
                                          int seq_len, int d, calibatt_dtype dt, int32_t* queue_ws,
-                                         calibatt_vlayout v_layout, void* vt_ws, void* ws, size_t ws_bytes,
-                                         void* stream);
+                                         calibatt_vlayout v_layout, void* ws, size_t ws_bytes, void* stream);
 size_t calibatt_anchor_ws_bytes(int B, int H, int frames, int grid_cols, int k_anchor, int d);
 
 /*

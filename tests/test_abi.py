@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert cal.calibatt_version() == 240
+    assert cal.calibatt_version() == 300
     for code, name in _lib.STATUS.items():
         assert cal.calibatt_status_string(code) != "unknown status"
     assert cal.calibatt_status_string(99) == "unknown status"
@@ -37,12 +37,13 @@ def test_version_and_strings(lib):
 
 V = ctypes.c_void_p
 P16, P32, P48, P64 = V(16), V(32), V(48), V(64)     # aligned fake addresses, never dereferenced
+# fake Q, K, V, O far enough apart not to overlap at any accepted size
+TQ, TK, TV, TO = V(1 << 36), V(2 << 36), V(3 << 36), V(4 << 36)
 
 
 def _sparse(lib, **kw):
-    a = dict(Q=P16, K=P32, V=P48, O=P64, row_ptr=V(128), col_idx=V(256), block=128, scale=0.1, B=1, H=2,
-             L=1024, seq_len=1000, d=128, dt=0, work_order=None, queue_ws=None, nnz=10, v_layout=1, vt_ws=None,
-             stream=None)
+    a = dict(Q=TQ, K=TK, V=TV, O=TO, row_ptr=V(128), col_idx=V(256), block=128, scale=0.1, B=1, H=2,
+             L=1024, seq_len=1000, d=128, dt=0, work_order=None, queue_ws=None, nnz=10, v_layout=1, stream=None)
     a.update(kw)
     return lib.calibatt_sparse_attn_fwd(*a.values())
 
@@ -52,7 +53,7 @@ def _sparse(lib, **kw):
     (dict(O=None), 1),
     (dict(row_ptr=None), 1),
     (dict(col_idx=None), 1),
-    (dict(Q=V(17)), 4),
+    (dict(Q=V((1 << 36) + 17)), 4),
     (dict(row_ptr=V(130)), 4),
     (dict(queue_ws=V(132)), 4),
     (dict(dt=7), 3),
@@ -66,10 +67,15 @@ def _sparse(lib, **kw):
     (dict(B=1024, H=64, L=65536), 2),
     (dict(nnz=-1), 5),
     (dict(nnz=2 * 8 * 8 + 1), 5),
-    (dict(v_layout=0), 1),                       # V given as [B, H, L, d] needs vt_ws
-    (dict(v_layout=0, vt_ws=V((1 << 30) + 8)), 4),
-    (dict(v_layout=0, vt_ws=V(16 + 4096)), 2),   # overlaps Q
     (dict(v_layout=2), 2),
+    (dict(v_layout=-1), 2),
+    (dict(scale=0.0), 2),
+    (dict(scale=-0.1), 2),
+    (dict(scale=float("nan")), 2),
+    (dict(scale=float("inf")), 2),
+    (dict(O=V((1 << 36) + 4096)), 2),            # O overlaps Q
+    (dict(O=V((3 << 36) - 4096)), 2),            # O overlaps K
+    (dict(V=V((4 << 36) + 1024 * 128 * 2)), 2),  # V overlaps O
 ])
 def test_sparse_rejects(lib, kw, status):
     assert _sparse(lib, **kw) == status
@@ -77,13 +83,16 @@ def test_sparse_rejects(lib, kw, status):
 
 
 def test_dense_and_mass_reject(lib):
-    def dense(*a, layout=1, vt=None):
-        return lib.calibatt_dense_attn_fwd(*a, layout, vt, None)
-    assert dense(None, P32, P48, P64, 128, 0.1, 1, 1, 256, 256, 128, 0, None) == 1
-    assert dense(P16, P32, P48, P64, 32, 0.1, 1, 1, 256, 256, 128, 0, None) == 7
-    assert dense(P16, P32, P48, P64, 128, 0.1, 1, 1, 256, 256, 128, 0, V(132)) == 4
-    assert dense(P16, P32, P48, P64, 128, 0.1, 1, 1, 256, 256, 128, 0, None, layout=0) == 1
-    assert dense(P16, P32, P48, P64, 128, 0.1, 1, 1, 256, 256, 128, 0, None, layout=0, vt=V(48)) == 2
+    def dense(*a, layout=1):
+        return lib.calibatt_dense_attn_fwd(*a, layout, None)
+    assert dense(None, TK, TV, TO, 128, 0.1, 1, 1, 256, 256, 128, 0, None) == 1
+    assert dense(TQ, TK, TV, TO, 32, 0.1, 1, 1, 256, 256, 128, 0, None) == 7
+    assert dense(TQ, TK, TV, TO, 128, 0.1, 1, 1, 256, 256, 128, 0, V(132)) == 4
+    assert dense(TQ, TK, TV, TO, 128, 0.1, 1, 1, 256, 256, 128, 0, None, layout=5) == 2
+    assert dense(TQ, TK, TV, TO, 128, 0.0, 1, 1, 256, 256, 128, 0, None) == 2
+    assert dense(TQ, TK, TV, TO, 128, float("nan"), 1, 1, 256, 256, 128, 0, None) == 2
+    assert dense(TQ, TK, TV, TQ, 128, 0.1, 1, 1, 256, 256, 128, 0, None) == 2, "O aliases Q"
+    assert lib.calibatt_block_mass(P16, P32, 1, 1, 256, 256, 128, 0, 128, -1.0, P48, P64, None) == 2, "scale"
     assert lib.calibatt_block_mass(P16, P32, 1, 1, 256, 256, 128, 1, 128, 0.1, P48, P64, None) == 7, "f32 mass"
     assert lib.calibatt_block_mass(P16, P32, 1, 1, 256, 300, 128, 0, 128, 0.1, P48, P64, None) == 2
     assert lib.calibatt_block_mass(P16, None, 1, 1, 256, 256, 128, 0, 128, 0.1, P48, P64, None) == 1
@@ -282,6 +291,7 @@ def test_repetition_entry_points_reject(lib):
     assert sim(ws_bytes=ws - 1) == 6
     assert sim(L=32760) == 2
     assert sim(lse=V((1 << 21) + 2)) == 4
+    assert sim(scale=float("-inf")) == 2
 
     n = ctypes.c_int32(0)
     heads = np.zeros(4, dtype=np.int32)
@@ -297,9 +307,9 @@ def test_repetition_entry_points_reject(lib):
     hl = np.array([3, 7], dtype=np.int32)
 
     def anchor(heads_arr=hl, **kw):
-        a = dict(Q=P16, K=P32, V=P48, O=P64, heads=heads_arr.ctypes.data_as(ctypes.c_void_p), n=len(heads_arr),
+        a = dict(Q=TQ, K=TK, V=TV, O=TO, heads=heads_arr.ctypes.data_as(ctypes.c_void_p), n=len(heads_arr),
                  F=21, R=30, C=52, k=5, scale=0.1, B=1, H=40, L=32768, S=32760, d=128, dt=0, queue=V(1 << 20),
-                 layout=1, vt=None, ws=V(1 << 30), ws_bytes=aws, stream=None)
+                 layout=1, ws=V(1 << 30), ws_bytes=aws, stream=None)
         a.update(kw)
         return lib.calibatt_anchor_attn_fwd(*a.values())
     assert anchor(Q=None) == 1
@@ -315,7 +325,9 @@ def test_repetition_entry_points_reject(lib):
     assert anchor(np.array([5, 5], dtype=np.int32)) == 2
     assert anchor(ws_bytes=aws - 1) == 6
     assert anchor(heads=None) == 1
-    assert anchor(layout=0) == 1
+    assert anchor(layout=3) == 2
+    assert anchor(scale=0.0) == 2
+    assert anchor(O=TK) == 2
     assert cal.calibatt_last_error() != ""
 
 
@@ -335,3 +347,4 @@ def test_single_pass_mass_rejects(lib):
     assert call(dt=1) == 7
     assert call(S=32769) == 2
     assert call(block=32) == 7
+    assert call(scale=0.0) == 2

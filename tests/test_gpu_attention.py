@@ -146,23 +146,50 @@ def test_transpose_v_exact(gpu, dtype, d):
     assert np.array_equal(Vt.float().cpu().numpy(), want)
 
 
-def test_v_transposed_input_bitwise(gpu):
-    """Passing V^T directly gives the same bits as passing V."""
-    cfg = small_cfg(H=3, L=1024, S=1000)
-    say("case: V^T input == V input, bitwise")
+@pytest.mark.parametrize("d,block,dtype", [(128, 128, "bf16"), (64, 128, "bf16"), (128, 64, "bf16"),
+                                           (64, 64, "bf16"), (64, 64, "f32")])
+def test_v_transposed_input_bitwise(gpu, d, block, dtype):
+    """Passing V^T gives the same bits as passing V: the kernels read either
+    layout into the same matrix-core operands."""
+    cfg = small_cfg(H=3, L=1024, S=1000, d=d, block=block, dtype=dtype)
+    say("case: V^T input == V input, bitwise", d, block, dtype)
     q, k, v = inputs(cfg)
     rng = np.random.default_rng(17)
     rp, ci = synth.random_csr(rng, cfg.H, cfg.nqb, cfg.nkb_valid, 0.5, empty_rows=1, full_rows=1)
-    Q, K, V = (to_dev(x, torch.bfloat16) for x in (q, k, v))
+    Q, K, V = (to_dev(x, TDT[dtype]) for x in (q, k, v))
     RP, CI = i32(rp), i32(ci)
     O1, O2 = torch.empty_like(Q), torch.empty_like(Q)
-    vt = cal.new_vt(Q)
-    cal.calibatt_sparse_attn_fwd(Q, K, V, O1, RP, CI, cfg.block, cfg.scale, cfg.S, vt_ws=vt)
+    cal.calibatt_sparse_attn_fwd(Q, K, V, O1, RP, CI, cfg.block, cfg.scale, cfg.S)
     Vt = cal.calibatt_transpose_v(V, seq_len=cfg.S)
     cal.calibatt_sparse_attn_fwd(Q, K, Vt, O2, RP, CI, cfg.block, cfg.scale, cfg.S, v_transposed=True)
     torch.cuda.synchronize()
     assert torch.equal(O1, O2)
-    assert torch.equal(vt, Vt), "the workspace holds V^T after the call"
+
+
+@pytest.mark.parametrize("d,block,dtype", [(128, 128, "bf16"), (64, 64, "bf16"), (64, 64, "f32")])
+def test_nan_padding_rows(gpu, d, block, dtype):
+    """Padded rows of Q, K and V (tokens >= seq_len) holding NaN: padded O rows
+    are still zero, and the valid rows equal those of zero padding bit for bit."""
+    cfg = small_cfg(H=2, L=1024, S=1000, d=d, block=block, dtype=dtype)
+    say("case: NaN in the padding of Q, K, V", d, block, dtype)
+    q, k, v = inputs(cfg)
+    rng = np.random.default_rng(29)
+    rp, ci = synth.random_csr(rng, cfg.H, cfg.nqb, cfg.nkb_valid, 0.5, empty_rows=1, full_rows=1)
+    RP, CI = i32(rp), i32(ci)
+    outs = []
+    for fill in (0.0, float("nan")):
+        Q, K, V = (to_dev(x, TDT[dtype]) for x in (q, k, v))
+        for t in (Q, K, V):
+            t[:, :, cfg.S:] = fill
+        for persistent in (False, True):
+            O = torch.full_like(Q, 3.0)
+            cal.calibatt_sparse_attn_fwd(Q, K, V, O, RP, CI, cfg.block, cfg.scale, cfg.S, None,
+                                         cal.new_queue("cuda:0") if persistent else None)
+            torch.cuda.synchronize()
+            assert torch.count_nonzero(O[:, :, cfg.S:].float()).item() == 0
+            outs.append(O)
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
 
 
 def test_row_lengths_one_to_nine_blocks(gpu):
