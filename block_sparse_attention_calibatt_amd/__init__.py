@@ -14,6 +14,7 @@ from .capi import (
     new_queue,
     calibatt_transpose_v,
     calibatt_sparse_attn_fwd,
+    calibatt_sparse_attn_fwd_noalloc,
     calibatt_dense_attn_fwd,
     calibatt_block_mass,
     calibatt_block_mass_single_pass,
@@ -46,6 +47,7 @@ __all__ = [
     "new_queue",
     "calibatt_transpose_v",
     "calibatt_sparse_attn_fwd",
+    "calibatt_sparse_attn_fwd_noalloc",
     "calibatt_dense_attn_fwd",
     "calibatt_block_mass",
     "calibatt_block_mass_single_pass",

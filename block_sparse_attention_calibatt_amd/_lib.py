@@ -35,6 +35,8 @@ _sz = ctypes.c_size_t
 SIGNATURES = {
     "calibatt_sparse_attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _f32, _i32, _i32, _i32,
                                         _i32, _i32, _i32, _vp, _vp, _i64, _i32, _vp]),
+    "calibatt_sparse_attn_fwd_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _f32, _i32, _i32, _i32,
+                                                _i32, _i32, _i32, _vp, _i64, _i32, _vp]),
     "calibatt_dense_attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _i32, _f32, _i32, _i32, _i32, _i32, _i32,
                                        _i32, _vp, _i32, _vp]),
     "calibatt_transpose_v": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),

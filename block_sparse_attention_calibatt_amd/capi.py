@@ -90,6 +90,27 @@ def calibatt_sparse_attn_fwd(Q, K, V, O, row_ptr, col_idx, block, scale, seq_len
     return O
 
 
+def calibatt_sparse_attn_fwd_noalloc(Q, K, V, O, row_ptr, col_idx, block, scale, seq_len=None,
+                                     work_order=None, v_transposed=False):
+    """calibatt_sparse_attn_fwd with its queue in the library's static scratch."""
+    B, H, L, d = _qkv(Q, K, V, O, v_transposed)
+    seq_len = L if seq_len is None else int(seq_len)
+    _dev_tensor(row_ptr, "row_ptr", torch.int32)
+    _dev_tensor(col_idx, "col_idx", torch.int32)
+    _need(block > 0 and L % block == 0, "L must be a multiple of block")
+    rows = H * (L // block)
+    _need(row_ptr.numel() == rows + 1, f"row_ptr must have H*nqb+1 = {rows + 1} entries")
+    if work_order is not None:
+        _dev_tensor(work_order, "work_order", torch.int32)
+        _need(work_order.numel() == rows + PARTS + 1, f"work_order must have H*nqb+9 = {rows + PARTS + 1} entries")
+    lib = load()
+    check(lib.calibatt_sparse_attn_fwd_noalloc(
+        _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(row_ptr), _ptr(col_idx), int(block), float(scale),
+        B, H, L, seq_len, d, _DT[Q.dtype], _ptr(work_order), col_idx.numel(),
+        V_BHDL if v_transposed else V_BHLD, _stream(Q)))
+    return O
+
+
 def calibatt_dense_attn_fwd(Q, K, V, O, block, scale, seq_len=None, queue_ws=None, v_transposed=False):
     B, H, L, d = _qkv(Q, K, V, O, v_transposed)
     seq_len = L if seq_len is None else int(seq_len)
@@ -444,6 +465,7 @@ __all__ = [
     "new_queue",
     "calibatt_transpose_v",
     "calibatt_sparse_attn_fwd",
+    "calibatt_sparse_attn_fwd_noalloc",
     "calibatt_dense_attn_fwd",
     "calibatt_block_mass",
     "calibatt_compile_ws_bytes",

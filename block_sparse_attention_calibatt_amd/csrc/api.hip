@@ -200,7 +200,61 @@ calibatt_status check_sparse_args(const void* Q, const void* K, const void* V, v
 
 }  // namespace
 
+// Scratch of calibatt_sparse_attn_fwd_noalloc: the persistent launch's
+// partition counters (kQueueInts int32 = 512 bytes, one 64-byte line per
+// partition).  Each GPU the library runs on holds its own copy until the
+// process ends.  In host code the name stands for no device address: the
+// address used in launches is the one hipGetSymbolAddress returns for the
+// current device, kept in g_scratch_ptr.
+static __device__ __align__(256) int32_t scratch[calibatt::kQueueInts];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+int32_t* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up on the first
+// call there.
+calibatt_status scratch_ptr(int32_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "querying the current device");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(CALIBATT_ERR_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", dev,
+                kMaxDevices - 1);
+  std::lock_guard<std::mutex> lk(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "looking up the static scratch on the current device");
+    if (!p || !aligned(p, 256)) return fail(CALIBATT_ERR_HIP, "the static scratch has no 256-byte aligned address");
+    g_scratch_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return CALIBATT_OK;
+}
+
+}  // namespace
+
 extern "C" {
+
+calibatt_status calibatt_sparse_attn_fwd_noalloc(const void* Q, const void* K, const void* V, void* O,
+                                                 const int32_t* row_ptr, const int32_t* col_idx, int block,
+                                                 float scale, int B, int H, int L, int seq_len, int d,
+                                                 calibatt_dtype dt, const int32_t* work_order, int64_t nnz,
+                                                 calibatt_vlayout v_layout, void* stream) {
+  calibatt_status s = check_sparse_args(Q, K, V, O, row_ptr, col_idx, block, scale, B, H, L, seq_len, d, dt,
+                                        work_order, nnz, v_layout);
+  if (s != CALIBATT_OK) return s;
+  // The persistent launch needs kQueueInts counters whatever the problem
+  // size, so no accepted size outgrows the array.
+  int32_t* queue = nullptr;
+  s = scratch_ptr(&queue);
+  if (s != CALIBATT_OK) return s;
+  return run_attention(Q, K, V, O, row_ptr, col_idx, block, scale, B, H, L, seq_len, d, dt, work_order, queue,
+                       v_layout, false, stream);
+}
 
 calibatt_status calibatt_sparse_attn_fwd(const void* Q, const void* K, const void* V, void* O,
                                          const int32_t* row_ptr, const int32_t* col_idx, int block,

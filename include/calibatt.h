@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define CALIBATT_VERSION 300 /* major * 100 + minor */
+#define CALIBATT_VERSION 301 /* major * 100 + minor */
 
 typedef enum {
   CALIBATT_OK = 0,
@@ -122,6 +122,26 @@ calibatt_status calibatt_sparse_attn_fwd(const void* Q, const void* K, const voi
                                          int seq_len, int d, calibatt_dtype dt,
                                          const int32_t* work_order, int32_t* queue_ws,
                                          int64_t nnz, calibatt_vlayout v_layout, void* stream);
+
+/*
+ * calibatt_sparse_attn_fwd for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments without queue_ws, same result bit for bit as
+ * calibatt_sparse_attn_fwd with a queue_ws (the persistent launch, always).
+ * The call allocates nothing: the queue counters live in a static device
+ * array of the library, 512 bytes per GPU, held until the process ends; its
+ * size does not grow with the problem, so every size calibatt_sparse_attn_fwd
+ * accepts fits.  The call re-zeroes the counters on `stream` with a kernel
+ * (no memset node).  All calls on one GPU share that array: calls that
+ * overlap in time on one GPU (other streams, other threads) race and must be
+ * serialised by the caller.  Devices 0..63 (CALIBATT_ERR_UNSUPPORTED beyond).
+ */
+calibatt_status calibatt_sparse_attn_fwd_noalloc(const void* Q, const void* K, const void* V, void* O,
+                                                 const int32_t* row_ptr, const int32_t* col_idx,
+                                                 int block, float scale, int B, int H, int L,
+                                                 int seq_len, int d, calibatt_dtype dt,
+                                                 const int32_t* work_order, int64_t nnz,
+                                                 calibatt_vlayout v_layout, void* stream);
 
 /*
  * Dense attention forward: the same computation with every valid key block

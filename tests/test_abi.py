@@ -19,7 +19,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _lib.header_symbols()
-    assert len(names) == 24
+    assert len(names) == 25
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     for n in names:
@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert cal.calibatt_version() == 300
+    assert cal.calibatt_version() == 301
     for code, name in _lib.STATUS.items():
         assert cal.calibatt_status_string(code) != "unknown status"
     assert cal.calibatt_status_string(99) == "unknown status"
@@ -79,6 +79,26 @@ def _sparse(lib, **kw):
 ])
 def test_sparse_rejects(lib, kw, status):
     assert _sparse(lib, **kw) == status
+    assert cal.calibatt_last_error() != ""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Q=None), 1),
+    (dict(row_ptr=V(130)), 4),
+    (dict(block=96), 7),
+    (dict(seq_len=1025), 2),
+    (dict(nnz=2 * 8 * 8 + 1), 5),
+    (dict(v_layout=2), 2),
+    (dict(scale=float("nan")), 2),
+    (dict(O=V((1 << 36) + 4096)), 2),
+])
+def test_sparse_noalloc_rejects(lib, kw, status):
+    """The variant without a queue workspace checks the same arguments the
+    same way, before any HIP call."""
+    a = dict(Q=TQ, K=TK, V=TV, O=TO, row_ptr=V(128), col_idx=V(256), block=128, scale=0.1, B=1, H=2,
+             L=1024, seq_len=1000, d=128, dt=0, work_order=None, nnz=10, v_layout=1, stream=None)
+    a.update(kw)
+    assert lib.calibatt_sparse_attn_fwd_noalloc(*a.values()) == status
     assert cal.calibatt_last_error() != ""
 
 
