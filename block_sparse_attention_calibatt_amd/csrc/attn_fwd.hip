@@ -446,11 +446,13 @@ __global__ __launch_bounds__(BLK * 2, (D == 128 && BLK == 64) ? 1 : 2) void attn
 // Geometry of the 128-token-block kernel: keys in 64-key sub-tiles; a K
 // stage holds one sub-tile as 64 rows of D/8 16-byte units, a V stage the
 // same sub-tile of V (64 rows, natural layout) or of V^T (D rows of 8 units).
-// Each wave group owns four stages: K0, K1, V0, V1.  The stages are four LDS
-// objects, each holding both groups' stage of that name, so that the DMA
-// into one stage and the operand reads of another are accesses to different
-// objects, which the compiler can tell apart (it would otherwise wait for
-// every DMA in flight before each read).
+// Each wave group owns four stages: K0, K1, V0, V1.  They sit in two LDS
+// objects, A = (K0, V1) and B = (K1, V0), each stage holding both groups'
+// halves.  A matrix phase with stage index TM reads K(TM) and V(TM^1), one
+// object, while its DMA fills K(TM^1) and V(TM), the other; so the DMA and
+// every LDS access of a phase touch different objects, which the compiler
+// can tell apart (it would otherwise wait for every DMA in flight before
+// each access).
 template <int D>
 struct PPGeo {
   static constexpr int CH = D / 8;
@@ -510,16 +512,13 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
   using G = PPGeo<D>;
   constexpr int CH = G::CH, DS = G::DS, DT = G::DT, KS = G::KS, NDMA = G::NDMA;
   constexpr int STAGE = G::STAGE, RB = G::RB;
-  __shared__ u32x4 lk0[2 * G::UNITS], lk1[2 * G::UNITS], lv0[2 * G::UNITS], lv1[2 * G::UNITS];
-  __shared__ int s_desc[2][8];        // per group: next row b, r (-1: none), list start, blocks, kb0, kb1
+  __shared__ u32x4 lA[4 * G::UNITS], lB[4 * G::UNITS];
+  __shared__ u32x4 s_ost[4 * 32 * 8];   // O staging: per wave of a group 32 rows x 64 columns
+  // per group: next row b, r (-1: none), list start, blocks; then kb0, kb1
+  __shared__ i32x4 s_desc[2][2];
   __shared__ int s_poff[kParts + 1];  // partition offsets of the work order
   __shared__ int s_fin[2];            // phase in which each group finished
-  __shared__ int s_fst[2][8];         // per group: the fetch state between calls
-  __shared__ int s_prev[2][2];        // per group: batch and row of the row whose O is due
-  // Arguments only the rare paths use (row fetch, row switch, O store) are
-  // read from LDS there, so that the compiler does not keep them, or values
-  // derived from them, in scalar registers through the phase loop.
-  __shared__ uint32_t s_arg[20];
+  __shared__ i32x2 s_prev[2];         // per group: batch and row of the row whose O is due
 
   const int nqb = (SPLITQ ? Lq : L) / BLK;
   const int rows = H * nqb;
@@ -533,8 +532,8 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
   // K and V rows past seq_len read as zero (buffer range check)
   const uint32_t k_bytes = (uint32_t)seq_len * RB;
   const uint32_t v_bytes = VT ? (uint32_t)L * RB : (uint32_t)seq_len * RB;
-  char* const kst[2] = {reinterpret_cast<char*>(lk0), reinterpret_cast<char*>(lk1)};
-  char* const vst[2] = {reinterpret_cast<char*>(lv0), reinterpret_cast<char*>(lv1)};
+  char* const kst[2] = {reinterpret_cast<char*>(lA), reinterpret_cast<char*>(lB)};
+  char* const vst[2] = {reinterpret_cast<char*>(lB) + 2 * STAGE, reinterpret_cast<char*>(lA) + 2 * STAGE};
   const int gbase = grp * STAGE;   // the group's half of each stage object
 
   // DMA lane patterns: instruction m of a stage writes LDS units 64m ..
@@ -593,34 +592,39 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
 
   // every stage starts as zeros: the first P*V of a group multiplies zero
   // probabilities with a V stage no tile has been loaded into yet
-  for (int u = threadIdx.x; u < 2 * G::UNITS; u += 512) lk0[u] = lk1[u] = lv0[u] = lv1[u] = u32x4{0u, 0u, 0u, 0u};
+  for (int u = threadIdx.x; u < 4 * G::UNITS; u += 512) lA[u] = lB[u] = u32x4{0u, 0u, 0u, 0u};
   if (threadIdx.x <= kParts) s_poff[threadIdx.x] = work_order ? work_order[rows + threadIdx.x] : 0;
-  if (threadIdx.x == 0) {
+  if (threadIdx.x < 2) s_fin[threadIdx.x] = 0x7fffffff;
+  __syncthreads();
+
+  // Arguments only the rare paths use (row fetch, row switch, O store) sit
+  // in the lanes of one vector register: lane 2i and 2i+1 the low and high
+  // word of pointer i of (Q, K, V, O, row_ptr, col_idx, work_order, queue),
+  // lane 16 H, lane 17 items, lane 18 c2.  They are read with readlane where
+  // needed; the register is re-declared live in every phase, so that the
+  // compiler cannot hoist those reads out of the phase loop and hold their
+  // results (or values derived from them) in scalar registers throughout.
+  uint32_t argv = 0;
+  {
     const void* const ptrs[8] = {Q, K, V, O, row_ptr, col_idx, work_order, queue};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      s_arg[2 * i] = (uint32_t)(uintptr_t)ptrs[i];
-      s_arg[2 * i + 1] = (uint32_t)((uintptr_t)ptrs[i] >> 32);
+      argv = lane == 2 * i ? (uint32_t)(uintptr_t)ptrs[i] : argv;
+      argv = lane == 2 * i + 1 ? (uint32_t)((uintptr_t)ptrs[i] >> 32) : argv;
     }
-    s_arg[16] = (uint32_t)H;
-    s_arg[17] = (uint32_t)items;
-    s_arg[18] = __float_as_uint(c2);
+    argv = lane == 16 ? (uint32_t)H : argv;
+    argv = lane == 17 ? (uint32_t)items : argv;
+    argv = lane == 18 ? __float_as_uint(c2) : argv;
   }
-  if (threadIdx.x < 2) {
-    s_fin[threadIdx.x] = 0x7fffffff;
-    s_fst[threadIdx.x][0] = blockIdx.x % kParts;   // partition to serve first
-    s_fst[threadIdx.x][1] = 0;                     // partitions tried
-  }
-  __syncthreads();
-
-  // (readfirstlane returns a signed int: each half goes through uint32_t so
-  // that a low word with bit 31 set is not sign-extended into the high word)
-  auto ap = [&](int i) __attribute__((always_inline)) -> uintptr_t {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane(s_arg[2 * i]);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane(s_arg[2 * i + 1]);
-    return (uintptr_t)lo | ((uintptr_t)hi << 32);
+  auto argw = [&](int i) __attribute__((always_inline)) -> uint32_t {
+    return (uint32_t)__builtin_amdgcn_readlane((int)argv, i);
   };
-  auto nheads = [&]() __attribute__((always_inline)) -> int { return __builtin_amdgcn_readfirstlane(s_arg[16]); };
+  // (each half goes through uint32_t, so that a low word with bit 31 set is
+  // not sign-extended into the high word)
+  auto ap = [&](int i) __attribute__((always_inline)) -> uintptr_t {
+    return (uintptr_t)argw(2 * i) | ((uintptr_t)argw(2 * i + 1) << 32);
+  };
+  auto nheads = [&]() __attribute__((always_inline)) -> int { return (int)argw(16); };
   auto part_len = [&](int p) __attribute__((always_inline)) -> int {
     if (ap(6)) return s_poff[p + 1] - s_poff[p];
     return ((nheads() - p + kParts - 1) / kParts) * nqb;
@@ -635,18 +639,15 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
   // 1 counter pop due, 2 pop in flight, 3 work-order entry in flight, 4 list
   // bounds in flight, 5 first key blocks in flight.  The rest of the fetch
   // state (partition, partitions tried, batch, row, list start, blocks) lives
-  // in LDS between calls, so that no scalar register holds it through the
-  // phase loop.
+  // in lanes 0-5 of fstv between calls, so that no scalar register holds it
+  // through the phase loop.
   int f_step = 1;
   int f_val = 0;   // result of the load in flight
+  int fstv = lane == 0 ? (int)(blockIdx.x % kParts) : 0;   // partition to serve first; none tried
   auto write_desc = [&](int b, int r, int beg, int n, int k0, int k1) __attribute__((always_inline)) {
     if (lane == 0) {
-      s_desc[grp][0] = b;
-      s_desc[grp][1] = r;
-      s_desc[grp][2] = beg;
-      s_desc[grp][3] = n;
-      s_desc[grp][4] = k0;
-      s_desc[grp][5] = k1;
+      s_desc[grp][0] = i32x4{b, r, beg, n};
+      s_desc[grp][1] = i32x4{k0, k1, 0, 0};
     }
   };
   // an empty row is written as zeros by the fetching wave
@@ -661,14 +662,15 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
     const g_i32* const ci_ = (const g_i32*)ap(5);
     const g_i32* const wo_ = (const g_i32*)ap(6);
     g_i32* const qu_ = (g_i32*)ap(7);
-    const int items_ = __builtin_amdgcn_readfirstlane(s_arg[17]);
+    const int items_ = (int)argw(17);
     const int rows_ = nheads() * nqb;
-    int f_p = __builtin_amdgcn_readfirstlane(s_fst[grp][0]);
-    int f_tries = __builtin_amdgcn_readfirstlane(s_fst[grp][1]);
-    int f_b = __builtin_amdgcn_readfirstlane(s_fst[grp][2]);
-    int f_r = __builtin_amdgcn_readfirstlane(s_fst[grp][3]);
-    int f_beg = __builtin_amdgcn_readfirstlane(s_fst[grp][4]);
-    int f_n = __builtin_amdgcn_readfirstlane(s_fst[grp][5]);
+    asm volatile("" : "+v"(fstv));
+    int f_p = __builtin_amdgcn_readlane(fstv, 0);
+    int f_tries = __builtin_amdgcn_readlane(fstv, 1);
+    int f_b = __builtin_amdgcn_readlane(fstv, 2);
+    int f_r = __builtin_amdgcn_readlane(fstv, 3);
+    int f_beg = __builtin_amdgcn_readlane(fstv, 4);
+    int f_n = __builtin_amdgcn_readlane(fstv, 5);
     auto issue_bounds = [&]() __attribute__((always_inline)) {
       if (DENSE) {
         write_desc(f_b, f_r, 0, nkb_valid, 0, nkb_valid > 1 ? 1 : 0);
@@ -746,14 +748,9 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
       if (f_step == 0 || !finish) break;
       if (f_step != 1) wait_vm();
     }
-    if (lane == 0) {
-      s_fst[grp][0] = f_p;
-      s_fst[grp][1] = f_tries;
-      s_fst[grp][2] = f_b;
-      s_fst[grp][3] = f_r;
-      s_fst[grp][4] = f_beg;
-      s_fst[grp][5] = f_n;
-    }
+    const int fs[6] = {f_p, f_tries, f_b, f_r, f_beg, f_n};
+#pragma unroll
+    for (int i = 0; i < 6; ++i) fstv = lane == i ? fs[i] : fstv;
   };
 
   // ---- the group's row state ----
@@ -829,7 +826,7 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
 #pragma unroll
     for (int s = 0; s < DS; ++s)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qreg[s][e] = (bf16)((float)qreg[s][e] * __uint_as_float(s_arg[18]));
+      for (int e = 0; e < 8; ++e) qreg[s][e] = (bf16)((float)qreg[s][e] * __uint_as_float(argw(18)));
   };
   // the group's reference (log2 units) and row sum; fresh until the
   // reference has been set from the maximum of a sub-tile with valid keys
@@ -844,14 +841,21 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
   float alpha = 1.f;
 
   // ---- prologue: each group's first row, its K(0) tile and Q ----
+  // the group's descriptor, read as two vectors (one LDS round trip)
+  auto row_desc = [&](int* v) __attribute__((always_inline)) {
+    const i32x4 d0 = s_desc[grp][0], d1 = s_desc[grp][1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_readfirstlane(d0[i]);
+    v[4] = __builtin_amdgcn_readfirstlane(d1[0]);
+    v[5] = __builtin_amdgcn_readfirstlane(d1[1]);
+  };
   if (w == 0) fetch(true);
   __syncthreads();
   {
-    const int r0 = __builtin_amdgcn_readfirstlane(s_desc[grp][1]);
-    if (r0 >= 0) {
-      set_row(__builtin_amdgcn_readfirstlane(s_desc[grp][0]), r0, __builtin_amdgcn_readfirstlane(s_desc[grp][2]),
-              __builtin_amdgcn_readfirstlane(s_desc[grp][3]), __builtin_amdgcn_readfirstlane(s_desc[grp][4]),
-              __builtin_amdgcn_readfirstlane(s_desc[grp][5]));
+    int dv[6];
+    row_desc(dv);
+    if (dv[1] >= 0) {
+      set_row(dv[0], dv[1], dv[2], dv[3], dv[4], dv[5]);
       if (!DENSE) {
         ck_cur = chunk_load(cbeg, cnb, 0);
         ck_nxt = chunk_load(cbeg, cnb, 1);
@@ -879,6 +883,7 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
   // matrix phase of stream cycle x (TM = x % 2 fixes the stages)
   auto mphase = [&](auto tmc) __attribute__((always_inline)) {
     constexpr int TM = decltype(tmc)::value;
+    asm volatile("" : "+v"(argv));
     if (__builtin_expect(!cur && !pend, 0)) {
       lds_barrier();
       return;
@@ -896,18 +901,18 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
     const bool last = TM == 1 && cur && j == cn - 1;
     int nb = 0, nr = 0;
     if (__builtin_expect(last, 0)) {
-      nr = __builtin_amdgcn_readfirstlane(s_desc[grp][1]);
+      int dv[6];
+      row_desc(dv);
+      nr = dv[1];
       nxt = nr >= 0;
       if (nxt) {
-        nb = __builtin_amdgcn_readfirstlane(s_desc[grp][0]);
+        nb = dv[0];
         rkd = make_rsrc((const bf16*)ap(1) + ((size_t)nb * nheads() + nr / nqb) * (size_t)L * D, k_bytes);
-        kd = __builtin_amdgcn_readfirstlane(s_desc[grp][4]) * BLK;
+        kd = dv[4] * BLK;
         // the current row's list is not read past this point
         if (!DENSE) {
-          const int nbeg = __builtin_amdgcn_readfirstlane(s_desc[grp][2]);
-          const int nn = __builtin_amdgcn_readfirstlane(s_desc[grp][3]);
-          ck_cur = chunk_load(nbeg, nn, 0);
-          ck_nxt = chunk_load(nbeg, nn, 1);
+          ck_cur = chunk_load(dv[2], dv[3], 0);
+          ck_nxt = chunk_load(dv[2], dv[3], 1);
         }
       }
     }
@@ -977,30 +982,58 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
   // vector phase of stream cycle x; gp is the global phase index
   auto vphase = [&](auto tmc, int gp) __attribute__((always_inline)) {
     constexpr int TM = decltype(tmc)::value;
+    asm volatile("" : "+v"(argv));
     if (__builtin_expect(!cur && !pend, 0)) {
+      // (nothing is in flight here; the wait tells the compiler so, which
+      // keeps it from waiting for the DMA of a later phase before the LDS
+      // accesses of the next)
+      wait_vm();
       lds_barrier();
       return;
     }
     if (__builtin_expect(pend, 0)) {
       // the previous row's last P*V ran in the matrix phase just ended: O =
-      // acc / l; padded query rows (and rows that saw no key) are zero
-      const int pb = __builtin_amdgcn_readfirstlane(s_prev[grp][0]);
-      const int pr = __builtin_amdgcn_readfirstlane(s_prev[grp][1]);
+      // acc / l; padded query rows (and rows that saw no key) are zero.
+      // In the accumulator layout a lane holds 8-byte pieces of one query's
+      // row, so a direct store would touch 32 rows with 16 bytes each.  The
+      // wave's 32 x D tile goes out through LDS instead, 64 columns at a
+      // time, and each store writes whole 128-byte lines.  The staging
+      // buffer is an LDS object of its own, which no DMA ever writes, so its
+      // accesses need no wait for the tiles in flight.
+      const i32x2 pv = s_prev[grp];
+      const int pb = __builtin_amdgcn_readfirstlane(pv[0]);
+      const int pr = __builtin_amdgcn_readfirstlane(pv[1]);
       const float l_tot = pair_sum(l_fin);
       const int q = (pr % nqb) * BLK + 32 * w + c;
       const bool valid = q < qlim && l_tot > 0.f;
       const float inv = valid ? 1.f / l_tot : 0.f;
-      g_bf16* const Ob = (g_bf16*)ap(3) + o_row(pb, pr) + (size_t)(32 * w + c) * D;
+      char* const stg = reinterpret_cast<char*>(s_ost) + w * (32 * 128);
+      g_bf16* const Ob = (g_bf16*)ap(3) + o_row(pb, pr) + (size_t)(32 * w) * D;
 #pragma unroll
-      for (int t = 0; t < DT; ++t) {
+      for (int hr = 0; hr < DT / 2; ++hr) {
+        // lane (g, c) holds query c, d = 32t + 8rq + 4g + e: 8-byte pieces of
+        // the staged row's 16-byte units 4(t - 2hr) + rq, the unit index
+        // XORed with c % 8
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          bf16x4 o;
+        for (int t = 2 * hr; t < 2 * hr + 2; ++t) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = valid ? (bf16)(oacc[t][4 * rq + e] * inv) : (bf16)0.f;
-          *(g_bf16x4*)(Ob + 32 * t + 8 * rq + 4 * g) = o;
+          for (int rq = 0; rq < 4; ++rq) {
+            f32x4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = valid ? oacc[t][4 * rq + e] * inv : 0.f;
+            *reinterpret_cast<bf16x4*>(stg + c * 128 + (((4 * (t - 2 * hr) + rq) ^ (c & 7)) * 16) + 8 * g) =
+                __builtin_convertvector(x, bf16x4);
+          }
+          oacc[t] = f32x16{};
         }
-        oacc[t] = f32x16{};
+        // read back: lane L takes unit L % 8 of row L / 8 (+ 8 rows per
+        // instruction), 64 columns of each row
+#pragma unroll 2
+        for (int i = 0; i < 4; ++i) {
+          const int row = 8 * i + lane / 8, u = lane % 8;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * 128 + ((u ^ (row & 7)) * 16));
+          *(g_u32x4*)(Ob + (size_t)row * D + 64 * hr + 8 * u) = v;
+        }
       }
       pend = false;
       if (!cur) {
@@ -1077,13 +1110,12 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
         // Every wave of the group writes the same row to s_prev; it is read
         // in the next phase, after the barrier.
         l_fin = l_run;
-        s_prev[grp][0] = cb;
-        s_prev[grp][1] = cr;
+        s_prev[grp] = i32x2{cb, cr};
         pend = true;
         if (nxt) {
-          set_row(__builtin_amdgcn_readfirstlane(s_desc[grp][0]), __builtin_amdgcn_readfirstlane(s_desc[grp][1]),
-                  __builtin_amdgcn_readfirstlane(s_desc[grp][2]), __builtin_amdgcn_readfirstlane(s_desc[grp][3]),
-                  __builtin_amdgcn_readfirstlane(s_desc[grp][4]), __builtin_amdgcn_readfirstlane(s_desc[grp][5]));
+          int dv[6];
+          row_desc(dv);
+          set_row(dv[0], dv[1], dv[2], dv[3], dv[4], dv[5]);
           ref = 0.f;
           l_run = 0.f;
           fresh = true;
