@@ -58,16 +58,23 @@ def kernel_source_hash():
 
 
 def traffic_from_profile(workload):
-    """HBM bytes per launch from the committed counter summary, if it covers this
-    workload and matches the current kernel source."""
+    """Bytes per launch from the committed counter summary, if it covers this
+    workload and matches the current kernel source: (traffic, extra), where
+    traffic counts what L2 fetched from and wrote to the memory side
+    (FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for a plain copy
+    of known size) and extra holds the memory-side request counters of the
+    same launch.  Both include reads the MALL serves, so they bound HBM bytes
+    from above."""
     try:
         with open(COUNTERS) as f:
             c = json.load(f)
     except (OSError, ValueError):
-        return None
+        return None, None
     if c.get("kernel_source_hash") != kernel_source_hash() or not c.get("workload", "").startswith(workload + ":"):
-        return None
-    return c.get("hbm_bytes_per_launch")
+        return None, None
+    extra = {k: c[k] for k in ("memory_side_read_bytes_per_launch", "memory_side_write_bytes_per_launch",
+                               "compulsory_bytes_per_launch") if k in c}
+    return c.get("traffic_bytes_per_launch"), (extra or None)
 
 
 def mfma_rate():
@@ -94,38 +101,104 @@ def copy_probe(mb):
     print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "launches": 3}))
 
 
-def cpu_baseline(q, k, v, rp, ci, cfg, budget_s):
-    """The float64 oracle on whole query blocks of the same inputs, until budget_s elapses."""
-    import oracle
+def host_info():
+    """The host the CPU figures come from: logical CPUs, the ones this process
+    may run on, the CPU model and the memory size."""
+    info = {"nproc": os.cpu_count()}
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count() or 1
-    items, flops = [], 0.0
-    t0 = time.perf_counter()
-    h = 0
-    qb = 0
-    while time.perf_counter() - t0 < budget_s and h < cfg.H:
-        it = (0, h, qb)
-        oracle.sparse_attention_rows(q, k, v, rp, ci, cfg.block, cfg.scale, cfg.S, [it])
-        r = h * cfg.nqb + qb
-        flops += tile_flops(cfg.block, cfg.d) * int(rp[r + 1] - rp[r])
-        items.append(it)
-        qb += 1
-        if qb == cfg.nqb:
-            qb, h = 0, h + 1
-    dt = time.perf_counter() - t0
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{len(items)} of {cfg.rows} query blocks (heads 0..{items[-1][1]}, in order) of the "
-                      f"same Wan inputs and mask, float64, {dt:.1f} s"}
+        info["affinity"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        info["affinity"] = None
+    model = mem = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+        with open("/proc/meminfo") as f:
+            kb = next((int(ln.split()[1]) for ln in f if ln.startswith("MemTotal")), None)
+            mem = round(kb / (1 << 20), 1) if kb else None
+    except OSError:
+        pass
+    info["cpu_model"] = model
+    info["ram_gib"] = mem
+    return info
+
+
+def _oracle_worker(job):
+    """One worker of the CPU baseline: the float64 oracle on whole query blocks
+    of its heads, in order, until its time budget is spent."""
+    folder, heads, budget_s, block, scale, seq_len, nqb, d = job
+    import oracle
+    q, k, v = (np.load(os.path.join(folder, n + ".npy"), mmap_mode="r") for n in ("q", "k", "v"))
+    rp = np.load(os.path.join(folder, "rp.npy"))
+    ci = np.load(os.path.join(folder, "ci.npy"))
+    t0 = time.time()
+    n, flops = 0, 0.0
+    for h in heads:
+        for qb in range(nqb):
+            if time.time() - t0 >= budget_s:
+                return t0, time.time(), n, flops
+            oracle.sparse_attention_rows(q, k, v, rp, ci, block, scale, seq_len, [(0, h, qb)])
+            r = h * nqb + qb
+            flops += tile_flops(block, d) * int(rp[r + 1] - rp[r])
+            n += 1
+    return t0, time.time(), n, flops
+
+
+def cpu_baseline(q, k, v, rp, ci, cfg, budget_s, workers=None):
+    """The float64 oracle on the same inputs and mask, as a pool over heads:
+    one process per usable core (at most 16 and at most H), each with one BLAS
+    thread, worker i taking heads i, i + W, ... and their query blocks in
+    order until budget_s elapses.  The processes are started fresh (spawn),
+    read the inputs from memory-mapped files, and run after the GPU work."""
+    import multiprocessing as mp
+    import shutil
+    import tempfile
+    from concurrent.futures import ProcessPoolExecutor
+    host = host_info()
+    usable = host["affinity"] or host["nproc"] or 1
+    W = max(1, min(usable, 16, cfg.H) if workers is None else workers)
+    shm = "/dev/shm" if os.path.isdir("/dev/shm") else None
+    folder = tempfile.mkdtemp(prefix="calibatt_cpu_", dir=shm)
+    saved = {n: os.environ.get(n) for n in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    try:
+        for n, a in (("q", q), ("k", k), ("v", v), ("rp", rp), ("ci", ci)):
+            np.save(os.path.join(folder, n + ".npy"), np.ascontiguousarray(a))
+        for n in saved:
+            os.environ[n] = "1"
+        jobs = [(folder, list(range(i, cfg.H, W)), budget_s, cfg.block, cfg.scale, cfg.S, cfg.nqb, cfg.d)
+                for i in range(W)]
+        # (a pool that raises if a worker dies, instead of starting new ones)
+        with ProcessPoolExecutor(max_workers=W, mp_context=mp.get_context("spawn")) as pool:
+            res = list(pool.map(_oracle_worker, jobs))
+    finally:
+        for n, val in saved.items():
+            if val is None:
+                os.environ.pop(n, None)
+            else:
+                os.environ[n] = val
+        shutil.rmtree(folder, ignore_errors=True)
+    t_start = min(r[0] for r in res)
+    t_end = max(r[1] for r in res)
+    n = sum(r[2] for r in res)
+    flops = sum(r[3] for r in res)
+    dt = t_end - t_start
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": W, "kind": "oracle",
+            "sample": f"{n} of {cfg.rows} query blocks of the same inputs and mask, float64, {W} processes "
+                      f"x 1 BLAS thread over heads (worker i: heads i, i+{W}, ..., blocks in order), "
+                      f"{dt:.1f} s wall",
+            "host": host}
 
 
 def cpu_extra(q, k, v, cfg, budget_s):
     """The float64 oracle on the dense call and on the calibration pooling, each on
     whole query blocks in order until budget_s elapses, scaled to one full call."""
     import oracle
-    out = {}
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except ImportError:
+        threads = None
+    out = {"process": "this one, serial over query blocks", "blas_threads": threads}
     nkv = cfg.nkb_valid
     rp = (np.arange(cfg.rows + 1) * nkv).astype(np.int32)
     ci = np.tile(np.arange(nkv), cfg.rows).astype(np.int32)
@@ -466,6 +539,7 @@ def main():
         cpu = cpu_baseline(q, k, v, rp0, ci0, cfg, args.cpu_seconds)
         cpu_more = cpu_extra(q, k, v, cfg, args.cpu_seconds / 2.5)
 
+    traffic = traffic_from_profile(cfg.name)
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -494,8 +568,11 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic_from_profile(cfg.name),
-            "kernel": "attn_fwd_pp_kernel<128,false,false>",
+            "traffic": traffic[0],
+            "traffic_kind": "bytes L2 exchanged with the memory side per launch (FETCH_SIZE and WRITE_SIZE "
+                            "scaled by a 1 GiB copy); includes reads the MALL serves, an upper bound on HBM bytes",
+            "traffic_counters": traffic[1],
+            "kernel": "attn_fwd_pp_kernel<128,false,false,false>",
             "avg_launch_ms": round(float(np.mean(launch_ms)), 4),
             "measured_mfma_rate": peak_probe,
             "frac_of_random_operand_rate": (round(achieved / peak_probe["random_operands_tflops"], 4)
