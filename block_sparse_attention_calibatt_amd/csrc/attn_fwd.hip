@@ -516,7 +516,6 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
   __shared__ u32x4 s_ost[4 * 32 * 8];   // O staging: per wave of a group 32 rows x 64 columns
   // per group: next row b, r (-1: none), list start, blocks; then kb0, kb1
   __shared__ i32x4 s_desc[2][2];
-  __shared__ int s_poff[kParts + 1];  // partition offsets of the work order
   __shared__ int s_fin[2];            // phase in which each group finished
   __shared__ i32x2 s_prev[2];         // per group: batch and row of the row whose O is due
 
@@ -593,14 +592,14 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
   // every stage starts as zeros: the first P*V of a group multiplies zero
   // probabilities with a V stage no tile has been loaded into yet
   for (int u = threadIdx.x; u < 4 * G::UNITS; u += 512) lA[u] = lB[u] = u32x4{0u, 0u, 0u, 0u};
-  if (threadIdx.x <= kParts) s_poff[threadIdx.x] = work_order ? work_order[rows + threadIdx.x] : 0;
   if (threadIdx.x < 2) s_fin[threadIdx.x] = 0x7fffffff;
   __syncthreads();
 
   // Arguments only the rare paths use (row fetch, row switch, O store) sit
   // in the lanes of one vector register: lane 2i and 2i+1 the low and high
   // word of pointer i of (Q, K, V, O, row_ptr, col_idx, work_order, queue),
-  // lane 16 H, lane 17 items, lane 18 c2.  They are read with readlane where
+  // lane 16 H, lane 17 items, lane 18 c2, lane 19 the batch entries, lanes
+  // 20-28 the work order's partition offsets.  They are read with readlane where
   // needed; the register is re-declared live in every phase, so that the
   // compiler cannot hoist those reads out of the phase loop and hold their
   // results (or values derived from them) in scalar registers throughout.
@@ -615,6 +614,9 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
     argv = lane == 16 ? (uint32_t)H : argv;
     argv = lane == 17 ? (uint32_t)items : argv;
     argv = lane == 18 ? __float_as_uint(c2) : argv;
+    argv = lane == 19 ? (uint32_t)(items / rows) : argv;
+    // lanes 20 .. 20+kParts: the partition offsets of the work order
+    if (work_order && lane >= 20 && lane <= 20 + kParts) argv = (uint32_t)work_order[rows + lane - 20];
   }
   auto argw = [&](int i) __attribute__((always_inline)) -> uint32_t {
     return (uint32_t)__builtin_amdgcn_readlane((int)argv, i);
@@ -625,10 +627,6 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
     return (uintptr_t)argw(2 * i) | ((uintptr_t)argw(2 * i + 1) << 32);
   };
   auto nheads = [&]() __attribute__((always_inline)) -> int { return (int)argw(16); };
-  auto part_len = [&](int p) __attribute__((always_inline)) -> int {
-    if (ap(6)) return s_poff[p + 1] - s_poff[p];
-    return ((nheads() - p + kParts - 1) / kParts) * nqb;
-  };
   auto o_row = [&](int b, int r) __attribute__((always_inline)) -> size_t {
     const int h = r / nqb, qb = r - h * nqb;
     return (((size_t)b * nheads() + h) * (size_t)nqb + qb) * (size_t)BLK * D;
@@ -643,6 +641,7 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
   // through the phase loop.
   int f_step = 1;
   int f_val = 0;   // result of the load in flight
+  int f_pop = 0;   // result of the queue pop in flight
   int fstv = lane == 0 ? (int)(blockIdx.x % kParts) : 0;   // partition to serve first; none tried
   auto write_desc = [&](int b, int r, int beg, int n, int k0, int k1) __attribute__((always_inline)) {
     if (lane == 0) {
@@ -663,6 +662,7 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
     const g_i32* const wo_ = (const g_i32*)ap(6);
     g_i32* const qu_ = (g_i32*)ap(7);
     const int items_ = (int)argw(17);
+    const int nb_ = (int)argw(19);   // batch entries
     const int rows_ = nheads() * nqb;
     asm volatile("" : "+v"(fstv));
     int f_p = __builtin_amdgcn_readlane(fstv, 0);
@@ -671,66 +671,70 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
     int f_r = __builtin_amdgcn_readlane(fstv, 3);
     int f_beg = __builtin_amdgcn_readlane(fstv, 4);
     int f_n = __builtin_amdgcn_readlane(fstv, 5);
-    auto issue_bounds = [&]() __attribute__((always_inline)) {
-      if (DENSE) {
-        write_desc(f_b, f_r, 0, nkb_valid, 0, nkb_valid > 1 ? 1 : 0);
-        f_step = 0;
-      } else {
-        if (lane < 2) f_val = rp_[f_r + lane];
-        f_step = 4;
-      }
-    };
-    auto issue_pop = [&]() __attribute__((always_inline)) {
-      if (!qu_) {   // no queue: workgroup i serves rows 2i and 2i+1 of the order, one per group
-        const int item = 2 * blockIdx.x + grp;
-        if (f_tries == 0 && item < items_) {
-          f_tries = 1;
-          f_b = item / rows_;
-          const int jr = item - f_b * rows_;
-          if (wo_) {
-            if (lane == 0) f_val = wo_[jr];
-            f_step = 3;
-          } else {
-            f_r = jr;
-            issue_bounds();
-          }
-        } else {
-          write_desc(0, -1, 0, 0, 0, 0);
-          f_step = 0;
-        }
-        return;
-      }
-      if (lane == 0) f_val = __hip_atomic_fetch_add(qu_ + f_p * kQueueStride, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      f_step = 2;
+    // rows of partition p per batch entry (offsets in lanes 20.. of argv)
+    auto part_len = [&](int p) __attribute__((always_inline)) -> int {
+      if (wo_) return (int)argw(21 + p) - (int)argw(20 + p);
+      return ((nheads() - p + kParts - 1) / kParts) * nqb;
     };
     for (;;) {
+      // The step's load: lanes 0-1 read ld[min(lane, lcap - 1)]; the queue
+      // pop is an atomic into f_pop.  The chain has this one load site, so
+      // its result stays in one register: with a load per step the compiler
+      // copies each result into a shared register, which waits for the load
+      // on the spot.
+      const g_i32* ld = nullptr;
+      int lcap = 0;
+      bool pop = false;
+      bool bounds = false;   // the row is known: its list bounds are next
       if (f_step == 1) {
-        issue_pop();
+        if (!qu_) {   // no queue: workgroup i serves rows 2i and 2i+1 of the order, one per group
+          const int item = 2 * blockIdx.x + grp;
+          if (f_tries == 0 && item < items_) {
+            f_tries = 1;
+            f_b = item / rows_;
+            const int jr = item - f_b * rows_;
+            if (wo_) {
+              ld = wo_ + jr;
+              lcap = 1;
+              f_step = 3;
+            } else {
+              f_r = jr;
+              bounds = true;
+            }
+          } else {
+            write_desc(0, -1, 0, 0, 0, 0);
+            f_step = 0;
+          }
+        } else {
+          pop = true;
+          f_step = 2;
+        }
       } else if (f_step == 2) {
-        const int k = __builtin_amdgcn_readfirstlane(f_val);
+        const int k = __builtin_amdgcn_readfirstlane(f_pop);
         const int len = part_len(f_p);
-        if (k >= (items_ / rows_) * len) {
+        if (k >= nb_ * len) {
           f_p = (f_p + 1) % kParts;
           if (++f_tries >= kParts) {
             write_desc(0, -1, 0, 0, 0, 0);
             f_step = 0;
           } else {
-            issue_pop();
+            pop = true;
           }
         } else {
-          f_b = k / len;
+          f_b = nb_ > 1 ? k / len : 0;
           const int jr = k - f_b * len;
           if (wo_) {
-            if (lane == 0) f_val = wo_[s_poff[f_p] + jr];
+            ld = wo_ + (int)argw(20 + f_p) + jr;
+            lcap = 1;
             f_step = 3;
           } else {
             f_r = (f_p + kParts * (jr / nqb)) * nqb + jr % nqb;
-            issue_bounds();
+            bounds = true;
           }
         }
       } else if (f_step == 3) {
         f_r = __builtin_amdgcn_readfirstlane(f_val);
-        issue_bounds();
+        bounds = true;
       } else if (f_step == 4) {
         f_beg = __builtin_amdgcn_readlane(f_val, 0);
         f_n = __builtin_amdgcn_readlane(f_val, 1) - f_beg;
@@ -738,13 +742,27 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
           zero_row(f_b, f_r);
           f_step = 1;
         } else {
-          if (lane < 2) f_val = ci_[f_beg + (lane < f_n ? lane : f_n - 1)];
+          ld = ci_ + f_beg;
+          lcap = f_n;
           f_step = 5;
         }
       } else if (f_step == 5) {
         write_desc(f_b, f_r, f_beg, f_n, __builtin_amdgcn_readlane(f_val, 0), __builtin_amdgcn_readlane(f_val, 1));
         f_step = 0;
       }
+      if (bounds) {
+        if (DENSE) {
+          write_desc(f_b, f_r, 0, nkb_valid, 0, nkb_valid > 1 ? 1 : 0);
+          f_step = 0;
+        } else {
+          ld = rp_ + f_r;
+          lcap = 2;
+          f_step = 4;
+        }
+      }
+      if (pop && lane == 0)
+        f_pop = __hip_atomic_fetch_add(qu_ + f_p * kQueueStride, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (ld && lane < 2) f_val = ld[lane < lcap ? lane : lcap - 1];
       if (f_step == 0 || !finish) break;
       if (f_step != 1) wait_vm();
     }
