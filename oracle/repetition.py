@@ -70,8 +70,16 @@ def _softmax_rows(q, k, scale, seq_len):
     return e / e.sum(axis=1, keepdims=True)
 
 
-def spatial_similarity(q, k, scale, seq_len, grid):
-    """Fig. 6 / Fig. S13 score per (b, h): mean cosine of vertically adjacent softmax rows."""
+def _pair_cosines(a, c):
+    return (a * c).sum(axis=1) / np.sqrt((a * a).sum(axis=1) * (c * c).sum(axis=1))
+
+
+def spatial_similarity(q, k, scale, seq_len, grid, pairs_per_pass=None):
+    """Fig. 6 / Fig. S13 score per (b, h): mean cosine of vertically adjacent softmax rows.
+
+    pairs_per_pass: form the softmax rows of that many adjacent pairs at a
+    time instead of the whole map (the same mean in bounded memory: the
+    cosines are summed pass by pass and divided by their count)."""
     q, k = (np.asarray(x, dtype=np.float64) for x in (q, k))
     B, H, L, d = q.shape
     F, R, C = grid
@@ -81,10 +89,17 @@ def spatial_similarity(q, k, scale, seq_len, grid):
     sim = np.zeros((B, H), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            P = _softmax_rows(q[b, h, :seq_len], k[b, h], scale, seq_len)
-            a, c = P[top], P[top + C]
-            cos = (a * c).sum(axis=1) / np.sqrt((a * a).sum(axis=1) * (c * c).sum(axis=1))
-            sim[b, h] = cos.mean()
+            if pairs_per_pass is None:
+                P = _softmax_rows(q[b, h, :seq_len], k[b, h], scale, seq_len)
+                sim[b, h] = _pair_cosines(P[top], P[top + C]).mean()
+            else:
+                tot = 0.0
+                for i in range(0, len(top), pairs_per_pass):
+                    t = top[i:i + pairs_per_pass]
+                    a = _softmax_rows(q[b, h, t], k[b, h], scale, seq_len)
+                    c = _softmax_rows(q[b, h, t + C], k[b, h], scale, seq_len)
+                    tot += _pair_cosines(a, c).sum()
+                sim[b, h] = tot / len(top)
     return sim
 
 

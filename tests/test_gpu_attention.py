@@ -261,10 +261,66 @@ def _sample_items(cfg, rng, n):
     return items
 
 
+def _head_ref(q, k, v, rp, ci, cfg, b, h, qbs):
+    """Oracle rows qbs of head h, batch entry b, computed from that head's
+    arrays (float64) and its slice of the kept lists alone."""
+    r0 = h * cfg.nqb
+    base = int(rp[r0])
+    rp_h = (np.asarray(rp[r0:r0 + cfg.nqb + 1], dtype=np.int64) - base)
+    ci_h = np.asarray(ci[base:int(rp[r0 + cfg.nqb])])
+    qh, kh, vh = (np.asarray(x[b:b + 1, h:h + 1], dtype=np.float64) for x in (q, k, v))
+    return oracle.sparse_attention_rows(qh, kh, vh, rp_h, ci_h, cfg.block, cfg.scale, cfg.S,
+                                        [(0, 0, qb) for qb in qbs])
+
+
+def _length_class_rows(rp):
+    """Rows by kept count: the longest, the first and last empty ones, and for
+    T = 64, 128, 192 (the kernel reads a row's list 64 entries at a time) a
+    row with exactly T and T + 1 entries and the shortest row above T."""
+    cnt = np.diff(np.asarray(rp, dtype=np.int64))
+    picks = {int(np.argmax(cnt))}
+    empty = np.nonzero(cnt == 0)[0]
+    if len(empty):
+        picks.update((int(empty[0]), int(empty[-1])))
+    for T in (64, 128, 192):
+        for want in (T, T + 1):
+            ex = np.nonzero(cnt == want)[0]
+            if len(ex):
+                picks.add(int(ex[0]))
+        above = np.nonzero(cnt > T)[0]
+        if len(above):
+            picks.add(int(above[np.argmin(cnt[above])]))
+    return sorted(picks)
+
+
+def _compare_rows(O, cfg, b, h, qbs, ref):
+    worst = 0.0
+    for qb, rr in zip(qbs, ref):
+        g = O[b, h, qb * cfg.block:(qb + 1) * cfg.block].float().cpu().numpy()
+        worst = max(worst, float(np.max(np.abs(g - rr))))
+    return worst
+
+
 def _full_size_check(cfg, rp, ci, seed_items, n_items, tol=2e-2):
+    """The persistent longest-first launch at full size against the oracle:
+    every row of the heaviest head, rows chosen by length class over the whole
+    mask, and sampled rows; padded rows zero, everything finite."""
     q, k, v = inputs(cfg)
     wo = oracle.lpt_work_order(rp, cfg.H, cfg.nqb)
     O = run_sparse(q, k, v, rp, ci, cfg, work_order=wo, persistent=True)
+    per_head = np.diff(np.asarray(rp, dtype=np.int64)[::cfg.nqb])
+    hw = int(np.argmax(per_head))
+    worst = _compare_rows(O, cfg, 0, hw, range(cfg.nqb), _head_ref(q, k, v, rp, ci, cfg, 0, hw, range(cfg.nqb)))
+    say(f"  whole head {hw} ({cfg.nqb} query blocks, {int(per_head[hw])} kept), max err {worst:.3e}")
+    assert worst <= tol
+    classes = _length_class_rows(rp)
+    cnt = np.diff(np.asarray(rp, dtype=np.int64))
+    worst = 0.0
+    for r in classes:
+        h, qb = divmod(r, cfg.nqb)
+        worst = max(worst, _compare_rows(O, cfg, 0, h, [qb], _head_ref(q, k, v, rp, ci, cfg, 0, h, [qb])))
+    say(f"  length-class rows {[(r, int(cnt[r])) for r in classes]}, max err {worst:.3e}")
+    assert worst <= tol
     items = _sample_items(cfg, np.random.default_rng(seed_items), n_items)
     ref = oracle.sparse_attention_rows(q, k, v, rp, ci, cfg.block, cfg.scale, cfg.S, items)
     worst = 0.0
@@ -278,31 +334,31 @@ def _full_size_check(cfg, rp, ci, seed_items, n_items, tol=2e-2):
     assert torch.isfinite(O.float()).all()
 
 
-def test_wan_full_size_sampled(gpu):
+def test_wan_full_size(gpu):
     cfg = synth.get_config("wan")
-    say("case: Wan full size, persistent + longest-first order, sampled rows")
+    say("case: Wan full size, persistent + longest-first order")
     rp, ci = synth.csr_for_config(cfg)
     _full_size_check(cfg, rp, ci, 11, 24)
 
 
-def test_wan720_full_size_sampled(gpu):
+def test_wan720_full_size(gpu):
     cfg = synth.get_config("wan720")
-    say("case: Wan 720p full size (591 blocks per head), sampled rows")
+    say("case: Wan 720p full size (591 blocks per head)")
     rp, ci = synth.csr_for_config(cfg)
     _full_size_check(cfg, rp, ci, 51, 12)
 
 
-def test_mochi_full_size_sampled(gpu):
+def test_mochi_full_size(gpu):
     cfg = synth.get_config("mochi")
-    say("case: Mochi full size, sampled rows")
+    say("case: Mochi full size")
     rp, ci = synth.csr_for_config(cfg)
     _full_size_check(cfg, rp, ci, 21, 24)
 
 
-def test_imbalance_sets_sampled(gpu):
+def test_imbalance_sets(gpu):
     cfg = synth.get_config("imbalance")
     for t in (0, 49):
-        say(f"case: imbalance set {t}, sampled rows")
+        say(f"case: imbalance set {t}")
         rp, ci = synth.csr_for_config(cfg, t)
         _full_size_check(cfg, rp, ci, 31 + t, 12)
 
@@ -321,3 +377,19 @@ def test_mochi_dense_sampled(gpu):
                 for (b, h, qb), rr in zip(items, ref))
     say(f"  max err {worst:.3e}")
     assert worst <= 2e-2
+
+
+def test_wan_dense_whole_head(gpu):
+    """The Wan-size dense launch: every row of one head against the oracle."""
+    cfg = synth.get_config("wan")
+    say("case: Wan dense, whole head 17")
+    q, k, v = inputs(cfg)
+    O = run_dense(q, k, v, cfg, persistent=True)
+    nkv = cfg.nkb_valid
+    rp = (np.arange(cfg.rows + 1) * nkv).astype(np.int64)
+    ci = np.tile(np.arange(nkv), cfg.rows).astype(np.int32)
+    h = 17
+    worst = _compare_rows(O, cfg, 0, h, range(cfg.nqb), _head_ref(q, k, v, rp, ci, cfg, 0, h, range(cfg.nqb)))
+    say(f"  max err {worst:.3e}")
+    assert worst <= 2e-2
+    assert torch.count_nonzero(O[:, :, cfg.S:].float()).item() == 0

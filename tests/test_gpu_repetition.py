@@ -66,7 +66,8 @@ def test_similarity_small(gpu, grid, d, H, repeat):
 
 def test_similarity_wan_full_size(gpu):
     """Wan shape, all 40 heads: repeated heads score 1, a partly repeated one
-    scores above every untouched head."""
+    scores above every untouched head, and that head's score equals the
+    oracle's (its softmax rows formed 2048 pairs at a time)."""
     cfg = synth.get_config("wan")
     say("case: spatial similarity, Wan full size")
     q, k, _ = inputs(cfg)
@@ -78,6 +79,9 @@ def test_similarity_wan_full_size(gpu):
     assert abs(got[0, 3] - 1.0) <= 1e-5 and abs(got[0, 17] - 1.0) <= 1e-5
     others = [h for h in range(cfg.H) if h not in (3, 17, 29)]
     assert got[0, 29] > max(got[0, h] for h in others)
+    ref = oracle.spatial_similarity(q[:, 29:30], k[:, 29:30], cfg.scale, cfg.S, cfg.grid, pairs_per_pass=2048)
+    say(f"  head 29: gpu {got[0, 29]:.6f} oracle {ref[0, 0]:.6f}")
+    assert abs(got[0, 29] - ref[0, 0]) <= SIM_TOL
 
 
 def test_similarity_with_pooling_lse(gpu):
