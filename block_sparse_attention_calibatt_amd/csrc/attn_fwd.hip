@@ -446,13 +446,14 @@ __global__ __launch_bounds__(BLK * 2, (D == 128 && BLK == 64) ? 1 : 2) void attn
 // Geometry of the 128-token-block kernel: keys in 64-key sub-tiles; a K
 // stage holds one sub-tile as 64 rows of D/8 16-byte units, a V stage the
 // same sub-tile of V (64 rows, natural layout) or of V^T (D rows of 8 units).
-// Each wave group owns four stages: K0, K1, V0, V1.  They sit in two LDS
-// objects, A = (K0, V1) and B = (K1, V0), each stage holding both groups'
-// halves.  A matrix phase with stage index TM reads K(TM) and V(TM^1), one
-// object, while its DMA fills K(TM^1) and V(TM), the other; so the DMA and
-// every LDS access of a phase touch different objects, which the compiler
-// can tell apart (it would otherwise wait for every DMA in flight before
-// each access).
+// Each wave group owns four stages: K0, K1, V0, V1.  The stages are four LDS
+// objects, each holding both groups' stage of that name, so that the DMA
+// into one stage and the operand reads of another are accesses to different
+// objects, which the compiler can tell apart (it would otherwise wait for
+// every DMA in flight before each read).  (Two objects of two stages each
+// would do the same, but put every read of one matrix phase past the 64 KiB
+// reach of the LDS instructions' immediate offset, which costs an address
+// add per read or two.)
 template <int D>
 struct PPGeo {
   static constexpr int CH = D / 8;
@@ -512,7 +513,7 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
   using G = PPGeo<D>;
   constexpr int CH = G::CH, DS = G::DS, DT = G::DT, KS = G::KS, NDMA = G::NDMA;
   constexpr int STAGE = G::STAGE, RB = G::RB;
-  __shared__ u32x4 lA[4 * G::UNITS], lB[4 * G::UNITS];
+  __shared__ u32x4 lk0[2 * G::UNITS], lk1[2 * G::UNITS], lv0[2 * G::UNITS], lv1[2 * G::UNITS];
   __shared__ u32x4 s_ost[4 * 32 * 8];   // O staging: per wave of a group 32 rows x 64 columns
   // per group: next row b, r (-1: none), list start, blocks; then kb0, kb1
   __shared__ i32x4 s_desc[2][2];
@@ -531,8 +532,8 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
   // K and V rows past seq_len read as zero (buffer range check)
   const uint32_t k_bytes = (uint32_t)seq_len * RB;
   const uint32_t v_bytes = VT ? (uint32_t)L * RB : (uint32_t)seq_len * RB;
-  char* const kst[2] = {reinterpret_cast<char*>(lA), reinterpret_cast<char*>(lB)};
-  char* const vst[2] = {reinterpret_cast<char*>(lB) + 2 * STAGE, reinterpret_cast<char*>(lA) + 2 * STAGE};
+  char* const kst[2] = {reinterpret_cast<char*>(lk0), reinterpret_cast<char*>(lk1)};
+  char* const vst[2] = {reinterpret_cast<char*>(lv0), reinterpret_cast<char*>(lv1)};
   const int gbase = grp * STAGE;   // the group's half of each stage object
 
   // DMA lane patterns: instruction m of a stage writes LDS units 64m ..
@@ -591,7 +592,7 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
 
   // every stage starts as zeros: the first P*V of a group multiplies zero
   // probabilities with a V stage no tile has been loaded into yet
-  for (int u = threadIdx.x; u < 4 * G::UNITS; u += 512) lA[u] = lB[u] = u32x4{0u, 0u, 0u, 0u};
+  for (int u = threadIdx.x; u < 2 * G::UNITS; u += 512) lk0[u] = lk1[u] = lv0[u] = lv1[u] = u32x4{0u, 0u, 0u, 0u};
   if (threadIdx.x < 2) s_fin[threadIdx.x] = 0x7fffffff;
   __syncthreads();
 
@@ -635,10 +636,12 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
   // ---- row fetch (wave 0 of each group) ----
   // f_step: 0 done (the group's descriptor holds the next row or none),
   // 1 counter pop due, 2 pop in flight, 3 work-order entry in flight, 4 list
-  // bounds in flight, 5 first key blocks in flight.  The rest of the fetch
-  // state (partition, partitions tried, batch, row, list start, blocks) lives
-  // in lanes 0-5 of fstv between calls, so that no scalar register holds it
-  // through the phase loop.
+  // bounds in flight.  The descriptor's fields go to LDS as they become
+  // known (no other wave reads it before the chain has ended and a barrier
+  // has passed), and the row's first two key blocks reach it by DMA, so the
+  // chain ends with the bounds step.  The partition and the partitions
+  // tried live in lanes 0-1 of fstv between calls, so that no scalar
+  // register holds them through the phase loop.
   int f_step = 1;
   int f_val = 0;   // result of the load in flight
   int f_pop = 0;   // result of the queue pop in flight
@@ -658,48 +661,33 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
   // run the chain to its end
   auto fetch = [&](bool finish) __attribute__((always_inline)) {
     const g_i32* const rp_ = (const g_i32*)ap(4);
-    const g_i32* const ci_ = (const g_i32*)ap(5);
     const g_i32* const wo_ = (const g_i32*)ap(6);
     g_i32* const qu_ = (g_i32*)ap(7);
-    const int items_ = (int)argw(17);
-    const int nb_ = (int)argw(19);   // batch entries
     const int rows_ = nheads() * nqb;
-    asm volatile("" : "+v"(fstv));
-    int f_p = __builtin_amdgcn_readlane(fstv, 0);
-    int f_tries = __builtin_amdgcn_readlane(fstv, 1);
-    int f_b = __builtin_amdgcn_readlane(fstv, 2);
-    int f_r = __builtin_amdgcn_readlane(fstv, 3);
-    int f_beg = __builtin_amdgcn_readlane(fstv, 4);
-    int f_n = __builtin_amdgcn_readlane(fstv, 5);
-    // rows of partition p per batch entry (offsets in lanes 20.. of argv)
-    auto part_len = [&](int p) __attribute__((always_inline)) -> int {
-      if (wo_) return (int)argw(21 + p) - (int)argw(20 + p);
-      return ((nheads() - p + kParts - 1) / kParts) * nqb;
-    };
     for (;;) {
-      // The step's load: lanes 0-1 read ld[min(lane, lcap - 1)]; the queue
-      // pop is an atomic into f_pop.  The chain has this one load site, so
-      // its result stays in one register: with a load per step the compiler
-      // copies each result into a shared register, which waits for the load
-      // on the spot.
+      // The step's load: lanes 0-1 read ld[lane < lcap ? lane : 0]; the
+      // queue pop is an atomic into f_pop.  One load site keeps the result
+      // in one register: with a load per step the compiler copies each
+      // result into a shared register, which waits for the load on the spot.
       const g_i32* ld = nullptr;
       int lcap = 0;
       bool pop = false;
-      bool bounds = false;   // the row is known: its list bounds are next
+      int r_known = -1;   // the row is known: its list bounds are next
       if (f_step == 1) {
         if (!qu_) {   // no queue: workgroup i serves rows 2i and 2i+1 of the order, one per group
+          asm volatile("" : "+v"(fstv));
           const int item = 2 * blockIdx.x + grp;
-          if (f_tries == 0 && item < items_) {
-            f_tries = 1;
-            f_b = item / rows_;
-            const int jr = item - f_b * rows_;
+          if (__builtin_amdgcn_readlane(fstv, 1) == 0 && item < (int)argw(17)) {
+            fstv = lane == 1 ? 1 : fstv;
+            const int b = item / rows_;
+            const int jr = item - b * rows_;
+            if (lane == 0) s_desc[grp][0][0] = b;
             if (wo_) {
               ld = wo_ + jr;
               lcap = 1;
               f_step = 3;
             } else {
-              f_r = jr;
-              bounds = true;
+              r_known = jr;
             }
           } else {
             write_desc(0, -1, 0, 0, 0, 0);
@@ -710,65 +698,79 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
           f_step = 2;
         }
       } else if (f_step == 2) {
+        asm volatile("" : "+v"(fstv));
         const int k = __builtin_amdgcn_readfirstlane(f_pop);
-        const int len = part_len(f_p);
+        int p = __builtin_amdgcn_readlane(fstv, 0);
+        const int len = wo_ ? (int)argw(21 + p) - (int)argw(20 + p) : ((nheads() - p + kParts - 1) / kParts) * nqb;
+        const int nb_ = (int)argw(19);   // batch entries
         if (k >= nb_ * len) {
-          f_p = (f_p + 1) % kParts;
-          if (++f_tries >= kParts) {
+          // this partition is drained: try the next one
+          const int tries = __builtin_amdgcn_readlane(fstv, 1) + 1;
+          p = (p + 1) % kParts;
+          fstv = lane == 0 ? p : fstv;
+          fstv = lane == 1 ? tries : fstv;
+          if (tries >= kParts) {
             write_desc(0, -1, 0, 0, 0, 0);
             f_step = 0;
           } else {
             pop = true;
           }
         } else {
-          f_b = nb_ > 1 ? k / len : 0;
-          const int jr = k - f_b * len;
+          const int b = nb_ > 1 ? k / len : 0;
+          const int jr = k - b * len;
+          if (lane == 0) s_desc[grp][0][0] = b;
           if (wo_) {
-            ld = wo_ + (int)argw(20 + f_p) + jr;
+            ld = wo_ + (int)argw(20 + p) + jr;
             lcap = 1;
             f_step = 3;
           } else {
-            f_r = (f_p + kParts * (jr / nqb)) * nqb + jr % nqb;
-            bounds = true;
+            r_known = (p + kParts * (jr / nqb)) * nqb + jr % nqb;
           }
         }
       } else if (f_step == 3) {
-        f_r = __builtin_amdgcn_readfirstlane(f_val);
-        bounds = true;
+        r_known = __builtin_amdgcn_readfirstlane(f_val);
       } else if (f_step == 4) {
-        f_beg = __builtin_amdgcn_readlane(f_val, 0);
-        f_n = __builtin_amdgcn_readlane(f_val, 1) - f_beg;
-        if (f_n <= 0) {
-          zero_row(f_b, f_r);
+        const int beg = __builtin_amdgcn_readlane(f_val, 0);
+        const int n = __builtin_amdgcn_readlane(f_val, 1) - beg;
+        if (n <= 0) {
+          const i32x4 d0 = s_desc[grp][0];
+          zero_row(__builtin_amdgcn_readfirstlane(d0[0]), __builtin_amdgcn_readfirstlane(d0[1]));
           f_step = 1;
         } else {
-          ld = ci_ + f_beg;
-          lcap = f_n;
-          f_step = 5;
+          if (lane == 0) {
+            s_desc[grp][0][2] = beg;
+            s_desc[grp][0][3] = n;
+          }
+          // the first two key blocks (the first twice for a one-block row)
+          // go by DMA into the descriptor's second vector, lanes 0 and 1
+          if (lane < 2)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(reinterpret_cast<const void*>(ap(5) + (uintptr_t)beg * 4), 0xffffffffu),
+                                                     (lds_void*)&s_desc[grp][1], 4, (lane < n ? lane : 0) * 4, 0,
+                                                     0, 0);
+          f_step = 0;
         }
-      } else if (f_step == 5) {
-        write_desc(f_b, f_r, f_beg, f_n, __builtin_amdgcn_readlane(f_val, 0), __builtin_amdgcn_readlane(f_val, 1));
-        f_step = 0;
       }
-      if (bounds) {
+      if (r_known >= 0) {
         if (DENSE) {
-          write_desc(f_b, f_r, 0, nkb_valid, 0, nkb_valid > 1 ? 1 : 0);
+          if (lane == 0) s_desc[grp][0] = i32x4{s_desc[grp][0][0], r_known, 0, nkb_valid};
+          if (lane == 0) s_desc[grp][1] = i32x4{0, nkb_valid > 1 ? 1 : 0, 0, 0};
           f_step = 0;
         } else {
-          ld = rp_ + f_r;
+          if (lane == 0) s_desc[grp][0][1] = r_known;
+          ld = rp_ + r_known;
           lcap = 2;
           f_step = 4;
         }
       }
-      if (pop && lane == 0)
-        f_pop = __hip_atomic_fetch_add(qu_ + f_p * kQueueStride, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (ld && lane < 2) f_val = ld[lane < lcap ? lane : lcap - 1];
+      if (pop && lane == 0) {
+        asm volatile("" : "+v"(fstv));
+        f_pop = __hip_atomic_fetch_add(qu_ + __builtin_amdgcn_readlane(fstv, 0) * kQueueStride, 1,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (ld && lane < 2) f_val = ld[lane < lcap ? lane : 0];
       if (f_step == 0 || !finish) break;
       if (f_step != 1) wait_vm();
     }
-    const int fs[6] = {f_p, f_tries, f_b, f_r, f_beg, f_n};
-#pragma unroll
-    for (int i = 0; i < 6; ++i) fstv = lane == i ? fs[i] : fstv;
   };
 
   // ---- the group's row state ----
@@ -867,7 +869,10 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
     v[4] = __builtin_amdgcn_readfirstlane(d1[0]);
     v[5] = __builtin_amdgcn_readfirstlane(d1[1]);
   };
-  if (w == 0) fetch(true);
+  if (w == 0) {
+    fetch(true);
+    wait_vm();   // the descriptor's key blocks arrive by DMA
+  }
   __syncthreads();
   {
     int dv[6];
