@@ -618,6 +618,11 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
     argv = lane == 19 ? (uint32_t)(items / rows) : argv;
     // lanes 20 .. 20+kParts: the partition offsets of the work order
     if (work_order && lane >= 20 && lane <= 20 + kParts) argv = (uint32_t)work_order[rows + lane - 20];
+    // lanes 29-30: m = floor(2^40 / nqb) + 1 (low, high word), for row /
+    // nqb without a division
+    const uint64_t m = (1ull << 40) / (uint32_t)nqb + 1u;
+    argv = lane == 29 ? (uint32_t)m : argv;
+    argv = lane == 30 ? (uint32_t)(m >> 32) : argv;
   }
   auto argw = [&](int i) __attribute__((always_inline)) -> uint32_t {
     return (uint32_t)__builtin_amdgcn_readlane((int)argv, i);
@@ -628,8 +633,15 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
     return (uintptr_t)argw(2 * i) | ((uintptr_t)argw(2 * i + 1) << 32);
   };
   auto nheads = [&]() __attribute__((always_inline)) -> int { return (int)argw(16); };
+  // r / nqb for a row index r < H * nqb: (r * m) >> 40 with m =
+  // floor(2^40 / nqb) + 1 is exact while r * nqb < 2^40; the host accepts
+  // only B*H*L*d < 2^31 with d >= 64, so r < 2^18 and nqb < 2^18
+  auto head_of = [&](int r) __attribute__((always_inline)) -> int {
+    const uint64_t m = (uint64_t)argw(29) | ((uint64_t)argw(30) << 32);
+    return (int)(((uint64_t)(uint32_t)r * m) >> 40);
+  };
   auto o_row = [&](int b, int r) __attribute__((always_inline)) -> size_t {
-    const int h = r / nqb, qb = r - h * nqb;
+    const int h = head_of(r), qb = r - h * nqb;
     return (((size_t)b * nheads() + h) * (size_t)nqb + qb) * (size_t)BLK * D;
   };
 
@@ -724,7 +736,8 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
             lcap = 1;
             f_step = 3;
           } else {
-            r_known = (p + kParts * (jr / nqb)) * nqb + jr % nqb;
+            const int hh = head_of(jr);
+            r_known = (p + kParts * hh) * nqb + (jr - hh * nqb);
           }
         }
       } else if (f_step == 3) {
@@ -813,7 +826,7 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
     kb0 = k0;
     kb1 = k1;
     cbase = 0;
-    const int h = r / nqb;
+    const int h = head_of(r);
     const size_t base = ((size_t)b * nheads() + h) * (size_t)L * D;
     rk = make_rsrc((const bf16*)ap(1) + base, k_bytes);
     rv = make_rsrc((const bf16*)ap(2) + base, v_bytes);
@@ -824,7 +837,7 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
   // output is zeroed anyway, but a non-finite value would also move the
   // wave's shared rescale decisions).
   auto q_load = [&](int b, int r, bf16x8* qr) __attribute__((always_inline)) {
-    const int h = r / nqb, qb = r - h * nqb;
+    const int h = head_of(r), qb = r - h * nqb;
     const int q = qb * BLK + 32 * w + c;
     const int qsrc = SPLITQ ? (q < q_valid ? anchor_token(q, grid_rows, grid_cols, k_anchor) : 0) : q;
     const g_bf16* src = (const g_bf16*)ap(0) + ((size_t)b * nheads() + h) * (size_t)L * D + (size_t)qsrc * D + 8 * g;
@@ -930,7 +943,7 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
       nxt = nr >= 0;
       if (nxt) {
         nb = dv[0];
-        rkd = make_rsrc((const bf16*)ap(1) + ((size_t)nb * nheads() + nr / nqb) * (size_t)L * D, k_bytes);
+        rkd = make_rsrc((const bf16*)ap(1) + ((size_t)nb * nheads() + head_of(nr)) * (size_t)L * D, k_bytes);
         kd = dv[4] * BLK;
         // the current row's list is not read past this point
         if (!DENSE) {
@@ -1027,7 +1040,7 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
       const int pb = __builtin_amdgcn_readfirstlane(pv[0]);
       const int pr = __builtin_amdgcn_readfirstlane(pv[1]);
       const float l_tot = pair_sum(l_fin);
-      const int q = (pr % nqb) * BLK + 32 * w + c;
+      const int q = (pr - head_of(pr) * nqb) * BLK + 32 * w + c;
       const bool valid = q < qlim && l_tot > 0.f;
       const float inv = valid ? 1.f / l_tot : 0.f;
       char* const stg = reinterpret_cast<char*>(s_ost) + w * (32 * 128);
