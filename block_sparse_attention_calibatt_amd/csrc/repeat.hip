@@ -43,29 +43,35 @@ __device__ __forceinline__ int source_anchor(int n, int R, int C, int k) {
   return (f * k + g) * C + x;
 }
 
-// One thread copies a 64-byte run of one output row (four 16-byte units);
-// grid.y enumerates the (batch entry, listed head) pairs, so the index
-// arithmetic stays in 32 bits.
+// U = D*sizeof(T)/16 lanes copy one output row, 16 bytes each, so a wave's
+// load or store covers 64/U consecutive rows (tokens next to each other in
+// a grid row take anchors next to each other too: both sides stay
+// contiguous).  A workgroup copies BC_PASSES groups of 256/U rows, its
+// loads all issued before its stores.  grid.y enumerates the (batch entry,
+// listed head) pairs, so the index arithmetic stays in 32 bits.
+constexpr int BC_PASSES = 4;
 template <typename T, int D>
 __global__ __launch_bounds__(256) void anchor_broadcast_kernel(const T* __restrict__ Oa, T* __restrict__ O,
                                                                HeadList hl, int H, int L, int Lq, int seq_len,
                                                                int R, int C, int k) {
   constexpr int U = D * (int)sizeof(T) / 16;   // 16-byte units per row
-  constexpr int RUNS = U / 4;                  // 64-byte runs per row
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= L * RUNS) return;
-  const int n = t / RUNS, run = t % RUNS;
+  constexpr int RPP = 256 / U;                 // rows per pass
+  const int u = threadIdx.x % U, rr = threadIdx.x / U;
+  const int row0 = blockIdx.x * (RPP * BC_PASSES) + rr;
   const int slot = blockIdx.y % hl.n, b = blockIdx.y / hl.n;
   const size_t bh = (size_t)b * H + hl.h[slot];
-  u32x4 v[4] = {};
-  if (n < seq_len) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(Oa + (bh * Lq + source_anchor(n, R, C, k)) * D) + 4 * run;
+  u32x4 v[BC_PASSES];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = src[i];
+  for (int p = 0; p < BC_PASSES; ++p) {
+    const int n = row0 + p * RPP;
+    v[p] = u32x4{0u, 0u, 0u, 0u};
+    if (n < seq_len) v[p] = reinterpret_cast<const u32x4*>(Oa + (bh * Lq + source_anchor(n, R, C, k)) * D)[u];
   }
-  u32x4* dst = reinterpret_cast<u32x4*>(O + (bh * L + n) * D) + 4 * run;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dst[i] = v[i];
+  for (int p = 0; p < BC_PASSES; ++p) {
+    const int n = row0 + p * RPP;
+    if (n < L) reinterpret_cast<u32x4*>(O + (bh * L + n) * D)[u] = v[p];
+  }
 }
 
 // Work order for the anchor rows: listed head i goes to partition i % 8, its
@@ -220,8 +226,8 @@ hipError_t launch_spatial_similarity(const SimArgs& a, hipStream_t st) {
 
 template <int D>
 static hipError_t anchor_broadcast(const AnchorArgs& a, hipStream_t st) {
-  constexpr int RUNS = D * 2 / 64;
-  const dim3 grid((unsigned)((a.L * RUNS + 255) / 256), (unsigned)(a.B * a.heads.n));
+  constexpr int rows_per_block = 256 / (D * 2 / 16) * BC_PASSES;
+  const dim3 grid((unsigned)((a.L + rows_per_block - 1) / rows_per_block), (unsigned)(a.B * a.heads.n));
   hipLaunchKernelGGL((anchor_broadcast_kernel<bf16, D>), grid, dim3(256), 0, st, (const bf16*)a.Oa, (bf16*)a.O,
                      a.heads, a.H, a.L, a.Lq, a.seq_len, a.rows, a.cols, a.k);
   return hipGetLastError();
