@@ -26,6 +26,10 @@ FLAGS = [
     "-shared",
     # packed fp32 ops stay off: the kernels are written for plain fp32 VALU
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # every atomic here is issued by one lane (queue pops); the atomic
+    # optimizer would turn each into a wave scan that waits for the atomic's
+    # return on the spot
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wno-unused-command-line-argument",
 ]
 
