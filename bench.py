@@ -415,6 +415,8 @@ def main():
                 "row_sparsity": round(1 - ka / R, 4),
                 "speedup_vs_dense": round(speedup(extra["dense_ms"], a_ms), 2) if "dense_ms" in extra else None,
                 "anchor_tile_tflops": round(a_flops / (a_ms * 1e-3) / 1e12, 1),
+                "parts_per_row": cal.calibatt_anchor_parts(cfg.B, cfg.H, cfg.grid, ka, cfg.L, cfg.S, cfg.d,
+                                                           torch.cuda.get_device_properties(dev).multi_processor_count),
             }
             del aws
         extra["anchor_rows_all_heads"] = rows_out

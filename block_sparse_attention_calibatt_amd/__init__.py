@@ -32,6 +32,7 @@ from .capi import (
     calibatt_spatial_similarity,
     calibatt_select_repetitive_heads,
     calibatt_anchor_ws_bytes,
+    calibatt_anchor_parts,
     calibatt_anchor_attn_fwd,
     calibatt_validate_csr,
     calibatt_status_string,
@@ -65,6 +66,7 @@ __all__ = [
     "calibatt_spatial_similarity",
     "calibatt_select_repetitive_heads",
     "calibatt_anchor_ws_bytes",
+    "calibatt_anchor_parts",
     "calibatt_anchor_attn_fwd",
     "calibatt_validate_csr",
     "calibatt_status_string",

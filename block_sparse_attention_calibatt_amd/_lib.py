@@ -66,6 +66,7 @@ SIGNATURES = {
     "calibatt_anchor_attn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32,
                                         _i32, _i32, _i32, _i32, _vp, _i32, _vp, _sz, _vp]),
     "calibatt_anchor_ws_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "calibatt_anchor_parts": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "calibatt_build_schedule": (_i32, [_vp, _i32, _i32, _vp, _vp]),
     "calibatt_validate_csr": (_i32, [_vp, _vp, _i32, _i32, _i64]),
     "calibatt_status_string": (ctypes.c_char_p, [_i32]),

@@ -401,6 +401,13 @@ def calibatt_anchor_ws_bytes(B, H, frames, grid_cols, k_anchor, d):
     return int(load().calibatt_anchor_ws_bytes(int(B), int(H), int(frames), int(grid_cols), int(k_anchor), int(d)))
 
 
+def calibatt_anchor_parts(B, n_heads, grid, k_anchor, L, seq_len, d, num_cu):
+    """Parts each anchor row is cut into (1, 2, 4 or 8); 0 for invalid arguments."""
+    F, _, C = (int(x) for x in grid)
+    return int(load().calibatt_anchor_parts(int(B), int(n_heads), F, C, int(k_anchor), int(L), int(seq_len), int(d),
+                                            int(num_cu)))
+
+
 def calibatt_anchor_attn_fwd(Q, K, V, O, heads, grid, k_anchor, scale, seq_len=None, queue_ws=None,
                              v_transposed=False, ws=None):
     """Anchor-row attention for the listed heads; other heads of O are left as they are."""

@@ -741,7 +741,7 @@ size_t calibatt_anchor_ws_bytes(int B, int H, int frames, int grid_cols, int k_a
   if (B < 1 || H < 1 || frames < 1 || grid_cols < 1 || k_anchor < 1 || (d != 64 && d != 128)) return 0;
   const long long Lq = (anchor_queries(frames, grid_cols, k_anchor) + 127) / 128 * 128;
   const size_t oa = ((size_t)B * H * Lq * d * 2 + 255) / 256 * 256;
-  return oa + ((size_t)H * (Lq / 128) + calibatt::kParts + 1) * sizeof(int32_t);
+  return oa + ((size_t)H * (Lq / 128) * calibatt::kMaxSplit + calibatt::kParts + 1) * sizeof(int32_t);
 }
 
 calibatt_status calibatt_anchor_attn_fwd(const void* Q, const void* K, const void* V, void* O,
@@ -811,6 +811,16 @@ calibatt_status calibatt_anchor_attn_fwd(const void* Q, const void* K, const voi
   e = calibatt::launch_anchor_fwd(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "launching anchor-row attention");
   return ok();
+}
+
+int calibatt_anchor_parts(int B, int n_heads, int frames, int grid_cols, int k_anchor, int L, int seq_len, int d,
+                          int num_cu) {
+  if (B < 1 || n_heads < 1 || frames < 1 || grid_cols < 1 || k_anchor < 1 || seq_len < 1 || L < seq_len ||
+      (d != 64 && d != 128) || num_cu < 1)
+    return 0;
+  const long long Lq = (anchor_queries(frames, grid_cols, k_anchor) + 127) / 128 * 128;
+  return 1 << calibatt::anchor_split_shift((long long)B * n_heads * (Lq / 128), 2 * num_cu, (seq_len + 127) / 128,
+                                           Lq, L, d);
 }
 
 calibatt_status calibatt_validate_csr(const int32_t* row_ptr, const int32_t* col_idx, int rows,

@@ -502,13 +502,19 @@ struct PPGeo {
 // SPLITQ: the rows are the anchor queries of the spatial-repetition heads:
 // query m < q_valid of head h is token anchor_token(m) of Q (read in place),
 // O is [B, H, Lq, d] with Lq a multiple of 128, rows h*(Lq/128) + qb; keys
-// still run over K and V of length L with seq_len valid.
+// still run over K and V of length L with seq_len valid.  With split_shift
+// = s > 0 each row is cut into S = 2^s parts over its key blocks (part p:
+// blocks [p*n/S, (p+1)*n/S) of the n = nkb_valid), work-order entries are
+// row*S + p, and O is [B, H, ostride, d]: part p's normalised output rows
+// from row p*Lq, then S*Lq floats of the parts' log-sum-exps (log2 units)
+// for a merge pass.
 template <int D, bool DENSE, bool SPLITQ, bool VT>
 __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     const int32_t* __restrict__ work_order, int32_t* __restrict__ queue, int items, int H, int L,
-    int seq_len, int nkb_valid, float c2, int Lq, int q_valid, int grid_rows, int grid_cols, int k_anchor) {
+    int seq_len, int nkb_valid, float c2, int Lq, int q_valid, int grid_rows, int grid_cols, int k_anchor,
+    int split_shift, int ostride) {
   constexpr int BLK = 128;
   using G = PPGeo<D>;
   constexpr int CH = G::CH, DS = G::DS, DT = G::DT, KS = G::KS, NDMA = G::NDMA;
@@ -521,7 +527,9 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
   __shared__ i32x2 s_prev[2];         // per group: batch and row of the row whose O is due
 
   const int nqb = (SPLITQ ? Lq : L) / BLK;
-  const int rows = H * nqb;
+  // SPLITQ: a work-order entry is row * 2^split_shift + part, the part
+  // running over its share of the key blocks
+  const int rows = (H * nqb) << (SPLITQ ? split_shift : 0);
   const int qlim = SPLITQ ? q_valid : seq_len;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -623,6 +631,11 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
     const uint64_t m = (1ull << 40) / (uint32_t)nqb + 1u;
     argv = lane == 29 ? (uint32_t)m : argv;
     argv = lane == 30 ? (uint32_t)(m >> 32) : argv;
+    // lanes 31-32 (SPLITQ): the part shift, and the output rows per head
+    if (SPLITQ) {
+      argv = lane == 31 ? (uint32_t)split_shift : argv;
+      argv = lane == 32 ? (uint32_t)ostride : argv;
+    }
   }
   auto argw = [&](int i) __attribute__((always_inline)) -> uint32_t {
     return (uint32_t)__builtin_amdgcn_readlane((int)argv, i);
@@ -640,8 +653,18 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
     const uint64_t m = (uint64_t)argw(29) | ((uint64_t)argw(30) << 32);
     return (int)(((uint64_t)(uint32_t)r * m) >> 40);
   };
-  auto o_row = [&](int b, int r) __attribute__((always_inline)) -> size_t {
+  // row and part of a work-order entry
+  auto row_of = [&](int e) __attribute__((always_inline)) -> int { return SPLITQ ? e >> argw(31) : e; };
+  auto part_of = [&](int e) __attribute__((always_inline)) -> int {
+    return SPLITQ ? e & ((1 << argw(31)) - 1) : 0;
+  };
+  // first element of entry e's output rows: O is [B, H, nqb*BLK, D], or with
+  // SPLITQ [B, H, ostride, D] holding part p's rows from row p*Lq
+  auto o_row = [&](int b, int e) __attribute__((always_inline)) -> size_t {
+    const int r = row_of(e);
     const int h = head_of(r), qb = r - h * nqb;
+    if (SPLITQ)
+      return (((size_t)b * nheads() + h) * (size_t)argw(32) + (size_t)part_of(e) * Lq + (size_t)qb * BLK) * D;
     return (((size_t)b * nheads() + h) * (size_t)nqb + qb) * (size_t)BLK * D;
   };
 
@@ -765,8 +788,12 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
       }
       if (r_known >= 0) {
         if (DENSE) {
-          if (lane == 0) s_desc[grp][0] = i32x4{s_desc[grp][0][0], r_known, 0, nkb_valid};
-          if (lane == 0) s_desc[grp][1] = i32x4{0, nkb_valid > 1 ? 1 : 0, 0, 0};
+          // (SPLITQ: part p runs over key blocks [p*n/S, (p+1)*n/S))
+          const int sh = SPLITQ ? (int)argw(31) : 0;
+          const int pt = SPLITQ ? r_known & ((1 << sh) - 1) : 0;
+          const int kb_b = (pt * nkb_valid) >> sh, kb_e = ((pt + 1) * nkb_valid) >> sh;
+          if (lane == 0) s_desc[grp][0] = i32x4{s_desc[grp][0][0], r_known, kb_b, kb_e - kb_b};
+          if (lane == 0) s_desc[grp][1] = i32x4{kb_b, kb_e - kb_b > 1 ? kb_b + 1 : kb_b, 0, 0};
           f_step = 0;
         } else {
           if (lane == 0) s_desc[grp][0][1] = r_known;
@@ -806,7 +833,7 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
   // key block i of the current row (i grows by one per call, clamped to the row)
   auto blk_at = [&](int i) __attribute__((always_inline)) -> int {
     i = i < cnb ? i : cnb - 1;
-    if (DENSE) return i;
+    if (DENSE) return SPLITQ ? cbeg + i : i;
     const bool adv = (i >> 6) != cbase;
     if (adv) {
       ++cbase;
@@ -826,7 +853,7 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
     kb0 = k0;
     kb1 = k1;
     cbase = 0;
-    const int h = head_of(r);
+    const int h = head_of(row_of(r));
     const size_t base = ((size_t)b * nheads() + h) * (size_t)L * D;
     rk = make_rsrc((const bf16*)ap(1) + base, k_bytes);
     rv = make_rsrc((const bf16*)ap(2) + base, v_bytes);
@@ -836,7 +863,8 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
   // padding holds its lane computes exactly what zero padding gives (its
   // output is zeroed anyway, but a non-finite value would also move the
   // wave's shared rescale decisions).
-  auto q_load = [&](int b, int r, bf16x8* qr) __attribute__((always_inline)) {
+  auto q_load = [&](int b, int e, bf16x8* qr) __attribute__((always_inline)) {
+    const int r = row_of(e);
     const int h = head_of(r), qb = r - h * nqb;
     const int q = qb * BLK + 32 * w + c;
     const int qsrc = SPLITQ ? (q < q_valid ? anchor_token(q, grid_rows, grid_cols, k_anchor) : 0) : q;
@@ -943,7 +971,7 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
       nxt = nr >= 0;
       if (nxt) {
         nb = dv[0];
-        rkd = make_rsrc((const bf16*)ap(1) + ((size_t)nb * nheads() + head_of(nr)) * (size_t)L * D, k_bytes);
+        rkd = make_rsrc((const bf16*)ap(1) + ((size_t)nb * nheads() + head_of(row_of(nr))) * (size_t)L * D, k_bytes);
         kd = dv[4] * BLK;
         // the current row's list is not read past this point
         if (!DENSE) {
@@ -1040,7 +1068,8 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
       const int pb = __builtin_amdgcn_readfirstlane(pv[0]);
       const int pr = __builtin_amdgcn_readfirstlane(pv[1]);
       const float l_tot = pair_sum(l_fin);
-      const int q = (pr - head_of(pr) * nqb) * BLK + 32 * w + c;
+      const int prr = row_of(pr);
+      const int q = (prr - head_of(prr) * nqb) * BLK + 32 * w + c;
       const bool valid = q < qlim && l_tot > 0.f;
       const float inv = valid ? 1.f / l_tot : 0.f;
       char* const stg = reinterpret_cast<char*>(s_ost) + w * (32 * 128);
@@ -1148,6 +1177,16 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
         l_fin = l_run;
         s_prev[grp] = i32x2{cb, cr};
         pend = true;
+        if (SPLITQ && argw(31) != 0) {
+          // a part's log-sum-exp (log2 units) for the merge of the parts:
+          // floats after the 2^shift parts' rows of the head's output rows
+          const float lt = pair_sum(l_run);
+          const int r = row_of(cr), h = head_of(r);
+          const int q = (r - h * nqb) * BLK + 32 * w + c;
+          g_f32* const lse = reinterpret_cast<g_f32*>(
+              (g_bf16*)ap(3) + (((size_t)cb * nheads() + h) * (size_t)argw(32) + ((size_t)Lq << argw(31))) * D);
+          if (g == 0) lse[(size_t)part_of(cr) * Lq + q] = lt > 0.f ? ref + __log2f(lt) : kNegInf;
+        }
         if (nxt) {
           int dv[6];
           row_desc(dv);
@@ -1352,7 +1391,7 @@ static hipError_t occupancy(Kern k, int threads, int* blocks_per_cu) {
 template <int D, bool DENSE, bool SPLITQ, bool VT>
 static hipError_t launch_pp(const AttnArgs& a, hipStream_t st) {
   const int Lq = SPLITQ ? a.Lq : a.L;
-  const int items = a.B * a.H * (Lq / 128);
+  const int items = (a.B * a.H * (Lq / 128)) << (SPLITQ ? a.split_shift : 0);
   const float c2 = a.scale * kLog2e;
   if (items == 0) return hipSuccess;
   // two rows in flight per workgroup (one per wave group)
@@ -1368,7 +1407,8 @@ static hipError_t launch_pp(const AttnArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((attn_fwd_pp_kernel<D, DENSE, SPLITQ, VT>), dim3(grid), dim3(512), 0, st, (const bf16*)a.Q,
                      (const bf16*)a.K, (const bf16*)a.V, (bf16*)a.O, a.row_ptr, a.col_idx, a.work_order, a.queue,
                      items, a.H, a.L, a.seq_len, a.nkb_valid, c2, Lq, SPLITQ ? a.q_valid : a.seq_len,
-                     a.grid_rows, a.grid_cols, a.k_anchor);
+                     a.grid_rows, a.grid_cols, a.k_anchor, SPLITQ ? a.split_shift : 0,
+                     SPLITQ && a.ostride > 0 ? a.ostride : Lq);
   return hipGetLastError();
 }
 

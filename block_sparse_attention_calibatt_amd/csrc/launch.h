@@ -27,6 +27,9 @@ struct AttnArgs {
   // with k_anchor anchors per frame; Q is read through the anchor map, O is
   // [B, H, Lq, d]
   int Lq = 0, q_valid = 0, grid_rows = 0, grid_cols = 0, k_anchor = 0;
+  // rows split into 2^split_shift parts over their key blocks; O then has
+  // ostride rows per head (the parts' rows and log-sum-exps)
+  int split_shift = 0, ostride = 0;
 };
 
 hipError_t launch_attention(const AttnArgs& a, bool dense, hipStream_t st);
@@ -61,6 +64,8 @@ hipError_t launch_row_lse(const MassArgs& a, hipStream_t st);
 // Heads handed to a kernel by value (kernel arguments), so that no device
 // list has to be written first.
 constexpr int kMaxListHeads = 256;
+// anchor rows are cut into at most this many parts over their key blocks
+constexpr int kMaxSplit = 8;
 struct HeadList {
   int n;
   int32_t h[kMaxListHeads];
@@ -87,7 +92,7 @@ struct AnchorArgs {
   bool v_transposed;
   void* O;
   void* Oa;        // [B, H, Lq, d]
-  int32_t* order;  // [H*(Lq/128) + kParts + 1]
+  int32_t* order;  // [H*(Lq/128)*kMaxSplit + kParts + 1]
   int32_t* queue;
   HeadList heads;
   int B, H, L, seq_len, d;
@@ -98,6 +103,9 @@ struct AnchorArgs {
 };
 
 hipError_t launch_anchor_fwd(const AnchorArgs& a, hipStream_t st);
+// log2 of the parts each anchor row is cut into over its key blocks (rows:
+// anchor rows of all listed heads and batch entries; groups: two per CU)
+int anchor_split_shift(long long rows, int groups, int nkb, long long Lq, long long L, int d);
 
 struct CompileArgs {
   const float* mass;

@@ -26,7 +26,9 @@
 // of the listed heads in its split-query mode (each query read in place
 // through the anchor map; keys: the full K and V) into a [B, H, Lq, d]
 // buffer (Lq = anchor count rounded up to 128), and every token's output
-// row is then copied from its anchor's.
+// row is then copied from its anchor's.  When the anchor rows are too few
+// for the device's wave groups, each row is cut into parts over its key
+// blocks, and a merge of the parts by their log-sum-exps comes first.
 #include "tiles.h"
 #include "launch.h"
 
@@ -74,25 +76,70 @@ __global__ __launch_bounds__(256) void anchor_broadcast_kernel(const T* __restri
   }
 }
 
-// Work order for the anchor rows: listed head i goes to partition i % 8, its
-// rows in order; the partition offsets follow the H*nqb row slots.
-__global__ __launch_bounds__(256) void anchor_order_kernel(HeadList hl, int H, int nqb, int32_t* __restrict__ order) {
-  const int rows = H * nqb;
+// Work order for the anchor rows: listed head i goes to partition i % 8,
+// its entries (row*S + part) part by part, rows in order within a part, so
+// that the rows in flight read the same key range; the partition offsets
+// follow the H*nqb*S entry slots.
+__global__ __launch_bounds__(256) void anchor_order_kernel(HeadList hl, int H, int nqb, int sh,
+                                                           int32_t* __restrict__ order) {
+  const int S = 1 << sh;
+  const int per_head = nqb * S;
+  const int slots = (H * nqb) << sh;
   auto part_heads = [&](int p) { return p < hl.n ? (hl.n - p + kParts - 1) / kParts : 0; };
-  for (int i = threadIdx.x; i < hl.n * nqb; i += 256) {
-    const int slot = i / nqb, qb = i - slot * nqb;
+  for (int i = threadIdx.x; i < hl.n * per_head; i += 256) {
+    const int slot = i / per_head, rem = i - slot * per_head;
+    const int pt = rem / nqb, qb = rem - pt * nqb;
     const int p = slot % kParts, j = slot / kParts;
     int off = 0;
-    for (int q = 0; q < p; ++q) off += part_heads(q) * nqb;
-    order[off + j * nqb + qb] = hl.h[slot] * nqb + qb;
+    for (int q = 0; q < p; ++q) off += part_heads(q) * per_head;
+    order[off + j * per_head + rem] = ((hl.h[slot] * nqb + qb) << sh) + pt;
   }
   if (threadIdx.x == 0) {
     int off = 0;
     for (int p = 0; p <= kParts; ++p) {
-      order[rows + p] = off;
-      if (p < kParts) off += part_heads(p) * nqb;
+      order[slots + p] = off;
+      if (p < kParts) off += part_heads(p) * per_head;
     }
   }
+}
+
+// Merge of the S = 2^sh parts of the anchor rows: for anchor query m < La of
+// listed head h, with part p's normalised output o_p and log-sum-exp l_p
+// (log2 units), O = sum_p 2^(l_p - l_max) o_p / sum_p 2^(l_p - l_max), the
+// softmax over all keys recombined from its key ranges.  The parts sit in
+// the head's rows of the final output (rows p*Lq .., then S*Lq floats of
+// l_p); the merged rows go to Oa [B, H, Lq, D].  U lanes per row, 16 bytes
+// (8 elements) each.
+template <int D>
+__global__ __launch_bounds__(256) void anchor_merge_kernel(const bf16* __restrict__ Op, bf16* __restrict__ Oa,
+                                                           HeadList hl, int H, int L, int Lq, int La, int sh) {
+  constexpr int U = D * 2 / 16;
+  const int u = threadIdx.x % U;
+  const int m = blockIdx.x * (256 / U) + threadIdx.x / U;
+  const int slot = blockIdx.y % hl.n, b = blockIdx.y / hl.n;
+  if (m >= La) return;
+  const size_t bh = (size_t)b * H + hl.h[slot];
+  const bf16* const base = Op + bh * L * D;
+  const float* const lse = reinterpret_cast<const float*>(base + ((size_t)Lq << sh) * D);
+  const int S = 1 << sh;
+  float mx = kNegInf;
+  for (int p = 0; p < S; ++p) mx = fmaxf(mx, lse[(size_t)p * Lq + m]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (mx > kNegInf) {
+    for (int p = 0; p < S; ++p) {
+      const float wp = fast_exp2(lse[(size_t)p * Lq + m] - mx);
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(base + ((size_t)p * Lq + m) * D + 8 * u);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += wp * (float)x[e];
+      wsum += wp;
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  bf16x8 y;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = (bf16)(acc[e] * inv);
+  *reinterpret_cast<bf16x8*>(Oa + (bh * Lq + m) * D + 8 * u) = y;
 }
 
 template <int D>
@@ -233,10 +280,37 @@ static hipError_t anchor_broadcast(const AnchorArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Parts per anchor row: every group of the persistent grid (two per CU)
+// takes whole rows, so few long rows leave groups idle at the end (k = 3 at
+// 40 heads x 26 rows: 1,040 rows on 512 groups, 3 rows on the busiest).
+// Cutting each row into S parts over its key blocks evens that out at the
+// price of one row switch per part (~4 key blocks of work) and a merge pass.
+// S = 2^sh <= kMaxSplit minimises ceil(rows*S/groups) * (ceil(n/S) + 4) over
+// n key blocks, a larger S only when it saves 2%; the parts must fit in the
+// output's head rows (S*Lq*(2d+4) bytes <= L*2d) and keep a block each.
+int anchor_split_shift(long long rows, int groups, int nkb, long long Lq, long long L, int d) {
+  int best = 0;
+  double best_cost = 0.0;
+  for (int sh = 0; (1 << sh) <= kMaxSplit; ++sh) {
+    const int S = 1 << sh;
+    if (S > nkb) break;
+    if (S > 1 && (long long)S * Lq * (2 * d + 4) > L * 2 * d) break;
+    const double waves = (double)((rows * S + groups - 1) / groups);
+    const double cost = waves * ((double)((nkb + S - 1) / S) + 4.0);
+    if (sh == 0 || cost < 0.98 * best_cost) {
+      best = sh;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
 hipError_t launch_anchor_fwd(const AnchorArgs& a, hipStream_t st) {
   if (a.heads.n == 0) return hipSuccess;
   const int nqb = a.Lq / 128;
-  hipLaunchKernelGGL(anchor_order_kernel, dim3(1), dim3(256), 0, st, a.heads, a.H, nqb, a.order);
+  const int nkb = (a.seq_len + 127) / 128;
+  const int sh = anchor_split_shift((long long)a.B * a.heads.n * nqb, 2 * a.num_cu, nkb, a.Lq, a.L, a.d);
+  hipLaunchKernelGGL(anchor_order_kernel, dim3(1), dim3(256), 0, st, a.heads, a.H, nqb, sh, a.order);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   AttnArgs t;
@@ -264,8 +338,27 @@ hipError_t launch_anchor_fwd(const AnchorArgs& a, hipStream_t st) {
   t.grid_rows = a.rows;
   t.grid_cols = a.cols;
   t.k_anchor = a.k;
+  t.split_shift = sh;
+  if (sh > 0) {
+    // the parts go to the listed heads' rows of O, which the copy below
+    // overwrites after the merge has read them
+    t.O = a.O;
+    t.ostride = a.L;
+  }
   e = launch_anchor_attention(t, st);
   if (e != hipSuccess) return e;
+  if (sh > 0) {
+    const int rpb = 256 / (a.d * 2 / 16);
+    const dim3 grid((unsigned)((a.La + rpb - 1) / rpb), (unsigned)(a.B * a.heads.n));
+    if (a.d == 128)
+      hipLaunchKernelGGL(anchor_merge_kernel<128>, grid, dim3(256), 0, st, (const bf16*)a.O, (bf16*)a.Oa, a.heads,
+                         a.H, a.L, a.Lq, a.La, sh);
+    else
+      hipLaunchKernelGGL(anchor_merge_kernel<64>, grid, dim3(256), 0, st, (const bf16*)a.O, (bf16*)a.Oa, a.heads,
+                         a.H, a.L, a.Lq, a.La, sh);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   return a.d == 128 ? anchor_broadcast<128>(a, st) : anchor_broadcast<64>(a, st);
 }
 

@@ -104,6 +104,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 // counters, and would make every later LDS wait also wait for it).
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) int32_t g_i32;
+typedef __attribute__((address_space(1))) float g_f32;
 typedef __attribute__((address_space(1))) __bf16 g_bf16;
 typedef __attribute__((address_space(1))) bf16x8 g_bf16x8;
 typedef __attribute__((address_space(1))) bf16x4 g_bf16x4;

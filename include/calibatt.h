@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define CALIBATT_VERSION 301 /* major * 100 + minor */
+#define CALIBATT_VERSION 302 /* major * 100 + minor */
 
 typedef enum {
   CALIBATT_OK = 0,
@@ -430,11 +430,15 @@ calibatt_status calibatt_select_repetitive_heads(const double* sim, int P, int H
  *   ws          calibatt_anchor_ws_bytes(B, H, frames, grid_cols, k_anchor,
  *               d) bytes (device), 256-byte aligned: the anchor outputs as
  *               [B, H, Lq, d] (Lq = frames * k_anchor * grid_cols rounded up
- *               to 128) and the row order.
+ *               to 128) and the row order (up to 8 entries per row).
  * The anchor queries run through the persistent dense kernel in a
  * split-query mode that reads each anchor query of Q in place (bf16 matrix
  * cores with float32 accumulation, float32 softmax, probabilities and O
- * rounded to bf16); a copy kernel then writes every token's row.
+ * rounded to bf16); a copy kernel then writes every token's row.  When the
+ * anchor rows are too few to keep every wave group of the device busy, each
+ * row is cut into 2, 4 or 8 parts over its key blocks; the parts' outputs
+ * (bf16) and log-sum-exps go to the listed heads' rows of O first, a merge
+ * kernel combines them into ws, and the copy then overwrites those rows.
  */
 calibatt_status calibatt_anchor_attn_fwd(const void* Q, const void* K, const void* V, void* O,
                                          const int32_t* heads, int n_heads, int frames, int grid_rows,
@@ -442,6 +446,18 @@ calibatt_status calibatt_anchor_attn_fwd(const void* Q, const void* K, const voi
                                          int seq_len, int d, calibatt_dtype dt, int32_t* queue_ws,
                                          calibatt_vlayout v_layout, void* ws, size_t ws_bytes, void* stream);
 size_t calibatt_anchor_ws_bytes(int B, int H, int frames, int grid_cols, int k_anchor, int d);
+
+/*
+ * Parts (1, 2, 4 or 8) calibatt_anchor_attn_fwd cuts each anchor row into,
+ * for n_heads listed heads on a device with num_cu compute units (two wave
+ * groups each, every group taking whole parts): the smallest S that
+ * minimises ceil(rows*S / groups) * (ceil(n/S) + 4), n = ceil(seq_len/128)
+ * key blocks and 4 blocks for a row switch, a larger S only when it saves
+ * 2%, with S <= n and S*Lq*(2d+4) <= L*2d bytes.  0 for invalid arguments.
+ * A host function (no device access).
+ */
+int calibatt_anchor_parts(int B, int n_heads, int frames, int grid_cols, int k_anchor, int L, int seq_len, int d,
+                          int num_cu);
 
 /*
  * Work order for calibatt_sparse_attn_fwd.  The pages do not describe a

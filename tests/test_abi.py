@@ -19,7 +19,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _lib.header_symbols()
-    assert len(names) == 25
+    assert len(names) == 26
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     for n in names:
@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert cal.calibatt_version() == 301
+    assert cal.calibatt_version() == 302
     for code, name in _lib.STATUS.items():
         assert cal.calibatt_status_string(code) != "unknown status"
     assert cal.calibatt_status_string(99) == "unknown status"
@@ -322,7 +322,8 @@ def test_repetition_entry_points_reject(lib):
 
     aws = lib.calibatt_anchor_ws_bytes(1, 40, 21, 52, 5, 128)
     lq = (21 * 5 * 52 + 127) // 128 * 128
-    assert aws == 40 * lq * 128 * 2 + (40 * lq // 128 + 9) * 4
+    # anchor outputs, then the order: up to 8 parts per row, 9 partition offsets
+    assert aws == 40 * lq * 128 * 2 + (40 * lq // 128 * 8 + 9) * 4
     assert lib.calibatt_anchor_ws_bytes(1, 40, 21, 52, 0, 128) == 0
     hl = np.array([3, 7], dtype=np.int32)
 
@@ -368,3 +369,29 @@ def test_single_pass_mass_rejects(lib):
     assert call(S=32769) == 2
     assert call(block=32) == 7
     assert call(scale=0.0) == 2
+
+
+def test_anchor_parts_rule(lib):
+    """Parts per anchor row: ceil(rows*S/groups) * (ceil(n/S) + 4) minimised,
+    a larger S only when 2% cheaper, within the O-capacity bound.  Wan (40
+    heads, 21 x 30 x 52 grid, 256 CUs): k = 3 gives 1,040 rows for 512
+    groups: costs 780 / 660 / 612 / 612 for S = 1 / 2 / 4 / 8, so 4; k = 5:
+    1,040 / 924 / 952 -> 2; k = 4: 780 / 792 / 748 -> 4; k = 10, 15 -> 1."""
+    wan = dict(B=1, n_heads=40, grid=(21, 30, 52), L=32768, seq_len=32760, d=128, num_cu=256)
+    assert [cal.calibatt_anchor_parts(k_anchor=k, **wan) for k in (15, 10, 5, 4, 3)] == [1, 1, 2, 4, 4]
+    # fewer CUs, more rows per group, less to gain: 64 CUs give 2,340 /
+    # 2,244 / 2,244 (S = 2), 32 CUs 4,420 / 4,356 (1.4%: S = 1)
+    assert cal.calibatt_anchor_parts(k_anchor=3, **dict(wan, num_cu=64)) == 2
+    assert cal.calibatt_anchor_parts(k_anchor=3, **dict(wan, num_cu=32)) == 1
+    # small grids: the capacity bound S*Lq*(2d+4) <= L*2d caps S
+    small = dict(B=1, n_heads=2, grid=(3, 5, 20), L=384, seq_len=300, d=128, num_cu=256)
+    assert cal.calibatt_anchor_parts(k_anchor=1, **small) == 2     # 2 rows, n = 3, capacity 2.95
+    assert cal.calibatt_anchor_parts(k_anchor=5, **small) == 1     # Lq = 384 = L
+    g8 = dict(B=1, n_heads=2, grid=(8, 8, 64), L=4096, seq_len=4096, d=128, num_cu=256)
+    assert cal.calibatt_anchor_parts(k_anchor=1, **g8) == 4        # capacity 7.9
+    g4 = dict(B=1, n_heads=2, grid=(4, 16, 64), L=4096, seq_len=4096, d=64, num_cu=256)
+    assert cal.calibatt_anchor_parts(k_anchor=1, **g4) == 8
+    assert cal.calibatt_anchor_parts(k_anchor=1, **dict(g4, seq_len=3 * 128)) == 2   # S <= n = 3
+    for bad in (dict(k_anchor=0), dict(k_anchor=1, d=96), dict(k_anchor=1, num_cu=0), dict(k_anchor=1, L=100)):
+        kw = dict(g8, **bad)
+        assert cal.calibatt_anchor_parts(**kw) == 0

@@ -209,6 +209,35 @@ def test_anchor_every_row_matches_dense(gpu):
     assert float((O.float() - Od.float()).abs().max()) <= TOL
 
 
+@pytest.mark.parametrize("grid,d,parts", [
+    ((8, 8, 64), 128, 4),
+    ((8, 8, 64), 64, 4),
+    ((4, 16, 64), 128, 8),
+    ((4, 16, 64), 64, 8),
+])
+def test_anchor_split_rows(gpu, grid, d, parts):
+    """Few anchor rows: each is cut into parts over its key blocks, the parts
+    written to the listed heads' rows of O and merged by their log-sum-exps
+    before the copy.  Against the oracle, and the copy still a copy."""
+    cfg = _grid_cfg(grid, d, 3, seed=95 + d)
+    heads = [2, 0]
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    got_parts = cal.calibatt_anchor_parts(cfg.B, len(heads), grid, 1, cfg.L, cfg.S, d, ncu)
+    say(f"case: anchor rows cut into parts, grid={grid} d={d} heads={heads} parts={got_parts} ({ncu} CUs)")
+    if ncu == 256:
+        assert got_parts == parts
+    q, k, v = inputs(cfg)
+    ref = oracle.anchor_attention(q, k, v, cfg.scale, cfg.S, grid, 1, heads)
+    for vt in (False, True):
+        O = _anchor_gpu(q, k, v, cfg, heads, 1, v_transposed=vt)
+        e = err(O[:, heads], ref)
+        say(f"  v_transposed={vt} max err {e:.3e}")
+        assert e <= TOL
+        _check_untouched(O, cfg, heads)
+        src = torch.from_numpy(_source_tokens(cfg, 1)).to("cuda:0")
+        assert torch.equal(O[:, heads, :cfg.S], O[:, heads][:, :, src]), "broadcast is a copy"
+
+
 def test_anchor_no_heads(gpu):
     grid = (2, 5, 13)
     cfg = _grid_cfg(grid, 128, 2, seed=81)
@@ -217,13 +246,17 @@ def test_anchor_no_heads(gpu):
     assert torch.all(O.float() == 7.0)
 
 
-def test_anchor_wan_full_size(gpu):
-    """Wan shape, 4 listed heads, k = 5 (Table S4's 83.3% row sparsity): every
+@pytest.mark.parametrize("k_anchor", [5, 3])
+def test_anchor_wan_full_size(gpu, k_anchor):
+    """Wan shape, 4 listed heads, k = 5 and 3 (Table S4's 83.3% and 90% row
+    sparsity; on 256 CUs these few rows are cut into 2 and 8 parts): every
     output of those heads against the oracle; heads 13 and 27 have queries
     that repeat down the rows, where the anchors reproduce dense attention."""
     cfg = synth.get_config("wan")
-    heads, k_anchor = [0, 13, 27, 39], 5
-    say(f"case: anchor attention, Wan full size, heads {heads}, k={k_anchor}")
+    heads = [0, 13, 27, 39]
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    parts = cal.calibatt_anchor_parts(cfg.B, len(heads), cfg.grid, k_anchor, cfg.L, cfg.S, cfg.d, ncu)
+    say(f"case: anchor attention, Wan full size, heads {heads}, k={k_anchor}, parts={parts}")
     q, k, v = inputs(cfg)
     synth.repeat_rows(q, cfg.grid, cfg.S, [13, 27], 0.0)
     O = _anchor_gpu(q, k, v, cfg, heads, k_anchor)
