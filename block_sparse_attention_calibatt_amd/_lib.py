@@ -45,10 +45,10 @@ SIGNATURES = {
     "calibatt_block_mass_single_pass": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
                                                _vp, _vp, _sz, _vp]),
     "calibatt_block_mass_ws_bytes": (_sz, [_i32, _i32, _i32, _i32]),
-    "calibatt_compile_masks": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i64,
+    "calibatt_compile_masks": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i64, _vp,
                                       ctypes.POINTER(_i64), _vp, _sz, _vp]),
     "calibatt_compile_masks_energy": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _i64, _i64, _i32, _vp, _vp,
-                                             _i64, ctypes.POINTER(_i64), _vp, _sz, _vp]),
+                                             _i64, _vp, ctypes.POINTER(_i64), _vp, _sz, _vp]),
     "calibatt_compile_ws_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "calibatt_share_timesteps": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_double, _vp, _vp,
                                         _vp, _vp, _vp, _i64, ctypes.POINTER(_i32), ctypes.POINTER(_i64), _vp, _sz,

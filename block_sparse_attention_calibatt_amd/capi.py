@@ -190,9 +190,17 @@ def calibatt_compile_ws_bytes(P, H, nqb, nkb):
     return int(load().calibatt_compile_ws_bytes(int(P), int(H), int(nqb), int(nkb)))
 
 
+def _work_order_arg(work_order, rows):
+    if work_order is not None:
+        _dev_tensor(work_order, "work_order", torch.int32)
+        _need(work_order.numel() == rows + PARTS + 1, f"work_order must have H*nqb+9 = {rows + PARTS + 1} entries")
+    return _ptr(work_order)
+
+
 def calibatt_compile_masks(mass, keep_topk, min_agree, nkb_valid=None, row_ptr=None, col_idx=None,
-                           ws=None):
-    """mass [P, H, nqb, nkb] float32 -> (row_ptr, col_idx) int32 device tensors."""
+                           ws=None, work_order=None):
+    """mass [P, H, nqb, nkb] float32 -> (row_ptr, col_idx) int32 device tensors; with
+    work_order (an [H*nqb + 9] int32 tensor) the set's work order is written too."""
     _dev_tensor(mass, "mass", torch.float32)
     _need(mass.dim() == 4, "mass must be [P, H, nqb, nkb]")
     P, H, nqb, nkb = mass.shape
@@ -212,8 +220,9 @@ def calibatt_compile_masks(mass, keep_topk, min_agree, nkb_valid=None, row_ptr=N
     _dev_tensor(ws, "ws", torch.uint8)
     nnz = ctypes.c_int64(0)
     lib = load()
+    wo = _work_order_arg(work_order, rows)
     check(lib.calibatt_compile_masks(_ptr(mass), P, H, nqb, nkb, nkb_valid, int(keep_topk),
-                                     int(min_agree), _ptr(row_ptr), _ptr(col_idx), col_idx.numel(),
+                                     int(min_agree), _ptr(row_ptr), _ptr(col_idx), col_idx.numel(), wo,
                                      ctypes.byref(nnz), _ptr(ws), ws.numel(), _stream(mass)))
     return row_ptr, col_idx[: nnz.value]
 
@@ -227,7 +236,8 @@ def _eps_fraction(eps):
     return e.numerator, e.denominator
 
 
-def calibatt_compile_masks_energy(mass, eps, min_agree, nkb_valid=None, row_ptr=None, col_idx=None, ws=None):
+def calibatt_compile_masks_energy(mass, eps, min_agree, nkb_valid=None, row_ptr=None, col_idx=None, ws=None,
+                                  work_order=None):
     """Energy-threshold compile: mass [P, H, nqb, nkb] float32 -> (row_ptr, col_idx) int32 device tensors."""
     _dev_tensor(mass, "mass", torch.float32)
     _need(mass.dim() == 4, "mass must be [P, H, nqb, nkb]")
@@ -249,8 +259,9 @@ def calibatt_compile_masks_energy(mass, eps, min_agree, nkb_valid=None, row_ptr=
     _dev_tensor(ws, "ws", torch.uint8)
     nnz = ctypes.c_int64(0)
     lib = load()
+    wo = _work_order_arg(work_order, rows)
     check(lib.calibatt_compile_masks_energy(_ptr(mass), P, H, nqb, nkb, nkb_valid, num, den, int(min_agree),
-                                            _ptr(row_ptr), _ptr(col_idx), col_idx.numel(), ctypes.byref(nnz),
+                                            _ptr(row_ptr), _ptr(col_idx), col_idx.numel(), wo, ctypes.byref(nnz),
                                             _ptr(ws), ws.numel(), _stream(mass)))
     return row_ptr, col_idx[: nnz.value]
 

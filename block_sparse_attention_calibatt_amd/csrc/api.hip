@@ -382,7 +382,8 @@ size_t calibatt_compile_ws_bytes(int P, int H, int nqb, int nkb) {
 static calibatt_status compile_common(const float* mass, int P, int H, int nqb, int nkb, int nkb_valid,
                                       int keep_topk, bool energy, long long eps_num, long long eps_den,
                                       int min_agree, int32_t* row_ptr, int32_t* col_idx, int64_t nnz_cap,
-                                      int64_t* nnz_out, void* ws, size_t ws_bytes, void* stream) {
+                                      int32_t* work_order, int64_t* nnz_out, void* ws, size_t ws_bytes,
+                                      void* stream) {
   if (!mass || !row_ptr || !nnz_out || !ws) return fail(CALIBATT_ERR_NULL, "mass, row_ptr, nnz_out and ws must be non-NULL");
   if (P < 1 || H < 1 || nqb < 1 || nkb < 1) return fail(CALIBATT_ERR_SHAPE, "P, H, nqb and nkb must be >= 1");
   if (nkb > calibatt::kMaxKeyBlocks) return fail(CALIBATT_ERR_UNSUPPORTED, "nkb=%d exceeds %d", nkb, calibatt::kMaxKeyBlocks);
@@ -396,8 +397,11 @@ static calibatt_status compile_common(const float* mass, int P, int H, int nqb, 
   if ((long long)P * rows * nkb >= (1LL << 40)) return fail(CALIBATT_ERR_SHAPE, "P*H*nqb*nkb too large");
   const size_t need = calibatt_compile_ws_bytes(P, H, nqb, nkb);
   if (ws_bytes < need) return fail(CALIBATT_ERR_CAPACITY, "ws_bytes=%zu < %zu required", ws_bytes, need);
-  if (!aligned(ws, 16) || !aligned(mass, 4) || !aligned(row_ptr, 4) || (col_idx && !aligned(col_idx, 4)))
-    return fail(CALIBATT_ERR_ALIGN, "ws must be 16-byte aligned; mass, row_ptr, col_idx 4-byte aligned");
+  if (!aligned(ws, 16) || !aligned(mass, 4) || !aligned(row_ptr, 4) || (col_idx && !aligned(col_idx, 4)) ||
+      (work_order && !aligned(work_order, 4)))
+    return fail(CALIBATT_ERR_ALIGN, "ws must be 16-byte aligned; mass, row_ptr, col_idx, work_order 4-byte aligned");
+  if (work_order && nqb > calibatt::kMaxKeyBlocks) return fail(CALIBATT_ERR_UNSUPPORTED, "nqb=%d exceeds %d", nqb, calibatt::kMaxKeyBlocks);
+  if (work_order && H > calibatt::kMaxHeads) return fail(CALIBATT_ERR_UNSUPPORTED, "H=%d exceeds %d", H, calibatt::kMaxHeads);
 
   calibatt::CompileArgs a;
   a.mass = mass;
@@ -430,26 +434,31 @@ static calibatt_status compile_common(const float* mass, int P, int H, int nqb, 
     e = calibatt::launch_compile_fill(a, st);
     if (e != hipSuccess) return hip_fail(e, "launching mask compile (fill)");
   }
+  if (work_order) {
+    e = calibatt::launch_schedule(row_ptr, H, nqb, work_order, st);
+    if (e != hipSuccess) return hip_fail(e, "launching work-order build");
+  }
   return ok();
 }
 
 calibatt_status calibatt_compile_masks(const float* mass, int P, int H, int nqb, int nkb,
                                        int nkb_valid, int keep_topk, int min_agree, int32_t* row_ptr,
-                                       int32_t* col_idx, int64_t nnz_cap, int64_t* nnz_out, void* ws,
-                                       size_t ws_bytes, void* stream) {
+                                       int32_t* col_idx, int64_t nnz_cap, int32_t* work_order, int64_t* nnz_out,
+                                       void* ws, size_t ws_bytes, void* stream) {
   return compile_common(mass, P, H, nqb, nkb, nkb_valid, keep_topk, false, 0, 1, min_agree, row_ptr, col_idx,
-                        nnz_cap, nnz_out, ws, ws_bytes, stream);
+                        nnz_cap, work_order, nnz_out, ws, ws_bytes, stream);
 }
 
 calibatt_status calibatt_compile_masks_energy(const float* mass, int P, int H, int nqb, int nkb,
                                               int nkb_valid, int64_t eps_num, int64_t eps_den, int min_agree,
                                               int32_t* row_ptr, int32_t* col_idx, int64_t nnz_cap,
-                                              int64_t* nnz_out, void* ws, size_t ws_bytes, void* stream) {
+                                              int32_t* work_order, int64_t* nnz_out, void* ws, size_t ws_bytes,
+                                              void* stream) {
   if (eps_den < 1 || eps_den > 2147483647LL || eps_num < 0 || eps_num > eps_den)
     return fail(CALIBATT_ERR_SHAPE, "eps = %lld/%lld must satisfy 0 <= eps_num <= eps_den, 1 <= eps_den < 2^31",
                 (long long)eps_num, (long long)eps_den);
   return compile_common(mass, P, H, nqb, nkb, nkb_valid, 0, true, eps_num, eps_den, min_agree, row_ptr, col_idx,
-                        nnz_cap, nnz_out, ws, ws_bytes, stream);
+                        nnz_cap, work_order, nnz_out, ws, ws_bytes, stream);
 }
 
 size_t calibatt_share_ws_bytes(int T, int H, int nqb, int nkb) {

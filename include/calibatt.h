@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define CALIBATT_VERSION 302 /* major * 100 + minor */
+#define CALIBATT_VERSION 303 /* major * 100 + minor */
 
 typedef enum {
   CALIBATT_OK = 0,
@@ -224,6 +224,9 @@ size_t calibatt_block_mass_ws_bytes(int B, int H, int L, int block);
  *   min_agree  0 <= min_agree <= P (ceil(rho * P) for agreement rho).
  *   row_ptr    [H*nqb + 1] int32 output (device).
  *   col_idx    [nnz_cap] int32 output (device).
+ *   work_order [H*nqb + 9] int32 output (device), or NULL: the work order
+ *              of the compiled set, as calibatt_build_schedule makes it,
+ *              enqueued on `stream` after the compile; written on OK only.
  *   nnz_out    (host) int64: number of kept blocks, set on OK and on
  *              CALIBATT_ERR_CAPACITY (then col_idx is not written; call
  *              again with a larger buffer).  H*nqb*nkb_valid always suffices.
@@ -234,7 +237,8 @@ size_t calibatt_block_mass_ws_bytes(int B, int H, int L, int block);
 calibatt_status calibatt_compile_masks(const float* mass, int P, int H, int nqb, int nkb,
                                        int nkb_valid, int keep_topk, int min_agree,
                                        int32_t* row_ptr, int32_t* col_idx, int64_t nnz_cap,
-                                       int64_t* nnz_out, void* ws, size_t ws_bytes, void* stream);
+                                       int32_t* work_order, int64_t* nnz_out, void* ws, size_t ws_bytes,
+                                       void* stream);
 
 /*
  * Mask compile with the energy-threshold row rule instead of a fixed count.
@@ -257,8 +261,8 @@ calibatt_status calibatt_compile_masks(const float* mass, int P, int H, int nqb,
 calibatt_status calibatt_compile_masks_energy(const float* mass, int P, int H, int nqb, int nkb,
                                               int nkb_valid, int64_t eps_num, int64_t eps_den,
                                               int min_agree, int32_t* row_ptr, int32_t* col_idx,
-                                              int64_t nnz_cap, int64_t* nnz_out, void* ws,
-                                              size_t ws_bytes, void* stream);
+                                              int64_t nnz_cap, int32_t* work_order, int64_t* nnz_out,
+                                              void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes calibatt_compile_masks(_energy) needs for these sizes (0 on bad sizes). */
 size_t calibatt_compile_ws_bytes(int P, int H, int nqb, int nkb);

@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert cal.calibatt_version() == 302
+    assert cal.calibatt_version() == 303
     for code, name in _lib.STATUS.items():
         assert cal.calibatt_status_string(code) != "unknown status"
     assert cal.calibatt_status_string(99) == "unknown status"
@@ -139,7 +139,7 @@ def test_compile_and_schedule_reject(lib):
     assert ws == 40 * 256 * 256 + 40 * 256 * 4
     assert lib.calibatt_compile_ws_bytes(0, 1, 1, 1) == 0
     base = dict(mass=P16, P=8, H=40, nqb=256, nkb=256, nkb_valid=256, K=64, t=4, row_ptr=P32, col_idx=P48,
-                cap=10, nnz=ctypes.byref(n), ws=P64, ws_bytes=ws, stream=None)
+                cap=10, wo=None, nnz=ctypes.byref(n), ws=P64, ws_bytes=ws, stream=None)
 
     def call(**kw):
         a = dict(base)
@@ -154,8 +154,10 @@ def test_compile_and_schedule_reject(lib):
     assert call(nkb=2048, nkb_valid=2048) == 7
     assert call(ws_bytes=ws - 1) == 6
     assert call(ws=V(72)) == 4
+    assert call(wo=V(66)) == 4                        # work_order must be 4-byte aligned
+    assert call(H=2048, nqb=8, nkb=8, nkb_valid=8, wo=V(80), ws_bytes=1 << 20) == 7   # too many heads to schedule
     ebase = dict(mass=P16, P=8, H=40, nqb=256, nkb=256, nkb_valid=256, num=1, den=20, t=4, row_ptr=P32,
-                 col_idx=P48, cap=10, nnz=ctypes.byref(n), ws=P64, ws_bytes=ws, stream=None)
+                 col_idx=P48, cap=10, wo=None, nnz=ctypes.byref(n), ws=P64, ws_bytes=ws, stream=None)
 
     def ecall(**kw):
         a = dict(ebase)

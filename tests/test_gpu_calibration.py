@@ -142,10 +142,13 @@ def test_compile_bitexact(gpu, case):
     say("case: compile", case)
     rng = np.random.default_rng(case["P"] * 1000 + case["nkb"])
     m = _masses(rng, case["P"], case["H"], case["nqb"], case["nkb"], case["kind"])
-    rp, ci = cal.calibatt_compile_masks(torch.from_numpy(m).cuda(), case["K"], case["t"], case["nv"])
+    wo = torch.full((case["H"] * case["nqb"] + 9,), -7, dtype=torch.int32, device="cuda")
+    rp, ci = cal.calibatt_compile_masks(torch.from_numpy(m).cuda(), case["K"], case["t"], case["nv"], work_order=wo)
     want_rp, want_ci = oracle.compile_masks(m, case["K"], case["t"], case["nv"])
     assert np.array_equal(rp.cpu().numpy(), want_rp)
     assert np.array_equal(ci.cpu().numpy(), want_ci)
+    # the optional work order of the compiled set: the schedule rule's, bit for bit
+    assert np.array_equal(wo.cpu().numpy(), oracle.lpt_work_order(want_rp, case["H"], case["nqb"]))
     say(f"  nnz {len(want_ci)}")
 
 
@@ -167,10 +170,12 @@ def test_compile_energy_bitexact(gpu, case):
     else:
         m = _masses(rng, case["P"], case["H"], case["nqb"], case["nkb"], case["kind"])
     eps = Fraction(case["eps"])
-    rp, ci = cal.calibatt_compile_masks_energy(torch.from_numpy(m).cuda(), eps, case["t"], case["nv"])
+    wo = torch.full((case["H"] * case["nqb"] + 9,), -7, dtype=torch.int32, device="cuda")
+    rp, ci = cal.calibatt_compile_masks_energy(torch.from_numpy(m).cuda(), eps, case["t"], case["nv"], work_order=wo)
     want_rp, want_ci = oracle.compile_masks_energy(m, eps, case["t"], case["nv"])
     assert np.array_equal(rp.cpu().numpy(), want_rp)
     assert np.array_equal(ci.cpu().numpy(), want_ci)
+    assert np.array_equal(wo.cpu().numpy(), oracle.lpt_work_order(want_rp, case["H"], case["nqb"]))
     say(f"  nnz {len(want_ci)}")
 
 
