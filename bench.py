@@ -534,6 +534,20 @@ def main():
 
     # the probe runs in its own process, after the timed work
     peak_probe = None if args.no_peak_probe else mfma_rate()
+    mix = (peak_probe or {}).get("pooling_mix_cycles_per_wave_tile")
+    if mix and "calib" in extra and cfg.block == 128 and cfg.d == 128:
+        # the single pass's bound from the probe: per SIMD, its wave-tiles
+        # (4 waves per 128-query block, one per 128-key tile) at the probe's
+        # cycles per wave-tile for products and vector work together, at
+        # the probe's clock; the pass runs its own clock, so this is a rate
+        # bound in cycles more than in time
+        wave_tiles = cfg.B * cfg.H * cfg.nqb * 4 * cfg.nkb_valid / (4 * peak_probe["cus"])
+        bound_ms = wave_tiles * mix["both"] / (mix["clock_ghz"][2] * 1e9) * 1e3
+        measured = extra["calib"]["block_mass_single_pass_ms_per_prompt"]
+        extra["calib"]["block_mass_single_pass_mix_bound"] = {
+            "bound": "matrix and vector issue on one SIMD (probe)", "wave_tiles_per_simd": round(wave_tiles),
+            "cycles_per_wave_tile": mix["both"], "probe_clock_ghz": mix["clock_ghz"][2],
+            "ms_at_probe_clock": round(bound_ms, 3), "frac": round(bound_ms / measured, 4)}
 
     cpu = cpu_more = None
     if not args.no_cpu:
