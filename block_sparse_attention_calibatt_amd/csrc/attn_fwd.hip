@@ -544,13 +544,23 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
   char* const vst[2] = {reinterpret_cast<char*>(lv0), reinterpret_cast<char*>(lv1)};
   const int gbase = grp * STAGE;   // the group's half of each stage object
 
-  // DMA lane patterns: instruction m of a stage writes LDS units 64m ..
-  // 64m+63; this wave issues m = w, w+4, ...  The K swizzle sees row bits
-  // 0..4 (m mod 4 = w), the natural-V swizzle only the lane.
+  // K stage layout (the group's half of a stage object): wave w's 1/4 holds
+  // the 16-byte key chunks CPW*w .. CPW*w + CPW-1 of all 64 keys (the d
+  // range of its own k-steps KPW*w ..), in NDMA row groups of RPI keys; in a
+  // row group key k's CPW units sit at k*CPW, ordered by chunk XOR kswz(k),
+  // so that 16 lanes reading one chunk of 16 consecutive keys meet 16
+  // distinct bank groups.  Each wave fetches its own quarter, one row group
+  // per DMA instruction, and starts its scores at its own k-steps: at the
+  // end of a vector phase its own DMA has landed, so it can read the next
+  // matrix phase's first operands before the barrier.
+  constexpr int CPW = CH / 4, RPI = 64 / CPW, KPW = CPW / 2;
+  auto kswz = [](int k) { return (k / (16 / CPW)) % CPW; };
+  // DMA lane patterns: a K instruction writes one row group (lane l: key
+  // l / CPW, unit l % CPW); a V instruction m writes LDS units 64m .. 64m+63
+  // (this wave issues m = w, w+4, ...), its swizzle seeing only the lane.
   int kpat, vpat;
   {
-    const int krow = w * (64 / CH) + lane / CH;
-    kpat = (lane / CH) * RB + (((lane % CH) ^ swz<CH>(krow)) * 16);
+    kpat = (lane / CPW) * RB + (((lane % CPW) ^ kswz(lane / CPW)) * 16);
     if (VT) {
       const int vrow = w * 8 + lane / 8;
       vpat = (lane / 8) * L * 2 + (((lane % 8) ^ swz<8>(vrow)) * 16);
@@ -567,9 +577,14 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
   constexpr int NV = VT ? KS : DT;
   int koffs[DS], voffs[NV];
   {
-    const int kx = g ^ swz<CH>(prow);
+    // score slot sl takes k-step (sl + KPW*w) mod DS: chunk 2s + g of key
+    // prow (+ 32 mt, an immediate)
+    const int kr = prow % RPI;
 #pragma unroll
-    for (int s = 0; s < DS; ++s) koffs[s] = gbase + (prow * CH + ((2 * s) ^ kx)) * 16;
+    for (int sl = 0; sl < DS; ++sl) {
+      const int ch = 2 * ((sl + KPW * w) % DS) + g;
+      koffs[sl] = gbase + ((ch / CPW) * NDMA + prow / RPI) * 1024 + (kr * CPW + ((ch % CPW) ^ kswz(kr))) * 16;
+    }
     if (VT) {
       const int vx = g ^ swz<8>(c);
 #pragma unroll
@@ -586,8 +601,8 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
   for (int s = 0; s < DS; ++s) asm volatile("" : "+v"(koffs[s]));
 #pragma unroll
   for (int i = 0; i < NV; ++i) asm volatile("" : "+v"(voffs[i]));
-  auto kread = [&](int st, int mt, int s) __attribute__((always_inline)) -> u32x4 {
-    return *reinterpret_cast<const u32x4*>(kst[st] + koffs[s] + mt * 32 * CH * 16);
+  auto kread = [&](int st, int mt, int sl) __attribute__((always_inline)) -> u32x4 {
+    return *reinterpret_cast<const u32x4*>(kst[st] + koffs[sl] + mt * (32 / RPI) * 1024);
   };
   // A operand of P*V product (t, ks) from V stage st
   auto vop = [&](int st, int t, int ks) __attribute__((always_inline)) -> u32x4 {
@@ -870,8 +885,9 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
     const int qsrc = SPLITQ ? (q < q_valid ? anchor_token(q, grid_rows, grid_cols, k_anchor) : 0) : q;
     const g_bf16* src = (const g_bf16*)ap(0) + ((size_t)b * nheads() + h) * (size_t)L * D + (size_t)qsrc * D + 8 * g;
     const bool live = SPLITQ || q < seq_len;
+    // in this wave's k-step order (slot s holds k-step (s + KPW*w) mod DS)
 #pragma unroll
-    for (int s = 0; s < DS; ++s) qr[s] = live ? *(const g_bf16x8*)(src + 16 * s) : bf16x8{};
+    for (int s = 0; s < DS; ++s) qr[s] = live ? *(const g_bf16x8*)(src + 16 * ((s + KPW * w) % DS)) : bf16x8{};
   };
 
   // the row's Q: raw bf16 from the load until it is scaled in place
@@ -925,11 +941,9 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
         ck_nxt = chunk_load(cbeg, cnb, 1);
       }
 #pragma unroll
-      for (int i = 0; i < NDMA; ++i) {
-        const int m = w + 4 * i;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kst[0] + gbase + m * 1024), 16, kpat,
-                                                 kb0 * BLK * RB + m * 1024, 0, 0);
-      }
+      for (int i = 0; i < NDMA; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kst[0] + gbase + (w * NDMA + i) * 1024), 16, kpat,
+                                                 (kb0 * BLK + i * RPI) * RB + w * CPW * 16, 0, 0);
       q_load(cb, cr, qreg);
       cur = true;
       f_step = 1;
@@ -943,6 +957,21 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
   __syncthreads();
   if (s_fin[0] < 0 && s_fin[1] < 0) return;
   int done = !cur;   // the group has finished (read through readfirstlane: uniform)
+
+  // operand ring of a matrix phase (each slot's pair read PF slots ahead);
+  // its first NPRE slots read this wave's own quarter of the K stage and are
+  // read before the phase, at the end of the vector phase before it (or
+  // here), once the wave's own DMA has landed
+  constexpr int PF = 2, NPRE = PF < KPW ? PF : KPW;
+  u32x4 ra[PF + 1][2];
+  auto pre_read = [&](int st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int sl = 0; sl < NPRE; ++sl) {
+      ra[sl][0] = kread(st, 0, sl);
+      ra[sl][1] = kread(st, 1, sl);
+    }
+  };
+  if (cur) pre_read(0);
 
   // matrix phase of stream cycle x (TM = x % 2 fixes the stages)
   auto mphase = [&](auto tmc) __attribute__((always_inline)) {
@@ -987,14 +1016,15 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
     int wq, wdst;
     asm volatile("s_mov_b32 %0, %1" : "=s"(wq) : "s"(w));
     asm volatile("s_mov_b32 %0, %1" : "=s"(wdst) : "s"(gbase));
+    const int kdst = wdst + wq * NDMA * 1024;
     wdst += wq * 1024;
     auto dma_share = [&](int s) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = s * 2 * NDMA / DS; i < (s + 1) * 2 * NDMA / DS; ++i) {
         const int m = wq + 4 * (i % NDMA);
         if (i < NDMA) {
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rkd, (lds_void*)(kst[TM ^ 1] + wdst + 4096 * i), 16,
-                                                   kpat, kd * RB + m * 1024, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rkd, (lds_void*)(kst[TM ^ 1] + kdst + 1024 * i), 16,
+                                                   kpat, (kd + i * RPI) * RB + wq * CPW * 16, 0, 0);
         } else {
           const int soff = VT ? vd * 2 + m * 16 * L : vd * RB + m * 1024;
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vst[TM] + wdst + 4096 * (i - NDMA)), 16,
@@ -1006,15 +1036,13 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
     // S(x) and P*V(x-1) run as one sequence of slots, each one pair of
     // products and the operand reads of the slot PF ahead
     constexpr int NSL = DS + DT * KS / 2;
-    constexpr int PF = 2;
     auto rd = [&](int sl, int h) __attribute__((always_inline)) -> u32x4 {
       if (sl < DS) return kread(TM, h, sl);
       const int i = 2 * (sl - DS) + h;
       return vop(TM ^ 1, i % DT, i / DT);
     };
-    u32x4 ra[PF + 1][2];
 #pragma unroll
-    for (int sl = 0; sl < PF; ++sl) {
+    for (int sl = NPRE; sl < PF; ++sl) {
       ra[sl][0] = rd(sl, 0);
       ra[sl][1] = rd(sl, 1);
     }
@@ -1210,6 +1238,7 @@ __global__ __launch_bounds__(512) void attn_fwd_pp_kernel(
       }
     }
     wait_vm();
+    if (__builtin_expect(cur, 1)) pre_read(TM ^ 1);
     lds_barrier();
   };
 
