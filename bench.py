@@ -347,15 +347,22 @@ def main():
     if not args.no_sweep and cfg.name == "wan":
         # time vs kept density: the structured Wan masks (band + frame + position
         # + random fill) at several targets, and uniform random masks below
-        # the structured floor
+        # the structured floor.  Every mask is made on the host first, and the
+        # points are timed back to back after the step has run again for a
+        # while: after an idle gap (host work) the clock ramps up anew, and a
+        # short low-density launch would be timed inside that ramp.
         sweep = []
         rng = np.random.default_rng(7)
         cases = [("random", 0.05), ("random", 0.10), ("random", 0.20), ("structured", 0.30),
                  ("structured", 0.50), ("structured", 0.70), ("structured", 0.90)]
+        sbanks = []
         for kind, target in cases:
             m = (synth.random_csr(rng, cfg.H, cfg.nqb, cfg.nkb_valid, target) if kind == "random"
                  else synth.wan_csr(cfg, 0, target=target))
-            sb = cal.MaskBank([m], cfg.H, cfg.nqb, cfg.nkb_valid, dev, validate=False)
+            sbanks.append((kind, cal.MaskBank([m], cfg.H, cfg.nqb, cfg.nkb_valid, dev, validate=False)))
+        for i in range(25):
+            step(i)
+        for kind, sb in sbanks:
             srp, sci, swo, _ = sb.lookup(0)
             for _ in range(2):
                 cal.calibatt_sparse_attn_fwd(Q, K, V, O, srp, sci, cfg.block, cfg.scale, cfg.S, swo, qws)
@@ -369,8 +376,10 @@ def main():
             nnz = int(sb.nnz[0])
             sweep.append({"mask": kind, "density": round(nnz / (cfg.rows * cfg.nkb_valid), 4), "ms": round(t_ms, 4),
                           "tflops": round(tile_flops(cfg.block, cfg.d) * cfg.B * nnz / (t_ms * 1e-3) / 1e12, 1)})
-            del sb
+        del sbanks
         extra["time_vs_density"] = sweep
+        slope, icpt = np.polyfit([p["density"] for p in sweep], [p["ms"] for p in sweep], 1)
+        extra["time_vs_density_fit"] = {"intercept_ms": round(float(icpt), 4), "ms_per_unit_density": round(float(slope), 3)}
 
     if not args.no_dense:
         for _ in range(2):
