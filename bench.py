@@ -264,20 +264,26 @@ def main():
         agree = -(-P * cfg.rho.numerator // cfg.rho.denominator)
         lse = torch.empty(cfg.B * cfg.H * cfg.L, dtype=torch.float32, device=dev)
         masses = torch.empty((P, cfg.H, cfg.nqb, cfg.nkb), dtype=torch.float32, device=dev)
-        pool_ms = 0.0
         mws = torch.empty(cal.calibatt_block_mass_ws_bytes(cfg.B, cfg.H, cfg.L, cfg.block), dtype=torch.uint8,
                           device=dev)
-        for p, seed in enumerate(cfg.prompt_seeds):
+        # every prompt's Q and K go to the GPU first (host generation leaves the
+        # GPU idle, and a pooling timed right after an idle gap runs inside the
+        # clock's ramp); then one untimed pooling, and the prompts back to back
+        prompts = []
+        for seed in cfg.prompt_seeds:
             qp, kp = synth.gen_qk(cfg, seed)
-            Qp, Kp = (torch.from_numpy(x).to(dev).to(torch.bfloat16).contiguous() for x in (qp, kp))
+            prompts.append(tuple(torch.from_numpy(x).to(dev).to(torch.bfloat16).contiguous() for x in (qp, kp)))
             del qp, kp
-            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            c0.record()
+        cal.calibatt_block_mass_single_pass(prompts[0][0], prompts[0][1], cfg.block, cfg.scale, lse, masses[0], cfg.S,
+                                            ws=mws)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for p, (Qp, Kp) in enumerate(prompts):
             cal.calibatt_block_mass_single_pass(Qp, Kp, cfg.block, cfg.scale, lse, masses[p], cfg.S, ws=mws)
-            c1.record()
-            torch.cuda.synchronize()
-            pool_ms += c0.elapsed_time(c1)
-            del Qp, Kp
+        c1.record()
+        torch.cuda.synchronize()
+        pool_ms = c0.elapsed_time(c1)
+        del prompts
         t_c = time.perf_counter()
         crp, cci = cal.calibatt_compile_masks(masses, keep, agree, cfg.nkb_valid)
         compile_ms = (time.perf_counter() - t_c) * 1e3
